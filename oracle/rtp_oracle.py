@@ -1,0 +1,242 @@
+"""CPU oracle for RTPurbo-style sparse attention.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  The HIP library never calls it and
+shares no code with it.
+
+Everything here is plain numpy in float64, one query row at a time, written
+from the method's definitions on the page "Full Attention Strikes Back:
+Transferring Full Attention into Sparse within Hundred Training Steps"
+(paper-graph-ui summary of arXiv 2605.16928), section 3.4:
+
+* "Low-Dimensional Projection Mechanism and Stage-1 Training": pre-RoPE
+  projections q_idx = W^Q q_pre, k_idx = W^K k_pre (r = 16, d_h = 128) and the
+  indexer score s(m, n) = q_idx . k_idx (score-computation equation).  The
+  workloads add the scale 1/sqrt(16); it is applied here as s / 4.
+* "Dynamic Top-p Selection Mechanism" (Eq. 5 and the equation after it):
+  softmax over the indexer scores of all cached keys, descending order, the
+  smallest prefix whose cumulative mass reaches p; then exact softmax
+  attention with post-RoPE q, k over the selected set only.
+* "Local Head Attention Pattern": the first n_sink tokens plus a causal
+  sliding window.
+
+Readings of points the page leaves open (each is also listed in the design doc):
+
+* index precision: q_idx / k_idx are the float64 dot products rounded once,
+  round-to-nearest-even, straight to the stored dtype (float32 or bfloat16);
+* "reaches" means cumulative mass >= p; equal scores are ordered by ascending
+  position; p >= 1 selects every candidate; the set is never empty;
+* candidates are the causal prefix including the query's own position;
+  sinks and window are not added to the retrieval set;
+* the window holds the W positions ending at and including the query
+  (pos - W < n <= pos); sinks n < n_sink are added without double counting.
+
+Pins (tests under ``tests/`` marked ``not gpu``): brute-force minimal subsets,
+dense causal attention from torch's SDPA when p = 1 and W >= L, closed forms
+(v == 1, window 1), exact rational rounding of the projection, the GQA union
+example and the Table 6 sparsity values.  Nothing in this module is "parity
+unpinned".
+"""
+from __future__ import annotations
+
+import dataclasses
+from fractions import Fraction
+from typing import Optional, Sequence
+
+import numpy as np
+
+HEAD_DIM = 128
+IDX_DIM = 16
+IDX_SCALE = 0.25          # 1 / sqrt(16)
+
+
+# ---------------------------------------------------------------- rounding
+def round_bf16(x) -> np.ndarray:
+    """Round float64 values once, to nearest even, onto the bfloat16 grid.
+
+    bfloat16 keeps 8 significant bits and float32's exponent range; the
+    result is returned as float64 holding bfloat16-representable values.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, e = np.frexp(x)                       # x = m * 2**e, 0.5 <= |m| < 1
+    e = np.maximum(e, -125)                  # subnormal range keeps quantum 2**-133
+    quantum = np.ldexp(1.0, e - 8)
+    y = np.rint(x / quantum) * quantum       # x / quantum is exact; rint is half-to-even
+    big = np.ldexp(2.0 - 2.0 ** -7, 127)
+    y = np.where(np.abs(y) > big, np.copysign(np.inf, x), y)
+    return np.where(x == 0, x, y)
+
+
+def round_to(x, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return round_bf16(x)
+    raise ValueError(dtype)
+
+
+def round_fraction_bf16(v: Fraction) -> Fraction:
+    """Exact round-half-even of a rational onto bfloat16 (for pinning ``project``)."""
+    if v == 0:
+        return Fraction(0)
+    sgn = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (max(e, -126) - 7)
+    n = a / quantum
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * quantum
+
+
+# ---------------------------------------------------------------- indexer
+def project(x_pre, w, dtype: str) -> np.ndarray:
+    """Low-dimensional projection W x_pre of pre-RoPE vectors, rounded once to ``dtype``.
+
+    x_pre: [..., 128]; w: [16, 128].  Returns [..., 16] float64 holding
+    ``dtype`` values.
+    """
+    x = np.asarray(x_pre, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    return round_to(x @ w.T, dtype)
+
+
+def indexer_scores(q_idx, k_idx) -> np.ndarray:
+    """s_n = (q_idx . k_idx_n) / sqrt(16) for every key row of k_idx [n, 16]."""
+    return (np.asarray(k_idx, dtype=np.float64) @ np.asarray(q_idx, dtype=np.float64)) * IDX_SCALE
+
+
+@dataclasses.dataclass
+class TopP:
+    selected: np.ndarray     # ascending candidate indices of the active set
+    count: int
+    order: np.ndarray        # candidates by (score desc, index asc)
+    prob: np.ndarray         # softmax mass of each candidate (by index)
+    cum: np.ndarray          # inclusive cumulative mass of each candidate (by index)
+    scores: np.ndarray       # the scores (by index)
+
+
+def top_p(scores, p: float) -> TopP:
+    """Dynamic top-p (Eq. 5): smallest descending-score prefix whose softmax mass reaches p."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.size
+    if n == 0:
+        raise ValueError("no candidates")
+    m = s.max()
+    e = np.exp(s - m)
+    prob = e / e.sum()
+    order = np.lexsort((np.arange(n), -s))
+    cum_sorted = np.cumsum(prob[order])
+    if p >= 1.0:
+        k = n
+    else:
+        k = int(np.searchsorted(cum_sorted, p, side="left")) + 1
+        k = min(max(k, 1), n)
+    cum = np.empty(n)
+    cum[order] = cum_sorted
+    return TopP(selected=np.sort(order[:k]), count=k, order=order, prob=prob, cum=cum, scores=s)
+
+
+def near_threshold(t: TopP, p: float, tol: float = 1e-5) -> np.ndarray:
+    """Mask of candidates whose cumulative mass lies within ``tol`` of the threshold p."""
+    return (t.cum >= p - tol) & (t.cum - t.prob <= p + tol)
+
+
+def set_ok(t: TopP, p: float, got: Sequence[int], tol: float = 1e-5):
+    """Is ``got`` the oracle set up to near-threshold tokens?  Returns (ok, n_differing)."""
+    n = t.scores.size
+    g = np.zeros(n, dtype=bool)
+    got = np.asarray(got, dtype=np.int64)
+    if got.size and (got.min() < 0 or got.max() >= n or np.unique(got).size != got.size):
+        return False, -1
+    g[got] = True
+    s = np.zeros(n, dtype=bool)
+    s[t.selected] = True
+    diff = g ^ s
+    if p >= 1.0:
+        return (not diff.any()), int(diff.sum())
+    ok = bool(np.all(near_threshold(t, p, tol)[diff]))
+    return ok, int(diff.sum())
+
+
+# ---------------------------------------------------------------- attention
+@dataclasses.dataclass
+class Attn:
+    out: np.ndarray          # [128]
+    lse: float               # natural-log sum of exp of the scaled logits over the set
+    weights: np.ndarray      # softmax weights over ``keys``
+    keys: np.ndarray         # key indices attended (ascending)
+
+
+def attend(q, K, V, keys) -> Attn:
+    """Exact softmax attention of one query over the key rows ``keys`` (equation after Eq. 5)."""
+    keys = np.asarray(keys, dtype=np.int64)
+    q = np.asarray(q, dtype=np.float64)
+    Kk = np.asarray(K[keys], dtype=np.float64)
+    Vk = np.asarray(V[keys], dtype=np.float64)
+    a = (Kk @ q) / np.sqrt(HEAD_DIM)
+    m = a.max()
+    e = np.exp(a - m)
+    l = e.sum()
+    w = e / l
+    return Attn(out=w @ Vk, lse=float(m + np.log(l)), weights=w, keys=keys)
+
+
+def local_keys(pos: int, window: int, n_sink: int) -> np.ndarray:
+    """Key positions of a local head: sinks n < n_sink plus pos - window < n <= pos."""
+    lo = max(0, pos - window + 1)
+    win = np.arange(lo, pos + 1)
+    sinks = np.arange(0, min(n_sink, pos + 1))
+    return np.union1d(sinks, win)
+
+
+@dataclasses.dataclass
+class RowResult:
+    attn: Attn
+    topp: Optional[TopP] = None
+    q_idx: Optional[np.ndarray] = None
+
+
+def retrieval_row(q, q_pre, w_q, K, V, k_idx, pos: int, p: float, dtype: str,
+                  keys: Optional[np.ndarray] = None) -> RowResult:
+    """A retrieval head for one query: project, score the causal prefix, top-p, attend.
+
+    ``k_idx`` holds the (already rounded) index keys of positions 0..pos.
+    ``keys`` overrides the attended set (used to re-evaluate the output on a
+    different valid set); the selection is still returned.
+    """
+    q_idx = project(q_pre, w_q, dtype)
+    s = indexer_scores(q_idx, k_idx[: pos + 1])
+    t = top_p(s, p)
+    sel = t.selected if keys is None else np.asarray(keys, dtype=np.int64)
+    return RowResult(attn=attend(q, K, V, sel), topp=t, q_idx=q_idx)
+
+
+def local_row(q, K, V, pos: int, window: int, n_sink: int) -> RowResult:
+    return RowResult(attn=attend(q, K, V, local_keys(pos, window, n_sink)))
+
+
+# ---------------------------------------------------------------- metrics
+def compute_sparsity(attended_per_head: Sequence[float], context_len: int) -> float:
+    """Mean over query heads of 1 - attended / L (Table 6, compute sparsity)."""
+    a = np.asarray(attended_per_head, dtype=np.float64)
+    return float(np.mean(1.0 - a / context_len))
+
+
+def kv_union(sets: Sequence[Sequence[int]]) -> np.ndarray:
+    """Tokens a KV head must keep: the union of its query heads' sets (GQA memory sparsity)."""
+    if not sets:
+        return np.zeros(0, dtype=np.int64)
+    return np.unique(np.concatenate([np.asarray(s, dtype=np.int64) for s in sets]))
+
+
+def memory_sparsity(sets_per_kv_head: Sequence[Sequence[Sequence[int]]], context_len: int) -> float:
+    """Mean over KV heads of 1 - |union of its query heads' sets| / L."""
+    u = [kv_union(g).size for g in sets_per_kv_head]
+    return float(np.mean(1.0 - np.asarray(u, dtype=np.float64) / context_len))

@@ -1,0 +1,363 @@
+"""Pins of the CPU oracle against facts fixed outside it (no GPU).
+
+Each ``check_*`` function compares the oracle with something it does not
+compute itself: brute-force enumeration, an independent library routine
+(torch SDPA, torch's float32->bfloat16 cast), exact rational arithmetic, a
+closed form of the mathematics, or numbers printed on the pages (fixtures
+under tests/golden/).  The ``test_mutation_*`` tests plant plausible mistakes
+in the oracle (on the CPU) and show that a pin fails.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import rtp_oracle as O
+from oracle.problem import Problem
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ rounding
+def check_bf16_matches_torch():
+    rng = np.random.default_rng(1)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-30, 30, 200000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy().astype(np.float64)
+    got = O.round_bf16(x.astype(np.float64))
+    assert np.array_equal(ref, got)
+
+
+def round_fraction(v: Fraction, sig_bits: int) -> Fraction:
+    """Exact round-half-even of a rational to ``sig_bits`` significant bits (normal range)."""
+    if v == 0:
+        return Fraction(0)
+    sgn = -1 if v < 0 else 1
+    a = abs(v)
+    e = 0
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (e - sig_bits + 1)
+    n = a / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * q
+
+
+def check_project_exact(dtype, n=300, seed=2):
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((16, 128)).astype(np.float32).astype(np.float64)
+    x = O.round_to(rng.standard_normal((n, 128)), dtype)
+    got = O.project(x, w, dtype)
+    bits = 8 if dtype == "bf16" else 24
+    for i in range(n):
+        for j in range(16):
+            exact = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x[i], w[j]))
+            assert Fraction(float(got[i, j])) == round_fraction(exact, bits), (i, j)
+
+
+def check_single_rounding():
+    # exact dot = 1 + 2^-8 + 2^-30 sits just above the bf16 midpoint between
+    # 1 and 1 + 2^-7: one rounding gives 1 + 2^-7, rounding through float32
+    # first would land on the midpoint and give 1.
+    w = np.zeros((16, 128))
+    w[0, 0] = 1.0
+    w[1, 1] = 1.0
+    x = np.zeros((1, 128))
+    x[0, 0] = 1.0 + 2.0 ** -8
+    x[0, 1] = 1.0 + 3 * 2.0 ** -8
+    x2 = x.copy()
+    x2[0, 0] = 1.0 + 2.0 ** -8 + 2.0 ** -30
+    assert O.project(x, w, "bf16")[0, 0] == 1.0                   # tie -> even
+    assert O.project(x, w, "bf16")[0, 1] == 1.0 + 2.0 ** -6        # tie -> even (up)
+    assert O.project(x2, w, "bf16")[0, 0] == 1.0 + 2.0 ** -7       # above the tie
+
+
+def test_bf16_matches_torch():
+    check_bf16_matches_torch()
+
+
+def test_project_exact_bf16():
+    check_project_exact("bf16")
+
+
+def test_project_exact_f32():
+    check_project_exact("f32", n=100)
+
+
+def test_project_single_rounding():
+    check_single_rounding()
+
+
+# ------------------------------------------------------------------ top-p
+def brute_force_min_count(prob, p):
+    n = len(prob)
+    for k in range(1, n + 1):
+        for sub in itertools.combinations(range(n), k):
+            if sum(prob[list(sub)]) >= p:
+                return k
+    return n
+
+
+def check_bruteforce(trials=120, seed=3):
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        n = int(rng.integers(1, 11))
+        s = rng.standard_normal(n) * rng.uniform(0.1, 4.0)
+        if t % 5 == 0:
+            s = np.round(s)                    # force ties
+        p = float(rng.choice([0.3, 0.5, 0.8, 0.9, 0.95, 0.99, rng.uniform(0.01, 0.999)]))
+        res = O.top_p(s, p)
+        prob = np.exp(s - s.max())
+        prob /= prob.sum()
+        kmin = brute_force_min_count(prob, p)
+        assert res.count == kmin, (s, p, res.count, kmin)
+        assert prob[res.selected].sum() >= p - 1e-12
+        # the set is a top-|S| prefix: every selected score >= every unselected one,
+        # and among equal scores the earlier positions are the selected ones
+        sel = set(res.selected.tolist())
+        for a in sel:
+            for b in range(n):
+                if b not in sel:
+                    assert s[a] > s[b] or (s[a] == s[b] and a < b)
+
+
+def check_uniform_exact():
+    # four equal scores: masses are exactly 1/4; p = 1/2 is reached by two
+    # tokens (the earliest positions), p just above needs three
+    r = O.top_p(np.zeros(4), 0.5)
+    assert r.count == 2 and r.selected.tolist() == [0, 1]
+    r = O.top_p(np.zeros(4), 0.5 + 1e-12)
+    assert r.count == 3 and r.selected.tolist() == [0, 1, 2]
+
+
+def check_gaussian_closed_form():
+    # q_idx = (4, 0, ..., 0) and k_idx ~ N(0, I_16) give s = q.k / 4 ~ N(0, 1).
+    # Under the tilted measure the mass above tau is Phi_bar(tau - 1), so the
+    # minimal top-p set covers a fraction Phi_bar(1 - Phi^-1(p)) of the keys.
+    from scipy.stats import norm
+    rng = np.random.default_rng(4)
+    n = 400000
+    k_idx = rng.standard_normal((n, 16))
+    q_idx = np.zeros(16)
+    q_idx[0] = 4.0
+    s = O.indexer_scores(q_idx, k_idx)
+    for p in (0.8, 0.9, 0.95):
+        frac = O.top_p(s, p).count / n
+        expect = norm.sf(1.0 - norm.ppf(p))
+        assert abs(frac - expect) < 0.006, (p, frac, expect)
+
+
+def test_topp_bruteforce():
+    check_bruteforce()
+
+
+def test_topp_uniform_exact():
+    check_uniform_exact()
+
+
+def test_topp_gaussian_closed_form():
+    check_gaussian_closed_form()
+
+
+def test_topp_extremes():
+    rng = np.random.default_rng(5)
+    s = rng.standard_normal(50)
+    assert O.top_p(s, 1.0).count == 50
+    r = O.top_p(s, 1e-9)
+    assert r.count == 1 and r.selected[0] == int(np.argmax(s))
+
+
+def test_topp_permutation_equivariant():
+    rng = np.random.default_rng(6)
+    s = rng.standard_normal(300)
+    perm = rng.permutation(300)
+    a = O.top_p(s, 0.9).selected
+    b = O.top_p(s[perm], 0.9).selected
+    assert sorted(perm[b].tolist()) == a.tolist()
+
+
+def test_near_threshold_rule():
+    s = np.zeros(4)
+    r = O.top_p(s, 0.5)
+    # token 2 (cum 0.75, prob 0.25): its cumulative mass minus its own mass is
+    # exactly p, so it is near the threshold; token 3 (cum 1.0) is not.
+    assert O.set_ok(r, 0.5, [0, 1, 2])[0]
+    assert not O.set_ok(r, 0.5, [0, 1, 2, 3])[0]
+    assert O.set_ok(r, 0.5, [0])[0]          # token 1 reaches p exactly: near
+    assert not O.set_ok(r, 0.5, [0, 3])[0]   # token 3 is far from the threshold
+    assert O.set_ok(r, 0.5, [0, 1])[0]
+
+
+# ------------------------------------------------------------------ attention
+def _problem(L, Hq, Hkv, ret, window, n_sink, p, dtype="f32", seed=7, decode=False, B=1):
+    rng = np.random.default_rng(seed)
+    R = len(ret)
+    lk = [L] * B
+    lq = [1] * B if decode else [L] * B
+    Tq, Tk = sum(lq), sum(lk)
+    q = O.round_to(rng.standard_normal((Tq, Hq, 128)), dtype)
+    k = O.round_to(rng.standard_normal((Tk, Hkv, 128)), dtype)
+    v = O.round_to(rng.standard_normal((Tk, Hkv, 128)), dtype)
+    q_pre = O.round_to(rng.standard_normal((Tq, R, 128)), dtype)
+    k_pre = O.round_to(rng.standard_normal((Tk, Hkv, 128)), dtype)
+    w = rng.standard_normal((R, 16, 128)).astype(np.float32).astype(np.float64)
+    return Problem(q=q, k=k, v=v, q_pre=q_pre, k_pre=k_pre, w_q=w, w_k=w,
+                   cu_q=np.cumsum([0] + lq).tolist(), cu_k=np.cumsum([0] + lk).tolist(),
+                   ret_heads=ret, top_p=[p] * B, window=window, n_sink=n_sink, dtype=dtype)
+
+
+def check_dense_equivalence():
+    L, Hq, Hkv = 40, 4, 2
+    pr = _problem(L, Hq, Hkv, ret=[0, 3], window=L, n_sink=4, p=1.0)
+    q = torch.from_numpy(pr.q).permute(1, 0, 2)[None]                 # [1, Hq, L, d]
+    k = torch.from_numpy(pr.k).permute(1, 0, 2)[None].repeat_interleave(Hq // Hkv, dim=1)
+    v = torch.from_numpy(pr.v).permute(1, 0, 2)[None].repeat_interleave(Hq // Hkv, dim=1)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True)[0]
+    for h in range(Hq):
+        for i in range(L):
+            got = pr.row(0, i, h).attn.out
+            assert np.allclose(got, ref[h, i].numpy(), atol=1e-12, rtol=0), (h, i)
+
+
+def check_decode_dense():
+    L, Hq, Hkv = 33, 4, 1
+    pr = _problem(L, Hq, Hkv, ret=[1], window=L, n_sink=0, p=1.0, decode=True, B=2)
+    for b in range(2):
+        k0 = pr.cu_k[b]
+        for h in range(Hq):
+            q = torch.from_numpy(pr.q[b, h])[None, None, None]
+            k = torch.from_numpy(pr.k[k0:k0 + L, 0])[None, None]
+            v = torch.from_numpy(pr.v[k0:k0 + L, 0])[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(q, k, v)[0, 0, 0].numpy()
+            assert np.allclose(pr.row(b, 0, h).attn.out, ref, atol=1e-12, rtol=0)
+
+
+def test_dense_equivalence_prefill():
+    check_dense_equivalence()
+
+
+def test_dense_equivalence_decode():
+    check_decode_dense()
+
+
+def test_weights_and_closed_forms():
+    pr = _problem(64, 2, 1, ret=[0], window=8, n_sink=2, p=0.9)
+    for i in range(64):
+        for h in range(2):
+            r = pr.row(0, i, h)
+            assert abs(r.attn.weights.sum() - 1.0) < 1e-12
+    pr.v[:] = 1.0
+    for i in range(64):
+        assert np.allclose(pr.row(0, i, 0).attn.out, 1.0, atol=1e-14)
+        assert np.allclose(pr.row(0, i, 1).attn.out, 1.0, atol=1e-14)
+    pr2 = _problem(64, 2, 1, ret=[0], window=1, n_sink=0, p=0.9)
+    for i in range(64):
+        assert np.array_equal(pr2.row(0, i, 1).attn.out, pr2.v[i, 0])
+
+
+def test_local_pattern_counts():
+    g = _golden("local_pattern.json")
+    keys = O.local_keys(100000, g["window"], g["n_sink"])
+    assert keys.size == g["max_attended"]
+    for pos in range(0, 40):
+        kk = O.local_keys(pos, 8, 4)
+        assert kk.size <= 12 and kk.max() == pos and np.all(np.diff(kk) > 0)
+        assert set(range(max(0, pos - 7), pos + 1)) <= set(kk.tolist())
+
+
+# ------------------------------------------------------------------ metrics (pages' numbers)
+def test_table6_compute_sparsity():
+    g = _golden("table6_sparsity.json")
+    for c in g["cases"]:
+        att = [c["active_tokens"]] * g["n_retrieval_heads"] + \
+              [g["local_attended"]] * (g["n_q_heads"] - g["n_retrieval_heads"])
+        got = 100.0 * O.compute_sparsity(att, c["context"])
+        assert round(got, 1) == c["compute_sparsity_pct"], (c, got)
+
+
+def test_gqa_union_example():
+    g = _golden("gqa_union.json")
+    assert O.kv_union(g["sets"]).tolist() == g["union"]
+    assert O.memory_sparsity([g["sets"]], 20) == 1.0 - 4 / 20
+
+
+# ------------------------------------------------------------------ generator
+def test_generator_rope_shift_invariance():
+    from synth.gen import rope_inplace
+    rng = np.random.default_rng(8)
+    q = torch.from_numpy(rng.standard_normal((1, 1, 128)))
+    k = torch.from_numpy(rng.standard_normal((1, 1, 128)))
+    def score(m, n):
+        a = rope_inplace(q.clone(), torch.tensor([m]), 1e6)
+        b = rope_inplace(k.clone(), torch.tensor([n]), 1e6)
+        return float((a * b).sum())
+    for (m, n, t) in [(5, 3, 100), (1000, 10, 77777), (0, 0, 5)]:
+        assert abs(score(m, n) - score(m + t, n + t)) < 1e-9
+
+
+def test_generator_projection_orthonormal():
+    from synth.gen import orthonormal_projection
+    w = orthonormal_projection(0).numpy()
+    assert np.allclose(w @ w.T, np.eye(16), atol=1e-12)
+
+
+# ------------------------------------------------------------------ planted mistakes
+def test_mutation_strict_threshold_caught(monkeypatch):
+    real = O.top_p
+
+    def strict(scores, p):
+        r = real(scores, p)
+        s = np.asarray(scores, dtype=np.float64)
+        cs = np.cumsum(r.prob[r.order])
+        k = min(int(np.searchsorted(cs, p, side="right")) + 1, s.size) if p < 1 else s.size
+        return O.TopP(np.sort(r.order[:k]), k, r.order, r.prob, r.cum, s)
+    monkeypatch.setattr(O, "top_p", strict)
+    with pytest.raises(AssertionError):
+        check_uniform_exact()
+
+
+def test_mutation_ascending_order_caught(monkeypatch):
+    real = O.top_p
+    monkeypatch.setattr(O, "top_p", lambda s, p: real(-np.asarray(s), p))
+    with pytest.raises(AssertionError):
+        check_bruteforce(trials=40)
+
+
+def test_mutation_missing_scale_caught(monkeypatch):
+    monkeypatch.setattr(O, "IDX_SCALE", 1.0)
+    with pytest.raises(AssertionError):
+        check_gaussian_closed_form()
+
+
+def test_mutation_double_rounding_caught(monkeypatch):
+    monkeypatch.setattr(O, "round_to", lambda x, dt: O.round_bf16(np.asarray(x).astype(np.float32))
+                        if dt == "bf16" else np.asarray(x, np.float64).astype(np.float32).astype(np.float64))
+    with pytest.raises(AssertionError):
+        check_single_rounding()
+
+
+def test_mutation_window_off_by_one_caught(monkeypatch):
+    real = O.local_keys
+    monkeypatch.setattr(O, "local_keys", lambda pos, w, ns: real(pos, w + 1, ns))
+    with pytest.raises(AssertionError):
+        test_local_pattern_counts()
+
+
+def test_mutation_attention_scale_caught(monkeypatch):
+    monkeypatch.setattr(O, "HEAD_DIM", 64)
+    with pytest.raises(AssertionError):
+        check_dense_equivalence()
