@@ -1,0 +1,217 @@
+// C ABI of the sparse-attention hot path: argument validation (host only, before
+// any launch) and dispatch to the kernel launchers.  See include/rtp.h for the
+// contract of every entry point.
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+
+using rtp::ProbDev;
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+void set_hip_error(hipError_t e) {
+  snprintf(g_err, sizeof(g_err), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return p != nullptr && ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
+
+rtp_status check_problem(const rtp_problem* pr, ProbDev* out) {
+  if (!pr) return RTP_ERR_INVALID_ARG;
+  if (pr->batch < 1) return RTP_ERR_INVALID_ARG;
+  if (pr->n_q_heads < 1 || pr->n_q_heads > RTP_MAX_HEADS) return RTP_ERR_INVALID_ARG;
+  if (pr->n_kv_heads < 1 || pr->n_q_heads % pr->n_kv_heads != 0) return RTP_ERR_INVALID_ARG;
+  if (pr->head_dim != 128 || pr->idx_dim != 16) return RTP_ERR_UNSUPPORTED;
+  if (pr->n_ret < 0 || pr->n_ret > pr->n_q_heads) return RTP_ERR_INVALID_ARG;
+  if (pr->n_ret > 0 && !pr->ret_heads) return RTP_ERR_INVALID_ARG;
+  for (int r = 0; r < pr->n_ret; ++r) {
+    const int h = pr->ret_heads[r];
+    if (h < 0 || h >= pr->n_q_heads) return RTP_ERR_INVALID_ARG;
+    if (r > 0 && h <= pr->ret_heads[r - 1]) return RTP_ERR_INVALID_ARG;  // distinct, ascending
+  }
+  if (pr->n_sink < 0 || pr->window < 1) return RTP_ERR_INVALID_ARG;
+  if (pr->n_sink > 64) return RTP_ERR_UNSUPPORTED;  // sinks must fit the first 64-key tile
+  if (pr->dtype != RTP_F32 && pr->dtype != RTP_BF16) return RTP_ERR_INVALID_ARG;
+  if (!aligned4(pr->cu_seqlens_q) || !aligned4(pr->cu_seqlens_k)) return RTP_ERR_INVALID_ARG;
+  if (pr->max_seqlen_q < 1 || pr->max_seqlen_k < 1) return RTP_ERR_INVALID_ARG;
+  if (pr->max_seqlen_q > pr->max_seqlen_k) return RTP_ERR_INVALID_ARG;
+  if (pr->total_q < 1 || pr->total_k < 1) return RTP_ERR_INVALID_ARG;
+  if (pr->total_q > (int64_t)pr->batch * pr->max_seqlen_q) return RTP_ERR_INVALID_ARG;
+  if (pr->total_k > (int64_t)pr->batch * pr->max_seqlen_k) return RTP_ERR_INVALID_ARG;
+  if (pr->total_q >= INT32_MAX || pr->total_k >= INT32_MAX) return RTP_ERR_UNSUPPORTED;
+  if (out) {
+    ProbDev& p = *out;
+    memset(&p, 0, sizeof(p));
+    p.batch = pr->batch;
+    p.Hq = pr->n_q_heads;
+    p.Hkv = pr->n_kv_heads;
+    p.R = pr->n_ret;
+    p.n_sink = pr->n_sink;
+    p.window = pr->window;
+    p.max_q = pr->max_seqlen_q;
+    p.max_k = pr->max_seqlen_k;
+    p.Tq = pr->total_q;
+    p.Tk = pr->total_k;
+    p.cu_q = pr->cu_seqlens_q;
+    p.cu_k = pr->cu_seqlens_k;
+    bool is_ret[RTP_MAX_HEADS] = {false};
+    for (int r = 0; r < p.R; ++r) {
+      p.ret_heads[r] = pr->ret_heads[r];
+      is_ret[pr->ret_heads[r]] = true;
+    }
+    p.n_local = 0;
+    for (int h = 0; h < p.Hq; ++h)
+      if (!is_ret[h]) p.local_heads[p.n_local++] = h;
+  }
+  return RTP_OK;
+}
+
+rtp_status finish(hipError_t e) {
+  if (e != hipSuccess) {
+    set_hip_error(e);
+    return RTP_ERR_HIP;
+  }
+  return RTP_OK;
+}
+
+size_t ws_need(const ProbDev& p, rtp_call call, rtp_sel_mode mode) {
+  switch (call) {
+    case RTP_CALL_SELECT:
+      return mode == RTP_SEL_LIST ? rtp::ws_select_decode(p) : rtp::ws_select_prefill(p);
+    case RTP_CALL_SPARSE_PREFILL:
+      return 0;
+    case RTP_CALL_SPARSE_DECODE:
+      return rtp::ws_attn_decode(p, p.R);
+    case RTP_CALL_LOCAL:
+      return p.max_q == 1 ? rtp::ws_attn_decode(p, p.n_local) : 0;
+  }
+  return 0;
+}
+
+rtp_status check_ws(const ProbDev& p, rtp_call call, rtp_sel_mode mode, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_need(p, call, mode);
+  if (need == 0) return RTP_OK;
+  if (ws_bytes < need) return RTP_ERR_WORKSPACE_TOO_SMALL;
+  if (!aligned16(ws)) return RTP_ERR_INVALID_ARG;
+  return RTP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rtp_workspace_size(const rtp_problem* prob, rtp_call call, rtp_sel_mode mode) {
+  ProbDev p;
+  if (check_problem(prob, &p) != RTP_OK) return 0;
+  return ws_need(p, call, mode);
+}
+
+rtp_status rtp_index_keys(const rtp_problem* prob, const void* k_pre, const float* w_k, void* k_idx,
+                          void* stream) {
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  if (p.R == 0) return RTP_OK;
+  if (!aligned16(k_pre) || !aligned16(w_k) || !aligned16(k_idx)) return RTP_ERR_INVALID_ARG;
+  return finish(rtp::launch_index_keys(p, prob->dtype == RTP_BF16, k_pre, w_k, k_idx, (hipStream_t)stream));
+}
+
+rtp_status rtp_select_topp(const rtp_problem* prob, const void* q_pre, const float* w_q, const void* k_idx,
+                           const float* top_p, rtp_sel_mode mode, const rtp_selection* sel, void* ws,
+                           size_t ws_bytes, void* stream) {
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  if (mode != RTP_SEL_LIST && mode != RTP_SEL_THRESHOLD) return RTP_ERR_INVALID_ARG;
+  if (p.R == 0) return RTP_OK;
+  if (!sel || !aligned16(q_pre) || !aligned16(w_q) || !aligned16(k_idx) || !aligned4(top_p))
+    return RTP_ERR_INVALID_ARG;
+  if (!aligned16(sel->q_idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
+  if (mode == RTP_SEL_LIST) {
+    if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
+    if (!aligned4(sel->idx)) return RTP_ERR_INVALID_ARG;
+    if ((sel->tau && !aligned4(sel->tau)) || (sel->tie_pos && !aligned4(sel->tie_pos))) return RTP_ERR_INVALID_ARG;
+  } else {
+    if (!aligned4(sel->tau) || !aligned4(sel->tie_pos)) return RTP_ERR_INVALID_ARG;
+  }
+  st = check_ws(p, RTP_CALL_SELECT, mode, ws, ws_bytes);
+  if (st != RTP_OK) return st;
+  const bool bf16 = prob->dtype == RTP_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == RTP_SEL_LIST)
+    return finish(rtp::launch_select_decode(p, bf16, q_pre, w_q, k_idx, top_p, *sel, ws, s));
+  return finish(rtp::launch_select_prefill(p, bf16, q_pre, w_q, k_idx, top_p, *sel, ws, s));
+}
+
+rtp_status rtp_sparse_attn_prefill(const rtp_problem* prob, const void* q, const void* k, const void* v,
+                                   const void* k_idx, const rtp_selection* sel, void* out, float* lse,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  if (p.R == 0) return RTP_OK;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(k_idx) || !aligned16(out))
+    return RTP_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return RTP_ERR_INVALID_ARG;
+  if (!sel || !aligned16(sel->q_idx) || !aligned4(sel->tau) || !aligned4(sel->tie_pos))
+    return RTP_ERR_INVALID_ARG;
+  return finish(rtp::launch_attn_prefill(p, prob->dtype == RTP_BF16, 0, q, k, v, k_idx, sel, out, lse,
+                                         (hipStream_t)stream));
+}
+
+rtp_status rtp_sparse_attn_decode(const rtp_problem* prob, const void* q, const void* k, const void* v,
+                                  const rtp_selection* sel, void* out, float* lse, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
+  if (p.R == 0) return RTP_OK;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RTP_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return RTP_ERR_INVALID_ARG;
+  if (!sel || !aligned4(sel->idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
+  st = check_ws(p, RTP_CALL_SPARSE_DECODE, RTP_SEL_LIST, ws, ws_bytes);
+  if (st != RTP_OK) return st;
+  return finish(rtp::launch_attn_decode(p, prob->dtype == RTP_BF16, 0, q, k, v, sel, out, lse, ws,
+                                        (hipStream_t)stream));
+}
+
+rtp_status rtp_local_attn(const rtp_problem* prob, const void* q, const void* k, const void* v, void* out,
+                          float* lse, void* ws, size_t ws_bytes, void* stream) {
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  if (p.n_local == 0) return RTP_OK;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RTP_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return RTP_ERR_INVALID_ARG;
+  const bool bf16 = prob->dtype == RTP_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.max_q == 1) {
+    if (p.Tq != p.batch) return RTP_ERR_INVALID_ARG;
+    st = check_ws(p, RTP_CALL_LOCAL, RTP_SEL_LIST, ws, ws_bytes);
+    if (st != RTP_OK) return st;
+    return finish(rtp::launch_attn_decode(p, bf16, 1, q, k, v, nullptr, out, lse, ws, s));
+  }
+  return finish(rtp::launch_attn_prefill(p, bf16, 1, q, k, v, nullptr, nullptr, out, lse, s));
+}
+
+const char* rtp_status_str(rtp_status s) {
+  switch (s) {
+    case RTP_OK: return "ok";
+    case RTP_ERR_INVALID_ARG: return "invalid argument";
+    case RTP_ERR_UNSUPPORTED: return "unsupported problem";
+    case RTP_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case RTP_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* rtp_last_hip_error(void) { return g_err; }
+
+}  // extern "C"

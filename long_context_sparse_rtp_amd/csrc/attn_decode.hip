@@ -1,0 +1,230 @@
+// Decode attention: one query per sequence, exact softmax over a key set.
+//
+//   retrieval heads: the LIST set chosen by top-p ("Full Attention Strikes
+//     Back ...", paper-graph-ui summary, section 3.4, the attention equation
+//     that follows Eq. 5: softmax restricted to the selected tokens, post-RoPE
+//     q and k, scale 1/sqrt(d_h));
+//   local heads: sinks n < n_sink plus the window pos - W < n <= pos
+//     (section 3.4 "Local Head Attention Pattern").
+//
+// The pages' decode kernel ("Hardware-Aware Fast Top-p Decoding Kernel",
+// Kernel 2) is bandwidth-bound: single-warp CTAs, registers only, online
+// softmax, split-KV with a final merge.  On gfx950 the same bound holds, so
+// the kernel is organised for HBM streaming instead of matrix cores:
+//   - a workgroup (4 wave64s) owns a split of 512 set entries of one
+//     (head, sequence) row; 16 lanes share a token, each lane holding 8 of the
+//     128 dims, so one K row and one V row are single coalesced 256-byte
+//     (bf16) segments;
+//   - four tokens per 16-lane group are loaded before any arithmetic so that
+//     every lane keeps 128 bytes of K/V in flight;
+//   - each group keeps an online-softmax state (max, sum, 8 accumulators) in
+//     registers; groups merge through LDS, splits merge in a second kernel by
+//     log-sum-exp.
+#include "common.h"
+#include "kernels.h"
+
+namespace rtp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kSplit = 512;
+constexpr int kGroups = kThreads / 16;   // 16-lane groups per workgroup
+constexpr int kUnroll = 4;
+constexpr int kPart = kHeadDim + 2;      // partial record: m, l, o[128]
+
+__host__ __device__ inline int max_splits(const ProbDev& p) { return (p.max_k + kSplit - 1) / kSplit; }
+
+struct RowInfo {
+  int h, b, qrow, k0, L, count, slot;
+};
+
+__device__ __forceinline__ RowInfo row_info(const ProbDev& p, int mode, int row, const rtp_selection* sel) {
+  RowInfo ri;
+  ri.b = row % p.batch;
+  const int hi = row / p.batch;
+  ri.k0 = p.cu_k[ri.b];
+  ri.L = p.cu_k[ri.b + 1] - ri.k0;
+  ri.qrow = p.cu_q[ri.b];
+  if (mode == 0) {
+    ri.slot = hi;
+    ri.h = p.ret_heads[hi];
+    ri.count = sel->count[(size_t)hi * p.Tq + ri.qrow];
+  } else {
+    ri.slot = -1;
+    ri.h = p.local_heads[hi];
+    const int W = min(p.window, ri.L);
+    const int ns = min(p.n_sink, ri.L - W);
+    ri.count = ns + W;
+  }
+  return ri;
+}
+
+// j-th key position of a local head's set: sinks first, then the window.
+__device__ __forceinline__ int local_token(const ProbDev& p, int L, int j) {
+  const int W = min(p.window, L);
+  const int ns = min(p.n_sink, L - W);
+  return (j < ns) ? j : (L - W + (j - ns));
+}
+
+template <typename T> struct RowVec;  // 8 elements of a row
+template <> struct RowVec<bf16_t> {
+  uint4 raw;
+  __device__ __forceinline__ void load(const bf16_t* p) { raw = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float get(int i) const {
+    const uint32_t w = (&raw.x)[i >> 1];
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+  }
+};
+template <> struct RowVec<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ float get(int i) const {
+    return i < 4 ? (&a.x)[i] : (&b.x)[i - 4];
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mode, const T* __restrict__ q,
+                                                               const T* __restrict__ k, const T* __restrict__ v,
+                                                               const rtp_selection sel, float* __restrict__ part) {
+  const int row = blockIdx.y;
+  const RowInfo ri = row_info(p, mode, row, &sel);
+  const int split = blockIdx.x;
+  const int j0 = split * kSplit;
+  if (j0 >= ri.count) return;
+  const int j1 = min(ri.count, j0 + kSplit);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int grp = tid >> 4, gl = tid & 15;
+  const int d0 = gl * 8;
+  const int g = kv_of(p, ri.h);
+  const size_t kstride = (size_t)p.Hkv * kHeadDim;
+  const T* kb = k + ((size_t)ri.k0 * p.Hkv + g) * kHeadDim + d0;
+  const T* vb = v + ((size_t)ri.k0 * p.Hkv + g) * kHeadDim + d0;
+  const int* list = (mode == 0) ? sel.idx + (size_t)ri.slot * p.Tk + ri.k0 : nullptr;
+
+  // query slice, pre-scaled so that exp2 gives the softmax of q.k / sqrt(128)
+  const float qscale = 0.08838834764831845f * kLog2e;
+  float qv[8];
+  {
+    RowVec<T> qq;
+    qq.load(q + ((size_t)ri.qrow * p.Hq + ri.h) * kHeadDim + d0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[i] = qq.get(i) * qscale;
+  }
+
+  float m = -INFINITY, l = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+
+  for (int jb = j0 + grp; jb < j1; jb += kGroups * kUnroll) {
+    RowVec<T> kr[kUnroll], vr[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int j = jb + u * kGroups;
+      ok[u] = j < j1;
+      const int n = ok[u] ? ((mode == 0) ? list[j] : local_token(p, ri.L, j)) : 0;
+      kr[u].load(kb + (size_t)n * kstride);
+      vr[u].load(vb + (size_t)n * kstride);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float a = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fmaf(qv[i], kr[u].get(i), a);
+      a += __shfl_xor(a, 1);
+      a += __shfl_xor(a, 2);
+      a += __shfl_xor(a, 4);
+      a += __shfl_xor(a, 8);
+      if (ok[u]) {
+        const float mn = fmaxf(m, a);
+        const float sc = __builtin_amdgcn_exp2f(m - mn);
+        const float pe = __builtin_amdgcn_exp2f(a - mn);
+        l = l * sc + pe;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = fmaf(pe, vr[u].get(i), o[i] * sc);
+        m = mn;
+      }
+    }
+  }
+
+  // merge the 16 groups of the workgroup
+  __shared__ float gm_s[kGroups], gl_s[kGroups];
+  __shared__ float go_s[kGroups][kHeadDim];
+  if (gl == 0) { gm_s[grp] = m; gl_s[grp] = l; }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) go_s[grp][d0 + i] = o[i];
+  __syncthreads();
+  float* rec = part + ((size_t)row * max_splits(p) + split) * kPart;
+  if (tid < kHeadDim) {
+    float M = -INFINITY;
+    for (int gi = 0; gi < kGroups; ++gi) M = fmaxf(M, gm_s[gi]);
+    float acc = 0.f, sum = 0.f;
+    for (int gi = 0; gi < kGroups; ++gi) {
+      if (gl_s[gi] > 0.f) {
+        const float w = __builtin_amdgcn_exp2f(gm_s[gi] - M);
+        acc = fmaf(go_s[gi][tid], w, acc);
+        sum = fmaf(gl_s[gi], w, sum);
+      }
+    }
+    rec[2 + tid] = acc;
+    if (tid == 0) { rec[0] = M; rec[1] = sum; }
+  }
+  (void)lane;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int mode, const rtp_selection sel,
+                                                                const float* __restrict__ part,
+                                                                T* __restrict__ out, float* __restrict__ lse) {
+  const int row = blockIdx.x;
+  const RowInfo ri = row_info(p, mode, row, &sel);
+  const int ns = (ri.count + kSplit - 1) / kSplit;
+  const float* rec = part + (size_t)row * max_splits(p) * kPart;
+  float M = -INFINITY;
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[(size_t)s * kPart]);
+  float acc = 0.f, sum = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float w = __builtin_amdgcn_exp2f(rec[(size_t)s * kPart] - M);
+    acc = fmaf(rec[(size_t)s * kPart + 2 + threadIdx.x], w, acc);
+    sum = fmaf(rec[(size_t)s * kPart + 1], w, sum);
+  }
+  out[((size_t)ri.qrow * p.Hq + ri.h) * kHeadDim + threadIdx.x] = Elem<T>::from_f(acc / sum);
+  if (lse && threadIdx.x == 0) lse[(size_t)ri.h * p.Tq + ri.qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
+}
+
+}  // namespace
+
+size_t ws_attn_decode(const ProbDev& p, int nheads) {
+  return sizeof(float) * (size_t)nheads * p.batch * max_splits(p) * kPart;
+}
+
+hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
+                              const void* v, const rtp_selection* sel, void* out, float* lse, void* ws,
+                              hipStream_t s) {
+  const int nheads = (mode == 0) ? p.R : p.n_local;
+  if (nheads == 0) return hipSuccess;
+  const int rows = nheads * p.batch;
+  rtp_selection sl = {};
+  if (sel) sl = *sel;
+  dim3 grid(max_splits(p), rows);
+  float* part = (float*)ws;
+  if (bf16) {
+    hipLaunchKernelGGL(attn_decode_kernel<bf16_t>, grid, dim3(kThreads), 0, s, p, mode, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, sl, part);
+    hipLaunchKernelGGL(attn_decode_combine<bf16_t>, dim3(rows), dim3(kHeadDim), 0, s, p, mode, sl, part,
+                       (bf16_t*)out, lse);
+  } else {
+    hipLaunchKernelGGL(attn_decode_kernel<float>, grid, dim3(kThreads), 0, s, p, mode, (const float*)q,
+                       (const float*)k, (const float*)v, sl, part);
+    hipLaunchKernelGGL(attn_decode_combine<float>, dim3(rows), dim3(kHeadDim), 0, s, p, mode, sl, part,
+                       (float*)out, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rtp

@@ -1,0 +1,386 @@
+// Prefill attention on matrix cores, for both head kinds.
+//
+//   MODE 0, retrieval heads: key n is attended by query i iff it is causal and
+//     in the top-p set of the row, S = {s_n > tau_i} U {s_n == tau_i, n <= tie_i}
+//     ("Full Attention Strikes Back ...", paper-graph-ui summary, section 3.4,
+//     Eq. 5 and the attention equation after it).  s_n is recomputed here
+//     with the same MFMA indexer tile the selection used, so membership is
+//     bit-identical to the selection.
+//   MODE 1, local heads: keys n <= pos with pos - n < W, plus sinks n < n_sink
+//     (section 3.4 "Local Head Attention Pattern").
+//
+// The pages give few details of their prefill kernel (retrieval heads run
+// dense there); this one is a flash-attention style loop written for gfx950:
+//   - workgroup = 4 wave64s, 128 query rows (32 per wave as two 16-column
+//     MFMA tiles), 64-key tiles;
+//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (f32 path: 16x16x4 steps), K
+//     tile staged row-major in LDS; the S^T output layout (a lane holds 4 keys
+//     of one query column) is already the B-operand layout of O^T = V^T P^T,
+//     so P goes from registers into the second product without a shuffle;
+//     V is staged transposed in LDS (rows = head dims) for the A operand;
+//   - online softmax in the log2 domain, row sums kept per lane and reduced
+//     once at the end; masked tiles of a wave skip both products.
+// LDS strides are padded so the fragment reads of one 8- or 16-lane phase hit
+// distinct banks.
+#include "common.h"
+#include "kernels.h"
+
+namespace rtp {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int BQ = 128;
+constexpr int KT = 64;
+
+template <typename T> struct Lds;
+template <> struct Lds<bf16_t> { static constexpr int kStr = 128 + 8; static constexpr int vStr = 64 + 4; };
+template <> struct Lds<float> { static constexpr int kStr = 128 + 4; static constexpr int vStr = 64 + 4; };
+
+// ---- B operand of O^T += V^T P^T from the four P values of two key subtiles
+__device__ __forceinline__ void make_pfrag(FragBF16& f, const float* a, const float* b) {
+  uint4 u;
+  u.x = pack_bf16x2(a[0], a[1]);
+  u.y = pack_bf16x2(a[2], a[3]);
+  u.z = pack_bf16x2(b[0], b[1]);
+  u.w = pack_bf16x2(b[2], b[3]);
+  f.v = __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void make_pfrag(FragF32& f, const float* a, const float* b) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { f.v[i] = a[i]; f.v[4 + i] = b[i]; }
+}
+
+// ---- A operand of O^T += V^T P^T: row d of V^T, keys (4g..4g+3) and (16+4g..16+4g+3)
+__device__ __forceinline__ void load_vfrag(FragBF16& f, const bf16_t* rowp) {
+  uint2 a = *reinterpret_cast<const uint2*>(rowp);
+  uint2 b = *reinterpret_cast<const uint2*>(rowp + 16);
+  uint4 u = {a.x, a.y, b.x, b.y};
+  f.v = __builtin_bit_cast(bf16x8, u);
+}
+__device__ __forceinline__ void load_vfrag(FragF32& f, const float* rowp) {
+  float4 a = *reinterpret_cast<const float4*>(rowp);
+  float4 b = *reinterpret_cast<const float4*>(rowp + 16);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// ---- stage one 64-key tile: K row-major, V transposed
+__device__ __forceinline__ void stage_tile(bf16_t* k_s, bf16_t* vt_s, const bf16_t* kg, const bf16_t* vg,
+                                           size_t rstride, int nvalid, int tid) {
+  constexpr int KS = Lds<bf16_t>::kStr, VS = Lds<bf16_t>::vStr;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = u * kThreads + tid;
+    const int key = e >> 4, ch = e & 15;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (key < nvalid) val = *reinterpret_cast<const uint4*>(kg + (size_t)key * rstride + ch * 8);
+    *reinterpret_cast<uint4*>(k_s + key * KS + ch * 8) = val;
+  }
+  const int kgp = tid & 15, dc = tid >> 4;
+  uint4 r[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int key = 4 * kgp + u;
+    r[u] = {0u, 0u, 0u, 0u};
+    if (key < nvalid) r[u] = *reinterpret_cast<const uint4*>(vg + (size_t)key * rstride + dc * 8);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t w0 = (&r[0].x)[e >> 1], w1 = (&r[1].x)[e >> 1];
+    const uint32_t w2 = (&r[2].x)[e >> 1], w3 = (&r[3].x)[e >> 1];
+    uint2 out;
+    if (e & 1) {
+      out.x = (w0 >> 16) | (w1 & 0xFFFF0000u);
+      out.y = (w2 >> 16) | (w3 & 0xFFFF0000u);
+    } else {
+      out.x = (w0 & 0xFFFFu) | (w1 << 16);
+      out.y = (w2 & 0xFFFFu) | (w3 << 16);
+    }
+    *reinterpret_cast<uint2*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = out;
+  }
+}
+__device__ __forceinline__ void stage_tile(float* k_s, float* vt_s, const float* kg, const float* vg,
+                                           size_t rstride, int nvalid, int tid) {
+  constexpr int KS = Lds<float>::kStr, VS = Lds<float>::vStr;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int e = u * kThreads + tid;
+    const int key = e >> 5, ch = e & 31;
+    float4 val = {0.f, 0.f, 0.f, 0.f};
+    if (key < nvalid) val = *reinterpret_cast<const float4*>(kg + (size_t)key * rstride + ch * 4);
+    *reinterpret_cast<float4*>(k_s + key * KS + ch * 4) = val;
+  }
+  const int kgp = tid & 15, dc = tid >> 4;
+  float r[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int key = 4 * kgp + u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[u][i] = 0.f;
+    if (key < nvalid) {
+      float4 a = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8);
+      float4 b = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8 + 4);
+      r[u][0] = a.x; r[u][1] = a.y; r[u][2] = a.z; r[u][3] = a.w;
+      r[u][4] = b.x; r[u][5] = b.y; r[u][6] = b.z; r[u][7] = b.w;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float4 o = {r[0][e], r[1][e], r[2][e], r[3][e]};
+    *reinterpret_cast<float4*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = o;
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void store_out4(T* dst, const float* v);
+template <>
+__device__ __forceinline__ void store_out4<bf16_t>(bf16_t* dst, const float* v) {
+  uint2 u;
+  u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = u;
+}
+template <>
+__device__ __forceinline__ void store_out4<float>(float* dst, const float* v) {
+  *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
+    ProbDev p, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const T* __restrict__ k_idx, const rtp_selection sel, T* __restrict__ out, float* __restrict__ lse) {
+  typedef typename Frag32<T>::type F;
+  typedef typename IdxFrag<T>::type IF;
+  constexpr int KS = Lds<T>::kStr, VS = Lds<T>::vStr;
+  __shared__ __attribute__((aligned(16))) T k_s[KT * KS];
+  __shared__ __attribute__((aligned(16))) T vt_s[kHeadDim * VS];
+
+  const int tiles_per_b = (p.max_q + BQ - 1) / BQ;
+  const int b = blockIdx.x / tiles_per_b;
+  const int qt = tiles_per_b - 1 - (int)(blockIdx.x % tiles_per_b);  // longest tiles first
+  const int hidx = blockIdx.y;
+  const int h = (MODE == 0) ? p.ret_heads[hidx] : p.local_heads[hidx];
+  const int g = kv_of(p, h);
+  const int q0 = p.cu_q[b], Lq = p.cu_q[b + 1] - q0;
+  const int k0 = p.cu_k[b], Lk = p.cu_k[b + 1] - k0;
+  const int i0 = qt * BQ;
+  if (i0 >= Lq) return;
+  const int off = Lk - Lq;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const size_t rstride = (size_t)p.Hkv * kHeadDim;
+  const T* kg = k + ((size_t)k0 * p.Hkv + g) * kHeadDim;
+  const T* vg = v + ((size_t)k0 * p.Hkv + g) * kHeadDim;
+
+  // ---- this wave's query rows: i0 + 32w + 16c + col
+  F qf[2][4];
+  int qi[2], qpos[2];
+  bool qok[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    qi[c] = i0 + 32 * w + 16 * c + col;
+    qok[c] = qi[c] < Lq;
+    qpos[c] = off + (qok[c] ? qi[c] : (Lq - 1));
+    const T* qp = q + ((size_t)(q0 + (qok[c] ? qi[c] : Lq - 1)) * p.Hq + h) * kHeadDim + 8 * grp;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) load_frag(qf[c][kc], qp + 32 * kc);
+  }
+  IF qxf[2];
+  float tau[2] = {0.f, 0.f};
+  int tie[2] = {0, 0};
+  const T* kxb = nullptr;
+  if (MODE == 0) {
+    const int r = hidx;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const size_t qr = (size_t)r * p.Tq + q0 + (qok[c] ? qi[c] : Lq - 1);
+      load_idx_frag(qxf[c], (const T*)sel.q_idx + qr * kIdxDim + 4 * grp);
+      tau[c] = sel.tau[qr];
+      tie[c] = sel.tie_pos[qr];
+    }
+    kxb = k_idx + ((size_t)r * p.Tk + k0) * kIdxDim;
+  }
+
+  const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
+  float m_[2] = {-INFINITY, -INFINITY}, l_[2] = {0.f, 0.f};
+  f32x4 oacc[2][8];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) oacc[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // ---- key tiles
+  const int pos_lo = off + i0;
+  const int pos_hi = off + min(i0 + BQ, Lq) - 1;
+  const int kt_last = pos_hi / KT;
+  int kt_first = 0;
+  bool sink_tile = false;
+  if (MODE == 1) {
+    kt_first = max(0, pos_lo - p.window + 1) / KT;
+    sink_tile = (p.n_sink > 0) && (kt_first > 0);
+  }
+  const int ntiles = kt_last - kt_first + 1 + (sink_tile ? 1 : 0);
+
+  for (int t = 0; t < ntiles; ++t) {
+    const bool sink_only = sink_tile && (t == 0);
+    const int kt = sink_only ? 0 : (kt_first + t - (sink_tile ? 1 : 0));
+    const int kbase = kt * KT;
+    __syncthreads();
+    stage_tile(k_s, vt_s, kg + (size_t)kbase * rstride, vg + (size_t)kbase * rstride, rstride,
+               min(KT, Lk - kbase), tid);
+    __syncthreads();
+
+    // membership of every (key, query) this lane holds
+    bool mem[2][4][4];
+    bool any = false;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      IF kxf;
+      if (MODE == 0) {
+        const int key = kbase + 16 * ks + col;
+        if (key < Lk) {
+          load_idx_frag(kxf, kxb + (size_t)key * kIdxDim + 4 * grp);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kxf.v[j] = 0;
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f32x4 sx;
+        if (MODE == 0) sx = idx_dot_tile(kxf, qxf[c]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kbase + 16 * ks + 4 * grp + i;
+          bool ok = qok[c] && key <= qpos[c];
+          if (MODE == 0) {
+            const float s = idx_score(sx[i]);
+            ok = ok && (s > tau[c] || (s == tau[c] && key <= tie[c]));
+          } else {
+            const bool in_win = (qpos[c] - key) < p.window;
+            const bool is_sink = key < p.n_sink;
+            ok = ok && (sink_only ? is_sink : (in_win || is_sink));
+          }
+          mem[c][ks][i] = ok;
+          any |= ok;
+        }
+      }
+    }
+    if (!__builtin_amdgcn_ballot_w64(any)) continue;
+
+    // S^T = K Q^T
+    f32x4 sacc[2][4];
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sacc[c][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        F kf;
+        load_frag(kf, k_s + (16 * ks + col) * KS + 32 * kc + 8 * grp);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) sacc[c][ks] = mma_k32(kf, qf[c][kc], sacc[c][ks]);
+      }
+    }
+
+    // online softmax (log2 domain)
+    F pf[2][2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float x[4][4];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[ks][i] = mem[c][ks][i] ? sacc[c][ks][i] * sl2 : -INFINITY;
+          tmax = fmaxf(tmax, x[ks][i]);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(m_[c], tmax);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = __builtin_amdgcn_exp2f(m_[c] - muse);
+      l_[c] *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) oacc[c][dt] *= alpha;
+      float ps = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[ks][i] = __builtin_amdgcn_exp2f(x[ks][i] - muse);
+          ps += x[ks][i];
+        }
+      l_[c] += ps;
+      m_[c] = mnew;
+      make_pfrag(pf[c][0], x[0], x[1]);
+      make_pfrag(pf[c][1], x[2], x[3]);
+    }
+
+    // O^T += V^T P^T
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        F vf;
+        load_vfrag(vf, vt_s + (16 * dt + col) * VS + 32 * kk + 4 * grp);
+#pragma unroll
+        for (int c = 0; c < 2; ++c) oacc[c][dt] = mma_k32(vf, pf[c][kk], oacc[c][dt]);
+      }
+    }
+  }
+
+  // ---- normalise and store
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float lt = l_[c];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    if (!qok[c]) continue;
+    const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
+    T* op = out + ((size_t)(q0 + qi[c]) * p.Hq + h) * kHeadDim;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      float vv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vv[i] = oacc[c][dt][i] * inv;
+      store_out4<T>(op + 16 * dt + 4 * grp, vv);
+    }
+    if (lse && grp == 0) lse[(size_t)h * p.Tq + q0 + qi[c]] = (m_[c] + __log2f(lt)) * 0.6931471805599453f;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
+                               const void* v, const void* k_idx, const rtp_selection* sel, void* out,
+                               float* lse, hipStream_t s) {
+  const int nheads = (mode == 0) ? p.R : p.n_local;
+  if (nheads == 0 || p.Tq == 0) return hipSuccess;
+  const int tiles_per_b = (p.max_q + BQ - 1) / BQ;
+  dim3 grid(tiles_per_b * p.batch, nheads);
+  rtp_selection sl = {};
+  if (sel) sl = *sel;
+  if (bf16) {
+    if (mode == 0)
+      hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 0>), grid, dim3(kThreads), 0, s, p, (const bf16_t*)q,
+                         (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)k_idx, sl, (bf16_t*)out, lse);
+    else
+      hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 1>), grid, dim3(kThreads), 0, s, p, (const bf16_t*)q,
+                         (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)k_idx, sl, (bf16_t*)out, lse);
+  } else {
+    if (mode == 0)
+      hipLaunchKernelGGL((attn_prefill_kernel<float, 0>), grid, dim3(kThreads), 0, s, p, (const float*)q,
+                         (const float*)k, (const float*)v, (const float*)k_idx, sl, (float*)out, lse);
+    else
+      hipLaunchKernelGGL((attn_prefill_kernel<float, 1>), grid, dim3(kThreads), 0, s, p, (const float*)q,
+                         (const float*)k, (const float*)v, (const float*)k_idx, sl, (float*)out, lse);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace rtp

@@ -1,0 +1,145 @@
+// Shared device helpers for the gfx950 kernels: element types, conversions,
+// MFMA tile wrappers and wave-level reductions.  Nothing here is specific to
+// one kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtp {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeadDim = 128;
+constexpr int kIdxDim = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf16_to_f32(bf16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Round-to-nearest-even float -> bfloat16 (finite inputs).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// Two floats -> two packed bfloat16 (hardware round-to-nearest-even on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  f32x2 v = {a, b};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Correctly rounded float64 -> bfloat16: keep 8 significant bits with
+// round-half-even applied directly to the double's 52-bit fraction (one
+// rounding); the bfloat16 subnormal range uses the fixed quantum 2^-133.
+__device__ __forceinline__ bf16_t f64_to_bf16_rne(double x) {
+  double ax = fabs(x);
+  if (ax < 1.1754943508222875e-38) {  // below 2^-126: fixed quantum 2^-133
+    double q = ldexp(rint(ldexp(x, 133)), -133);
+    return (bf16_t)(__float_as_uint((float)q) >> 16);
+  }
+  uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint64_t drop = (1ull << 45) - 1ull;  // 52 - 7 fraction bits dropped
+  u += drop + ((u >> 45) & 1ull);
+  u &= ~drop;
+  float f = (float)__longlong_as_double((long long)u);  // exact, or +-inf on overflow
+  return (bf16_t)(__float_as_uint(f) >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static __device__ __forceinline__ float to_f(float x) { return x; }
+  static __device__ __forceinline__ float from_f(float x) { return x; }
+  static __device__ __forceinline__ float from_d(double x) { return (float)x; }  // RNE
+};
+template <> struct Elem<bf16_t> {
+  static __device__ __forceinline__ float to_f(bf16_t x) { return bf16_to_f32(x); }
+  static __device__ __forceinline__ bf16_t from_f(float x) { return f32_to_bf16(x); }
+  static __device__ __forceinline__ bf16_t from_d(double x) { return f64_to_bf16_rne(x); }
+};
+
+// ------------------------------------------------------------ MFMA fragments
+// 16x16 tiles, wave64.  Operand fragment for "k-chunk of 32": lane l holds row
+// (or column) l%16 and the 8 k-values 8*(l/16) .. 8*(l/16)+7.  The output
+// fragment holds rows 4*(l/16)+i (i = 0..3) of column l%16.
+struct FragBF16 { bf16x8 v; };
+struct FragF32 { float v[8]; };
+
+template <typename T> struct Frag32;
+template <> struct Frag32<bf16_t> { typedef FragBF16 type; };
+template <> struct Frag32<float> { typedef FragF32 type; };
+
+__device__ __forceinline__ f32x4 mma_k32(const FragBF16& a, const FragBF16& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, c, 0, 0, 0);
+}
+// Float32 operands: eight 16x16x4 steps, step j taking slot j of every lane.
+__device__ __forceinline__ f32x4 mma_k32(const FragF32& a, const FragF32& b, f32x4 c) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+  return c;
+}
+
+// Load 8 consecutive elements as an operand fragment.
+__device__ __forceinline__ void load_frag(FragBF16& f, const bf16_t* p) {
+  f.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+__device__ __forceinline__ void load_frag(FragF32& f, const float* p) {
+  float4 a = reinterpret_cast<const float4*>(p)[0];
+  float4 b = reinterpret_cast<const float4*>(p)[1];
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+  f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
+}
+
+// Indexer operand: 16-dim vectors, lane l holds row l%16 dims 4*(l/16)..+3.
+struct IdxFragBF16 { short4v v; };
+struct IdxFragF32 { float v[4]; };
+template <typename T> struct IdxFrag;
+template <> struct IdxFrag<bf16_t> { typedef IdxFragBF16 type; };
+template <> struct IdxFrag<float> { typedef IdxFragF32 type; };
+
+__device__ __forceinline__ void load_idx_frag(IdxFragBF16& f, const bf16_t* p) {
+  f.v = __builtin_bit_cast(short4v, *reinterpret_cast<const uint2*>(p));
+}
+__device__ __forceinline__ void load_idx_frag(IdxFragF32& f, const float* p) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+}
+
+// Raw indexer dot products q_idx . k_idx for a 16 (keys) x 16 (queries) tile:
+// A = index keys, B = index queries.  Every kernel that needs an indexer score
+// goes through this one function, so a given (key, query) pair always gets the
+// same float32 value.
+__device__ __forceinline__ f32x4 idx_dot_tile(const IdxFragBF16& kf, const IdxFragBF16& qf) {
+  f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(kf.v, qf.v, z, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 idx_dot_tile(const IdxFragF32& kf, const IdxFragF32& qf) {
+  f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(kf.v[j], qf.v[j], c, 0, 0, 0);
+  return c;
+}
+
+// The indexer score s = (q_idx . k_idx) / sqrt(16); the scale is exact.
+__device__ __forceinline__ float idx_score(float dot) { return dot * 0.25f; }
+
+// ------------------------------------------------------------ reductions
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+}  // namespace rtp

@@ -1,0 +1,46 @@
+// Internal interface between the C ABI layer (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/rtp.h"
+
+namespace rtp {
+
+// Problem description passed by value to every kernel.
+struct ProbDev {
+  int batch, Hq, Hkv, R, n_sink, window, n_local;
+  int max_q, max_k;
+  int64_t Tq, Tk;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int ret_heads[RTP_MAX_HEADS];    // slot -> query head
+  int local_heads[RTP_MAX_HEADS];  // local index -> query head
+};
+
+__host__ __device__ inline int kv_of(const ProbDev& p, int h) { return (h * p.Hkv) / p.Hq; }
+
+// Workspace layouts (bytes), shared by rtp_workspace_size and the launchers.
+size_t ws_select_decode(const ProbDev& p);
+size_t ws_select_prefill(const ProbDev& p);
+size_t ws_attn_decode(const ProbDev& p, int nheads);
+
+hipError_t launch_index_keys(const ProbDev& p, bool bf16, const void* k_pre, const float* w_k,
+                             void* k_idx, hipStream_t s);
+hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
+                                const void* k_idx, const float* top_p, const rtp_selection& sel,
+                                void* ws, hipStream_t s);
+hipError_t launch_select_prefill(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
+                                 const void* k_idx, const float* top_p, const rtp_selection& sel,
+                                 void* ws, hipStream_t s);
+// mode 0: retrieval heads over sel LIST; mode 1: local heads over window + sinks
+hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
+                              const void* v, const rtp_selection* sel, void* out, float* lse,
+                              void* ws, hipStream_t s);
+// mode 0: retrieval heads with THRESHOLD membership; mode 1: local heads
+hipError_t launch_attn_prefill(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
+                               const void* v, const void* k_idx, const rtp_selection* sel,
+                               void* out, float* lse, hipStream_t s);
+
+}  // namespace rtp

@@ -5,26 +5,36 @@ uses: q / out [T_q, Hq, 128], k / v / k_pre [T_k, Hkv, 128], q_pre
 [T_q, R, 128], cumulative sequence offsets, and query i of sequence b at
 position L_k(b) - L_q(b) + i.  GQA groups are contiguous:
 kv(h) = floor(h * Hkv / Hq).
+
+Tensors may be numpy arrays or CPU torch tensors of any float dtype; slices
+are converted to float64 on first use and cached per (sequence, KV head).
 """
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, List, Optional, Sequence, Tuple
+from typing import Any, Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
 from . import rtp_oracle as O
 
 
+def _f64(x) -> np.ndarray:
+    if isinstance(x, np.ndarray):
+        return x.astype(np.float64, copy=False)
+    import torch  # tensors handed over by the tests
+    return x.detach().to(torch.float64).cpu().numpy()
+
+
 @dataclasses.dataclass
 class Problem:
-    q: np.ndarray            # [T_q, Hq, 128] float64 (stored values)
-    k: np.ndarray            # [T_k, Hkv, 128]
-    v: np.ndarray
-    q_pre: np.ndarray        # [T_q, R, 128]
-    k_pre: np.ndarray        # [T_k, Hkv, 128]
-    w_q: np.ndarray          # [R, 16, 128]
-    w_k: np.ndarray          # [R, 16, 128]
+    q: Any                   # [T_q, Hq, 128]
+    k: Any                   # [T_k, Hkv, 128]
+    v: Any
+    q_pre: Any               # [T_q, R, 128]
+    k_pre: Any               # [T_k, Hkv, 128]
+    w_q: Any                 # [R, 16, 128]
+    w_k: Any                 # [R, 16, 128]
     cu_q: Sequence[int]
     cu_k: Sequence[int]
     ret_heads: Sequence[int]
@@ -32,8 +42,8 @@ class Problem:
     window: int
     n_sink: int
     dtype: str               # "f32" | "bf16"
-    k_idx: Optional[np.ndarray] = None   # [R, T_k, 16] stored index keys (decode inputs)
-    _kidx_cache: Dict[Tuple[int, int], np.ndarray] = dataclasses.field(default_factory=dict)
+    k_idx: Any = None        # [R, T_k, 16] stored index keys (decode inputs), optional
+    _cache: Dict[Tuple, np.ndarray] = dataclasses.field(default_factory=dict)
 
     @property
     def n_q_heads(self) -> int:
@@ -58,51 +68,56 @@ class Problem:
         lk = int(self.cu_k[b + 1]) - int(self.cu_k[b])
         return lk - lq + i
 
+    def _kv(self, name: str, b: int, g: int) -> np.ndarray:
+        key = (name, b, g)
+        if key not in self._cache:
+            k0, k1 = self.seq_range_k(b)
+            self._cache[key] = _f64(getattr(self, name)[k0:k1, g])
+        return self._cache[key]
+
+    def w(self, which: str, r: int) -> np.ndarray:
+        key = (which, r)
+        if key not in self._cache:
+            self._cache[key] = _f64(getattr(self, which)[r])
+        return self._cache[key]
+
     def index_keys(self, b: int, r: int) -> np.ndarray:
         """k_idx rows of sequence b for retrieval slot r ([L_b, 16])."""
-        key = (b, r)
-        if key not in self._kidx_cache:
+        key = ("kidx", b, r)
+        if key not in self._cache:
             k0, k1 = self.seq_range_k(b)
             if self.k_idx is not None:
-                self._kidx_cache[key] = np.asarray(self.k_idx[r, k0:k1], dtype=np.float64)
+                self._cache[key] = _f64(self.k_idx[r, k0:k1])
             else:
                 g = self.kv_of(self.ret_heads[r])
-                self._kidx_cache[key] = O.project(self.k_pre[k0:k1, g], self.w_k[r], self.dtype)
-        return self._kidx_cache[key]
+                self._cache[key] = O.project(self._kv("k_pre", b, g), self.w("w_k", r), self.dtype)
+        return self._cache[key]
 
-    def all_index_keys(self) -> np.ndarray:
-        """[R, T_k, 16] index cache for every retrieval slot (what the decode inputs hold)."""
-        R = len(self.ret_heads)
-        out = np.zeros((R, self.k.shape[0], O.IDX_DIM))
-        for r in range(R):
-            g = self.kv_of(self.ret_heads[r])
-            out[r] = O.project(self.k_pre[:, g], self.w_k[r], self.dtype)
-        return out
+    def q_row(self, qi: int, h: int) -> np.ndarray:
+        return _f64(self.q[qi, h])
 
     def row(self, b: int, i: int, h: int, keys: Optional[np.ndarray] = None) -> O.RowResult:
         """Oracle result of query row i of sequence b on head h."""
         pos = self.pos_of(b, i)
-        k0, k1 = self.seq_range_k(b)
         g = self.kv_of(h)
-        K = self.k[k0:k1, g]
-        V = self.v[k0:k1, g]
+        K = self._kv("k", b, g)
+        V = self._kv("v", b, g)
         qi = int(self.cu_q[b]) + i
         r = self.slot_of(h)
         if r >= 0:
-            return O.retrieval_row(self.q[qi, h], self.q_pre[qi, r], self.w_q[r], K, V,
-                                   self.index_keys(b, r), pos, float(self.top_p[b]),
-                                   self.dtype, keys=keys)
-        return O.local_row(self.q[qi, h], K, V, pos, self.window, self.n_sink)
+            return O.retrieval_row(self.q_row(qi, h), _f64(self.q_pre[qi, r]), self.w("w_q", r), K, V,
+                                   self.index_keys(b, r), pos, float(self.top_p[b]), self.dtype, keys=keys)
+        return O.local_row(self.q_row(qi, h), K, V, pos, self.window, self.n_sink)
 
 
-def from_inputs(inp, k_idx: Optional[np.ndarray] = None) -> Problem:
-    """Build a Problem from ``synth.Inputs`` (torch tensors on any device)."""
-    def np64(t):
-        return t.detach().float().cpu().numpy().astype(np.float64)
+def from_inputs(inp, k_idx=None) -> Problem:
+    """Build a Problem from ``synth.Inputs`` (tensors are copied to host memory, not converted)."""
+    def host(t):
+        return t.detach().cpu() if t is not None else None
     cfg = inp.cfg
     return Problem(
-        q=np64(inp.q), k=np64(inp.k), v=np64(inp.v), q_pre=np64(inp.q_pre),
-        k_pre=np64(inp.k_pre), w_q=np64(inp.w), w_k=np64(inp.w),
+        q=host(inp.q), k=host(inp.k), v=host(inp.v), q_pre=host(inp.q_pre), k_pre=host(inp.k_pre),
+        w_q=host(inp.w), w_k=host(inp.w),
         cu_q=inp.cu_q.cpu().tolist(), cu_k=inp.cu_k.cpu().tolist(),
         ret_heads=list(cfg.ret_heads), top_p=[float(x) for x in inp.top_p.cpu().tolist()],
-        window=cfg.window, n_sink=cfg.n_sink, dtype=cfg.dtype, k_idx=k_idx)
+        window=cfg.window, n_sink=cfg.n_sink, dtype=cfg.dtype, k_idx=host(k_idx))

@@ -1,0 +1,231 @@
+"""Helpers for the GPU parity tests: run the HIP path through the C ABI and compare
+it with the CPU oracle row by row.  Imported by tests only."""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from oracle import rtp_oracle as O
+from oracle.problem import Problem, from_inputs
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def sync():
+    torch.cuda.synchronize()
+
+
+def run_prefill(inp) -> Dict[str, torch.Tensor]:
+    """Prefill path: index keys -> THRESHOLD select -> sparse attention + local attention."""
+    import long_context_sparse_rtp_amd as rtp
+    prob = rtp.Problem.from_inputs(inp)
+    k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w)
+    sel = rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_THRESHOLD)
+    out = torch.full_like(inp.q, float("nan"))
+    lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=inp.q.device)
+    rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel, out, lse)
+    rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse)
+    sync()
+    return dict(k_idx=k_idx, q_idx=sel.q_idx, tau=sel.tau, tie=sel.tie_pos, count=sel.count, out=out, lse=lse)
+
+
+def run_decode(inp, k_idx: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """Decode path with a precomputed index cache: LIST select -> sparse decode + local decode."""
+    import long_context_sparse_rtp_amd as rtp
+    prob = rtp.Problem.from_inputs(inp)
+    sel = rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_LIST)
+    out = torch.full_like(inp.q, float("nan"))
+    lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=inp.q.device)
+    rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse)
+    rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse)
+    sync()
+    return dict(q_idx=sel.q_idx, idx=sel.idx, count=sel.count, tau=sel.tau, tie=sel.tie_pos, out=out, lse=lse)
+
+
+def oracle_index_keys(pr: Problem, dtype: torch.dtype, device) -> torch.Tensor:
+    """[R, T_k, 16] index cache computed by the oracle, stored in ``dtype`` (exactly representable)."""
+    R = len(pr.ret_heads)
+    Tk = pr.k.shape[0]
+    out = torch.empty((R, Tk, 16), dtype=dtype)
+    for r in range(R):
+        g = pr.kv_of(pr.ret_heads[r])
+        for c0 in range(0, Tk, 1 << 18):
+            c1 = min(Tk, c0 + (1 << 18))
+            x = pr.k_pre[c0:c1, g].to(torch.float64).numpy()
+            out[r, c0:c1] = torch.from_numpy(O.project(x, pr.w("w_k", r), pr.dtype)).to(dtype)
+    return out.to(device)
+
+
+def to_host(d: Dict[str, torch.Tensor]) -> Dict[str, np.ndarray]:
+    h = {}
+    for k, v in d.items():
+        if v is None:
+            continue
+        t = v.detach().cpu()
+        h[k] = t.to(torch.float64).numpy() if t.is_floating_point() else t.numpy()
+    return h
+
+
+def near_midpoint(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Elements whose float64 value lies within 1e-12 (relative) of a rounding midpoint of ``dtype``."""
+    bits = 8 if dtype == "bf16" else 24
+    _, e = np.frexp(x)
+    q = np.ldexp(1.0, e - bits)
+    frac = x / q - np.floor(x / q)
+    return np.abs(frac - 0.5) < 1e-12 * np.abs(x / q) + 1e-300
+
+
+def check_index_keys(pr: Problem, gpu_kidx: np.ndarray, rows: Optional[np.ndarray] = None) -> int:
+    """Bit-exact comparison with the oracle projection; returns the number of mismatches
+    (mismatches at float64 rounding midpoints, where the float64 dot itself is ambiguous,
+    are not counted)."""
+    bad = 0
+    Tk = pr.k.shape[0]
+    rows = np.arange(Tk) if rows is None else rows
+    for r, h in enumerate(pr.ret_heads):
+        g = pr.kv_of(h)
+        x = pr.k_pre[torch.as_tensor(rows), g].to(torch.float64).numpy()
+        exact = x @ pr.w("w_k", r).T
+        ref = O.round_to(exact, pr.dtype)
+        got = gpu_kidx[r, rows]
+        diff = got != ref
+        if diff.any():
+            diff &= ~near_midpoint(exact, pr.dtype)
+        bad += int(diff.sum())
+    return bad
+
+
+def _amb_eps(q_idx: np.ndarray, k_idx: np.ndarray) -> np.ndarray:
+    # bound on |float32 MFMA score - float64 score| (products are exact; 16 fp32 additions)
+    return 2.0 ** -19 * (np.abs(k_idx) @ np.abs(q_idx)) * O.IDX_SCALE + 1e-30
+
+
+def check_retrieval_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.ndarray], tol: float):
+    """Compare one retrieval-head row (THRESHOLD output).  Returns (ok, info)."""
+    r = pr.slot_of(h)
+    qi = int(pr.cu_q[b]) + i
+    res = pr.row(b, i, h)
+    info = {}
+    if not np.array_equal(g["q_idx"][r, qi], res.q_idx):
+        return False, {"why": "q_idx mismatch"}
+    p = float(pr.top_p[b])
+    tau = g["tau"][r, qi]
+    count = int(g["count"][r, qi])
+    t = res.topp
+    pos = pr.pos_of(b, i)
+    if p >= 1.0:
+        G_list = [np.arange(pos + 1)]
+    else:
+        eps = _amb_eps(res.q_idx, pr.index_keys(b, r)[: pos + 1])
+        s = t.scores
+        sure = np.nonzero(s > tau + eps)[0]
+        amb = np.nonzero(np.abs(s - tau) <= eps)[0]
+        k_amb = count - sure.size
+        info.update(n_amb=int(amb.size))
+        if k_amb < 0 or k_amb > amb.size:
+            return False, {"why": f"count {count} inconsistent (sure {sure.size}, amb {amb.size})"}
+        if math.comb(amb.size, k_amb) > 256:
+            return False, {"why": f"too many ambiguous tokens ({amb.size})"}
+        G_list = [np.sort(np.concatenate([sure, np.array(c, dtype=np.int64)]))
+                  for c in itertools.combinations(amb.tolist(), k_amb)]
+    pr_k = pr._kv("k", b, pr.kv_of(h))
+    pr_v = pr._kv("v", b, pr.kv_of(h))
+    qv = pr.q_row(qi, h)
+    best = None
+    for G in G_list:
+        ok_set, ndiff = O.set_ok(t, p, G)
+        if not ok_set:
+            continue
+        a = O.attend(qv, pr_k, pr_v, G)
+        err = float(np.max(np.abs(g["out"][qi, h] - a.out)))
+        lerr = abs(float(g["lse"][h, qi]) - a.lse)
+        if err <= tol and lerr <= max(tol, 1e-4):
+            return True, dict(info, err=err, lerr=lerr, ndiff=ndiff)
+        best = (err, lerr) if best is None or err < best[0] else best
+    return False, dict(info, why="no valid set matches", best=best, count=count, oracle_count=t.count)
+
+
+def check_list_row(pr: Problem, b: int, h: int, g: Dict[str, np.ndarray], tol: float):
+    """Compare one retrieval-head decode row (LIST output)."""
+    r = pr.slot_of(h)
+    qi = int(pr.cu_q[b])
+    res = pr.row(b, 0, h)
+    if not np.array_equal(g["q_idx"][r, qi], res.q_idx):
+        return False, {"why": "q_idx mismatch"}
+    k0, k1 = pr.seq_range_k(b)
+    count = int(g["count"][r, qi])
+    G = g["idx"][r, k0:k0 + count].astype(np.int64)
+    if count < 1 or np.any(np.diff(G) <= 0) or G.min() < 0 or G.max() >= k1 - k0:
+        return False, {"why": "list not ascending / out of range", "count": count}
+    p = float(pr.top_p[b])
+    ok_set, ndiff = O.set_ok(res.topp, p, G)
+    if not ok_set:
+        return False, {"why": "set differs beyond near-threshold tokens", "count": count,
+                       "oracle_count": res.topp.count, "ndiff": ndiff}
+    a = O.attend(pr.q_row(qi, h), pr._kv("k", b, pr.kv_of(h)), pr._kv("v", b, pr.kv_of(h)), G)
+    err = float(np.max(np.abs(g["out"][qi, h] - a.out)))
+    lerr = abs(float(g["lse"][h, qi]) - a.lse)
+    ok = err <= tol and lerr <= max(tol, 1e-4)
+    return ok, dict(err=err, lerr=lerr, ndiff=ndiff, count=count)
+
+
+def check_local_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.ndarray], tol: float):
+    qi = int(pr.cu_q[b]) + i
+    a = pr.row(b, i, h).attn
+    err = float(np.max(np.abs(g["out"][qi, h] - a.out)))
+    lerr = abs(float(g["lse"][h, qi]) - a.lse)
+    return err <= tol and lerr <= max(tol, 1e-4), dict(err=err, lerr=lerr)
+
+
+def check_rows(pr: Problem, g: Dict[str, np.ndarray], rows: Sequence[Tuple[int, int]], heads: Sequence[int],
+               tol: float, decode: bool = False, workers: int = 1):
+    """Check every (row, head); returns (n_checked, failures list, stats)."""
+    tasks = [(b, i, h) for (b, i) in rows for h in heads]
+    results = _map(_check_task, [(pr, g, t, tol, decode) for t in tasks], workers)
+    fails = [(t, info) for t, (ok, info) in zip(tasks, results) if not ok]
+    errs = [info.get("err", 0.0) for ok, info in results if ok]
+    ndiff = sum(info.get("ndiff", 0) or 0 for ok, info in results if ok)
+    stats = dict(max_err=max(errs) if errs else 0.0, n=len(tasks), set_diffs=ndiff)
+    return len(tasks), fails, stats
+
+
+_SHARED = {}
+
+
+def _check_task(args):
+    pr, g, (b, i, h), tol, decode = args
+    if pr.slot_of(h) >= 0:
+        if decode:
+            return check_list_row(pr, b, h, g, tol)
+        return check_retrieval_row(pr, b, i, h, g, tol)
+    return check_local_row(pr, b, i, h, g, tol)
+
+
+def _worker_task(idx):
+    args = _SHARED["args"][idx]
+    return _check_task(args)
+
+
+def _map(fn, arglist, workers):
+    if workers <= 1 or len(arglist) < 8:
+        return [fn(a) for a in arglist]
+    import multiprocessing as mp
+    _SHARED["args"] = arglist
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        out = pool.map(_worker_task, range(len(arglist)), chunksize=max(1, len(arglist) // (4 * workers)))
+    _SHARED.clear()
+    return out
+
+
+def n_workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
