@@ -1,0 +1,294 @@
+"""Benchmark of the sparse-attention hot path on one MI355X.
+
+A step of the prefill workload (128K tokens, 32 query / 4 KV heads, bf16) is
+one full pass of the path: index-key projection, THRESHOLD top-p selection,
+sparse attention of the 4 retrieval heads and sink+window attention of the 28
+local heads.  A step of the decode workload (batch 8 x 32K, index cache already
+built) is LIST selection, sparse decode attention and local decode attention.
+Inputs are seeded synthetic tensors resident in HBM before timing starts.
+
+Prints one JSON line: ``value`` is prefill tokens/s; the decode step time, the
+per-kernel times, the roofline of the dominant kernel and the CPU oracle
+baseline ride along in the same line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn prefill tokens/s @128K and decode step µs @32K, 1 MI355X, % roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the stream the kernels run on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.acc = {}
+
+    def run(self, name, fn):
+        e0 = self.torch.cuda.Event(enable_timing=True)
+        e1 = self.torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        fn()
+        e1.record(self.stream)
+        self.acc.setdefault(name, []).append((e0, e1))
+
+    def means_ms(self):
+        return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.acc.items()}
+
+
+def bench_prefill(args, torch, rtp, synth):
+    cfg = synth.PREFILL_128K
+    dev = "cuda"
+    inp = synth.make_inputs(cfg, dev)
+    prob = rtp.Problem.from_inputs(inp)
+    stream = torch.cuda.current_stream()
+    k_idx = torch.empty((cfg.n_ret, inp.total_k, 16), dtype=inp.q.dtype, device=dev)
+    sel = rtp.Selection.empty(prob, rtp.RTP_SEL_THRESHOLD, dev)
+    ws_sel = torch.empty(max(16, rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SELECT, rtp.RTP_SEL_THRESHOLD)),
+                         dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp.q)
+    lse = torch.empty((cfg.n_q_heads, inp.total_q), dtype=torch.float32, device=dev)
+
+    def step(t: Timer = None):
+        calls = [
+            ("index_keys", lambda: rtp.rtp_index_keys(prob, inp.k_pre, inp.w, k_idx, stream=stream)),
+            ("select_topp", lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p,
+                                                        rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream=stream)),
+            ("sparse_attn_prefill", lambda: rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel,
+                                                                        out, lse, stream=stream)),
+            ("local_attn", lambda: rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, stream=stream)),
+        ]
+        for name, fn in calls:
+            if t is None:
+                fn()
+            else:
+                t.run(name, fn)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t = Timer(torch, stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step(t)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per = t.means_ms()
+
+    # algorithmic work (sets measured from this run's selection)
+    L, d, r = cfg.seqlen, 128, 16
+    sum_S = float(sel.count.to(torch.float64).sum().item())
+    causal_pairs = L * (L + 1) / 2
+    n_local = cfg.n_q_heads - cfg.n_ret
+    W, ns = cfg.window, cfg.n_sink
+    i = torch.arange(L, dtype=torch.float64)
+    local_keys = torch.minimum(i + 1, torch.full_like(i, W)) + torch.clamp(torch.minimum(i - W + 1, torch.full_like(i, ns)), min=0)
+    sum_local = float(local_keys.sum().item()) * n_local
+    flops = {
+        "sparse_attn_prefill": 4 * d * sum_S,
+        "local_attn": 4 * d * sum_local,
+        "select_topp": 2 * r * causal_pairs * cfg.n_ret,
+    }
+    total_flops = sum(flops.values())
+    bytes_ik = inp.total_k * cfg.n_ret * (d * 2 + r * 2)
+    return dict(ms=ms, per_kernel_ms=per, flops=flops, total_flops=total_flops, sum_S=sum_S,
+                mean_frac_selected=sum_S / (cfg.n_ret * causal_pairs), bytes_index_keys=bytes_ik,
+                tokens=L, cfg=cfg, inp=inp, sel=sel)
+
+
+def bench_decode(args, torch, rtp, synth):
+    cfg = synth.DECODE_32K
+    dev = "cuda"
+    inp = synth.make_inputs(cfg, dev)
+    prob = rtp.Problem.from_inputs(inp)
+    stream = torch.cuda.current_stream()
+    k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w, stream=stream)   # cache built before timing
+    sel = rtp.Selection.empty(prob, rtp.RTP_SEL_LIST, dev)
+    ws_sel = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SELECT, rtp.RTP_SEL_LIST), dtype=torch.uint8,
+                         device=dev)
+    ws_dec = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SPARSE_DECODE), dtype=torch.uint8, device=dev)
+    ws_loc = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_LOCAL), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(inp.q)
+    lse = torch.empty((cfg.n_q_heads, inp.total_q), dtype=torch.float32, device=dev)
+
+    def step(t: Timer = None):
+        calls = [
+            ("select_topp", lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_LIST,
+                                                        sel, ws_sel, stream=stream)),
+            ("sparse_attn_decode", lambda: rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse,
+                                                                      ws_dec, stream=stream)),
+            ("local_attn", lambda: rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, ws_loc, stream=stream)),
+        ]
+        for name, fn in calls:
+            if t is None:
+                fn()
+            else:
+                t.run(name, fn)
+
+    steps = args.decode_steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    t = Timer(torch, stream)
+    for _ in range(steps):
+        step(t)
+    torch.cuda.synchronize()
+    per = t.means_ms()
+
+    counts = sel.count.to(torch.float64).cpu()
+    B, L, W, ns = cfg.batch, cfg.seqlen, cfg.window, cfg.n_sink
+    kv_row = 2 * 128 * 2            # K + V bytes per token per KV head
+    sparse_bytes = float(counts.sum().item()) * kv_row
+    local_keys = min(W, L) + min(ns, max(0, L - W))
+    local_bytes = B * cfg.n_kv_heads * local_keys * kv_row   # each KV group's window once
+    idx_bytes = cfg.n_ret * B * L * 16 * 2
+    qo_bytes = B * cfg.n_q_heads * 128 * 2 * 2
+    return dict(ms=ms, per_kernel_ms=per, bytes=dict(sparse_attn_decode=sparse_bytes, local_attn=local_bytes,
+                                                     select_topp=idx_bytes, q_out=qo_bytes),
+                total_bytes=sparse_bytes + local_bytes + idx_bytes + qo_bytes,
+                mean_frac_selected=float(counts.mean().item()) / L)
+
+
+def cpu_baseline(args, pre):
+    """The oracle, untuned, on a bounded sample of the prefill workload's query rows."""
+    import numpy as np
+    import multiprocessing as mp
+    from oracle.problem import from_inputs
+    cfg, inp = pre["cfg"], pre["inp"]
+    pr = from_inputs(inp)
+    L = cfg.seqlen
+    heads = list(range(cfg.n_q_heads))
+    # warm the per-KV-head float64 caches before forking so workers share them
+    for h in heads:
+        pr._kv("k", 0, pr.kv_of(h))
+        pr._kv("v", 0, pr.kv_of(h))
+    for r in range(cfg.n_ret):
+        pr.index_keys(0, r)
+    rng = np.random.default_rng(0)
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    cores = max(1, min(cores, 16))
+    global _PR
+    _PR = pr
+    t0 = time.time()
+    done_rows, cost_rows = 0, 0.0
+    with mp.get_context("fork").Pool(cores) as pool:
+        while time.time() - t0 < args.cpu_seconds:
+            rows = rng.integers(0, L, size=cores).tolist()
+            res = pool.map(_cpu_row_all_heads, rows)
+            done_rows += len(rows)
+    wall = time.time() - t0
+    # rows drawn uniformly over [0, L) so their mean cost is the mean over the prefill
+    tok_s = done_rows / wall
+    return dict(value=tok_s, unit="tokens/s", cores=cores, kind="oracle",
+                sample=f"{done_rows} query rows drawn uniformly from the 128K prefill, all 32 heads each, "
+                       f"float64 numpy, {cores} worker processes, {wall:.1f} s")
+
+
+_PR = None
+
+
+def _cpu_row_all_heads(i):
+    pr = _PR
+    for h in range(pr.n_q_heads):
+        pr.row(0, int(i), h)
+    return i
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import torch
+    import long_context_sparse_rtp_amd as rtp
+    import synth
+    rtp.library()  # fail loudly if the HIP library is missing
+    print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
+
+    line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic"}
+    pre = dec = None
+    if args.only in ("prefill", "both"):
+        print("[bench] prefill 128K ...", file=sys.stderr, flush=True)
+        pre = bench_prefill(args, torch, rtp, synth)
+        tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
+        per = pre["per_kernel_ms"]
+        dom = max(("sparse_attn_prefill", "local_attn", "select_topp"), key=lambda k: per[k])
+        fl = {k: pre["flops"][k] / (per[k] * 1e-3) / 1e12 for k in pre["flops"]}
+        line.update(value=tok_s, unit="tokens/s", ms_per_step=pre["ms"])
+        line["config"] = {"workload": "prefill_128k: L=131072 causal, 32 q / 4 kv heads, d=128, bf16, "
+                                      "4 retrieval heads (top-p 0.9, 16-dim indexer), 28 local heads "
+                                      "(window 2048 + 4 sinks)",
+                          "global_batch": 1, "seq_len": pre["tokens"], "parallelism": "none (1 GPU)"}
+        rt = per[dom]
+        ach = pre["flops"][dom] / (rt * 1e-3) / 1e12
+        line["roofline"] = {"kernel": dom, "bound": "mfma" if dom != "select_topp" else "alu",
+                            "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        line["prefill"] = {"ms_per_step": pre["ms"], "per_kernel_ms": per,
+                           "per_kernel_tflops": fl,
+                           "algorithmic_tflop": pre["total_flops"] / 1e12,
+                           "step_frac_of_mfma_roofline": (pre["total_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e12 * 1e3)
+                           / pre["ms"],
+                           "mean_selected_fraction": pre["mean_frac_selected"]}
+    if args.only in ("decode", "both"):
+        print("[bench] decode 32K x 8 ...", file=sys.stderr, flush=True)
+        dec = bench_decode(args, torch, rtp, synth)
+        per = dec["per_kernel_ms"]
+        line["decode"] = {"workload": "decode_32k_b8: batch 8, KV 32768, 32 q / 4 kv heads, bf16, "
+                                      "4 retrieval heads (top-p 0.95), local window 1024 + 4 sinks",
+                          "step_us": dec["ms"] * 1e3, "per_kernel_us": {k: v * 1e3 for k, v in per.items()},
+                          "algorithmic_bytes": dec["total_bytes"],
+                          "achieved_GBps": dec["total_bytes"] / (dec["ms"] * 1e-3) / 1e9,
+                          "step_frac_of_hbm_roofline": dec["total_bytes"] / (HBM_PEAK_GBS * 1e9) / (dec["ms"] * 1e-3),
+                          "mean_selected_fraction": dec["mean_frac_selected"]}
+        if pre is None:
+            line.update(value=dec["ms"] * 1e3, unit="us", higher_is_better=False, ms_per_step=dec["ms"])
+    if pre is not None and not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(args, pre)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -47,7 +47,7 @@ __device__ __forceinline__ bf16_t f64_to_bf16_rne(double x) {
   }
   uint64_t u = (uint64_t)__double_as_longlong(x);
   const uint64_t drop = (1ull << 45) - 1ull;  // 52 - 7 fraction bits dropped
-  u += drop + ((u >> 45) & 1ull);
+  u += (drop >> 1) + ((u >> 45) & 1ull);  // half of the dropped range, ties to even
   u &= ~drop;
   float f = (float)__longlong_as_double((long long)u);  // exact, or +-inf on overflow
   return (bf16_t)(__float_as_uint(f) >> 16);

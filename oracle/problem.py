@@ -94,7 +94,16 @@ class Problem:
         return self._cache[key]
 
     def q_row(self, qi: int, h: int) -> np.ndarray:
-        return _f64(self.q[qi, h])
+        key = ("q", qi, h)
+        if key not in self._cache:
+            self._cache[key] = _f64(self.q[qi, h])
+        return self._cache[key]
+
+    def q_pre_row(self, qi: int, r: int) -> np.ndarray:
+        key = ("qp", qi, r)
+        if key not in self._cache:
+            self._cache[key] = _f64(self.q_pre[qi, r])
+        return self._cache[key]
 
     def row(self, b: int, i: int, h: int, keys: Optional[np.ndarray] = None) -> O.RowResult:
         """Oracle result of query row i of sequence b on head h."""
@@ -105,7 +114,7 @@ class Problem:
         qi = int(self.cu_q[b]) + i
         r = self.slot_of(h)
         if r >= 0:
-            return O.retrieval_row(self.q_row(qi, h), _f64(self.q_pre[qi, r]), self.w("w_q", r), K, V,
+            return O.retrieval_row(self.q_row(qi, h), self.q_pre_row(qi, r), self.w("w_q", r), K, V,
                                    self.index_keys(b, r), pos, float(self.top_p[b]), self.dtype, keys=keys)
         return O.local_row(self.q_row(qi, h), K, V, pos, self.window, self.n_sink)
 

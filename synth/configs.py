@@ -52,6 +52,8 @@ class Config:
     peaky_frac: float = 0.0        # fraction of sequences that carry needles
     # how many query rows the oracle verifies (0 = all)
     verify_rows: int = 0
+    # explicit per-sequence KV lengths (prefill: L_q = L_k; decode: L_q = 1)
+    seqlens: Optional[Tuple[int, ...]] = None
 
     @property
     def n_ret(self) -> int:

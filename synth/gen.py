@@ -140,6 +140,10 @@ class Inputs:
 
 
 def _lengths(cfg: Config):
+    if cfg.seqlens is not None:
+        lk = [int(x) for x in cfg.seqlens]
+        assert len(lk) == cfg.batch
+        return (list(lk) if cfg.kind == "prefill" else [1] * cfg.batch), lk
     if cfg.kind == "prefill":
         return [cfg.seqlen] * cfg.batch, [cfg.seqlen] * cfg.batch
     if cfg.ragged:

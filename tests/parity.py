@@ -118,13 +118,20 @@ def check_retrieval_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.nda
     count = int(g["count"][r, qi])
     t = res.topp
     pos = pr.pos_of(b, i)
+    tie = int(g["tie"][r, qi])
     if p >= 1.0:
         G_list = [np.arange(pos + 1)]
     else:
+        if not (0 <= tie <= pos):
+            return False, {"why": f"tie_pos {tie} outside [0, {pos}]"}
         eps = _amb_eps(res.q_idx, pr.index_keys(b, r)[: pos + 1])
         s = t.scores
-        sure = np.nonzero(s > tau + eps)[0]
-        amb = np.nonzero(np.abs(s - tau) <= eps)[0]
+        n = np.arange(s.size)
+        # the crossing token is at tie_pos; tokens with exactly its score are admitted
+        # by position, as the threshold rule says
+        same = s == s[tie]
+        sure = np.nonzero((s > tau + eps) & ~same | (same & (n <= tie)))[0]
+        amb = np.nonzero((np.abs(s - tau) <= eps) & ~same)[0]
         k_amb = count - sure.size
         info.update(n_amb=int(amb.size))
         if k_amb < 0 or k_amb > amb.size:
@@ -182,10 +189,26 @@ def check_local_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.ndarray
     return err <= tol and lerr <= max(tol, 1e-4), dict(err=err, lerr=lerr)
 
 
+def warm(pr: Problem, tasks) -> None:
+    """Convert every slice the tasks need to float64 numpy now (before any fork)."""
+    for (b, i, h) in tasks:
+        g = pr.kv_of(h)
+        pr._kv("k", b, g)
+        pr._kv("v", b, g)
+        qi = int(pr.cu_q[b]) + i
+        pr.q_row(qi, h)
+        r = pr.slot_of(h)
+        if r >= 0:
+            pr.index_keys(b, r)
+            pr.w("w_q", r)
+            pr.q_pre_row(qi, r)
+
+
 def check_rows(pr: Problem, g: Dict[str, np.ndarray], rows: Sequence[Tuple[int, int]], heads: Sequence[int],
                tol: float, decode: bool = False, workers: int = 1):
     """Check every (row, head); returns (n_checked, failures list, stats)."""
     tasks = [(b, i, h) for (b, i) in rows for h in heads]
+    warm(pr, tasks)
     results = _map(_check_task, [(pr, g, t, tol, decode) for t in tasks], workers)
     fails = [(t, info) for t, (ok, info) in zip(tasks, results) if not ok]
     errs = [info.get("err", 0.0) for ok, info in results if ok]
@@ -224,8 +247,9 @@ def _map(fn, arglist, workers):
 
 
 def n_workers() -> int:
+    """Oracle worker processes: a few, so that the GPU process count stays small."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
         n = os.cpu_count() or 1
-    return max(1, min(16, n))
+    return max(1, min(8, n))
