@@ -108,8 +108,17 @@ def project(x_pre, w, dtype: str) -> np.ndarray:
 
 
 def indexer_scores(q_idx, k_idx) -> np.ndarray:
-    """s_n = (q_idx . k_idx_n) / sqrt(16) for every key row of k_idx [n, 16]."""
-    return (np.asarray(k_idx, dtype=np.float64) @ np.asarray(q_idx, dtype=np.float64)) * IDX_SCALE
+    """s_n = (q_idx . k_idx_n) / sqrt(16) for every key row of k_idx [n, 16].
+
+    The 16 products are summed in a fixed order for every row, so equal index
+    keys always get equal scores and exact ties are broken by position only.
+    """
+    k = np.asarray(k_idx, dtype=np.float64)
+    q = np.asarray(q_idx, dtype=np.float64)
+    acc = np.zeros(k.shape[0])
+    for j in range(q.size):
+        acc += k[:, j] * q[j]
+    return acc * IDX_SCALE
 
 
 @dataclasses.dataclass

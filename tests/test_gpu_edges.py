@@ -127,5 +127,10 @@ def test_selection_deterministic():
     k_idx = rtp.rtp_index_keys(rtp.Problem.from_inputs(dinp), dinp.k_pre, dinp.w)
     a = P.run_decode(dinp, k_idx)
     b = P.run_decode(dinp, k_idx)
-    for k in ("idx", "count", "out"):
+    for k in ("count", "out", "tau", "tie"):
         assert torch.equal(a[k], b[k]), k
+    cu = dinp.cu_k.cpu().tolist()
+    for r in range(dcfg.n_ret):
+        for bb in range(dcfg.batch):
+            c = int(a["count"][r, bb])
+            assert torch.equal(a["idx"][r, cu[bb]:cu[bb] + c], b["idx"][r, cu[bb]:cu[bb] + c])
