@@ -100,7 +100,8 @@ typedef struct {
 typedef struct {
   void *q_idx;       /* (dev) [R, T_q, 16] dtype: rounded indexer queries, written by select */
   float *tau;        /* (dev) THRESHOLD: [R, T_q] score threshold (-inf when p >= 1) */
-  int32_t *tie_pos;  /* (dev) THRESHOLD: [R, T_q] last admitted position among scores == tau */
+  int32_t *tie_pos;  /* (dev) THRESHOLD: [R, T_q] last admitted position among scores == tau
+                        (INT32_MAX: all of them) */
   int32_t *count;    /* (dev) [R, T_q] size of the selected set */
   int32_t *idx;      /* (dev) LIST: [R, T_k]; slot (r, b) starts at r*T_k + cu_seqlens_k[b] */
 } rtp_selection;
@@ -136,7 +137,8 @@ RTP_API rtp_status rtp_index_keys(const rtp_problem *prob, const void *k_pre, co
  *   mode LIST (decode; requires max_seqlen_q == 1, else RTP_ERR_UNSUPPORTED):
  *     writes sel->idx (ascending key positions, within the sequence) and sel->count.
  *   mode THRESHOLD (any L_q): writes sel->tau, sel->tie_pos, sel->count with
- *     S = {n <= pos : s_n > tau} U {n <= pos : s_n == tau and n <= tie_pos}.
+ *     S = {n <= pos : s_n > tau} U {n <= pos : s_n == tau and n <= tie_pos};
+ *     tie_pos = INT32_MAX when no token scoring exactly tau is left out.
  *   sel->q_idx is always written.  ws: rtp_workspace_size(prob, RTP_CALL_SELECT, mode) bytes.
  */
 RTP_API rtp_status rtp_select_topp(const rtp_problem *prob, const void *q_pre, const float *w_q,

@@ -65,72 +65,93 @@ __device__ __forceinline__ void load_vfrag(FragF32& f, const float* rowp) {
   f.v[4] = b.x; f.v[5] = b.y; f.v[6] = b.z; f.v[7] = b.w;
 }
 
-// ---- stage one 64-key tile: K row-major, V transposed
-__device__ __forceinline__ void stage_tile(bf16_t* k_s, bf16_t* vt_s, const bf16_t* kg, const bf16_t* vg,
-                                           size_t rstride, int nvalid, int tid) {
-  constexpr int KS = Lds<bf16_t>::kStr, VS = Lds<bf16_t>::vStr;
+// ---- staging of one 64-key tile: global -> registers (issued early, one tile
+// ahead) -> LDS (K row-major, V transposed)
+template <typename T> struct Stage;
+template <> struct Stage<bf16_t> {
+  uint4 k[4], v[4];
+  __device__ __forceinline__ void load(const bf16_t* kg, const bf16_t* vg, size_t rstride, int nvalid, int tid) {
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int e = u * kThreads + tid;
-    const int key = e >> 4, ch = e & 15;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (key < nvalid) val = *reinterpret_cast<const uint4*>(kg + (size_t)key * rstride + ch * 8);
-    *reinterpret_cast<uint4*>(k_s + key * KS + ch * 8) = val;
-  }
-  const int kgp = tid & 15, dc = tid >> 4;
-  uint4 r[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int key = 4 * kgp + u;
-    r[u] = {0u, 0u, 0u, 0u};
-    if (key < nvalid) r[u] = *reinterpret_cast<const uint4*>(vg + (size_t)key * rstride + dc * 8);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t w0 = (&r[0].x)[e >> 1], w1 = (&r[1].x)[e >> 1];
-    const uint32_t w2 = (&r[2].x)[e >> 1], w3 = (&r[3].x)[e >> 1];
-    uint2 out;
-    if (e & 1) {
-      out.x = (w0 >> 16) | (w1 & 0xFFFF0000u);
-      out.y = (w2 >> 16) | (w3 & 0xFFFF0000u);
-    } else {
-      out.x = (w0 & 0xFFFFu) | (w1 << 16);
-      out.y = (w2 & 0xFFFFu) | (w3 << 16);
+    for (int u = 0; u < 4; ++u) {
+      const int e = u * kThreads + tid;
+      const int key = e >> 4, ch = e & 15;
+      k[u] = {0u, 0u, 0u, 0u};
+      if (key < nvalid) k[u] = *reinterpret_cast<const uint4*>(kg + (size_t)key * rstride + ch * 8);
     }
-    *reinterpret_cast<uint2*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = out;
-  }
-}
-__device__ __forceinline__ void stage_tile(float* k_s, float* vt_s, const float* kg, const float* vg,
-                                           size_t rstride, int nvalid, int tid) {
-  constexpr int KS = Lds<float>::kStr, VS = Lds<float>::vStr;
+    const int kgp = tid & 15, dc = tid >> 4;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int e = u * kThreads + tid;
-    const int key = e >> 5, ch = e & 31;
-    float4 val = {0.f, 0.f, 0.f, 0.f};
-    if (key < nvalid) val = *reinterpret_cast<const float4*>(kg + (size_t)key * rstride + ch * 4);
-    *reinterpret_cast<float4*>(k_s + key * KS + ch * 4) = val;
-  }
-  const int kgp = tid & 15, dc = tid >> 4;
-  float r[4][8];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int key = 4 * kgp + u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[u][i] = 0.f;
-    if (key < nvalid) {
-      float4 a = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8);
-      float4 b = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8 + 4);
-      r[u][0] = a.x; r[u][1] = a.y; r[u][2] = a.z; r[u][3] = a.w;
-      r[u][4] = b.x; r[u][5] = b.y; r[u][6] = b.z; r[u][7] = b.w;
+    for (int u = 0; u < 4; ++u) {
+      const int key = 4 * kgp + u;
+      v[u] = {0u, 0u, 0u, 0u};
+      if (key < nvalid) v[u] = *reinterpret_cast<const uint4*>(vg + (size_t)key * rstride + dc * 8);
     }
   }
+  __device__ __forceinline__ void store(bf16_t* k_s, bf16_t* vt_s, int tid) const {
+    constexpr int KS = Lds<bf16_t>::kStr, VS = Lds<bf16_t>::vStr;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    float4 o = {r[0][e], r[1][e], r[2][e], r[3][e]};
-    *reinterpret_cast<float4*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = o;
+    for (int u = 0; u < 4; ++u) {
+      const int e = u * kThreads + tid;
+      const int key = e >> 4, ch = e & 15;
+      *reinterpret_cast<uint4*>(k_s + key * KS + ch * 8) = k[u];
+    }
+    const int kgp = tid & 15, dc = tid >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w0 = (&v[0].x)[e >> 1], w1 = (&v[1].x)[e >> 1];
+      const uint32_t w2 = (&v[2].x)[e >> 1], w3 = (&v[3].x)[e >> 1];
+      uint2 out;
+      if (e & 1) {
+        out.x = (w0 >> 16) | (w1 & 0xFFFF0000u);
+        out.y = (w2 >> 16) | (w3 & 0xFFFF0000u);
+      } else {
+        out.x = (w0 & 0xFFFFu) | (w1 << 16);
+        out.y = (w2 & 0xFFFFu) | (w3 << 16);
+      }
+      *reinterpret_cast<uint2*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = out;
+    }
   }
-}
+};
+template <> struct Stage<float> {
+  float4 k[8];
+  float v[4][8];
+  __device__ __forceinline__ void load(const float* kg, const float* vg, size_t rstride, int nvalid, int tid) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = u * kThreads + tid;
+      const int key = e >> 5, ch = e & 31;
+      k[u] = {0.f, 0.f, 0.f, 0.f};
+      if (key < nvalid) k[u] = *reinterpret_cast<const float4*>(kg + (size_t)key * rstride + ch * 4);
+    }
+    const int kgp = tid & 15, dc = tid >> 4;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int key = 4 * kgp + u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
+      if (key < nvalid) {
+        float4 a = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8);
+        float4 b = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8 + 4);
+        v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+        v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+      }
+    }
+  }
+  __device__ __forceinline__ void store(float* k_s, float* vt_s, int tid) const {
+    constexpr int KS = Lds<float>::kStr, VS = Lds<float>::vStr;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int e = u * kThreads + tid;
+      const int key = e >> 5, ch = e & 31;
+      *reinterpret_cast<float4*>(k_s + key * KS + ch * 4) = k[u];
+    }
+    const int kgp = tid & 15, dc = tid >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float4 o = {v[0][e], v[1][e], v[2][e], v[3][e]};
+      *reinterpret_cast<float4*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = o;
+    }
+  }
+};
 
 template <typename T>
 __device__ __forceinline__ void store_out4(T* dst, const float* v);
@@ -146,25 +167,41 @@ __device__ __forceinline__ void store_out4<float>(float* dst, const float* v) {
   *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
+// Work order: blockIdx -> (query tile, head).  Consecutive workgroups on one
+// XCD (block ids are dealt round-robin over the 8 XCDs) take the heads of one
+// query tile, so heads that share a KV group reuse that XCD's L2; query tiles
+// go longest-first so the causal tail does not straggle.
+struct Work { int b, qt, hidx; bool ok; };
+__device__ __forceinline__ Work work_of(int bid, int nheads, int batch, int tiles_per_b) {
+  Work wk;
+  const int t = bid >> 3, x = bid & 7;
+  const int unit = (t / nheads) * 8 + x;
+  wk.hidx = t % nheads;
+  wk.ok = unit < batch * tiles_per_b;
+  wk.b = unit % batch;
+  wk.qt = tiles_per_b - 1 - unit / batch;
+  return wk;
+}
+
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
-    ProbDev p, const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const T* __restrict__ k_idx, const rtp_selection sel, T* __restrict__ out, float* __restrict__ lse) {
+    ProbDev p, int nheads, int tiles_per_b, const T* __restrict__ q, const T* __restrict__ k,
+    const T* __restrict__ v, const T* __restrict__ k_idx, const rtp_selection sel, T* __restrict__ out,
+    float* __restrict__ lse) {
   typedef typename Frag32<T>::type F;
   typedef typename IdxFrag<T>::type IF;
   constexpr int KS = Lds<T>::kStr, VS = Lds<T>::vStr;
-  __shared__ __attribute__((aligned(16))) T k_s[KT * KS];
-  __shared__ __attribute__((aligned(16))) T vt_s[kHeadDim * VS];
+  __shared__ __attribute__((aligned(16))) T k_s[2][KT * KS];
+  __shared__ __attribute__((aligned(16))) T vt_s[2][kHeadDim * VS];
 
-  const int tiles_per_b = (p.max_q + BQ - 1) / BQ;
-  const int b = blockIdx.x / tiles_per_b;
-  const int qt = tiles_per_b - 1 - (int)(blockIdx.x % tiles_per_b);  // longest tiles first
-  const int hidx = blockIdx.y;
+  const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b);
+  if (!wk.ok) return;
+  const int b = wk.b, hidx = wk.hidx;
   const int h = (MODE == 0) ? p.ret_heads[hidx] : p.local_heads[hidx];
   const int g = kv_of(p, h);
   const int q0 = p.cu_q[b], Lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_k[b], Lk = p.cu_k[b + 1] - k0;
-  const int i0 = qt * BQ;
+  const int i0 = wk.qt * BQ;
   if (i0 >= Lq) return;
   const int off = Lk - Lq;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -186,20 +223,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) load_frag(qf[c][kc], qp + 32 * kc);
   }
+  const int wpos_lo = off + min(i0 + 32 * w, Lq - 1);
+  const int wpos_hi = off + min(i0 + 32 * w + 31, Lq - 1);
   IF qxf[2];
-  float tau[2] = {0.f, 0.f};
+  float tau4[2] = {0.f, 0.f};
   int tie[2] = {0, 0};
+  bool exact_ties = false;
   const T* kxb = nullptr;
   if (MODE == 0) {
-    const int r = hidx;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const size_t qr = (size_t)r * p.Tq + q0 + (qok[c] ? qi[c] : Lq - 1);
+      const size_t qr = (size_t)hidx * p.Tq + q0 + (qok[c] ? qi[c] : Lq - 1);
       load_idx_frag(qxf[c], (const T*)sel.q_idx + qr * kIdxDim + 4 * grp);
-      tau[c] = sel.tau[qr];
+      tau4[c] = sel.tau[qr] * 4.f;   // compare raw dot products: dot / 4 vs tau is exact
       tie[c] = sel.tie_pos[qr];
+      exact_ties |= (tie[c] != 0x7FFFFFFF);
     }
-    kxb = k_idx + ((size_t)r * p.Tk + k0) * kIdxDim;
+    exact_ties = __builtin_amdgcn_ballot_w64(exact_ties) != 0;
+    kxb = k_idx + ((size_t)hidx * p.Tk + k0) * kIdxDim;
   }
 
   const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
@@ -210,7 +251,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- key tiles
+  // ---- key tiles of the workgroup
   const int pos_lo = off + i0;
   const int pos_hi = off + min(i0 + BQ, Lq) - 1;
   const int kt_last = pos_hi / KT;
@@ -221,117 +262,148 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
     sink_tile = (p.n_sink > 0) && (kt_first > 0);
   }
   const int ntiles = kt_last - kt_first + 1 + (sink_tile ? 1 : 0);
+  auto tile_of = [&](int t) { return (sink_tile && t == 0) ? 0 : (kt_first + t - (sink_tile ? 1 : 0)); };
+
+  Stage<T> st;
+  st.load(kg, vg, rstride, min(KT, Lk), tid);
+  st.store(k_s[0], vt_s[0], tid);
+  __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const bool sink_only = sink_tile && (t == 0);
-    const int kt = sink_only ? 0 : (kt_first + t - (sink_tile ? 1 : 0));
-    const int kbase = kt * KT;
-    __syncthreads();
-    stage_tile(k_s, vt_s, kg + (size_t)kbase * rstride, vg + (size_t)kbase * rstride, rstride,
-               min(KT, Lk - kbase), tid);
-    __syncthreads();
+    const int kbase = tile_of(t) * KT;
+    const int buf = t & 1;
+    if (t + 1 < ntiles) {
+      const int nb = tile_of(t + 1) * KT;
+      st.load(kg + (size_t)nb * rstride, vg + (size_t)nb * rstride, rstride, min(KT, Lk - nb), tid);
+    }
 
-    // membership of every (key, query) this lane holds
-    bool mem[2][4][4];
-    bool any = false;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      IF kxf;
+    // wave-uniform tile classification
+    bool skip = kbase > wpos_hi;                                    // all keys in this wave's future
+    bool need_mask = kbase + KT - 1 > wpos_lo;                      // crosses the diagonal
+    if (MODE == 1) {
+      if (sink_only) {
+        need_mask = true;
+      } else {
+        skip |= (kbase + KT - 1) < (wpos_lo - p.window + 1) && kbase >= p.n_sink;  // wholly before every window
+        need_mask |= (wpos_hi - kbase) >= p.window;                                // window edge inside
+      }
+    }
+    if (!skip) {
+      IF kxf[4];
       if (MODE == 0) {
-        const int key = kbase + 16 * ks + col;
-        if (key < Lk) {
-          load_idx_frag(kxf, kxb + (size_t)key * kIdxDim + 4 * grp);
-        } else {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) kxf.v[j] = 0;
+        for (int ks = 0; ks < 4; ++ks) {
+          const int key = kbase + 16 * ks + col;
+          if (key < Lk) {
+            load_idx_frag(kxf[ks], kxb + (size_t)key * kIdxDim + 4 * grp);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) kxf[ks].v[j] = 0;
+          }
         }
       }
+      // S^T = K Q^T
+      f32x4 sacc[2][4];
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) sacc[c][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T* kt_s = k_s[buf];
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          F kf;
+          load_frag(kf, kt_s + (16 * ks + col) * KS + 32 * kc + 8 * grp);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) sacc[c][ks] = mma_k32(kf, qf[c][kc], sacc[c][ks]);
+        }
+      }
+      // membership
+      if (MODE == 0) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const f32x4 dx = idx_dot_tile(kxf[ks], qxf[c]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kbase + 16 * ks + 4 * grp + i;
+              bool ok = exact_ties ? (dx[i] > tau4[c] || (dx[i] == tau4[c] && key <= tie[c])) : (dx[i] >= tau4[c]);
+              if (need_mask) ok = ok && qok[c] && key <= qpos[c];
+              sacc[c][ks][i] = ok ? sacc[c][ks][i] : -INFINITY;
+            }
+          }
+        }
+      } else if (need_mask) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int key = kbase + 16 * ks + 4 * grp + i;
+              const bool is_sink = key < p.n_sink;
+              const bool in_win = (qpos[c] - key) < p.window;
+              bool ok = qok[c] && key <= qpos[c] && (sink_only ? is_sink : (in_win || is_sink));
+              sacc[c][ks][i] = ok ? sacc[c][ks][i] : -INFINITY;
+            }
+      }
+
+      // online softmax (log2 domain)
+      F pf[2][2];
+      bool live = false;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        f32x4 sx;
-        if (MODE == 0) sx = idx_dot_tile(kxf, qxf[c]);
+        float tmax = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kbase + 16 * ks + 4 * grp + i;
-          bool ok = qok[c] && key <= qpos[c];
-          if (MODE == 0) {
-            const float s = idx_score(sx[i]);
-            ok = ok && (s > tau[c] || (s == tau[c] && key <= tie[c]));
-          } else {
-            const bool in_win = (qpos[c] - key) < p.window;
-            const bool is_sink = key < p.n_sink;
-            ok = ok && (sink_only ? is_sink : (in_win || is_sink));
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[c][ks][i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float mnew = fmaxf(m_[c], tmax * sl2);
+        live |= (mnew != -INFINITY);
+        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+        const float alpha = __builtin_amdgcn_exp2f(m_[c] - muse);
+        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+          l_[c] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) oacc[c][dt] *= alpha;
+        }
+        float ps = 0.f;
+        float x[4][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[c][ks][i], sl2, -muse));
+            ps += x[ks][i];
           }
-          mem[c][ks][i] = ok;
-          any |= ok;
+        l_[c] += ps;
+        m_[c] = mnew;
+        make_pfrag(pf[c][0], x[0], x[1]);
+        make_pfrag(pf[c][1], x[2], x[3]);
+      }
+
+      // O^T += V^T P^T
+      if (__builtin_amdgcn_ballot_w64(live)) {
+        const T* vtt = vt_s[buf];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) {
+            F vf;
+            load_vfrag(vf, vtt + (16 * dt + col) * VS + 32 * kk + 4 * grp);
+#pragma unroll
+            for (int c = 0; c < 2; ++c) oacc[c][dt] = mma_k32(vf, pf[c][kk], oacc[c][dt]);
+          }
         }
       }
     }
-    if (!__builtin_amdgcn_ballot_w64(any)) continue;
-
-    // S^T = K Q^T
-    f32x4 sacc[2][4];
-#pragma unroll
-    for (int c = 0; c < 2; ++c)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sacc[c][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        F kf;
-        load_frag(kf, k_s + (16 * ks + col) * KS + 32 * kc + 8 * grp);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) sacc[c][ks] = mma_k32(kf, qf[c][kc], sacc[c][ks]);
-      }
-    }
-
-    // online softmax (log2 domain)
-    F pf[2][2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      float x[4][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[ks][i] = mem[c][ks][i] ? sacc[c][ks][i] * sl2 : -INFINITY;
-          tmax = fmaxf(tmax, x[ks][i]);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(m_[c], tmax);
-      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = __builtin_amdgcn_exp2f(m_[c] - muse);
-      l_[c] *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) oacc[c][dt] *= alpha;
-      float ps = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[ks][i] = __builtin_amdgcn_exp2f(x[ks][i] - muse);
-          ps += x[ks][i];
-        }
-      l_[c] += ps;
-      m_[c] = mnew;
-      make_pfrag(pf[c][0], x[0], x[1]);
-      make_pfrag(pf[c][1], x[2], x[3]);
-    }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        F vf;
-        load_vfrag(vf, vt_s + (16 * dt + col) * VS + 32 * kk + 4 * grp);
-#pragma unroll
-        for (int c = 0; c < 2; ++c) oacc[c][dt] = mma_k32(vf, pf[c][kk], oacc[c][dt]);
-      }
-    }
+    if (t + 1 < ntiles) st.store(k_s[buf ^ 1], vt_s[buf ^ 1], tid);
+    __syncthreads();
   }
 
   // ---- normalise and store
@@ -362,24 +434,19 @@ hipError_t launch_attn_prefill(const ProbDev& p, bool bf16, int mode, const void
   const int nheads = (mode == 0) ? p.R : p.n_local;
   if (nheads == 0 || p.Tq == 0) return hipSuccess;
   const int tiles_per_b = (p.max_q + BQ - 1) / BQ;
-  dim3 grid(tiles_per_b * p.batch, nheads);
+  const int units = tiles_per_b * p.batch;
+  dim3 grid((unsigned)(((units + 7) / 8) * 8 * nheads));
   rtp_selection sl = {};
   if (sel) sl = *sel;
+#define RTP_LAUNCH(TT, MM)                                                                                    \
+  hipLaunchKernelGGL((attn_prefill_kernel<TT, MM>), grid, dim3(kThreads), 0, s, p, nheads, tiles_per_b,       \
+                     (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)k_idx, sl, (TT*)out, lse)
   if (bf16) {
-    if (mode == 0)
-      hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 0>), grid, dim3(kThreads), 0, s, p, (const bf16_t*)q,
-                         (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)k_idx, sl, (bf16_t*)out, lse);
-    else
-      hipLaunchKernelGGL((attn_prefill_kernel<bf16_t, 1>), grid, dim3(kThreads), 0, s, p, (const bf16_t*)q,
-                         (const bf16_t*)k, (const bf16_t*)v, (const bf16_t*)k_idx, sl, (bf16_t*)out, lse);
+    if (mode == 0) RTP_LAUNCH(bf16_t, 0); else RTP_LAUNCH(bf16_t, 1);
   } else {
-    if (mode == 0)
-      hipLaunchKernelGGL((attn_prefill_kernel<float, 0>), grid, dim3(kThreads), 0, s, p, (const float*)q,
-                         (const float*)k, (const float*)v, (const float*)k_idx, sl, (float*)out, lse);
-    else
-      hipLaunchKernelGGL((attn_prefill_kernel<float, 1>), grid, dim3(kThreads), 0, s, p, (const float*)q,
-                         (const float*)k, (const float*)v, (const float*)k_idx, sl, (float*)out, lse);
+    if (mode == 0) RTP_LAUNCH(float, 0); else RTP_LAUNCH(float, 1);
   }
+#undef RTP_LAUNCH
   return hipGetLastError();
 }
 

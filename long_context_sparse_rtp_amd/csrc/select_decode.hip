@@ -392,6 +392,8 @@ __global__ __launch_bounds__(kThreads) void select_decode_kernel(
         tau_s = sv[j];
         tie_s = (int)(uint32_t)(cand_s[i] & 0xFFFFFFFFull);
         count_s = (int)cabove_s + i + 1;
+        // the candidates hold every token scoring exactly tau: if none is left out, S = {s >= tau}
+        if (!(i + 1 < nc && (uint32_t)(cand_s[i + 1] >> 32) == (uint32_t)(cand_s[i] >> 32))) tie_s = 0x7FFFFFFF;
       }
       pre += mj;
     }

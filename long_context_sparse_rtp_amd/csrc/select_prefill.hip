@@ -5,7 +5,8 @@
 // prefix n <= pos, softmax of s_n = q_idx . k_idx_n / 4, keys by descending
 // score (ties: ascending position), the smallest prefix whose mass reaches p.
 // The result of a row is (tau, tie_pos, count): S = {s > tau} U {s == tau,
-// n <= tie_pos}.  Lists are never materialised (a 128K prefill would need
+// n <= tie_pos}; tie_pos = INT_MAX when no token scoring exactly tau is left
+// out, so that S = {s >= tau}.  Lists are never materialised (a 128K prefill would need
 // ~10^10 entries per head).
 //
 // A workgroup (4 wave64s) owns 16 query rows of one retrieval head; the rows
@@ -345,6 +346,10 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
           rc.tau = __uint_as_float((kk & 0x80000000u) ? (kk & 0x7FFFFFFFu) : ~kk);
           rc.tie = (int)(uint32_t)(cd[jstar] & 0xFFFFFFFFull);
           rc.count = (int)cbetter_s[tid] + jstar + 1;
+          // every token scoring exactly tau is a candidate unless the position key was needed;
+          // if none of them is left out, the set is simply {s >= tau}
+          const bool excluded = (jstar + 1 < nc) && ((uint32_t)(cd[jstar + 1] >> 32) == (uint32_t)(cd[jstar] >> 32));
+          if (rc.kind < 2 && !excluded) rc.tie = 0x7FFFFFFF;
         }
         rc.phase = PH_DONE;
       }

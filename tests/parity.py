@@ -119,27 +119,37 @@ def check_retrieval_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.nda
     t = res.topp
     pos = pr.pos_of(b, i)
     tie = int(g["tie"][r, qi])
+    INT_MAX = 2 ** 31 - 1
     if p >= 1.0:
         G_list = [np.arange(pos + 1)]
     else:
-        if not (0 <= tie <= pos):
+        if not (0 <= tie <= pos or tie == INT_MAX):
             return False, {"why": f"tie_pos {tie} outside [0, {pos}]"}
         eps = _amb_eps(res.q_idx, pr.index_keys(b, r)[: pos + 1])
         s = t.scores
         n = np.arange(s.size)
-        # the crossing token is at tie_pos; tokens with exactly its score are admitted
-        # by position, as the threshold rule says
-        same = s == s[tie]
-        sure = np.nonzero((s > tau + eps) & ~same | (same & (n <= tie)))[0]
+        if tie != INT_MAX:
+            # the crossing token is at tie_pos; tokens with exactly its score are
+            # admitted by position, as the threshold rule says
+            same = s == s[tie]
+        else:
+            same = np.zeros(s.size, dtype=bool)
+        sure = np.nonzero(((s > tau + eps) & ~same) | (same & (n <= tie)))[0]
         amb = np.nonzero((np.abs(s - tau) <= eps) & ~same)[0]
         k_amb = count - sure.size
         info.update(n_amb=int(amb.size))
         if k_amb < 0 or k_amb > amb.size:
             return False, {"why": f"count {count} inconsistent (sure {sure.size}, amb {amb.size})"}
-        if math.comb(amb.size, k_amb) > 256:
+        # tokens with equal float64 scores (equal index keys) share their float32 score,
+        # so under {s >= tau} they are in or out together
+        vals, inv = np.unique(s[amb], return_inverse=True)
+        groups = [amb[inv == j] for j in range(vals.size)]
+        sizes = [gg.size for gg in groups]
+        combos = [c for kk in range(len(groups) + 1) for c in itertools.combinations(range(len(groups)), kk)
+                  if sum(sizes[j] for j in c) == k_amb] if len(groups) <= 12 else None
+        if combos is None or len(combos) > 256:
             return False, {"why": f"too many ambiguous tokens ({amb.size})"}
-        G_list = [np.sort(np.concatenate([sure, np.array(c, dtype=np.int64)]))
-                  for c in itertools.combinations(amb.tolist(), k_amb)]
+        G_list = [np.sort(np.concatenate([sure] + [groups[j] for j in c])).astype(np.int64) for c in combos]
     pr_k = pr._kv("k", b, pr.kv_of(h))
     pr_v = pr._kv("v", b, pr.kv_of(h))
     qv = pr.q_row(qi, h)
