@@ -11,8 +11,11 @@
 //
 // The pages give few details of their prefill kernel (retrieval heads run
 // dense there); this one is a flash-attention style loop written for gfx950:
-//   - workgroup = 4 wave64s, 128 query rows (32 per wave as two 16-column
-//     MFMA tiles), 64-key tiles;
+//   - workgroup = 8 wave64s, 256 query rows (32 per wave as two 16-column
+//     MFMA tiles), 64-key tiles: every staged K/V tile feeds 256 queries, which
+//     halves the re-reads of the causal K/V prefix against 128-row tiles;
+//   - the next tile's K/V is loaded into registers while the current one is
+//     computed and written to the other half of a double-buffered LDS;
 //   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (f32 path: 16x16x4 steps), K
 //     tile staged row-major in LDS; the S^T output layout (a lane holds 4 keys
 //     of one query column) is already the B-operand layout of O^T = V^T P^T,
@@ -29,9 +32,9 @@ namespace rtp {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BQ = 128;
-constexpr int KT = 64;
+constexpr int kThreads = 512;   // 8 wave64s
+constexpr int BQ = 256;         // query rows per workgroup (32 per wave)
+constexpr int KT = 64;          // keys per tile
 
 template <typename T> struct Lds;
 template <> struct Lds<bf16_t> { static constexpr int kStr = 128 + 8; static constexpr int vStr = 64 + 4; };
@@ -68,20 +71,23 @@ __device__ __forceinline__ void load_vfrag(FragF32& f, const float* rowp) {
 // ---- staging of one 64-key tile: global -> registers (issued early, one tile
 // ahead) -> LDS (K row-major, V transposed)
 template <typename T> struct Stage;
+// bf16: K as 16-byte row chunks (16 lanes per key row); V as pairs of keys x 8
+// dims, written transposed as packed key pairs.
 template <> struct Stage<bf16_t> {
-  uint4 k[4], v[4];
+  static constexpr int kU = KT * kHeadDim / 8 / kThreads;   // 16-byte K chunks per thread
+  uint4 k[kU], v[2];
   __device__ __forceinline__ void load(const bf16_t* kg, const bf16_t* vg, size_t rstride, int nvalid, int tid) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int e = u * kThreads + tid;
       const int key = e >> 4, ch = e & 15;
       k[u] = {0u, 0u, 0u, 0u};
       if (key < nvalid) k[u] = *reinterpret_cast<const uint4*>(kg + (size_t)key * rstride + ch * 8);
     }
-    const int kgp = tid & 15, dc = tid >> 4;
+    const int kp = tid & 31, dc = tid >> 5;   // keys 2kp, 2kp+1; dims 8dc..8dc+7
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = 4 * kgp + u;
+    for (int u = 0; u < 2; ++u) {
+      const int key = 2 * kp + u;
       v[u] = {0u, 0u, 0u, 0u};
       if (key < nvalid) v[u] = *reinterpret_cast<const uint4*>(vg + (size_t)key * rstride + dc * 8);
     }
@@ -89,43 +95,36 @@ template <> struct Stage<bf16_t> {
   __device__ __forceinline__ void store(bf16_t* k_s, bf16_t* vt_s, int tid) const {
     constexpr int KS = Lds<bf16_t>::kStr, VS = Lds<bf16_t>::vStr;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int e = u * kThreads + tid;
       const int key = e >> 4, ch = e & 15;
       *reinterpret_cast<uint4*>(k_s + key * KS + ch * 8) = k[u];
     }
-    const int kgp = tid & 15, dc = tid >> 4;
+    const int kp = tid & 31, dc = tid >> 5;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const uint32_t w0 = (&v[0].x)[e >> 1], w1 = (&v[1].x)[e >> 1];
-      const uint32_t w2 = (&v[2].x)[e >> 1], w3 = (&v[3].x)[e >> 1];
-      uint2 out;
-      if (e & 1) {
-        out.x = (w0 >> 16) | (w1 & 0xFFFF0000u);
-        out.y = (w2 >> 16) | (w3 & 0xFFFF0000u);
-      } else {
-        out.x = (w0 & 0xFFFFu) | (w1 << 16);
-        out.y = (w2 & 0xFFFFu) | (w3 << 16);
-      }
-      *reinterpret_cast<uint2*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = out;
+      const uint32_t pr = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+      *reinterpret_cast<uint32_t*>(vt_s + (8 * dc + e) * VS + 2 * kp) = pr;
     }
   }
 };
 template <> struct Stage<float> {
-  float4 k[8];
-  float v[4][8];
+  static constexpr int kU = KT * kHeadDim / 4 / kThreads;   // 16-byte K chunks per thread
+  float4 k[kU];
+  float v[2][8];
   __device__ __forceinline__ void load(const float* kg, const float* vg, size_t rstride, int nvalid, int tid) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int e = u * kThreads + tid;
       const int key = e >> 5, ch = e & 31;
       k[u] = {0.f, 0.f, 0.f, 0.f};
       if (key < nvalid) k[u] = *reinterpret_cast<const float4*>(kg + (size_t)key * rstride + ch * 4);
     }
-    const int kgp = tid & 15, dc = tid >> 4;
+    const int kp = tid & 31, dc = tid >> 5;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = 4 * kgp + u;
+    for (int u = 0; u < 2; ++u) {
+      const int key = 2 * kp + u;
 #pragma unroll
       for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
       if (key < nvalid) {
@@ -139,16 +138,16 @@ template <> struct Stage<float> {
   __device__ __forceinline__ void store(float* k_s, float* vt_s, int tid) const {
     constexpr int KS = Lds<float>::kStr, VS = Lds<float>::vStr;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kU; ++u) {
       const int e = u * kThreads + tid;
       const int key = e >> 5, ch = e & 31;
       *reinterpret_cast<float4*>(k_s + key * KS + ch * 4) = k[u];
     }
-    const int kgp = tid & 15, dc = tid >> 4;
+    const int kp = tid & 31, dc = tid >> 5;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      float4 o = {v[0][e], v[1][e], v[2][e], v[3][e]};
-      *reinterpret_cast<float4*>(vt_s + (8 * dc + e) * VS + 4 * kgp) = o;
+      float2 o = {v[0][e], v[1][e]};
+      *reinterpret_cast<float2*>(vt_s + (8 * dc + e) * VS + 2 * kp) = o;
     }
   }
 };
@@ -184,7 +183,7 @@ __device__ __forceinline__ Work work_of(int bid, int nheads, int batch, int tile
 }
 
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     ProbDev p, int nheads, int tiles_per_b, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ k_idx, const rtp_selection sel, T* __restrict__ out,
     float* __restrict__ lse) {
@@ -265,7 +264,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_prefill_kernel(
   auto tile_of = [&](int t) { return (sink_tile && t == 0) ? 0 : (kt_first + t - (sink_tile ? 1 : 0)); };
 
   Stage<T> st;
-  st.load(kg, vg, rstride, min(KT, Lk), tid);
+  {
+    const int fb = tile_of(0) * KT;
+    st.load(kg + (size_t)fb * rstride, vg + (size_t)fb * rstride, rstride, min(KT, Lk - fb), tid);
+  }
   st.store(k_s[0], vt_s[0], tid);
   __syncthreads();
 

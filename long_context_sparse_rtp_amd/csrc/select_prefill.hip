@@ -6,8 +6,8 @@
 // score (ties: ascending position), the smallest prefix whose mass reaches p.
 // The result of a row is (tau, tie_pos, count): S = {s > tau} U {s == tau,
 // n <= tie_pos}; tie_pos = INT_MAX when no token scoring exactly tau is left
-// out, so that S = {s >= tau}.  Lists are never materialised (a 128K prefill would need
-// ~10^10 entries per head).
+// out, so that S = {s >= tau}.  Lists are never materialised (a 128K prefill
+// would need ~10^10 entries per head).
 //
 // A workgroup (4 wave64s) owns 16 query rows of one retrieval head; the rows
 // are the 16 columns of the shared MFMA indexer tile and the four waves take
@@ -15,19 +15,22 @@
 // each sweep over the keys recomputes them with the same MFMA, so every sweep
 // (and the attention kernel) sees identical float32 values.
 //
-// Per token the sweeps use
-//   y    = (s - top) * log2(e)   top >= max s (Cauchy-Schwarz bound, or the
-//                                 exact row max after a rebase)
-//   mass = 2^y as 32-bit fixed point, summed in 64-bit LDS integers (exact,
-//          order-independent: results do not depend on wave interleaving)
-//   K    = floor(-y * 2^20) saturated to 32 bits (monotone in s)
-// Sweep 1 histograms the mass over 256 bins of K >> 16 (16 per octave, the
-// last one open-ended) and scans for the bin where the cumulative mass reaches
-// p * Z.  Refinement sweeps histogram (mass, count) over the next 8 bits of K
-// inside the chosen range until the crossing range holds at most 128 tokens;
-// a collect sweep then gathers them, they are sorted by (score desc, position
-// asc) and the crossing token gives tau and tie_pos.  Exact ties too large to
-// collect switch the key to the score's bit pattern and then to the position.
+// Per token the sweeps use one FMA of the raw indexer dot product:
+//   u    = (top - s) * log2(e) * 16   sixteenths of an octave below top
+//          (top >= max s: a Cauchy-Schwarz bound, or a rebased one)
+//   mass = 2^(-u/16) as 31-bit fixed point, summed in 64-bit LDS integers
+//          (exact and order-independent: the result is deterministic)
+//   K    = floor(u * 2^16) clamped to 32 bits (the same FMA with both
+//          operands scaled by 2^16, so K >> 16 == floor(u) exactly)
+// Sweep 1 histograms the mass over 256 bins of floor(u) (the last one open-
+// ended) and scans for the bin where the cumulative mass reaches p * Z.
+// Refinement sweeps histogram (mass, count) over the next 8 bits of K inside
+// the chosen range (counting the tokens above it on the first pass) until the
+// crossing range holds at most 128 tokens; a collect sweep then gathers them,
+// they are sorted by (score desc, position asc) and the crossing token gives
+// tau and tie_pos.  Exact ties too large to collect switch the key to the
+// score's bit pattern and then to the position (general path, degenerate
+// inputs only).
 #include "common.h"
 #include "kernels.h"
 
@@ -39,6 +42,7 @@ constexpr int kThreads = 256;
 constexpr int kRows = 16;
 constexpr int kNB = 256;
 constexpr int kCap = 128;
+constexpr float kMaxK = 4294967040.f;      // largest float below 2^32
 
 enum { PH_HIST1 = 0, PH_REFINE = 1, PH_COLLECT = 2, PH_DONE = 3 };
 
@@ -46,6 +50,10 @@ __device__ __forceinline__ uint32_t desc_key(float s) {
   uint32_t u = __float_as_uint(s);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ~u;
+}
+__device__ __forceinline__ float undesc_key(uint32_t k) {
+  const uint32_t a = ~k;
+  return __uint_as_float((a & 0x80000000u) ? (a & 0x7FFFFFFFu) : ~a);
 }
 
 struct RowCtl {
@@ -58,10 +66,26 @@ struct RowCtl {
   int sh;                     // digit shift of the range
   int phase, kind;
   int pos;
+  uint32_t cabove;            // tokens strictly better than the range
+  int counted;                // cabove holds the count above the first-level bin
   float tau;
   int tie, count;
-  float smax;
 };
+
+// Per-lane constants of a row for one sweep.
+struct RowK {
+  float a20, b20;   // u20 = fma(dot, a20, b20); u16 = fma(dot, a20 / 2^16, b20 / 2^16)
+  float lo_f, hi_f; // float range of u20 for the fast range test
+  uint32_t lo;
+  int sh, kind, pos;
+  uint32_t kfix, dfix;
+  bool fast;        // the float range test is exact
+};
+
+__device__ __forceinline__ uint32_t key20(float u20) { return (uint32_t)__builtin_amdgcn_fmed3f(u20, 0.f, kMaxK); }
+__device__ __forceinline__ uint32_t mass31(float u16) {
+  return (uint32_t)(__builtin_amdgcn_exp2f(u16 * -0.0625f) * 2147483648.f);
+}
 
 __global__ void kidx_norm_clear(uint32_t* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -96,8 +120,8 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
     const float* __restrict__ top_p, rtp_selection sel, const uint32_t* __restrict__ kn2) {
   typedef typename IdxFrag<T>::type IF;
   const int tiles_per_b = (p.max_q + kRows - 1) / kRows;
-  const int b = blockIdx.x / tiles_per_b;
-  const int qt = tiles_per_b - 1 - (int)(blockIdx.x % tiles_per_b);  // longest rows first
+  const int b = blockIdx.x % p.batch;
+  const int qt = tiles_per_b - 1 - (int)(blockIdx.x / p.batch);  // longest rows first
   const int r = blockIdx.y;
   const int q0 = p.cu_q[b], Lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_k[b], Lk = p.cu_k[b + 1] - k0;
@@ -109,16 +133,16 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
 
   __shared__ T qidx_s[kRows][kIdxDim];
   __shared__ RowCtl ctl[kRows];
-  __shared__ unsigned long long hm_s[kNB][kRows];     // mass, or candidates (aliased)
+  __shared__ unsigned long long hm_s[kNB][kRows];     // masses, or candidates (aliased)
   __shared__ uint32_t hc_s[kNB][kRows];               // counts
   __shared__ int ccount_s[kRows];
   __shared__ uint32_t cbetter_s[kRows];
-  __shared__ float smax_s[4][kRows];
-  __shared__ int any_s;
+  __shared__ int sweep_s;
   unsigned long long* cand = &hm_s[0][0];             // [kRows][kCap] during a collect sweep
   static_assert(kRows * kCap <= kNB * kRows, "candidate buffer must fit in the histogram");
 
-  // ---- indexer queries of the 16 rows (float64, fixed order, rounded once)
+  // ---- indexer queries of the 16 rows (float64, fixed order, rounded once);
+  // rows past the end repeat the last row and are not written back
   {
     const int rr = tid >> 4, j = tid & 15;
     const int i = min(i0 + rr, Lq - 1);
@@ -133,8 +157,7 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
   __syncthreads();
   if (tid < kRows) {
     RowCtl& c = ctl[tid];
-    const int i = i0 + tid;
-    c.pos = (i < Lq) ? off + i : -1;
+    c.pos = off + min(i0 + tid, Lq - 1);
     c.pval = top_p[b];
     float qn = 0.f;
 #pragma unroll
@@ -145,120 +168,177 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
     const float kn = __uint_as_float(kn2[r * p.batch + b]);
     c.top = sqrtf(qn * kn) * 0.25f * 1.0009765625f + 1e-30f;
     c.above = 0ull;
+    c.cabove = 0u;
+    c.counted = 0;
     c.lo = 0u; c.sh = 16; c.kind = 0; c.kfix = 0u; c.dfix = 0u;
-    c.smax = -INFINITY;
-    c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = (c.pos >= 0) ? c.pos + 1 : 0;
+    c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = c.pos + 1;
     c.target = 1.0;
-    if (c.pos < 0) {
-      c.phase = PH_DONE;
-    } else if (!(c.pval < 1.f)) {
-      c.phase = PH_DONE;
-      c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = c.pos + 1;
-    } else {
-      c.phase = PH_HIST1;
-    }
+    c.phase = (c.pval < 1.f) ? PH_HIST1 : PH_DONE;   // p >= 1 (or NaN): every key
   }
   __syncthreads();
 
   IF qxf;
   load_idx_frag(qxf, &qidx_s[col][4 * grp]);
   const T* kxb = k_idx + ((size_t)r * p.Tk + k0) * kIdxDim;
+  const int p0 = off + i0;                           // smallest position of the 16 rows
   const int pos_hi = off + min(i0 + kRows, Lq) - 1;
   const int ntile = pos_hi / 16 + 1;
+  const int nfull = p0 / 16;                         // tiles entirely below every row's position
+
+  auto tile_dot = [&](int t) -> f32x4 {
+    IF kxf;
+    const int key = 16 * t + col;
+    if (key < Lk) {
+      load_idx_frag(kxf, kxb + (size_t)key * kIdxDim + 4 * grp);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kxf.v[j] = 0;
+    }
+    return idx_dot_tile(kxf, qxf);
+  };
 
   for (int iter = 0; iter < 64; ++iter) {
-    // ---- which kind of sweep: every row taking part is in the same phase, so the
-    // candidate buffer can share LDS with the histograms
     if (tid == 0) {
       int k = PH_DONE;
       for (int rr = 0; rr < kRows; ++rr) k = min(k, ctl[rr].phase);
-      any_s = k;
+      sweep_s = k;
     }
     __syncthreads();
-    const int sweep = any_s;
+    const int sweep = sweep_s;
     if (sweep == PH_DONE) break;
-    const RowCtl c = ctl[col];
-    const bool active = (c.phase == sweep);
-    // clear the histograms / candidate counters
+    // per-lane constants of this lane's row
+    RowK rk;
+    {
+      const RowCtl& c = ctl[col];
+      const bool active = c.phase == sweep;
+      rk.a20 = -kLog2e * 4.f * 65536.f;            // -(log2(e) / 4) * 16 * 2^16
+      rk.b20 = c.top * kLog2e * 16.f * 65536.f;
+      rk.lo = c.lo;
+      rk.sh = c.sh;
+      rk.kind = c.kind;
+      rk.kfix = c.kfix;
+      rk.dfix = c.dfix;
+      rk.pos = active ? c.pos : -1;
+      const int width = (sweep == PH_REFINE) ? c.sh + 8 : c.sh;
+      // the float test of K's range is exact when both ends are multiples of 256 below 2^32
+      rk.fast = (c.kind == 0) && (width >= 8);
+      rk.lo_f = (c.lo == 0u) ? -INFINITY : (float)c.lo;
+      const double hi = (double)c.lo + (double)(1ull << min(width, 32));
+      rk.hi_f = (hi >= 4294967040.0) ? INFINITY : (float)hi;
+    }
     for (int e = tid; e < kNB * kRows; e += kThreads) { (&hm_s[0][0])[e] = 0ull; (&hc_s[0][0])[e] = 0u; }
     if (tid < kRows) { ccount_s[tid] = 0; cbetter_s[tid] = 0u; }
     __syncthreads();
 
-    const float c1 = kLog2e * 0.25f;        // y = dot * c1 - top * log2e
-    const float c0 = -c.top * kLog2e;
-    const int width_sh = (sweep == PH_REFINE) ? (c.sh + 8) : c.sh;
-    const int lim = active ? c.pos : -1;    // keys n <= lim take part
-    float smax = -INFINITY;
+    const bool all_fast = __builtin_amdgcn_ballot_w64(!rk.fast) == 0;
+    const float a16 = rk.a20 * (1.f / 65536.f), b16 = rk.b20 * (1.f / 65536.f);
     uint32_t better = 0u;
 
-    for (int t = w; t < ntile; t += 4) {
-      const int kb = 16 * t;
-      IF kxf;
-      const int keyA = kb + col;
-      if (keyA < Lk) {
-        load_idx_frag(kxf, kxb + (size_t)keyA * kIdxDim + 4 * grp);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) kxf.v[j] = 0;
-      }
-      const f32x4 dot = idx_dot_tile(kxf, qxf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = kb + 4 * grp + i;
-        if (n > lim) continue;  // causal, and rows not in this sweep
-        const float y = fmaf(dot[i], c1, c0);
-        const uint32_t K = (uint32_t)__builtin_amdgcn_fmed3f(-y * 1048576.f, 0.f, 4294967040.f);
-        if (sweep == PH_HIST1) {
-          smax = fmaxf(smax, dot[i]);
-          const uint32_t bin = min(K >> 16, (uint32_t)(kNB - 1));
-          const float m = __builtin_amdgcn_exp2f(y);
-          const uint32_t mf = (uint32_t)fminf(m * 4294967296.f, 4294967040.f);
-          atomicAdd(&hm_s[bin][col], (unsigned long long)mf);
-          continue;
-        }
-        uint32_t key = K;
-        bool ok = true;
-        const float s = idx_score(dot[i]);
-        if (c.kind >= 1) {
-          const uint32_t dk = desc_key(s);
-          ok = (K == c.kfix);
-          if (c.kind == 1) {
-            key = dk;
-          } else {
-            ok = ok && (dk == c.dfix);
-            key = (uint32_t)n;
-          }
-          if (sweep == PH_COLLECT) {
-            const bool bt = (K < c.kfix) ||
-                            (K == c.kfix && (c.kind == 1 ? dk < c.lo
-                                                         : (dk < c.dfix || (dk == c.dfix && (uint32_t)n < c.lo))));
-            better += bt ? 1u : 0u;
-          }
-        } else if (sweep == PH_COLLECT) {
-          better += (K < c.lo) ? 1u : 0u;
-        }
-        const uint32_t dk2 = key - c.lo;
-        const bool inr = ok && ((width_sh >= 32) ? (key >= c.lo) : ((dk2 >> width_sh) == 0u));
-        if (!inr) continue;
-        if (sweep == PH_REFINE) {
-          const uint32_t dig = dk2 >> c.sh;
-          const float m = __builtin_amdgcn_exp2f(y);
-          const uint32_t mf = (uint32_t)fminf(m * 4294967296.f, 4294967040.f);
-          atomicAdd(&hm_s[dig][col], (unsigned long long)mf);
-          atomicAdd(&hc_s[dig][col], 1u);
-        } else {
-          const int slot = atomicAdd(&ccount_s[col], 1);
-          if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
-        }
-      }
-    }
-    // per-row reductions of this sweep
     if (sweep == PH_HIST1) {
-      smax = fmaxf(smax, __shfl_xor(smax, 16));
-      smax = fmaxf(smax, __shfl_xor(smax, 32));
-      if (grp == 0) smax_s[w][col] = smax;
+      auto body = [&](const f32x4& d, int t, bool check) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * t + 4 * grp + i;
+          if (check && n > rk.pos) continue;
+          const float u16 = fmaf(d[i], a16, b16);
+          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u16, 0.f, (float)(kNB - 1));
+          atomicAdd(&hm_s[bin][col], (unsigned long long)mass31(u16));
+        }
+      };
+      int t = w;
+      for (; t + 4 < nfull; t += 8) {
+        const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + 4);
+        body(d0, t, false);
+        body(d1, t + 4, false);
+      }
+      for (; t < ntile; t += 4) body(tile_dot(t), t, t >= nfull);
+    } else if (sweep == PH_REFINE && all_fast) {
+      auto body = [&](const f32x4& d, int t, bool check) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * t + 4 * grp + i;
+          if (check && n > rk.pos) continue;
+          const float u20 = fmaf(d[i], rk.a20, rk.b20);
+          better += (u20 < rk.lo_f) ? 1u : 0u;
+          if (u20 >= rk.lo_f && u20 < rk.hi_f) {
+            const uint32_t dig = (key20(u20) - rk.lo) >> rk.sh;
+            atomicAdd(&hm_s[dig][col], (unsigned long long)mass31(u20 * (1.f / 65536.f)));
+            atomicAdd(&hc_s[dig][col], 1u);
+          }
+        }
+      };
+      int t = w;
+      for (; t + 4 < nfull; t += 8) {
+        const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + 4);
+        body(d0, t, false);
+        body(d1, t + 4, false);
+      }
+      for (; t < ntile; t += 4) body(tile_dot(t), t, t >= nfull);
+    } else if (sweep == PH_COLLECT && all_fast) {
+      auto body = [&](const f32x4& d, int t, bool check) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * t + 4 * grp + i;
+          if (check && n > rk.pos) continue;
+          const float u20 = fmaf(d[i], rk.a20, rk.b20);
+          if (u20 >= rk.lo_f && u20 < rk.hi_f) {
+            const int slot = atomicAdd(&ccount_s[col], 1);
+            if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(idx_score(d[i])) << 32) | (uint32_t)n;
+          }
+        }
+      };
+      int t = w;
+      for (; t + 4 < nfull; t += 8) {
+        const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + 4);
+        body(d0, t, false);
+        body(d1, t + 4, false);
+      }
+      for (; t < ntile; t += 4) body(tile_dot(t), t, t >= nfull);
+    } else {
+      // general path: integer keys and the tie key spaces
+      for (int t = w; t < ntile; t += 4) {
+        const f32x4 d = tile_dot(t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = 16 * t + 4 * grp + i;
+          if (n > rk.pos) continue;
+          const float u20 = fmaf(d[i], rk.a20, rk.b20);
+          const uint32_t K = key20(u20);
+          const float s = idx_score(d[i]);
+          uint32_t key = K;
+          bool ok = true;
+          bool bt;
+          if (rk.kind >= 1) {
+            const uint32_t dk = desc_key(s);
+            ok = (K == rk.kfix);
+            if (rk.kind == 1) {
+              key = dk;
+              bt = (K < rk.kfix) || (K == rk.kfix && dk < rk.lo);
+            } else {
+              ok = ok && (dk == rk.dfix);
+              key = (uint32_t)n;
+              bt = (K < rk.kfix) || (K == rk.kfix && (dk < rk.dfix || (dk == rk.dfix && (uint32_t)n < rk.lo)));
+            }
+          } else {
+            bt = K < rk.lo;
+          }
+          const int width = (sweep == PH_REFINE) ? rk.sh + 8 : rk.sh;
+          const uint32_t dk2 = key - rk.lo;
+          const bool inr = ok && ((width >= 32) ? (key >= rk.lo) : ((dk2 >> width) == 0u));
+          if (sweep == PH_REFINE) better += bt ? 1u : 0u;
+          if (!inr) continue;
+          if (sweep == PH_REFINE) {
+            const uint32_t dig = dk2 >> rk.sh;
+            atomicAdd(&hm_s[dig][col], (unsigned long long)mass31(u20 * (1.f / 65536.f)));
+            atomicAdd(&hc_s[dig][col], 1u);
+          } else {
+            const int slot = atomicAdd(&ccount_s[col], 1);
+            if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
+          }
+        }
+      }
     }
-    if (sweep == PH_COLLECT) {
+    if (sweep == PH_REFINE) {
       better += __shfl_xor(better, 16);
       better += __shfl_xor(better, 32);
       if (grp == 0) atomicAdd(&cbetter_s[col], better);
@@ -269,14 +349,19 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
     if (tid < kRows && ctl[tid].phase == sweep) {
       RowCtl& rc = ctl[tid];
       if (rc.phase == PH_HIST1) {
-        float sm = fmaxf(fmaxf(smax_s[0][tid], smax_s[1][tid]), fmaxf(smax_s[2][tid], smax_s[3][tid]));
-        sm = idx_score(sm);
-        if ((sm - rc.top) * kLog2e < -8.f) {
-          // loose bound: rebase on the exact row maximum and histogram again
-          rc.top = sm;
+        unsigned long long Z = 0ull;
+        int blo = -1;
+        for (int bi = 0; bi < kNB; ++bi) {
+          const unsigned long long hv = hm_s[bi][tid];
+          if (blo < 0 && hv != 0ull) blo = bi;
+          Z += hv;
+        }
+        if (blo >= 128 || Z == 0ull) {
+          // loose bound (the best token sits >= 8 octaves below it): lower the
+          // reference to just above the best token and histogram again
+          const int bl = (blo < 0) ? kNB - 1 : blo;
+          rc.top = rc.top - (float)(bl - 1) * 0.0625f / kLog2e;
         } else {
-          unsigned long long Z = 0ull;
-          for (int bi = 0; bi < kNB; ++bi) Z += hm_s[bi][tid];
           rc.target = fmax((double)rc.pval * (double)Z, 1.0);
           unsigned long long cm = 0ull;
           int bstar = kNB - 1;
@@ -284,7 +369,7 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
             if ((double)(cm + hm_s[bi][tid]) >= rc.target) { bstar = bi; break; }
             cm += hm_s[bi][tid];
           }
-          if (bstar == kNB - 1) {  // open-ended last bin: recompute what lies before it
+          if (bstar == kNB - 1) {
             cm = 0ull;
             for (int bi = 0; bi < kNB - 1; ++bi) cm += hm_s[bi][tid];
           }
@@ -294,23 +379,31 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
           rc.phase = PH_REFINE;
         }
       } else if (rc.phase == PH_REFINE) {
+        if (!rc.counted) {   // the first refinement counted the tokens above the first-level bin
+          rc.cabove = cbetter_s[tid];
+          rc.counted = 1;
+        }
         unsigned long long cm = rc.above;
+        uint32_t cc = rc.cabove;
         int dstar = -1;
         uint32_t cnt = 0u;
         for (int d = 0; d < kNB; ++d) {
           if (hc_s[d][tid] == 0u) continue;
           if ((double)(cm + hm_s[d][tid]) >= rc.target) { dstar = d; cnt = hc_s[d][tid]; break; }
           cm += hm_s[d][tid];
+          cc += hc_s[d][tid];
         }
         if (dstar < 0) {  // rounding left the target just beyond the range: take its last digit
           cm = rc.above;
+          cc = rc.cabove;
           for (int d = 0; d < kNB; ++d) {
             if (hc_s[d][tid] == 0u) continue;
             dstar = d; cnt = hc_s[d][tid];
           }
-          for (int d = 0; d < dstar; ++d) cm += hm_s[d][tid];
+          for (int d = 0; d < dstar; ++d) { cm += hm_s[d][tid]; cc += hc_s[d][tid]; }
         }
         rc.above = cm;
+        rc.cabove = cc;
         rc.lo = rc.lo + ((uint32_t)dstar << rc.sh);
         if (cnt <= (uint32_t)kCap) {
           rc.phase = PH_COLLECT;
@@ -332,20 +425,18 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
         }
         unsigned long long cm = rc.above;
         int jstar = nc - 1;
+        const float b16r = rc.top * kLog2e * 16.f * 65536.f * (1.f / 65536.f);
+        const float a16r = -kLog2e * 4.f * 65536.f * (1.f / 65536.f);
         for (int a = 0; a < nc; ++a) {
-          const uint32_t kk = ~(uint32_t)(cd[a] >> 32);
-          const float s = __uint_as_float((kk & 0x80000000u) ? (kk & 0x7FFFFFFFu) : ~kk);
-          const float y = fmaf(s * 4.f, kLog2e * 0.25f, -rc.top * kLog2e);
-          const float m = __builtin_amdgcn_exp2f(y);
-          const uint32_t mf = (uint32_t)fminf(m * 4294967296.f, 4294967040.f);
+          const float s = undesc_key((uint32_t)(cd[a] >> 32));
+          const uint32_t mf = mass31(fmaf(s * 4.f, a16r, b16r));
           if ((double)(cm + mf) >= rc.target) { jstar = a; break; }
           cm += mf;
         }
         if (nc > 0) {
-          const uint32_t kk = ~(uint32_t)(cd[jstar] >> 32);
-          rc.tau = __uint_as_float((kk & 0x80000000u) ? (kk & 0x7FFFFFFFu) : ~kk);
+          rc.tau = undesc_key((uint32_t)(cd[jstar] >> 32));
           rc.tie = (int)(uint32_t)(cd[jstar] & 0xFFFFFFFFull);
-          rc.count = (int)cbetter_s[tid] + jstar + 1;
+          rc.count = (int)rc.cabove + jstar + 1;
           // every token scoring exactly tau is a candidate unless the position key was needed;
           // if none of them is left out, the set is simply {s >= tau}
           const bool excluded = (jstar + 1 < nc) && ((uint32_t)(cd[jstar + 1] >> 32) == (uint32_t)(cd[jstar] >> 32));
