@@ -85,9 +85,9 @@ size_t ws_need(const ProbDev& p, rtp_call call, rtp_sel_mode mode) {
     case RTP_CALL_SPARSE_PREFILL:
       return 0;
     case RTP_CALL_SPARSE_DECODE:
-      return rtp::ws_attn_decode(p, p.R);
+      return rtp::ws_attn_decode(p, 0);
     case RTP_CALL_LOCAL:
-      return p.max_q == 1 ? rtp::ws_attn_decode(p, p.n_local) : 0;
+      return p.max_q == 1 ? rtp::ws_attn_decode(p, 1) : 0;
   }
   return 0;
 }

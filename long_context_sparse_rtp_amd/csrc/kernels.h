@@ -24,7 +24,7 @@ __host__ __device__ inline int kv_of(const ProbDev& p, int h) { return (h * p.Hk
 // Workspace layouts (bytes), shared by rtp_workspace_size and the launchers.
 size_t ws_select_decode(const ProbDev& p);
 size_t ws_select_prefill(const ProbDev& p);
-size_t ws_attn_decode(const ProbDev& p, int nheads);
+size_t ws_attn_decode(const ProbDev& p, int mode);  // mode 0: retrieval heads, 1: local heads
 
 hipError_t launch_index_keys(const ProbDev& p, bool bf16, const void* k_pre, const float* w_k,
                              void* k_idx, hipStream_t s);

@@ -223,15 +223,32 @@ __global__ __launch_bounds__(kThreads) void select_decode_kernel(
     return;
   }
 
+  // every pass over the row's scores keeps 8 independent loads in flight per thread
+  auto for_scores = [&](auto&& fn) {
+    constexpr int U = 8;
+    for (int n0 = tid; n0 < L; n0 += U * kThreads) {
+      float sv8[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * kThreads;
+        sv8[u] = (n < L) ? sc[n] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int n = n0 + u * kThreads;
+        if (n < L) fn(sv8[u], n);
+      }
+    }
+  };
+
   // ---- L1 histogram
   for (int i = tid; i < kNB; i += kThreads) { hm_s[i] = 0ull; hc_s[i] = 0u; }
   __syncthreads();
-  for (int n = tid; n < L; n += kThreads) {
-    const float s = sc[n];
+  for_scores([&](float s, int n) {
     const uint32_t bin = l1_bin(s, M);
     atomicAdd(&hm_s[bin], (unsigned long long)mass_fix(s, M));
     atomicAdd(&hc_s[bin], 1u);
-  }
+  });
   __syncthreads();
 
   // ---- scan: first bin whose inclusive cumulative mass reaches p * Z
@@ -270,15 +287,14 @@ __global__ __launch_bounds__(kThreads) void select_decode_kernel(
     const int nshift = shift - nbits;
     for (int i = tid; i < kNB; i += kThreads) { hm_s[i] = 0ull; hc_s[i] = 0u; }
     __syncthreads();
-    for (int n = tid; n < L; n += kThreads) {
-      const float s = sc[n];
-      if ((int)l1_bin(s, M) != bin1) continue;
+    for_scores([&](float s, int n) {
+      if ((int)l1_bin(s, M) != bin1) return;
       const uint32_t key = desc_key(s);
-      if (shift < 32 && (key >> shift) != prefix) continue;
+      if (shift < 32 && (key >> shift) != prefix) return;
       const uint32_t dig = (key >> nshift) & ((1u << nbits) - 1u);
       atomicAdd(&hm_s[dig], (unsigned long long)mass_fix(s, M));
       atomicAdd(&hc_s[dig], 1u);
-    }
+    });
     __syncthreads();
     if (tid == 0) {
       unsigned long long cm = above_s;
@@ -302,10 +318,9 @@ __global__ __launch_bounds__(kThreads) void select_decode_kernel(
     // exact ties (identical scores): admit them by ascending position.
     // The tied score value: any token with key == prefix.
     __shared__ float tie_val_s;
-    for (int n = tid; n < L; n += kThreads) {
-      const float s = sc[n];
+    for_scores([&](float s, int n) {
       if ((int)l1_bin(s, M) == bin1 && desc_key(s) == prefix) tie_val_s = s;
-    }
+    });
     __syncthreads();
     const float tv = tie_val_s;
     const unsigned long long mt = (unsigned long long)mass_fix(tv, M);
@@ -341,21 +356,22 @@ __global__ __launch_bounds__(kThreads) void select_decode_kernel(
     // ---- collect the candidates of the final bin
     if (tid == 0) ncand_s = 0;
     __syncthreads();
-    for (int n = tid; n < L; n += kThreads) {
-      const float s = sc[n];
-      if ((int)l1_bin(s, M) != bin1) continue;
-      if (shift < 32 && (desc_key(s) >> shift) != prefix) continue;
+    for_scores([&](float s, int n) {
+      if ((int)l1_bin(s, M) != bin1) return;
+      if (shift < 32 && (desc_key(s) >> shift) != prefix) return;
       const int slot = atomicAdd(&ncand_s, 1);
       cand_s[slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
-    }
+    });
     __syncthreads();
     const int nc = ncand_s;
-    for (int i = nc + tid; i < kCap; i += kThreads) cand_s[i] = ~0ull;
+    int npow = 64;
+    while (npow < nc) npow <<= 1;
+    for (int i = nc + tid; i < npow; i += kThreads) cand_s[i] = ~0ull;
     __syncthreads();
-    // bitonic sort, ascending (score desc, position asc)
-    for (int k = 2; k <= kCap; k <<= 1) {
+    // bitonic sort of the padded candidates, ascending (score desc, position asc)
+    for (int k = 2; k <= npow; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < kCap; i += kThreads) {
+        for (int i = tid; i < npow; i += kThreads) {
           const int ixj = i ^ j;
           if (ixj > i) {
             const unsigned long long a = cand_s[i], bb = cand_s[ixj];
@@ -402,23 +418,28 @@ __global__ __launch_bounds__(kThreads) void select_decode_kernel(
 
   const float tau = tau_s;
   const int tie_pos = tie_s;
-  // ---- emit the ascending list
+  // ---- emit the ascending list: 8 consecutive positions per thread per round
   int run = 0;
-  for (int base = 0; base < L; base += 4 * kThreads) {
-    int f[4];
-    uint32_t lc2 = 0;
+  constexpr int E = 8;
+  for (int base = 0; base < L; base += E * kThreads) {
+    float sv8[E];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int n = base + 4 * tid + j;
-      f[j] = (n < L) && is_member(sc[n], n, tau, tie_pos);
-      lc2 += f[j];
+    for (int j = 0; j < E; ++j) {
+      const int n = base + E * tid + j;
+      sv8[j] = (n < L) ? sc[n] : 0.f;
+    }
+    uint32_t fl = 0u, lc2 = 0u;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const int n = base + E * tid + j;
+      if (n < L && is_member(sv8[j], n, tau, tie_pos)) { fl |= 1u << j; ++lc2; }
     }
     uint32_t tot2;
     uint32_t ex = block_exscan<uint32_t>(lc2, scan_u32, tot2);
     int o = run + (int)ex;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (f[j]) out_idx[o++] = base + 4 * tid + j;
+    for (int j = 0; j < E; ++j) {
+      if (fl & (1u << j)) out_idx[o++] = base + E * tid + j;
     }
     run += (int)tot2;
   }
