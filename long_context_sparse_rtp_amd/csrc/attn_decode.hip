@@ -229,26 +229,64 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
   }
 }
 
+// Log-sum-exp merge of a row's split partials: split weights first (one load
+// per thread), then every thread sums its head dim over the splits with
+// independent loads.
 template <typename T>
 __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int mode, const rtp_selection sel,
                                                                 const int* __restrict__ pre,
                                                                 const float* __restrict__ part,
                                                                 T* __restrict__ out, float* __restrict__ lse) {
+  constexpr int kMaxS = 256;
+  __shared__ float wgt_s[kMaxS];
+  __shared__ float red_s[2];
+  __shared__ float sum_s;
   const int row = blockIdx.x;
+  const int tid = threadIdx.x;
   const RowInfo ri = row_info(p, mode, row, sel);
   const int s0 = pre[row], s1 = pre[row + 1];
-  const float* rec = part + (size_t)s0 * kPart;
   const int ns = s1 - s0;
-  float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) M = fmaxf(M, rec[(size_t)s * kPart]);
-  float acc = 0.f, sum = 0.f;
-  for (int s = 0; s < ns; ++s) {
-    const float w = __builtin_amdgcn_exp2f(rec[(size_t)s * kPart] - M);
-    acc = fmaf(rec[(size_t)s * kPart + 2 + threadIdx.x], w, acc);
-    sum = fmaf(rec[(size_t)s * kPart + 1], w, sum);
+  const float* rec = part + (size_t)s0 * kPart;
+  float acc = 0.f, M = -INFINITY, sum = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += kMaxS) {
+    const int cn = min(kMaxS, ns - c0);
+    // block max of the split maxima of this chunk
+    float mloc = -INFINITY;
+    for (int s = tid; s < cn; s += kHeadDim) mloc = fmaxf(mloc, rec[(size_t)(c0 + s) * kPart]);
+    mloc = wave_max(mloc);
+    if ((tid & 63) == 0) red_s[tid >> 6] = mloc;
+    __syncthreads();
+    const float mc = fmaxf(red_s[0], red_s[1]);
+    const float Mn = fmaxf(M, mc);
+    const float scale = __builtin_amdgcn_exp2f(M - Mn);
+    acc *= scale;
+    sum *= scale;
+    M = Mn;
+    for (int s = tid; s < cn; s += kHeadDim) {
+      const float* rr = rec + (size_t)(c0 + s) * kPart;
+      wgt_s[s] = __builtin_amdgcn_exp2f(rr[0] - M);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float sl = 0.f;
+      for (int s = 0; s < cn; ++s) sl = fmaf(rec[(size_t)(c0 + s) * kPart + 1], wgt_s[s], sl);
+      sum_s = sl;
+    }
+    int s = 0;
+    for (; s + 8 <= cn; s += 8) {
+      float v8[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v8[u] = rec[(size_t)(c0 + s + u) * kPart + 2 + tid];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = fmaf(v8[u], wgt_s[s + u], acc);
+    }
+    for (; s < cn; ++s) acc = fmaf(rec[(size_t)(c0 + s) * kPart + 2 + tid], wgt_s[s], acc);
+    __syncthreads();
+    sum += sum_s;
+    __syncthreads();
   }
-  out[((size_t)ri.qrow * p.Hq + ri.h) * kHeadDim + threadIdx.x] = Elem<T>::from_f(acc / sum);
-  if (lse && threadIdx.x == 0) lse[(size_t)ri.h * p.Tq + ri.qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
+  out[((size_t)ri.qrow * p.Hq + ri.h) * kHeadDim + tid] = Elem<T>::from_f(acc / sum);
+  if (lse && tid == 0) lse[(size_t)ri.h * p.Tq + ri.qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
 }
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }

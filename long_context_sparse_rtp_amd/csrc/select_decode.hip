@@ -126,17 +126,24 @@ __global__ __launch_bounds__(kThreads) void select_decode_kernel(
   __shared__ float red_s[kThreads / 64];
   __shared__ int last_s;
 
-  // ---- the rounded indexer query (float64, fixed order: every workgroup gets the same bits)
-  if (tid < kIdxDim) {
-    const T* x = q_pre + ((size_t)qrow * p.R + r) * kHeadDim;
-    const float* w = w_q + ((size_t)r * kIdxDim + tid) * kHeadDim;
-    double acc = 0.0;
-    for (int d = 0; d < kHeadDim; ++d) acc = fma((double)Elem<T>::to_f(x[d]), (double)w[d], acc);
-    T qv = Elem<T>::from_d(acc);
-    q_s[tid] = qv;
-    if (c == 0) ((T*)sel.q_idx)[((size_t)r * p.Tq + qrow) * kIdxDim + tid] = qv;
+  // ---- the rounded indexer query (float64, fixed order: every workgroup gets the same bits);
+  // the pre-RoPE row and W^Q are staged in LDS first
+  {
+    __shared__ float wl[kIdxDim * (kHeadDim + 1)];
+    __shared__ float xl[kHeadDim];
+    for (int e = tid; e < kIdxDim * kHeadDim; e += kThreads)
+      wl[(e >> 7) * (kHeadDim + 1) + (e & 127)] = w_q[(size_t)r * kIdxDim * kHeadDim + e];
+    if (tid < kHeadDim) xl[tid] = Elem<T>::to_f(q_pre[((size_t)qrow * p.R + r) * kHeadDim + tid]);
+    __syncthreads();
+    if (tid < kIdxDim) {
+      double acc = 0.0;
+      for (int d = 0; d < kHeadDim; ++d) acc = fma((double)xl[d], (double)wl[tid * (kHeadDim + 1) + d], acc);
+      T qv = Elem<T>::from_d(acc);
+      q_s[tid] = qv;
+      if (c == 0) ((T*)sel.q_idx)[((size_t)r * p.Tq + qrow) * kIdxDim + tid] = qv;
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
   // B operand: the query replicated in all 16 columns
   IF qf;

@@ -142,15 +142,23 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
   static_assert(kRows * kCap <= kNB * kRows, "candidate buffer must fit in the histogram");
 
   // ---- indexer queries of the 16 rows (float64, fixed order, rounded once);
-  // rows past the end repeat the last row and are not written back
+  // rows past the end repeat the last row and are not written back.  The 16
+  // pre-RoPE rows and W^Q are staged in LDS (inside the histogram space) first.
   {
+    float* wl = reinterpret_cast<float*>(&hm_s[0][0]);        // [16][129] (padded rows)
+    T* xl = reinterpret_cast<T*>(wl + kIdxDim * (kHeadDim + 1)); // [16][128]
+    for (int e = tid; e < kIdxDim * kHeadDim; e += kThreads) {
+      wl[(e >> 7) * (kHeadDim + 1) + (e & 127)] = w_q[(size_t)r * kIdxDim * kHeadDim + e];
+      const int row = min(i0 + (e >> 7), Lq - 1);
+      xl[e] = q_pre[((size_t)(q0 + row) * p.R + r) * kHeadDim + (e & 127)];
+    }
+    __syncthreads();
     const int rr = tid >> 4, j = tid & 15;
-    const int i = min(i0 + rr, Lq - 1);
-    const T* x = q_pre + ((size_t)(q0 + i) * p.R + r) * kHeadDim;
-    const float* wr = w_q + ((size_t)r * kIdxDim + j) * kHeadDim;
     double acc = 0.0;
-    for (int d = 0; d < kHeadDim; ++d) acc = fma((double)Elem<T>::to_f(x[d]), (double)wr[d], acc);
+    for (int d = 0; d < kHeadDim; ++d)
+      acc = fma((double)Elem<T>::to_f(xl[rr * kHeadDim + d]), (double)wl[j * (kHeadDim + 1) + d], acc);
     const T qv = Elem<T>::from_d(acc);
+    __syncthreads();
     qidx_s[rr][j] = qv;
     if (i0 + rr < Lq) ((T*)sel.q_idx)[((size_t)r * p.Tq + q0 + i0 + rr) * kIdxDim + j] = qv;
   }
