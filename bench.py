@@ -91,16 +91,19 @@ def bench_prefill(args, torch, rtp, synth):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    t = Timer(torch, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(args.steps):
-        step(t)
+        step()
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    # per-kernel breakdown in a second, separately bracketed pass
+    t = Timer(torch, stream)
+    for _ in range(max(1, min(args.steps, 3))):
+        step(t)
+    torch.cuda.synchronize()
     per = t.means_ms()
 
     # algorithmic work (sets measured from this run's selection)

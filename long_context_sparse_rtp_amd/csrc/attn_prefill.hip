@@ -25,6 +25,8 @@
 //     once at the end; masked tiles of a wave skip both products.
 // LDS strides are padded so the fragment reads of one 8- or 16-lane phase hit
 // distinct banks.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -322,21 +324,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
           for (int c = 0; c < 2; ++c) sacc[c][ks] = mma_k32(kf, qf[c][kc], sacc[c][ks]);
         }
       }
-      // membership
+      // membership: branch-free masks; the variant (exact ties, boundary tile)
+      // is fixed per tile so each inner loop is straight-line code
       if (MODE == 0) {
+        auto apply = [&](auto exact_t, auto mask_t) {
+          constexpr bool kExact = decltype(exact_t)::value;
+          constexpr bool kMask = decltype(mask_t)::value;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
+          for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const f32x4 dx = idx_dot_tile(kxf[ks], qxf[c]);
+            for (int c = 0; c < 2; ++c) {
+              const f32x4 dx = idx_dot_tile(kxf[ks], qxf[c]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int key = kbase + 16 * ks + 4 * grp + i;
-              bool ok = exact_ties ? (dx[i] > tau4[c] || (dx[i] == tau4[c] && key <= tie[c])) : (dx[i] >= tau4[c]);
-              if (need_mask) ok = ok && qok[c] && key <= qpos[c];
-              sacc[c][ks][i] = ok ? sacc[c][ks][i] : -INFINITY;
+              for (int i = 0; i < 4; ++i) {
+                const int key = kbase + 16 * ks + 4 * grp + i;
+                bool ok;
+                if (kExact) ok = (dx[i] > tau4[c]) | ((dx[i] == tau4[c]) & (key <= tie[c]));
+                else ok = dx[i] >= tau4[c];
+                if (kMask) ok = ok & (key <= qpos[c]);
+                sacc[c][ks][i] = ok ? sacc[c][ks][i] : -INFINITY;
+              }
             }
           }
+        };
+        if (exact_ties) {
+          if (need_mask) apply(std::true_type{}, std::true_type{}); else apply(std::true_type{}, std::false_type{});
+        } else {
+          if (need_mask) apply(std::false_type{}, std::true_type{}); else apply(std::false_type{}, std::false_type{});
         }
       } else if (need_mask) {
 #pragma unroll
@@ -348,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
               const int key = kbase + 16 * ks + 4 * grp + i;
               const bool is_sink = key < p.n_sink;
               const bool in_win = (qpos[c] - key) < p.window;
-              bool ok = qok[c] && key <= qpos[c] && (sink_only ? is_sink : (in_win || is_sink));
+              const bool ok = (key <= qpos[c]) & (sink_only ? is_sink : (in_win | is_sink));
               sacc[c][ks][i] = ok ? sacc[c][ks][i] : -INFINITY;
             }
       }
