@@ -20,7 +20,7 @@ Transferring Full Attention into Sparse within Hundred Training Steps"
 * "Local Head Attention Pattern": the first n_sink tokens plus a causal
   sliding window.
 
-Readings of points the page leaves open (each is also listed in the design doc):
+Readings of points the page leaves open:
 
 * index precision: q_idx / k_idx are the float64 dot products rounded once,
   round-to-nearest-even, straight to the stored dtype (float32 or bfloat16);
