@@ -4,7 +4,9 @@ A step of the prefill workload (128K tokens, 32 query / 4 KV heads, bf16) is
 one full pass of the path: index-key projection, THRESHOLD top-p selection,
 sparse attention of the 4 retrieval heads and sink+window attention of the 28
 local heads.  A step of the decode workload (batch 8 x 32K, index cache already
-built) is LIST selection, sparse decode attention and local decode attention.
+built) is LIST selection then sparse decode attention on the main stream, with local
+decode attention on a second stream (overlapping them); both streams join at the
+end of the step.
 Inputs are seeded synthetic tensors resident in HBM before timing starts.
 
 Prints one JSON line: ``value`` is prefill tokens/s; the decode step time, the
@@ -142,6 +144,8 @@ def bench_decode(args, torch, rtp, synth):
     out = torch.empty_like(inp.q)
     lse = torch.empty((cfg.n_q_heads, inp.total_q), dtype=torch.float32, device=dev)
 
+    side = torch.cuda.Stream()   # default priority, like the main stream
+
     def step(t: Timer = None):
         calls = [
             ("select_topp", lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_LIST,
@@ -150,11 +154,20 @@ def bench_decode(args, torch, rtp, synth):
                                                                       ws_dec, stream=stream)),
             ("local_attn", lambda: rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, ws_loc, stream=stream)),
         ]
-        for name, fn in calls:
-            if t is None:
-                fn()
-            else:
+        if t is not None:   # per-kernel breakdown: everything in order on one stream
+            for name, fn in calls:
                 t.run(name, fn)
+            return
+        # the step: local heads on a second stream, overlapping selection + sparse attention
+        fork = torch.cuda.Event()
+        fork.record(stream)
+        side.wait_event(fork)
+        rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, ws_loc, stream=side)
+        calls[0][1]()
+        calls[1][1]()
+        join = torch.cuda.Event()
+        join.record(side)
+        stream.wait_event(join)
 
     steps = args.decode_steps
     for _ in range(args.warmup):

@@ -66,6 +66,18 @@ rtp_status check_problem(const rtp_problem* pr, ProbDev* out) {
     p.n_local = 0;
     for (int h = 0; h < p.Hq; ++h)
       if (!is_ret[h]) p.local_heads[p.n_local++] = h;
+    p.n_ltiles = 0;
+    for (int i = 0; i < p.n_local; ++i) {
+      const int t = p.n_ltiles - 1;
+      if (t >= 0 && p.ltile_cnt[t] < rtp::attn_decode_tile_heads() &&
+          rtp::kv_of(p, p.local_heads[p.ltile_start[t]]) == rtp::kv_of(p, p.local_heads[i])) {
+        ++p.ltile_cnt[t];
+      } else {
+        p.ltile_start[p.n_ltiles] = i;
+        p.ltile_cnt[p.n_ltiles] = 1;
+        ++p.n_ltiles;
+      }
+    }
   }
   return RTP_OK;
 }
@@ -133,6 +145,7 @@ rtp_status rtp_select_topp(const rtp_problem* prob, const void* q_pre, const flo
   if (!aligned16(sel->q_idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
   if (mode == RTP_SEL_LIST) {
     if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
+    if (p.max_k > rtp::select_decode_max_keys()) return RTP_ERR_UNSUPPORTED;
     if (!aligned4(sel->idx)) return RTP_ERR_INVALID_ARG;
     if ((sel->tau && !aligned4(sel->tau)) || (sel->tie_pos && !aligned4(sel->tie_pos))) return RTP_ERR_INVALID_ARG;
   } else {
@@ -173,6 +186,7 @@ rtp_status rtp_sparse_attn_decode(const rtp_problem* prob, const void* q, const 
   if (st != RTP_OK) return st;
   if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
   if (p.R == 0) return RTP_OK;
+  if ((int64_t)p.R * p.batch > rtp::attn_decode_max_rows()) return RTP_ERR_UNSUPPORTED;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RTP_ERR_INVALID_ARG;
   if (lse && !aligned4(lse)) return RTP_ERR_INVALID_ARG;
   if (!sel || !aligned4(sel->idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
@@ -194,6 +208,7 @@ rtp_status rtp_local_attn(const rtp_problem* prob, const void* q, const void* k,
   hipStream_t s = (hipStream_t)stream;
   if (p.max_q == 1) {
     if (p.Tq != p.batch) return RTP_ERR_INVALID_ARG;
+    if ((int64_t)p.n_ltiles * p.batch > rtp::attn_decode_max_rows()) return RTP_ERR_UNSUPPORTED;
     st = check_ws(p, RTP_CALL_LOCAL, RTP_SEL_LIST, ws, ws_bytes);
     if (st != RTP_OK) return st;
     return finish(rtp::launch_attn_decode(p, bf16, 1, q, k, v, nullptr, out, lse, ws, s));

@@ -11,16 +11,22 @@
 // Kernel 2) is bandwidth-bound: single-warp CTAs, registers only, online
 // softmax, split-KV with a final merge.  On gfx950 the same bound holds, so
 // the kernel is organised for HBM streaming instead of matrix cores:
-//   - the set of every (head, sequence) row is cut into splits of 512 entries;
-//     the splits of all rows form one flat work list (prefix sums of the
-//     per-row split counts, computed on the device) that a fixed grid walks
-//     round-robin, so ragged rows and sparse sets leave no idle workgroups;
+//   - a row is (retrieval slot, sequence), or (tile of local heads of one KV
+//     group, sequence); tiles hold one head at present: holding several lets
+//     a K/V row feed all of them, but costs more in cross-lane reductions;
+//   - every row's key set is cut into splits of 512 entries; the splits of all
+//     rows form one flat work list (prefix sums of the per-row split counts,
+//     computed by every workgroup) that a fixed grid walks round-robin, so
+//     ragged rows and sparse sets leave no idle workgroups;
+//   - a split's key positions are staged in LDS with one coalesced read, so
+//     the K/V gathers never wait on the list;
 //   - 16 lanes share a token, each lane holding 8 of the 128 dims, so one K
-//     row and one V row are single coalesced 256-byte (bf16) segments; four
-//     tokens per 16-lane group are loaded before any arithmetic;
-//   - each group keeps an online-softmax state (max, sum, 8 accumulators) in
-//     registers; groups merge through LDS, splits merge in a second kernel by
-//     log-sum-exp.
+//     row and one V row are single coalesced 256-byte (bf16) segments; each
+//     16-lane group keeps two batches of 4 tokens in flight (the next batch
+//     is requested before the current one is used);
+//   - each group keeps an online-softmax state (max, sum, 8 accumulators) per
+//     head in registers; groups merge through LDS, splits merge in a second
+//     kernel by log-sum-exp.
 #include "common.h"
 #include "kernels.h"
 
@@ -29,15 +35,21 @@ namespace rtp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSplit = 512;
+constexpr int kSplit = 512;              // entries per split (retrieval rows)
+constexpr int kSplitTile = 512;          // entries per split (local-head rows)
+__host__ __device__ constexpr int split_of(int mode) { return mode == 0 ? kSplit : kSplitTile; }
 constexpr int kGroups = kThreads / 16;   // 16-lane groups per workgroup
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 4;               // tokens per group per batch
+constexpr int kStep = kGroups * kUnroll; // tokens per workgroup per batch
 constexpr int kPart = kHeadDim + 2;      // partial record: m, l, o[128]
-constexpr int kMaxGrid = 2048;
-constexpr int kMaxRowsLds = 4096;        // rows whose split prefix is cached in LDS
+constexpr int kWgPerCu = 4;              // resident workgroups per CU (VGPR-bound)
+constexpr int kMaxRowsLds = 8192;        // rows per call + 1 (the split prefix lives in LDS)
+constexpr int kMaxTileHeads = 1;         // local heads per row (one: the tile form costs more in cross-lane
+                                         // reductions than it saves in L2 reads)
 
 struct RowInfo {
-  int h, b, qrow, k0, L, count, slot;
+  int b, qrow, k0, L, count, g, nh;
+  int hfirst;   // mode 0: the query head; mode 1: index of the tile's first local head
 };
 
 __device__ __forceinline__ RowInfo row_info(const ProbDev& p, int mode, int row, const rtp_selection& sel) {
@@ -48,17 +60,22 @@ __device__ __forceinline__ RowInfo row_info(const ProbDev& p, int mode, int row,
   ri.L = p.cu_k[ri.b + 1] - ri.k0;
   ri.qrow = p.cu_q[ri.b];
   if (mode == 0) {
-    ri.slot = hi;
-    ri.h = p.ret_heads[hi];
+    ri.hfirst = p.ret_heads[hi];
+    ri.nh = 1;
+    ri.g = kv_of(p, ri.hfirst);
     ri.count = sel.count[(size_t)hi * p.Tq + ri.qrow];
   } else {
-    ri.slot = -1;
-    ri.h = p.local_heads[hi];
+    ri.hfirst = p.ltile_start[hi];
+    ri.nh = p.ltile_cnt[hi];
+    ri.g = kv_of(p, p.local_heads[ri.hfirst]);
     const int W = min(p.window, ri.L);
     const int ns = min(p.n_sink, ri.L - W);
     ri.count = ns + W;
   }
   return ri;
+}
+__device__ __forceinline__ int head_of(const ProbDev& p, int mode, const RowInfo& ri, int i) {
+  return (mode == 0) ? ri.hfirst : p.local_heads[ri.hfirst + i];
 }
 
 // j-th key position of a local head's set: sinks first, then the window.
@@ -88,57 +105,58 @@ template <> struct RowVec<float> {
   }
 };
 
-// Split prefix over rows: pre[r] = sum of ceil(count / kSplit) of rows before r; pre[rows] = total.
-__global__ __launch_bounds__(1024) void split_prefix_kernel(ProbDev p, int mode, int rows, const rtp_selection sel,
-                                                            int* __restrict__ pre) {
-  __shared__ int wsum[16];
-  __shared__ int carry_s;
-  if (threadIdx.x == 0) carry_s = 0;
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  for (int base = 0; base < rows; base += 1024) {
-    const int r = base + threadIdx.x;
-    int v = 0;
-    if (r < rows) {
-      const RowInfo ri = row_info(p, mode, r, sel);
-      v = (ri.count + kSplit - 1) / kSplit;
-    }
-    int inc = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(inc, d);
-      if (lane >= d) inc += y;
-    }
-    if (lane == 63) wsum[wid] = inc;
-    __syncthreads();
-    int off = carry_s;
-    for (int w2 = 0; w2 < wid; ++w2) off += wsum[w2];
-    if (r < rows) pre[r] = off + inc - v;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      int t = 0;
-      for (int w2 = 0; w2 < 16; ++w2) t += wsum[w2];
-      carry_s += t;
-    }
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) pre[rows] = carry_s;
-}
-
-template <typename T>
+// H: heads per row this instantiation holds (1: retrieval slots, 8: local tiles)
+template <typename T, int H>
 __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mode, int rows, const T* __restrict__ q,
                                                                const T* __restrict__ k, const T* __restrict__ v,
-                                                               const rtp_selection sel, const int* __restrict__ pre,
+                                                               const rtp_selection sel, int* __restrict__ pre,
                                                                float* __restrict__ part) {
-  __shared__ int pre_s[kMaxRowsLds + 1];
+  extern __shared__ int pre_s[];   // [rows + 1], sized at launch
+  __shared__ int idx_s[kSplit];
+  __shared__ int wsum_s[kThreads / 64];
   __shared__ float gm_s[kGroups], gl_s[kGroups];
   __shared__ float go_s[kGroups][kHeadDim];
-  const bool lds_pre = rows <= kMaxRowsLds;
-  if (lds_pre)
-    for (int i = threadIdx.x; i <= rows; i += kThreads) pre_s[i] = pre[i];
-  __syncthreads();
-  const int total = lds_pre ? pre_s[rows] : pre[rows];
   const int tid = threadIdx.x;
+  // split prefix over the rows (every workgroup computes it; block 0 publishes it
+  // for the combine kernel): pre[r] = sum of ceil(count / split) over rows before r.
+  // Rows are dealt to threads round-robin so all their counts load at once.
+  {
+    constexpr int PR = kMaxRowsLds / kThreads;
+    const int nchunks = rows / kThreads + 1;   // chunks holding rows 0..rows
+    int vv[PR];
+#pragma unroll
+    for (int t = 0; t < PR; ++t) {
+      const int r = t * kThreads + tid;
+      vv[t] = 0;
+      if (r < rows) vv[t] = (row_info(p, mode, r, sel).count + split_of(mode) - 1) / split_of(mode);
+    }
+    const int lane = tid & 63, wid = tid >> 6;
+    int carry = 0;
+#pragma unroll
+    for (int t = 0; t < PR; ++t) {
+      if (t >= nchunks) break;
+      int inc = vv[t];
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(inc, d);
+        if (lane >= d) inc += y;
+      }
+      if (lane == 63) wsum_s[wid] = inc;
+      __syncthreads();
+      int off = carry, tot = 0;
+      for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+        if (w2 < wid) off += wsum_s[w2];
+        tot += wsum_s[w2];
+      }
+      const int r = t * kThreads + tid;
+      if (r <= rows) pre_s[r] = off + inc - vv[t];
+      carry += tot;
+      __syncthreads();
+    }
+    if (blockIdx.x == 0)
+      for (int r = tid; r <= rows; r += kThreads) pre[r] = pre_s[r];
+  }
+  const int total = pre_s[rows];
   const int grp = tid >> 4, gl = tid & 15;
   const int d0 = gl * 8;
   const size_t kstride = (size_t)p.Hkv * kHeadDim;
@@ -149,90 +167,119 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
     int lo = 0, hi = rows - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      const int pv = lds_pre ? pre_s[mid] : pre[mid];
-      if (pv <= wi) lo = mid; else hi = mid - 1;
+      if (pre_s[mid] <= wi) lo = mid; else hi = mid - 1;
     }
     const int row = lo;
-    const int split = wi - (lds_pre ? pre_s[row] : pre[row]);
+    const int split = wi - pre_s[row];
     const RowInfo ri = row_info(p, mode, row, sel);
-    const int j0 = split * kSplit;
-    const int j1 = min(ri.count, j0 + kSplit);
-    const int g = kv_of(p, ri.h);
-    const T* kb = k + ((size_t)ri.k0 * p.Hkv + g) * kHeadDim + d0;
-    const T* vb = v + ((size_t)ri.k0 * p.Hkv + g) * kHeadDim + d0;
-    const int* list = (mode == 0) ? sel.idx + (size_t)ri.slot * p.Tk + ri.k0 : nullptr;
-
-    float qv[8];
-    {
-      RowVec<T> qq;
-      qq.load(q + ((size_t)ri.qrow * p.Hq + ri.h) * kHeadDim + d0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qv[i] = qq.get(i) * qscale;
+    const int nh = min(ri.nh, H);
+    const int j0 = split * split_of(mode);
+    const int j1 = min(ri.count, j0 + split_of(mode));
+    const T* kb = k + ((size_t)ri.k0 * p.Hkv + ri.g) * kHeadDim + d0;
+    const T* vb = v + ((size_t)ri.k0 * p.Hkv + ri.g) * kHeadDim + d0;
+    // the split's key positions, staged once (coalesced)
+    if (mode == 0) {
+      const int* list = sel.idx + (size_t)(row / p.batch) * p.Tk + ri.k0;
+      for (int j = j0 + tid; j < j1; j += kThreads) idx_s[j - j0] = list[j];
+    } else {
+      for (int j = j0 + tid; j < j1; j += kThreads) idx_s[j - j0] = local_token(p, ri.L, j);
     }
-    float m = -INFINITY, l = 0.f, o[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = 0.f;
 
-    for (int jb = j0 + grp; jb < j1; jb += kGroups * kUnroll) {
-      RowVec<T> kr[kUnroll], vr[kUnroll];
-      bool ok[kUnroll];
+    float qv[H][8];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const int hh = (h < nh) ? head_of(p, mode, ri, h) : head_of(p, mode, ri, 0);
+      RowVec<T> qq;
+      qq.load(q + ((size_t)ri.qrow * p.Hq + hh) * kHeadDim + d0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qv[h][i] = qq.get(i) * qscale;
+    }
+    float m[H], l[H], o[H][8];
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[h][i] = 0.f;
+    }
+    __syncthreads();
+
+    // two batches of kUnroll tokens per group in flight
+    RowVec<T> ka[kUnroll], va[kUnroll], kb2[kUnroll], vb2[kUnroll];
+    auto load = [&](RowVec<T>* kr, RowVec<T>* vr, int jb) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int j = jb + u * kGroups;
-        ok[u] = j < j1;
-        const int n = ok[u] ? ((mode == 0) ? list[j] : local_token(p, ri.L, j)) : 0;
+        const int n = (j < j1) ? idx_s[j - j0] : idx_s[0];
         kr[u].load(kb + (size_t)n * kstride);
         vr[u].load(vb + (size_t)n * kstride);
       }
+    };
+    auto compute = [&](const RowVec<T>* kr, const RowVec<T>* vr, int jb) {
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
-        float a = 0.f;
+        const bool ok = (jb + u * kGroups) < j1;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = fmaf(qv[i], kr[u].get(i), a);
-        a += __shfl_xor(a, 1);
-        a += __shfl_xor(a, 2);
-        a += __shfl_xor(a, 4);
-        a += __shfl_xor(a, 8);
-        if (ok[u]) {
-          const float mn = fmaxf(m, a);
-          const float sc = __builtin_amdgcn_exp2f(m - mn);
-          const float pe = __builtin_amdgcn_exp2f(a - mn);
-          l = l * sc + pe;
+        for (int h = 0; h < H; ++h) {
+          if (h >= nh) break;
+          float a = 0.f;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = fmaf(pe, vr[u].get(i), o[i] * sc);
-          m = mn;
+          for (int i = 0; i < 8; ++i) a = fmaf(qv[h][i], kr[u].get(i), a);
+          a = row16_sum(a);
+          if (ok) {
+            const float mn = fmaxf(m[h], a);
+            const float sc = __builtin_amdgcn_exp2f(m[h] - mn);
+            const float pe = __builtin_amdgcn_exp2f(a - mn);
+            l[h] = l[h] * sc + pe;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[h][i] = fmaf(pe, vr[u].get(i), o[h][i] * sc);
+            m[h] = mn;
+          }
         }
       }
+    };
+    const int jfirst = j0 + grp;
+    if (jfirst < j1) load(ka, va, jfirst);
+    for (int jb = jfirst; jb < j1; jb += 2 * kStep) {
+      const bool has_b = jb + kStep < j1;
+      if (has_b) load(kb2, vb2, jb + kStep);
+      compute(ka, va, jb);
+      if (jb + 2 * kStep < j1) load(ka, va, jb + 2 * kStep);
+      if (has_b) compute(kb2, vb2, jb + kStep);
     }
 
-    // merge the 16 groups of the workgroup
-    if (gl == 0) { gm_s[grp] = m; gl_s[grp] = l; }
+    // merge the 16 groups of the workgroup, one head at a time
 #pragma unroll
-    for (int i = 0; i < 8; ++i) go_s[grp][d0 + i] = o[i];
-    __syncthreads();
-    float* rec = part + (size_t)wi * kPart;
-    if (tid < kHeadDim) {
-      float M = -INFINITY;
-      for (int gi = 0; gi < kGroups; ++gi) M = fmaxf(M, gm_s[gi]);
-      float acc = 0.f, sum = 0.f;
-      for (int gi = 0; gi < kGroups; ++gi) {
-        if (gl_s[gi] > 0.f) {
-          const float wgt = __builtin_amdgcn_exp2f(gm_s[gi] - M);
-          acc = fmaf(go_s[gi][tid], wgt, acc);
-          sum = fmaf(gl_s[gi], wgt, sum);
+    for (int h = 0; h < H; ++h) {
+      if (h >= nh) break;
+      if (gl == 0) { gm_s[grp] = m[h]; gl_s[grp] = l[h]; }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) go_s[grp][d0 + i] = o[h][i];
+      __syncthreads();
+      float* rec = part + ((size_t)wi * H + h) * kPart;
+      if (tid < kHeadDim) {
+        float M = -INFINITY;
+        for (int gi = 0; gi < kGroups; ++gi) M = fmaxf(M, gm_s[gi]);
+        float acc = 0.f, sum = 0.f;
+        for (int gi = 0; gi < kGroups; ++gi) {
+          if (gl_s[gi] > 0.f) {
+            const float wgt = __builtin_amdgcn_exp2f(gm_s[gi] - M);
+            acc = fmaf(go_s[gi][tid], wgt, acc);
+            sum = fmaf(gl_s[gi], wgt, sum);
+          }
         }
+        rec[2 + tid] = acc;
+        if (tid == 0) { rec[0] = M; rec[1] = sum; }
       }
-      rec[2 + tid] = acc;
-      if (tid == 0) { rec[0] = M; rec[1] = sum; }
+      __syncthreads();
     }
-    __syncthreads();
   }
 }
 
-// Log-sum-exp merge of a row's split partials: split weights first (one load
-// per thread), then every thread sums its head dim over the splits with
+// Log-sum-exp merge of a (row, head)'s split partials: split weights first (one
+// load per thread), then every thread sums its head dim over the splits with
 // independent loads.
-template <typename T>
+template <typename T, int H>
 __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int mode, const rtp_selection sel,
                                                                 const int* __restrict__ pre,
                                                                 const float* __restrict__ part,
@@ -241,18 +288,20 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int m
   __shared__ float wgt_s[kMaxS];
   __shared__ float red_s[2];
   __shared__ float sum_s;
-  const int row = blockIdx.x;
+  const int row = blockIdx.x / H, h = blockIdx.x % H;
   const int tid = threadIdx.x;
   const RowInfo ri = row_info(p, mode, row, sel);
+  if (h >= ri.nh) return;
+  const int head = head_of(p, mode, ri, h);
   const int s0 = pre[row], s1 = pre[row + 1];
   const int ns = s1 - s0;
-  const float* rec = part + (size_t)s0 * kPart;
+  auto rec_of = [&](int s) { return part + ((size_t)(s0 + s) * H + h) * kPart; };
   float acc = 0.f, M = -INFINITY, sum = 0.f;
   for (int c0 = 0; c0 < ns; c0 += kMaxS) {
     const int cn = min(kMaxS, ns - c0);
     // block max of the split maxima of this chunk
     float mloc = -INFINITY;
-    for (int s = tid; s < cn; s += kHeadDim) mloc = fmaxf(mloc, rec[(size_t)(c0 + s) * kPart]);
+    for (int s = tid; s < cn; s += kHeadDim) mloc = fmaxf(mloc, rec_of(c0 + s)[0]);
     mloc = wave_max(mloc);
     if ((tid & 63) == 0) red_s[tid >> 6] = mloc;
     __syncthreads();
@@ -262,40 +311,40 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int m
     acc *= scale;
     sum *= scale;
     M = Mn;
-    for (int s = tid; s < cn; s += kHeadDim) {
-      const float* rr = rec + (size_t)(c0 + s) * kPart;
-      wgt_s[s] = __builtin_amdgcn_exp2f(rr[0] - M);
-    }
+    for (int s = tid; s < cn; s += kHeadDim) wgt_s[s] = __builtin_amdgcn_exp2f(rec_of(c0 + s)[0] - M);
     __syncthreads();
     if (tid == 0) {
       float sl = 0.f;
-      for (int s = 0; s < cn; ++s) sl = fmaf(rec[(size_t)(c0 + s) * kPart + 1], wgt_s[s], sl);
+      for (int s = 0; s < cn; ++s) sl = fmaf(rec_of(c0 + s)[1], wgt_s[s], sl);
       sum_s = sl;
     }
     int s = 0;
     for (; s + 8 <= cn; s += 8) {
       float v8[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v8[u] = rec[(size_t)(c0 + s + u) * kPart + 2 + tid];
+      for (int u = 0; u < 8; ++u) v8[u] = rec_of(c0 + s + u)[2 + tid];
 #pragma unroll
       for (int u = 0; u < 8; ++u) acc = fmaf(v8[u], wgt_s[s + u], acc);
     }
-    for (; s < cn; ++s) acc = fmaf(rec[(size_t)(c0 + s) * kPart + 2 + tid], wgt_s[s], acc);
+    for (; s < cn; ++s) acc = fmaf(rec_of(c0 + s)[2 + tid], wgt_s[s], acc);
     __syncthreads();
     sum += sum_s;
     __syncthreads();
   }
-  out[((size_t)ri.qrow * p.Hq + ri.h) * kHeadDim + tid] = Elem<T>::from_f(acc / sum);
-  if (lse && tid == 0) lse[(size_t)ri.h * p.Tq + ri.qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
+  out[((size_t)ri.qrow * p.Hq + head) * kHeadDim + tid] = Elem<T>::from_f(acc / sum);
+  if (lse && tid == 0) lse[(size_t)head * p.Tq + ri.qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
 }
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+inline int rows_of(const ProbDev& p, int mode) { return ((mode == 0) ? p.R : p.n_ltiles) * p.batch; }
+inline int heads_per_row(int mode) { return (mode == 0) ? 1 : kMaxTileHeads; }
 
 // upper bound on the number of splits (every row's set holds at most L_b entries)
 inline size_t max_work(const ProbDev& p, int mode, int rows) {
   if (mode == 1) {
     const int cnt = min(p.window, p.max_k) + p.n_sink;
-    return (size_t)rows * ((cnt + kSplit - 1) / kSplit);
+    return (size_t)rows * ((cnt + kSplitTile - 1) / kSplitTile);
   }
   const size_t per_row = (size_t)(p.max_k + kSplit - 1) / kSplit;
   const size_t by_total = (size_t)((p.Tk + kSplit - 1) / kSplit) + (size_t)p.batch;  // sum over sequences
@@ -304,35 +353,47 @@ inline size_t max_work(const ProbDev& p, int mode, int rows) {
 
 }  // namespace
 
+int attn_decode_max_rows() { return kMaxRowsLds - 1; }
+int attn_decode_tile_heads() { return kMaxTileHeads; }
+
 size_t ws_attn_decode(const ProbDev& p, int mode) {
-  const int rows = ((mode == 0) ? p.R : p.n_local) * p.batch;
-  return align256(sizeof(int) * (size_t)(rows + 1)) + sizeof(float) * max_work(p, mode, rows) * kPart;
+  const int rows = rows_of(p, mode);
+  return align256(sizeof(int) * (size_t)(rows + 1)) +
+         sizeof(float) * max_work(p, mode, rows) * heads_per_row(mode) * kPart;
 }
 
 hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
                               const void* v, const rtp_selection* sel, void* out, float* lse, void* ws,
                               hipStream_t s) {
-  const int nheads = (mode == 0) ? p.R : p.n_local;
-  if (nheads == 0) return hipSuccess;
-  const int rows = nheads * p.batch;
+  const int rows = rows_of(p, mode);
+  if (rows == 0) return hipSuccess;
   rtp_selection sl = {};
   if (sel) sl = *sel;
   int* pre = (int*)ws;
   float* part = (float*)((char*)ws + align256(sizeof(int) * (size_t)(rows + 1)));
-  hipLaunchKernelGGL(split_prefix_kernel, dim3(1), dim3(1024), 0, s, p, mode, rows, sl, pre);
   const size_t mw = max_work(p, mode, rows);
-  const unsigned grid = (unsigned)max((size_t)1, min((size_t)kMaxGrid, mw));
+  // a resident grid: every workgroup walks several work items, so the row prefix is
+  // computed once per workgroup and no launch round waits on the previous one
+  int n_cu = 256, dev = 0, cu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+    n_cu = cu;
+  const unsigned grid = (unsigned)max((size_t)1, min((size_t)n_cu * kWgPerCu, mw));
+  const size_t lds = sizeof(int) * (size_t)(rows + 1);
+  const unsigned cgrid = (unsigned)(rows * heads_per_row(mode));
+#define RTP_LAUNCH(TT, HH)                                                                                        \
+  do {                                                                                                            \
+    hipLaunchKernelGGL((attn_decode_kernel<TT, HH>), dim3(grid), dim3(kThreads), lds, s, p, mode, rows,             \
+                       (const TT*)q, (const TT*)k, (const TT*)v, sl, pre, part);                                  \
+    hipLaunchKernelGGL((attn_decode_combine<TT, HH>), dim3(cgrid), dim3(kHeadDim), 0, s, p, mode, sl,             \
+                       (const int*)pre, part, (TT*)out, lse);                                                     \
+  } while (0)
   if (bf16) {
-    hipLaunchKernelGGL(attn_decode_kernel<bf16_t>, dim3(grid), dim3(kThreads), 0, s, p, mode, rows, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, sl, (const int*)pre, part);
-    hipLaunchKernelGGL(attn_decode_combine<bf16_t>, dim3(rows), dim3(kHeadDim), 0, s, p, mode, sl, (const int*)pre,
-                       part, (bf16_t*)out, lse);
+    if (mode == 0) RTP_LAUNCH(bf16_t, 1); else RTP_LAUNCH(bf16_t, kMaxTileHeads);
   } else {
-    hipLaunchKernelGGL(attn_decode_kernel<float>, dim3(grid), dim3(kThreads), 0, s, p, mode, rows, (const float*)q,
-                       (const float*)k, (const float*)v, sl, (const int*)pre, part);
-    hipLaunchKernelGGL(attn_decode_combine<float>, dim3(rows), dim3(kHeadDim), 0, s, p, mode, sl, (const int*)pre,
-                       part, (float*)out, lse);
+    if (mode == 0) RTP_LAUNCH(float, 1); else RTP_LAUNCH(float, kMaxTileHeads);
   }
+#undef RTP_LAUNCH
   return hipGetLastError();
 }
 

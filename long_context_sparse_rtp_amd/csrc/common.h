@@ -131,6 +131,22 @@ __device__ __forceinline__ f32x4 idx_dot_tile(const IdxFragF32& kf, const IdxFra
 __device__ __forceinline__ float idx_score(float dot) { return dot * 0.25f; }
 
 // ------------------------------------------------------------ reductions
+// Data-parallel-primitive moves within a row of 16 lanes (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Sum over each row of 16 lanes, identical in all 16 lanes: a butterfly over
+// lane pairs (xor 1, xor 2 via quad permutes, then the half-row and row mirrors),
+// so every lane adds the same pairs in the same order.
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]
+  x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  x += dpp_mov<0x141>(x);   // row_half_mirror
+  x += dpp_mov<0x140>(x);   // row_mirror
+  return x;
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

@@ -17,14 +17,22 @@ struct ProbDev {
   const int32_t* cu_k;
   int ret_heads[RTP_MAX_HEADS];    // slot -> query head
   int local_heads[RTP_MAX_HEADS];  // local index -> query head
+  // local heads grouped by KV head, at most attn_decode_tile_heads() per tile: tile t covers
+  // local_heads[ltile_start[t] .. ltile_start[t] + ltile_cnt[t])
+  int n_ltiles;
+  int ltile_start[RTP_MAX_HEADS];
+  int ltile_cnt[RTP_MAX_HEADS];
 };
 
 __host__ __device__ inline int kv_of(const ProbDev& p, int h) { return (h * p.Hkv) / p.Hq; }
 
 // Workspace layouts (bytes), shared by rtp_workspace_size and the launchers.
 size_t ws_select_decode(const ProbDev& p);
+int select_decode_max_keys();   // longest sequence LIST selection accepts
 size_t ws_select_prefill(const ProbDev& p);
 size_t ws_attn_decode(const ProbDev& p, int mode);  // mode 0: retrieval heads, 1: local heads
+int attn_decode_max_rows();   // (head, sequence) rows one decode attention call accepts
+int attn_decode_tile_heads(); // local heads of one KV group handled together in decode
 
 hipError_t launch_index_keys(const ProbDev& p, bool bf16, const void* k_pre, const float* w_k,
                              void* k_idx, hipStream_t s);

@@ -5,25 +5,35 @@
 // indexer scores s_n = q_idx . k_idx_n / 4 of all cached keys, keys taken by
 // descending score (ties: ascending position), the smallest prefix whose mass
 // reaches p.  Token-exact; the pages' own kernel ("Hardware-Aware Fast Top-p
-// Decoding Kernel") approximates with 64-token blocks and a 256-bin
-// histogram - kept here only as the idea of a sort-free histogram threshold
-// finished by the last workgroup.
+// Decoding Kernel") approximates with 64-token blocks and a 256-bin histogram
+// finished by the last CTA - kept here as the idea of a sort-free histogram
+// threshold.
 //
-// Kernel 1 (grid: key chunks x (slot, sequence)): every workgroup projects the
-// query (float64, rounded once), scores its 4096-key chunk with the shared
-// MFMA indexer tile, writes the float32 scores to the workspace and its chunk
-// maximum.  The last workgroup of a row (atomic ticket) then runs the exact
-// selection on that row alone:
-//   L1  mass histogram of 2048 bins over u = (M - s) log2(e) (64 per octave,
-//       last bin open-ended), masses as 32-bit fixed point of 2^(s-M) summed
-//       in 64-bit integers (order-independent, so the result is deterministic);
-//   scan for the bin where the cumulative mass reaches p * Z;
-//   collect that bin's tokens (score, position) - or, if it holds more than
-//       1024, refine with radix digits of the score's bit pattern, and finally
-//       rank exact ties by position;
-//   sort the candidates by (score desc, position asc) and find the crossing
-//       token: tau = its score, tie_pos = its position;
-//   emit the ascending list {n : s_n > tau or (s_n == tau and n <= tie_pos)}.
+// A row (retrieval slot, sequence) is cut into units of 4096 keys and every
+// kernel runs one workgroup per unit, so the whole device works on each step.
+// Workgroups never wait on each other inside a kernel (no device-wide fences
+// or tickets); the three kernel boundaries are the only synchronisation.
+//
+//  1. score: project the query (float64, fixed order, rounded once), score the
+//     unit's keys (fixed-order float32 FMA chain), store the scores, and
+//     histogram the unit's mass over 4096 bins of 1/128 octave.  Bins sit on
+//     an absolute grid a(s) = floor(s * 128 * log2(e)); a unit's bin
+//     j = A_u - a(s) counts down from the bin A_u of its own maximum, and a
+//     token's mass is 38-bit fixed point of 2^(s log2 e - (A_u + 1) / 128).
+//     Mass and count share one 64-bit LDS integer per bin (count << 51), so
+//     one atomic per token keeps the sums exact and order-independent.
+//  2. collect: every unit merges the row's unit histograms (unit u shifted by
+//     A - A_u bins and scaled by 2^((A_u - A) / 128) in float64, in a fixed
+//     order, so all workgroups of the row reach bit-identical sums), finds the
+//     row bin where the cumulative mass reaches p * Z, counts its own tokens
+//     above that bin and stores its tokens inside the bin as candidates.
+//  3. emit: every unit ranks the row's candidates by (score desc, position
+//     asc), walks their masses to the crossing token (tau, tie_pos, count),
+//     derives its output offset from the per-unit counts and writes its
+//     members in ascending order.  A crossing bin too crowded for the
+//     candidate lists (mass piled on near-identical scores) is resolved from
+//     the row's stored scores, with radix digits of the score's bit pattern
+//     and then positions.
 #include "common.h"
 #include "kernels.h"
 
@@ -32,54 +42,116 @@ namespace rtp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChunk = 4096;
-constexpr int kNB = 2048;        // histogram bins per level
-constexpr int kCap = 1024;       // candidate capacity (power of two, bitonic sort)
-constexpr float kBinsPerOctave = 64.f;
+constexpr int kChunk = 4096;                  // keys per unit
+constexpr int kPer = kChunk / kThreads;       // keys per thread
+constexpr int kNB = 4096;                     // bins per unit / row histogram
+constexpr int kBinsPerPass = 2048;            // row bins merged per pass (8 per thread)
+constexpr int kCapUnit = 1024;                // candidates stored per unit
+constexpr int kCap = 4096;                    // candidates per row (ranked in LDS)
+constexpr int kMaxUnits = 1024;               // units per row (4M keys)
+constexpr float kBinScale = 128.f * kLog2e;   // bins per unit of score
+constexpr int kCountShift = 51;
+constexpr unsigned long long kMassMask = (1ull << kCountShift) - 1ull;
 
-struct DecodeWs {
-  float* scores;       // [R * Tk]
-  float* cmax;         // [R * B * max_chunks]
-  uint32_t* ticket;    // [R * B]
+struct UnitMeta {
+  int A;                      // absolute bin of the unit maximum
+  int used;                   // highest non-empty unit bin (-1: empty unit)
+  unsigned long long Z;       // sum of the unit's fixed-point masses
+};
+struct UnitCnt {
+  uint32_t above;             // unit tokens in row bins before the crossing bin
+  uint32_t inbin;             // unit tokens in the crossing bin
+};
+enum { ROW_NORMAL = 0, ROW_ALL = 1, ROW_EMPTY = 2 };
+struct RowState {
+  double above;               // merged mass of the row bins before the crossing bin
+  double target;              // p * Z
+  int mode;
+  int A;
+  int jstar;
+  uint32_t cabove;            // tokens before the crossing bin
+  uint32_t bincnt;            // tokens in the crossing bin
+  int pad;
 };
 
-__host__ __device__ inline int max_chunks(const ProbDev& p) { return (p.max_k + kChunk - 1) / kChunk; }
+struct DecodeWs {
+  float* scores;               // [R * Tk]
+  UnitMeta* meta;              // [nslots]
+  unsigned long long* hist;    // [nslots * kNB]
+  UnitCnt* ucnt;               // [nslots]
+  double* fu;                  // [nslots]: 2^((A_u - A) / 128) of the row merge
+  unsigned long long* cand;    // [nslots * kCapUnit]: (desc_key << 32) | position
+  RowState* rows;              // [nrows]
+};
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+__host__ __device__ inline int max_units(const ProbDev& p) { return (p.max_k + kChunk - 1) / kChunk; }
+// Unit slots per retrieval slot: sequence b's units start at cu_k[b] / kChunk + b,
+// which leaves room for ceil(L_b / kChunk) units (and one for an empty sequence).
+__host__ __device__ inline int64_t slots_per_r(const ProbDev& p) { return p.Tk / kChunk + p.batch + 1; }
 
-__host__ __device__ inline DecodeWs carve(const ProbDev& p, void* ws) {
-  char* b = (char*)ws;
-  DecodeWs w;
+inline size_t ws_layout(const ProbDev& p, void* base, DecodeWs* w) {
+  const int64_t nslots = (int64_t)p.R * slots_per_r(p);
+  const int64_t nrows = (int64_t)p.R * p.batch;
+  char* b = (char*)base;
   size_t o = 0;
-  w.scores = (float*)(b + o);
-  o = align256(o + sizeof(float) * (size_t)p.R * p.Tk);
-  w.cmax = (float*)(b + o);
-  o = align256(o + sizeof(float) * (size_t)p.R * p.batch * max_chunks(p));
-  w.ticket = (uint32_t*)(b + o);
-  return w;
+  auto take = [&](size_t bytes) { char* q = b ? b + o : nullptr; o = align256(o + bytes); return q; };
+  char* s = take(sizeof(float) * (size_t)p.R * p.Tk);
+  char* m = take(sizeof(UnitMeta) * nslots);
+  char* h = take(sizeof(unsigned long long) * nslots * kNB);
+  char* uc = take(sizeof(UnitCnt) * nslots);
+  char* fu = take(sizeof(double) * nslots);
+  char* cd = take(sizeof(unsigned long long) * nslots * kCapUnit);
+  char* rs = take(sizeof(RowState) * nrows);
+  if (w) {
+    w->scores = (float*)s; w->meta = (UnitMeta*)m; w->hist = (unsigned long long*)h;
+    w->ucnt = (UnitCnt*)uc; w->fu = (double*)fu; w->cand = (unsigned long long*)cd; w->rows = (RowState*)rs;
+  }
+  return o;
 }
 
-// Per-token quantities every pass of the selection computes the same way.
-__device__ __forceinline__ uint32_t mass_fix(float s, float M) {
-  const float y = (s - M) * kLog2e;
-  const float m = __builtin_amdgcn_exp2f(y);
-  return (uint32_t)fminf(m * 4294967296.f, 4294967040.f);
+// ---- per-token quantities; every kernel computes them the same way
+// absolute bin, clamped to +-2^24 so that bin differences never overflow
+__device__ __forceinline__ int abs_bin(float s) {
+  return (int)__builtin_amdgcn_fmed3f(floorf(s * kBinScale), -16777216.f, 16777216.f);
 }
-__device__ __forceinline__ uint32_t l1_bin(float s, float M) {
-  const float y = (s - M) * kLog2e;
-  return (uint32_t)fminf(fmaxf(-y * kBinsPerOctave, 0.f), (float)(kNB - 1));
+__device__ __forceinline__ unsigned long long mass38(float s, int A_u) {
+  const float e = fminf(fmaf(s, kLog2e, -(float)(A_u + 1) * (1.f / 128.f)), 0.f);
+  return (unsigned long long)(__builtin_amdgcn_exp2f(e) * 274877906944.f);   // 2^38
 }
+__device__ __forceinline__ double unit_scale(int A_u, int A) { return exp2((double)(A_u - A) * (1.0 / 128.0)); }
 // Order-preserving key, descending in s: smaller key = higher score.
 __device__ __forceinline__ uint32_t desc_key(float s) {
   uint32_t u = __float_as_uint(s);
   u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending in s
   return ~u;
 }
+__device__ __forceinline__ float undesc_key(uint32_t k) {
+  const uint32_t a = ~k;
+  return __uint_as_float((a & 0x80000000u) ? (a & 0x7FFFFFFFu) : ~a);
+}
 __device__ __forceinline__ bool is_member(float s, int n, float tau, int tie_pos) {
   return s > tau || (s == tau && n <= tie_pos);
 }
 
-// Block-wide exclusive scan of one value per thread (256 threads).
+struct RowGeom {
+  int r, b, row, k0, L, U, qrow;
+  int64_t slot0;   // slot of unit 0 of this row
+};
+__device__ __forceinline__ RowGeom row_geom(const ProbDev& p, int row) {
+  RowGeom g;
+  g.row = row;
+  g.r = row / p.batch;
+  g.b = row % p.batch;
+  g.k0 = p.cu_k[g.b];
+  g.L = p.cu_k[g.b + 1] - g.k0;
+  g.U = max(1, (g.L + kChunk - 1) / kChunk);
+  g.qrow = p.cu_q[g.b];
+  g.slot0 = (int64_t)g.r * slots_per_r(p) + g.k0 / kChunk + g.b;
+  return g;
+}
+
+// ---- block-wide helpers (256 threads, fixed evaluation order)
 template <typename V>
 __device__ V block_exscan(V x, V* tmp /* >= 4 */, V& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -99,389 +171,751 @@ __device__ V block_exscan(V x, V* tmp /* >= 4 */, V& total) {
     if (w < wid) off += tmp[w];
     total += tmp[w];
   }
+  __syncthreads();
   return off + inc - x;
 }
-
-__global__ void clear_u32(uint32_t* p, int n) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+template <typename V>
+__device__ V block_max(V x, V* tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  __syncthreads();
+  if (lane == 0) tmp[wid] = x;
+  __syncthreads();
+  V m = tmp[0];
+#pragma unroll
+  for (int w = 1; w < kThreads / 64; ++w) m = max(m, tmp[w]);
+  __syncthreads();
+  return m;
+}
+__device__ double block_sum_f64(double x, double* tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  __syncthreads();
+  if (lane == 0) tmp[wid] = x;
+  __syncthreads();
+  const double t = (tmp[0] + tmp[1]) + (tmp[2] + tmp[3]);
+  __syncthreads();
+  return t;
+}
+// exclusive float64 scan over the threads (fixed order), plus the total
+__device__ double block_exscan_f64(double x, double* tmp, double& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  double inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[wid] = inc;
+  __syncthreads();
+  double off = 0.0;
+  for (int w = 0; w < wid; ++w) off += tmp[w];
+  total = ((tmp[0] + tmp[1]) + tmp[2]) + tmp[3];
+  __syncthreads();
+  return off + (inc - x);
 }
 
+// One key's 16 index values as raw registers, loaded ahead of use.
+template <typename T> struct KeyRaw;
+template <> struct KeyRaw<bf16_t> {
+  uint4 a, b;
+  __device__ __forceinline__ void load(const bf16_t* kp) {
+    a = reinterpret_cast<const uint4*>(kp)[0];
+    b = reinterpret_cast<const uint4*>(kp)[1];
+  }
+  __device__ __forceinline__ float dot(const float* q) const {
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc = fmaf(q[2 * i], __uint_as_float(w[i] << 16), acc);
+      acc = fmaf(q[2 * i + 1], __uint_as_float(w[i] & 0xFFFF0000u), acc);
+    }
+    return acc;
+  }
+};
+template <> struct KeyRaw<float> {
+  float4 v[4];
+  __device__ __forceinline__ void load(const float* kp) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = reinterpret_cast<const float4*>(kp)[i];
+  }
+  __device__ __forceinline__ float dot(const float* q) const {
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc = fmaf(q[4 * i], v[i].x, acc);
+      acc = fmaf(q[4 * i + 1], v[i].y, acc);
+      acc = fmaf(q[4 * i + 2], v[i].z, acc);
+      acc = fmaf(q[4 * i + 3], v[i].w, acc);
+    }
+    return acc;
+  }
+};
+
+// 8 consecutive elements of a pre-RoPE query row (or of W^Q) as float
+__device__ __forceinline__ void load8(const bf16_t* p, float* x) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { x[2 * i] = __uint_as_float(w[i] << 16); x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u); }
+}
+__device__ __forceinline__ void load8(const float* p, float* x) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// ======================================================================= 1. score
 template <typename T>
-__global__ __launch_bounds__(kThreads) void select_decode_kernel(
-    ProbDev p, const T* __restrict__ q_pre, const float* __restrict__ w_q, const T* __restrict__ k_idx,
-    const float* __restrict__ top_p, rtp_selection sel, DecodeWs ws) {
-  typedef typename IdxFrag<T>::type IF;
-  const int row = blockIdx.y;  // r * batch + b
-  const int r = row / p.batch, b = row % p.batch;
-  const int k0 = p.cu_k[b];
-  const int L = p.cu_k[b + 1] - k0;
-  const int nch = (L + kChunk - 1) / kChunk;
+__global__ __launch_bounds__(kThreads) void sel_dec_score(ProbDev p, const T* __restrict__ q_pre,
+                                                          const float* __restrict__ w_q,
+                                                          const T* __restrict__ k_idx, rtp_selection sel,
+                                                          DecodeWs ws) {
+  const RowGeom g = row_geom(p, blockIdx.y);
   const int c = blockIdx.x;
-  if (c >= nch) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int qrow = p.cu_q[b];  // one query per sequence
+  if (c >= g.U || g.U > kMaxUnits) return;
+  const int tid = threadIdx.x;
+  const int64_t slot = g.slot0 + c;
 
   __shared__ T q_s[kIdxDim];
-  __shared__ float red_s[kThreads / 64];
-  __shared__ int last_s;
+  __shared__ unsigned long long hist_s[kNB];
+  __shared__ int red_i[kThreads / 64];
+  __shared__ unsigned long long red_u[kThreads / 64];
 
-  // ---- the rounded indexer query (float64, fixed order: every workgroup gets the same bits);
-  // the pre-RoPE row and W^Q are staged in LDS first
+  // keys n = c*kChunk + tid + 256 j: a wave reads consecutive 32/64-byte rows.  The
+  // first batch of keys is requested before the query projection so the loads overlap it.
+  constexpr int kB = kPer;
+  const T* kb = k_idx + ((size_t)g.r * p.Tk + g.k0) * kIdxDim;
+  float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
+  const int n0 = c * kChunk + tid;
+  KeyRaw<T> raw[kB];
+  auto load_batch = [&](int jb) {
+#pragma unroll
+    for (int t = 0; t < kB; ++t) {
+      const int n = min(n0 + (jb + t) * kThreads, g.L - 1);
+      raw[t].load(kb + (size_t)max(n, 0) * kIdxDim);
+    }
+  };
+  if (g.L > 0) load_batch(0);
+
+  // ---- the rounded indexer query: 16 threads per output dim, 8 products each in
+  // float64, combined by a fixed shuffle tree and rounded once
   {
-    __shared__ float wl[kIdxDim * (kHeadDim + 1)];
-    __shared__ float xl[kHeadDim];
-    for (int e = tid; e < kIdxDim * kHeadDim; e += kThreads)
-      wl[(e >> 7) * (kHeadDim + 1) + (e & 127)] = w_q[(size_t)r * kIdxDim * kHeadDim + e];
-    if (tid < kHeadDim) xl[tid] = Elem<T>::to_f(q_pre[((size_t)qrow * p.R + r) * kHeadDim + tid]);
-    __syncthreads();
-    if (tid < kIdxDim) {
-      double acc = 0.0;
-      for (int d = 0; d < kHeadDim; ++d) acc = fma((double)xl[d], (double)wl[tid * (kHeadDim + 1) + d], acc);
-      T qv = Elem<T>::from_d(acc);
-      q_s[tid] = qv;
-      if (c == 0) ((T*)sel.q_idx)[((size_t)r * p.Tq + qrow) * kIdxDim + tid] = qv;
+    const int dim = tid >> 4, part = tid & 15;
+    float x[8], wv[8];
+    load8(q_pre + ((size_t)g.qrow * p.R + g.r) * kHeadDim + part * 8, x);
+    load8(w_q + ((size_t)g.r * kIdxDim + dim) * kHeadDim + part * 8, wv);
+    double acc = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fma((double)x[i], (double)wv[i], acc);
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+    if (part == 0) {
+      const T qv = Elem<T>::from_d(acc);
+      q_s[dim] = qv;
+      if (c == 0) ((T*)sel.q_idx)[((size_t)g.r * p.Tq + g.qrow) * kIdxDim + dim] = qv;
     }
-    __syncthreads();
   }
-
-  // B operand: the query replicated in all 16 columns
-  IF qf;
-  load_idx_frag(qf, &q_s[4 * (lane >> 4)]);
-
-  // ---- scores of this chunk: 16-key MFMA tiles, waves interleaved
-  const T* kbase = k_idx + ((size_t)r * p.Tk + k0) * kIdxDim;
-  float* sbase = ws.scores + (size_t)r * p.Tk + k0;
-  float tmax = -INFINITY;
-  const int n0 = c * kChunk;
-  const int nend = min(L, n0 + kChunk);
-  for (int t0 = n0 + 16 * wid; t0 < nend; t0 += 16 * (kThreads / 64)) {
-    const int key = t0 + (lane & 15);
-    IF kf;
-    if (key < nend) {
-      load_idx_frag(kf, kbase + (size_t)key * kIdxDim + 4 * (lane >> 4));
-    } else {
+  for (int e = tid; e < kNB; e += kThreads) hist_s[e] = 0ull;
+  __syncthreads();
+  float q[kIdxDim];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kf.v[j] = 0;
-    }
-    f32x4 acc = idx_dot_tile(kf, qf);
-    if ((lane & 15) == 0) {
-      const int kb = t0 + 4 * (lane >> 4);
+  for (int d = 0; d < kIdxDim; ++d) q[d] = Elem<T>::to_f(q_s[d]);
+
+  float s[kPer];
+  float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (kb + i < nend) {
-          const float s = idx_score(acc[i]);
-          sbase[kb + i] = s;
-          tmax = fmaxf(tmax, s);
-        }
+  for (int jb = 0; jb < kPer; jb += kB) {
+    if (jb > 0 && g.L > 0) load_batch(jb);
+#pragma unroll
+    for (int t = 0; t < kB; ++t) {
+      const int n = n0 + (jb + t) * kThreads;
+      s[jb + t] = -INFINITY;
+      if (n < g.L) {
+        s[jb + t] = idx_score(raw[t].dot(q));
+        mx = fmaxf(mx, s[jb + t]);
       }
     }
   }
-  tmax = wave_max(tmax);
-  if (lane == 0) red_s[wid] = tmax;
-  __threadfence();  // every thread's score stores reach device scope before the ticket
-  __syncthreads();
-  if (tid == 0) {
-    float m = red_s[0];
-    for (int w = 1; w < kThreads / 64; ++w) m = fmaxf(m, red_s[w]);
-    ws.cmax[(size_t)row * max_chunks(p) + c] = m;
-    __threadfence();
-    const uint32_t old = atomicAdd(&ws.ticket[row], 1u);
-    last_s = (old == (uint32_t)(nch - 1));
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    if (n < g.L) sb[n] = s[j];
   }
-  __syncthreads();
-  if (!last_s) return;
-  __threadfence();
+  // unit maximum through an order-preserving integer image of the float
+  auto ord = [](float f) { const int i = __float_as_int(f); return i ^ ((i >> 31) & 0x7FFFFFFF); };
+  const int best = block_max<int>(ord(mx), red_i);
+  const bool empty = (g.L == 0) || (c * kChunk >= g.L);
+  const float umax = empty ? 0.f : __int_as_float(best ^ ((best >> 31) & 0x7FFFFFFF));
+  const int A_u = abs_bin(umax);
 
-  // ================= the last workgroup of the row: exact selection
-  __shared__ unsigned long long hm_s[kNB];
-  __shared__ uint32_t hc_s[kNB];
-  __shared__ unsigned long long cand_s[kCap];   // (desc_key(s) << 32) | pos
-  __shared__ unsigned long long scan_u64[kThreads / 64];
-  __shared__ uint32_t scan_u32[kThreads / 64];
-  __shared__ float M_s;
-  __shared__ int ncand_s;
-  __shared__ unsigned long long above_s;   // fixed-point mass strictly before the chosen bin
-  __shared__ uint32_t cabove_s;            // tokens strictly before the chosen bin
-  __shared__ int bin_s;
-  __shared__ uint32_t bincnt_s;
-  __shared__ float tau_s;
-  __shared__ int tie_s;
-  __shared__ int count_s;
-
-  if (tid == 0) {
-    float m = -INFINITY;
-    for (int i = 0; i < nch; ++i) m = fmaxf(m, ws.cmax[(size_t)row * max_chunks(p) + i]);
-    M_s = m;
+  // histogram: one 64-bit atomic per token carries (count << 51) + mass
+  unsigned long long zloc = 0ull;
+  int used = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    if (n < g.L) {
+      const int bin = max(0, min(kNB - 1, A_u - abs_bin(s[j])));
+      const unsigned long long m = mass38(s[j], A_u);
+      atomicAdd(&hist_s[bin], m | (1ull << kCountShift));
+      zloc += m;
+      used = max(used, bin);
+    }
   }
-  __syncthreads();
-  const float M = M_s;
-  const float pp = top_p[b];
-  const float* sc = ws.scores + (size_t)r * p.Tk + k0;
-  int* out_idx = sel.idx + (size_t)r * p.Tk + k0;
+  unsigned long long Z;
+  (void)block_exscan<unsigned long long>(zloc, red_u, Z);
+  used = block_max<int>(used, red_i);   // its barriers also order the histogram atomics before the copy
+  unsigned long long* hg = ws.hist + slot * kNB;
+  for (int e = tid; e <= used; e += kThreads) hg[e] = hist_s[e];
+  if (tid == 0) {
+    UnitMeta mt;
+    mt.A = A_u;
+    mt.used = empty ? -1 : used;
+    mt.Z = Z;
+    ws.meta[slot] = mt;
+  }
+}
 
-  if (!(pp < 1.f)) {  // p >= 1 (or NaN): every key
-    for (int n = tid; n < L; n += kThreads) out_idx[n] = n;
-    if (tid == 0) {
-      sel.count[(size_t)r * p.Tq + qrow] = L;
-      if (sel.tau) sel.tau[(size_t)r * p.Tq + qrow] = -INFINITY;
-      if (sel.tie_pos) sel.tie_pos[(size_t)r * p.Tq + qrow] = 0x7FFFFFFF;
+// Row merge shared by the collect and emit kernels: reference bin A and the
+// per-unit scale factors (identical in every workgroup of the row).
+struct Merge {
+  int A;
+  double Z;
+};
+__device__ Merge row_merge(const DecodeWs& ws, const RowGeom& g, int* A_s, int* used_s, double* f_s, int* itmp,
+                           double* dtmp) {
+  const int tid = threadIdx.x;
+  int amax = -2147483647 - 1;
+  constexpr int PU = kMaxUnits / kThreads;
+  unsigned long long zu[PU];
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid + t * kThreads;
+    zu[t] = 0ull;
+    if (u < g.U) {
+      const UnitMeta mt = ws.meta[g.slot0 + u];
+      A_s[u] = mt.A;
+      used_s[u] = mt.used;
+      zu[t] = mt.Z;
+      if (mt.used >= 0) amax = max(amax, mt.A);
+    }
+  }
+  Merge m;
+  m.A = block_max<int>(amax, itmp);
+  double zl = 0.0;
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid + t * kThreads;
+    if (u < g.U) {
+      const double f = (used_s[u] >= 0) ? unit_scale(A_s[u], m.A) : 0.0;
+      f_s[u] = f;
+      zl += (double)zu[t] * f;
+    }
+  }
+  m.Z = block_sum_f64(zl, dtmp);   // its barriers also publish f_s
+  return m;
+}
+
+// ======================================================================= 2. collect
+__global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const float* __restrict__ top_p,
+                                                            DecodeWs ws) {
+  const RowGeom g = row_geom(p, blockIdx.y);
+  const int c = blockIdx.x;
+  if (c >= g.U || g.U > kMaxUnits) return;
+  const int tid = threadIdx.x;
+  const int64_t slot = g.slot0 + c;
+  const float pp = top_p[g.b];
+
+  if (g.L == 0 || !(pp < 1.f)) {   // nothing to choose: empty row, or every key
+    if (c == 0 && tid == 0) {
+      RowState rs = {};
+      rs.mode = (g.L == 0) ? ROW_EMPTY : ROW_ALL;
+      ws.rows[g.row] = rs;
     }
     return;
   }
 
-  // every pass over the row's scores keeps 8 independent loads in flight per thread
-  auto for_scores = [&](auto&& fn) {
-    constexpr int U = 8;
-    for (int n0 = tid; n0 < L; n0 += U * kThreads) {
-      float sv8[U];
+  // this unit's scores, requested before the merge so the loads overlap it
+  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
+  const int n0 = c * kChunk + tid;
+  float s[kPer];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int n = n0 + u * kThreads;
-        sv8[u] = (n < L) ? sc[n] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int n = n0 + u * kThreads;
-        if (n < L) fn(sv8[u], n);
-      }
-    }
-  };
-
-  // ---- L1 histogram
-  for (int i = tid; i < kNB; i += kThreads) { hm_s[i] = 0ull; hc_s[i] = 0u; }
-  __syncthreads();
-  for_scores([&](float s, int n) {
-    const uint32_t bin = l1_bin(s, M);
-    atomicAdd(&hm_s[bin], (unsigned long long)mass_fix(s, M));
-    atomicAdd(&hc_s[bin], 1u);
-  });
-  __syncthreads();
-
-  // ---- scan: first bin whose inclusive cumulative mass reaches p * Z
-  constexpr int kPer = kNB / kThreads;
-  unsigned long long lm = 0ull;
-  uint32_t lc = 0u;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) { lm += hm_s[tid * kPer + j]; lc += hc_s[tid * kPer + j]; }
-  unsigned long long Z;
-  const unsigned long long pre_m = block_exscan<unsigned long long>(lm, scan_u64, Z);
-  uint32_t Ncnt;
-  const uint32_t pre_c = block_exscan<uint32_t>(lc, scan_u32, Ncnt);
-  const double target = fmax((double)pp * (double)Z, 1.0);
-  if ((double)pre_m < target && target <= (double)(pre_m + lm)) {
-    unsigned long long cm = pre_m;
-    uint32_t cc = pre_c;
-    for (int j = 0; j < kPer; ++j) {
-      const int bi = tid * kPer + j;
-      if ((double)(cm + hm_s[bi]) >= target) {
-        bin_s = bi; above_s = cm; cabove_s = cc; bincnt_s = hc_s[bi];
-        break;
-      }
-      cm += hm_s[bi];
-      cc += hc_s[bi];
-    }
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    s[j] = (n < g.L) ? sb[n] : -INFINITY;
   }
-  __syncthreads();
-  const int bin1 = bin_s;
 
-  // ---- narrow the candidate set until it fits: radix digits of desc_key(s)
-  // within bin1 (levels of 11, 11 and 10 bits); prefix/shift describe the range.
-  uint32_t prefix = 0u;
-  int shift = 32;          // key bits already fixed: (32 - shift)
-  while (bincnt_s > (uint32_t)kCap && shift > 0) {
-    const int nbits = (shift >= 11) ? 11 : shift;
-    const int nshift = shift - nbits;
-    for (int i = tid; i < kNB; i += kThreads) { hm_s[i] = 0ull; hc_s[i] = 0u; }
-    __syncthreads();
-    for_scores([&](float s, int n) {
-      if ((int)l1_bin(s, M) != bin1) return;
-      const uint32_t key = desc_key(s);
-      if (shift < 32 && (key >> shift) != prefix) return;
-      const uint32_t dig = (key >> nshift) & ((1u << nbits) - 1u);
-      atomicAdd(&hm_s[dig], (unsigned long long)mass_fix(s, M));
-      atomicAdd(&hc_s[dig], 1u);
-    });
-    __syncthreads();
-    if (tid == 0) {
-      unsigned long long cm = above_s;
-      uint32_t cc = cabove_s;
-      for (int d = 0; d < (1 << nbits); ++d) {
-        if (hc_s[d] == 0u) continue;
-        if ((double)(cm + hm_s[d]) >= target) {
-          above_s = cm; cabove_s = cc; bincnt_s = hc_s[d]; bin_s = d;
-          break;
+  __shared__ int A_s[kMaxUnits];
+  __shared__ int used_s[kMaxUnits];
+  __shared__ double f_s[kMaxUnits];
+  __shared__ double dtmp[kThreads / 64];
+  __shared__ int itmp[kThreads / 64];
+  __shared__ uint32_t utmp[kThreads / 64];
+  __shared__ int jstar_s, lastne_s;
+  __shared__ double above_s;
+  __shared__ uint32_t cabove_s, bincnt_s;
+
+  const Merge mg = row_merge(ws, g, A_s, used_s, f_s, itmp, dtmp);
+  const int A = mg.A;
+  const double target = fmax((double)pp * mg.Z, 1.0);
+
+  // ---- row bins, kBinsPerPass at a time (8 consecutive per thread): the first bin
+  // whose cumulative mass reaches the target.  A bin's mass above is computed by
+  // exactly one thread, so every bin has one well-defined value.
+  constexpr int BT = kBinsPerPass / kThreads;
+  if (tid == 0) { jstar_s = kNB; lastne_s = -1; }
+  __syncthreads();
+  double carry = 0.0;
+  uint32_t ccarry = 0u;
+  int my_last = -1;
+  double my_last_above = 0.0;
+  uint32_t my_last_cab = 0u, my_last_cnt = 0u;
+  for (int base = 0; base < kNB; base += kBinsPerPass) {
+    const int J0 = base + tid * BT;
+    double mb[BT];
+    uint32_t cb[BT];
+#pragma unroll
+    for (int i = 0; i < BT; ++i) { mb[i] = 0.0; cb[i] = 0u; }
+    // four units' bins in flight at once
+    for (int u0 = 0; u0 < g.U; u0 += 4) {
+      unsigned long long e[4][BT];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = u0 + k;
+        const int used = (u < g.U) ? used_s[u] : -1;
+        const int d = (u < g.U) ? A - A_s[u] : 0;
+        const unsigned long long* hu = ws.hist + (g.slot0 + min(u, g.U - 1)) * kNB;
+#pragma unroll
+        for (int i = 0; i < BT; ++i) {
+          const int jl = J0 + i - d;
+          e[k][i] = (jl >= 0 && jl <= used && J0 + i < kNB - 1) ? hu[jl] : 0ull;
         }
-        cm += hm_s[d];
-        cc += hc_s[d];
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int u = u0 + k;
+        if (u >= g.U) continue;
+        const int used = used_s[u];
+        if (J0 + BT - 1 == kNB - 1 && used >= 0) {   // the last row bin also takes every deeper unit bin
+          const unsigned long long* hu = ws.hist + (g.slot0 + u) * kNB;
+          for (int j = max(kNB - 1 - (A - A_s[u]), 0); j <= used; ++j) e[k][BT - 1] += hu[j];
+        }
+        const double f = f_s[u];
+#pragma unroll
+        for (int i = 0; i < BT; ++i) {
+          mb[i] += (double)(e[k][i] & kMassMask) * f;
+          cb[i] += (uint32_t)(e[k][i] >> kCountShift);
+        }
       }
     }
+    double tm = 0.0;
+    uint32_t tc = 0u;
+#pragma unroll
+    for (int i = 0; i < BT; ++i) { tm += mb[i]; tc += cb[i]; }
+    double ptot;
+    uint32_t ctot;
+    double pre = carry + block_exscan_f64(tm, dtmp, ptot);
+    uint32_t cpre = ccarry + block_exscan<uint32_t>(tc, utmp, ctot);
+    int mine = -1;
+    double mine_above = 0.0;
+    uint32_t mine_cab = 0u, mine_cnt = 0u;
+#pragma unroll
+    for (int i = 0; i < BT; ++i) {
+      if (cb[i] > 0u) {
+        if (mine < 0 && pre + mb[i] >= target) { mine = J0 + i; mine_above = pre; mine_cab = cpre; mine_cnt = cb[i]; }
+        my_last = J0 + i; my_last_above = pre; my_last_cab = cpre; my_last_cnt = cb[i];
+      }
+      pre += mb[i];
+      cpre += cb[i];
+    }
+    if (mine >= 0) atomicMin(&jstar_s, mine);
     __syncthreads();
-    prefix = (shift < 32 ? (prefix << nbits) : 0u) | (uint32_t)bin_s;
-    shift = nshift;
+    if (jstar_s < kNB) {
+      if (mine == jstar_s) { above_s = mine_above; cabove_s = mine_cab; bincnt_s = mine_cnt; }
+      __syncthreads();
+      break;
+    }
+    carry += ptot;
+    ccarry += ctot;
   }
+  if (jstar_s == kNB) {   // rounding left the target just out of reach: the last non-empty bin
+    atomicMax(&lastne_s, my_last);
+    __syncthreads();
+    if (my_last >= 0 && my_last == lastne_s) {
+      jstar_s = my_last; above_s = my_last_above; cabove_s = my_last_cab; bincnt_s = my_last_cnt;
+    }
+    __syncthreads();
+  }
+  const int jstar = jstar_s;
 
-  if (bincnt_s > (uint32_t)kCap) {
-    // exact ties (identical scores): admit them by ascending position.
-    // The tied score value: any token with key == prefix.
-    __shared__ float tie_val_s;
-    for_scores([&](float s, int n) {
-      if ((int)l1_bin(s, M) == bin1 && desc_key(s) == prefix) tie_val_s = s;
-    });
-    __syncthreads();
-    const float tv = tie_val_s;
-    const unsigned long long mt = (unsigned long long)mass_fix(tv, M);
-    // k = number of tied tokens needed: smallest k with above + k * mt >= target
-    const double need = target - (double)above_s;
-    long long kneed = (mt > 0) ? (long long)ceil(need / (double)mt) : (long long)bincnt_s;
-    if (kneed < 1) kneed = 1;
-    if (kneed > (long long)bincnt_s) kneed = bincnt_s;
-    // position of the kneed-th tied token: block-wide running count in position order
-    __shared__ int tiepos_s;
-    __shared__ int run_s;
-    if (tid == 0) run_s = 0;
-    __syncthreads();
-    for (int base = 0; base < L; base += kThreads) {
-      const int n = base + tid;
-      const uint32_t f = (n < L && sc[n] == tv) ? 1u : 0u;
-      uint32_t tot;
-      const uint32_t ex = block_exscan<uint32_t>(f, scan_u32, tot);
-      const int before = run_s;
-      if (f && (long long)(before + ex + 1) == kneed) tiepos_s = n;
-      __syncthreads();
-      if (tid == 0) run_s = before + (int)tot;
-      __syncthreads();
-      if ((long long)run_s >= kneed) break;
+  // ---- this unit: tokens above the crossing bin, and the bin's tokens as candidates
+  uint32_t nabove = 0u, nbin = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    if (n < g.L) {
+      const int J = min(kNB - 1, A - abs_bin(s[j]));
+      nabove += (J < jstar) ? 1u : 0u;
+      nbin += (J == jstar) ? 1u : 0u;
     }
-    if (tid == 0) {
-      tau_s = tv;
-      tie_s = tiepos_s;
-      count_s = (int)cabove_s + (int)kneed;
+  }
+  uint32_t tot_above, tot_bin;
+  (void)block_exscan<uint32_t>(nabove, utmp, tot_above);
+  uint32_t o = block_exscan<uint32_t>(nbin, utmp, tot_bin);
+  unsigned long long* cd = ws.cand + slot * kCapUnit;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    if (n < g.L && min(kNB - 1, A - abs_bin(s[j])) == jstar) {
+      if (o < (uint32_t)kCapUnit) cd[o] = ((unsigned long long)desc_key(s[j]) << 32) | (uint32_t)n;
+      ++o;
     }
-    __syncthreads();
+  }
+  if (tid == 0) {
+    UnitCnt uc = {tot_above, tot_bin};
+    ws.ucnt[slot] = uc;
+    ws.fu[slot] = f_s[c];
+    if (c == 0) {
+      RowState rs;
+      rs.above = above_s;
+      rs.target = target;
+      rs.mode = ROW_NORMAL;
+      rs.A = A;
+      rs.jstar = jstar;
+      rs.cabove = cabove_s;
+      rs.bincnt = bincnt_s;
+      rs.pad = 0;
+      ws.rows[g.row] = rs;
+    }
+  }
+}
+
+// ======================================================================= 3. emit
+__global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selection sel, DecodeWs ws) {
+  const RowGeom g = row_geom(p, blockIdx.y);
+  const int c = blockIdx.x;
+  if (c >= g.U || g.U > kMaxUnits) return;
+  const int tid = threadIdx.x;
+  const RowState rs = ws.rows[g.row];
+  if (rs.mode == ROW_EMPTY) {
+    if (c == 0 && tid == 0) {
+      sel.count[(size_t)g.r * p.Tq + g.qrow] = 0;
+      if (sel.tau) sel.tau[(size_t)g.r * p.Tq + g.qrow] = INFINITY;
+      if (sel.tie_pos) sel.tie_pos[(size_t)g.r * p.Tq + g.qrow] = 0x7FFFFFFF;
+    }
+    return;
+  }
+  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
+  int* out = sel.idx + (size_t)g.r * p.Tk + g.k0;
+  // kPer consecutive keys per thread, so the unit's members come out ascending
+  const int nb = c * kChunk + tid * kPer;
+  float s[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) s[j] = (nb + j < g.L) ? sb[nb + j] : -INFINITY;
+
+  __shared__ int A_s[kMaxUnits];
+  __shared__ double f_s[kMaxUnits];
+  __shared__ uint32_t cmem_s[kMaxUnits];     // members per unit among the candidates
+  __shared__ uint32_t cbase_s[kMaxUnits];
+  __shared__ unsigned long long cand_s[kCap];
+  __shared__ short order_s[kCap];            // candidate index by rank
+  __shared__ double dtmp[kThreads / 64];
+  __shared__ int itmp[kThreads / 64];
+  __shared__ uint32_t utmp[kThreads / 64];
+  __shared__ float tau_s;
+  __shared__ int tie_s, count_s, js_s;
+  __shared__ uint32_t off_s;
+
+  float tau = -INFINITY;
+  int tie = 0x7FFFFFFF;
+  uint32_t off = 0u;
+  const bool all = (rs.mode == ROW_ALL);
+  if (all) {
+    off = (uint32_t)(c * kChunk);
+    if (c == 0 && tid == 0) {
+      sel.count[(size_t)g.r * p.Tq + g.qrow] = g.L;
+      if (sel.tau) sel.tau[(size_t)g.r * p.Tq + g.qrow] = -INFINITY;
+      if (sel.tie_pos) sel.tie_pos[(size_t)g.r * p.Tq + g.qrow] = 0x7FFFFFFF;
+    }
   } else {
-    // ---- collect the candidates of the final bin
-    if (tid == 0) ncand_s = 0;
-    __syncthreads();
-    for_scores([&](float s, int n) {
-      if ((int)l1_bin(s, M) != bin1) return;
-      if (shift < 32 && (desc_key(s) >> shift) != prefix) return;
-      const int slot = atomicAdd(&ncand_s, 1);
-      cand_s[slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
-    });
-    __syncthreads();
-    const int nc = ncand_s;
-    int npow = 64;
-    while (npow < nc) npow <<= 1;
-    for (int i = nc + tid; i < npow; i += kThreads) cand_s[i] = ~0ull;
-    __syncthreads();
-    // bitonic sort of the padded candidates, ascending (score desc, position asc)
-    for (int k = 2; k <= npow; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < npow; i += kThreads) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const unsigned long long a = cand_s[i], bb = cand_s[ixj];
-            const bool up = ((i & k) == 0);
-            if ((a > bb) == up) { cand_s[i] = bb; cand_s[ixj] = a; }
+    const int A = rs.A;
+    const double target = rs.target;
+    // per unit: reference bin and scale of the row merge, candidate count
+    constexpr int PU = kMaxUnits / kThreads;
+    uint32_t nin = 0u, cmax = 0u;
+    uint32_t vin[PU];
+#pragma unroll
+    for (int t = 0; t < PU; ++t) {
+      const int u = tid * PU + t;
+      vin[t] = 0u;
+      if (u < g.U) {
+        A_s[u] = ws.meta[g.slot0 + u].A;
+        f_s[u] = ws.fu[g.slot0 + u];
+        vin[t] = ws.ucnt[g.slot0 + u].inbin;
+        cmem_s[u] = 0u;
+      }
+      nin += vin[t];
+      cmax = max(cmax, vin[t]);
+    }
+    uint32_t ntot;
+    uint32_t run = block_exscan<uint32_t>(nin, utmp, ntot);
+#pragma unroll
+    for (int t = 0; t < PU; ++t) {
+      const int u = tid * PU + t;
+      if (u < g.U) cbase_s[u] = run;
+      run += vin[t];
+    }
+    cmax = block_max<uint32_t>(cmax, utmp);
+    const bool fits = (ntot == rs.bincnt) && (ntot <= (uint32_t)kCap) && (cmax <= (uint32_t)kCapUnit) && ntot > 0u;
+
+    if (fits) {
+      const int nc = (int)ntot;
+      // gather: candidate k belongs to the last unit whose base is <= k
+      for (int kk = tid; kk < nc; kk += kThreads) {
+        int lo = 0, hi = g.U - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (cbase_s[mid] <= (uint32_t)kk) lo = mid; else hi = mid - 1;
+        }
+        cand_s[kk] = ws.cand[(g.slot0 + lo) * kCapUnit + (kk - (int)cbase_s[lo])];
+      }
+      __syncthreads();
+      // rank of every candidate in (desc_key, position) order: keys are distinct
+      for (int i = tid; i < nc; i += kThreads) {
+        const unsigned long long ki = cand_s[i];
+        int rank = 0;
+        for (int j = 0; j < nc; ++j) rank += (cand_s[j] < ki) ? 1 : 0;
+        order_s[rank] = (short)i;
+      }
+      __syncthreads();
+      // cumulative masses in rank order: G consecutive ranks per thread, fixed order
+      constexpr int G = kCap / kThreads;
+      double ms[G];
+      double loc = 0.0;
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+        const int rk = tid * G + t;
+        ms[t] = 0.0;
+        if (rk < nc) {
+          const unsigned long long kv = cand_s[order_s[rk]];
+          const float sv = undesc_key((uint32_t)(kv >> 32));
+          const uint32_t n = (uint32_t)(kv & 0xFFFFFFFFull);
+          const int u = (int)min(n / (uint32_t)kChunk, (uint32_t)(g.U - 1));
+          ms[t] = (double)mass38(sv, A_s[u]) * f_s[u];
+        }
+        loc += ms[t];
+      }
+      double tt;
+      double pre = block_exscan_f64(loc, dtmp, tt) + rs.above;
+      if (tid == 0) js_s = nc - 1;   // if rounding hides the crossing: the last candidate
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < G; ++t) {
+        const int rk = tid * G + t;
+        pre += ms[t];
+        if (rk < nc && pre >= target) { atomicMin(&js_s, rk); break; }
+      }
+      __syncthreads();
+      const int js = js_s;
+      if (tid == 0) {
+        const unsigned long long kv = cand_s[order_s[js]];
+        tau_s = undesc_key((uint32_t)(kv >> 32));
+        tie_s = (int)(uint32_t)(kv & 0xFFFFFFFFull);
+        // every token scoring exactly tau is a candidate: if none is left out, S = {s >= tau}
+        if (!(js + 1 < nc && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
+        count_s = (int)rs.cabove + js + 1;
+      }
+      for (int rk = tid; rk <= js; rk += kThreads) {
+        const uint32_t n = (uint32_t)(cand_s[order_s[rk]] & 0xFFFFFFFFull);
+        atomicAdd(&cmem_s[min(n / (uint32_t)kChunk, (uint32_t)(g.U - 1))], 1u);
+      }
+      __syncthreads();
+      // offset of this unit: members of the units before it
+      uint32_t ol = 0u;
+      for (int u = tid; u < c; u += kThreads) ol += ws.ucnt[g.slot0 + u].above + cmem_s[u];
+      uint32_t otot;
+      (void)block_exscan<uint32_t>(ol, utmp, otot);
+      if (tid == 0) off_s = otot;
+      __syncthreads();
+    } else {
+      // ---- crowded crossing bin: resolve it from the row's scores, radix digits of
+      // desc_key inside the bin (11 + 11 + 10 bits), then exact ties by position
+      // digit histograms share the candidate buffer (used only once the range fits)
+      unsigned long long* hm2 = cand_s;
+      uint32_t* hc2 = reinterpret_cast<uint32_t*>(cand_s + 2048);
+      __shared__ int dig_s;
+      __shared__ double ab_s;
+      __shared__ uint32_t cab_s, cnt_s;
+      const int jstar = rs.jstar;
+      if (tid == 0) { ab_s = rs.above; cab_s = rs.cabove; cnt_s = rs.bincnt; }
+      __syncthreads();
+      auto in_bin = [&](float sv) { return min(kNB - 1, A - abs_bin(sv)) == jstar; };
+      uint32_t prefix = 0u;
+      int shift = 32;
+      while (cnt_s > (uint32_t)kCap && shift > 0) {
+        const int nbits = (shift >= 11) ? 11 : shift;
+        const int nshift = shift - nbits;
+        for (int i = tid; i < 2048; i += kThreads) { hm2[i] = 0ull; hc2[i] = 0u; }
+        __syncthreads();
+        // digit masses in fixed point relative to the row reference (exact sums)
+        for (int n = tid; n < g.L; n += kThreads) {
+          const float sv = sb[n];
+          if (!in_bin(sv)) continue;
+          const uint32_t key = desc_key(sv);
+          if (shift < 32 && (key >> shift) != prefix) continue;
+          const uint32_t dg = (key >> nshift) & ((1u << nbits) - 1u);
+          atomicAdd(&hm2[dg], mass38(sv, A));
+          atomicAdd(&hc2[dg], 1u);
+        }
+        __syncthreads();
+        if (tid == 0) {
+          double cm = ab_s;
+          uint32_t cc = cab_s;
+          int dsel = -1;
+          bool found = false;
+          for (int d = 0; d < (1 << nbits); ++d) {
+            if (hc2[d] == 0u) continue;
+            dsel = d;
+            if (cm + (double)hm2[d] >= target) { found = true; break; }
+            cm += (double)hm2[d];
+            cc += hc2[d];
           }
+          if (dsel < 0) dsel = 0;
+          if (!found) {  // rounding hid the crossing: the last non-empty digit
+            cm = ab_s; cc = cab_s;
+            for (int d = 0; d < dsel; ++d) { cm += (double)hm2[d]; cc += hc2[d]; }
+          }
+          ab_s = cm; cab_s = cc; cnt_s = hc2[dsel]; dig_s = dsel;
+        }
+        __syncthreads();
+        prefix = (shift < 32 ? (prefix << nbits) : 0u) | (uint32_t)dig_s;
+        shift = nshift;
+      }
+      if (cnt_s > (uint32_t)kCap) {
+        // exact ties: the tied value is the key `prefix`; admit them by ascending position
+        const float tv = undesc_key(prefix);
+        const double mt = (double)mass38(tv, A);
+        const double need = target - ab_s;
+        long long kneed = (mt > 0.0) ? (long long)ceil(need / mt) : (long long)cnt_s;
+        kneed = max(1ll, min(kneed, (long long)cnt_s));
+        __shared__ int runt_s, tiepos_s;
+        if (tid == 0) { runt_s = 0; tiepos_s = -1; }
+        __syncthreads();
+        for (int base = 0; base < g.L; base += kThreads) {
+          const int n = base + tid;
+          const uint32_t f = (n < g.L && sb[n] == tv) ? 1u : 0u;
+          uint32_t tt;
+          const uint32_t ex = block_exscan<uint32_t>(f, utmp, tt);
+          const int before = runt_s;
+          if (f && (long long)(before + (int)ex + 1) == kneed) tiepos_s = n;
+          __syncthreads();
+          if (tid == 0) runt_s = before + (int)tt;
+          __syncthreads();
+          if ((long long)runt_s >= kneed) break;
+        }
+        if (tid == 0) { tau_s = tv; tie_s = tiepos_s; count_s = (int)cab_s + (int)kneed; }
+        __syncthreads();
+      } else {
+        // the remaining range fits: collect it, rank it and walk it
+        __shared__ int nc_s;
+        if (tid == 0) nc_s = 0;
+        __syncthreads();
+        for (int n = tid; n < g.L; n += kThreads) {
+          const float sv = sb[n];
+          if (!in_bin(sv)) continue;
+          if (shift < 32 && (desc_key(sv) >> shift) != prefix) continue;
+          const int sl = atomicAdd(&nc_s, 1);
+          if (sl < kCap) cand_s[sl] = ((unsigned long long)desc_key(sv) << 32) | (uint32_t)n;
+        }
+        __syncthreads();
+        const int nc = min(nc_s, kCap);
+        for (int i = tid; i < nc; i += kThreads) {
+          const unsigned long long ki = cand_s[i];
+          int rank = 0;
+          for (int j = 0; j < nc; ++j) rank += (cand_s[j] < ki) ? 1 : 0;
+          order_s[rank] = (short)i;
+        }
+        __syncthreads();
+        if (tid == 0) {
+          double cm = ab_s;
+          int js = max(nc - 1, 0);
+          for (int i = 0; i < nc; ++i) {
+            const float sv = undesc_key((uint32_t)(cand_s[order_s[i]] >> 32));
+            const double mi = (double)mass38(sv, A);
+            if (cm + mi >= target) { js = i; break; }
+            cm += mi;
+          }
+          const unsigned long long kv = cand_s[order_s[js]];
+          tau_s = undesc_key((uint32_t)(kv >> 32));
+          tie_s = (int)(uint32_t)(kv & 0xFFFFFFFFull);
+          if (!(js + 1 < nc && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
+          count_s = (int)cab_s + js + 1;
         }
         __syncthreads();
       }
+      // offset of this unit: members among the keys before it
+      const float tv = tau_s;
+      const int tp = tie_s;
+      uint32_t ol = 0u;
+      for (int n = tid; n < c * kChunk && n < g.L; n += kThreads) ol += is_member(sb[n], n, tv, tp) ? 1u : 0u;
+      uint32_t otot;
+      (void)block_exscan<uint32_t>(ol, utmp, otot);
+      if (tid == 0) off_s = otot;
+      __syncthreads();
     }
-    // crossing candidate: 4 consecutive candidates per thread
-    unsigned long long cm = 0ull;
-    float sv[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid * 4 + j;
-      if (i < nc) {
-        const uint32_t kk = (uint32_t)(cand_s[i] >> 32);
-        const uint32_t asc = ~kk;
-        const uint32_t bits = (asc & 0x80000000u) ? (asc & 0x7FFFFFFFu) : ~asc;
-        sv[j] = __uint_as_float(bits);
-        cm += mass_fix(sv[j], M);
-      } else {
-        sv[j] = 0.f;
-      }
+    tau = tau_s;
+    tie = tie_s;
+    off = off_s;
+    if (c == 0 && tid == 0) {
+      sel.count[(size_t)g.r * p.Tq + g.qrow] = count_s;
+      if (sel.tau) sel.tau[(size_t)g.r * p.Tq + g.qrow] = tau;
+      if (sel.tie_pos) sel.tie_pos[(size_t)g.r * p.Tq + g.qrow] = tie;
     }
-    unsigned long long tot;
-    unsigned long long pre = block_exscan<unsigned long long>(cm, scan_u64, tot) + above_s;
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid * 4 + j;
-      if (i >= nc) break;
-      const unsigned long long mj = mass_fix(sv[j], M);
-      if ((double)pre < target && (double)(pre + mj) >= target) {
-        tau_s = sv[j];
-        tie_s = (int)(uint32_t)(cand_s[i] & 0xFFFFFFFFull);
-        count_s = (int)cabove_s + i + 1;
-        // the candidates hold every token scoring exactly tau: if none is left out, S = {s >= tau}
-        if (!(i + 1 < nc && (uint32_t)(cand_s[i + 1] >> 32) == (uint32_t)(cand_s[i] >> 32))) tie_s = 0x7FFFFFFF;
-      }
-      pre += mj;
-    }
-    __syncthreads();
   }
 
-  const float tau = tau_s;
-  const int tie_pos = tie_s;
-  // ---- emit the ascending list: 8 consecutive positions per thread per round
-  int run = 0;
-  constexpr int E = 8;
-  for (int base = 0; base < L; base += E * kThreads) {
-    float sv8[E];
+  // ---- this unit's members, ascending
+  uint32_t fl = 0u, cnt = 0u;
 #pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int n = base + E * tid + j;
-      sv8[j] = (n < L) ? sc[n] : 0.f;
-    }
-    uint32_t fl = 0u, lc2 = 0u;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const int n = base + E * tid + j;
-      if (n < L && is_member(sv8[j], n, tau, tie_pos)) { fl |= 1u << j; ++lc2; }
-    }
-    uint32_t tot2;
-    uint32_t ex = block_exscan<uint32_t>(lc2, scan_u32, tot2);
-    int o = run + (int)ex;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      if (fl & (1u << j)) out_idx[o++] = base + E * tid + j;
-    }
-    run += (int)tot2;
+  for (int j = 0; j < kPer; ++j) {
+    const int n = nb + j;
+    const bool m = (n < g.L) && (all || is_member(s[j], n, tau, tie));
+    fl |= (m ? 1u : 0u) << j;
+    cnt += m ? 1u : 0u;
   }
-  if (tid == 0) {
-    sel.count[(size_t)r * p.Tq + qrow] = count_s;
-    if (sel.tau) sel.tau[(size_t)r * p.Tq + qrow] = tau;
-    if (sel.tie_pos) sel.tie_pos[(size_t)r * p.Tq + qrow] = tie_pos;
-  }
+  uint32_t tt;
+  uint32_t o = off + block_exscan<uint32_t>(cnt, utmp, tt);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if ((fl & (1u << j)) && o < (uint32_t)g.L) out[o++] = nb + j;
 }
 
 }  // namespace
 
-size_t ws_select_decode(const ProbDev& p) {
-  size_t o = 0;
-  o = align256(o + sizeof(float) * (size_t)p.R * p.Tk);
-  o = align256(o + sizeof(float) * (size_t)p.R * p.batch * max_chunks(p));
-  o = align256(o + sizeof(uint32_t) * (size_t)p.R * p.batch);
-  return o;
-}
+size_t ws_select_decode(const ProbDev& p) { return ws_layout(p, nullptr, nullptr); }
 
 hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
                                 const void* k_idx, const float* top_p, const rtp_selection& sel,
                                 void* ws, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
-  DecodeWs w = carve(p, ws);
+  DecodeWs w;
+  ws_layout(p, ws, &w);
   const int nrows = p.R * p.batch;
-  hipLaunchKernelGGL(clear_u32, dim3((nrows + 255) / 256), dim3(256), 0, s, w.ticket, nrows);
-  dim3 grid(max_chunks(p), nrows);
+  dim3 grid(max(1, max_units(p)), nrows);
   if (bf16)
-    hipLaunchKernelGGL(select_decode_kernel<bf16_t>, grid, dim3(kThreads), 0, s, p, (const bf16_t*)q_pre,
-                       w_q, (const bf16_t*)k_idx, top_p, sel, w);
+    hipLaunchKernelGGL(sel_dec_score<bf16_t>, grid, dim3(kThreads), 0, s, p, (const bf16_t*)q_pre, w_q,
+                       (const bf16_t*)k_idx, sel, w);
   else
-    hipLaunchKernelGGL(select_decode_kernel<float>, grid, dim3(kThreads), 0, s, p, (const float*)q_pre,
-                       w_q, (const float*)k_idx, top_p, sel, w);
+    hipLaunchKernelGGL(sel_dec_score<float>, grid, dim3(kThreads), 0, s, p, (const float*)q_pre, w_q,
+                       (const float*)k_idx, sel, w);
+  hipLaunchKernelGGL(sel_dec_collect, grid, dim3(kThreads), 0, s, p, top_p, w);
+  hipLaunchKernelGGL(sel_dec_emit, grid, dim3(kThreads), 0, s, p, sel, w);
   return hipGetLastError();
 }
+
+int select_decode_max_keys() { return kMaxUnits * kChunk; }
 
 }  // namespace rtp
