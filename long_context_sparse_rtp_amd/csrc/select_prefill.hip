@@ -15,22 +15,24 @@
 // each sweep over the keys recomputes them with the same MFMA, so every sweep
 // (and the attention kernel) sees identical float32 values.
 //
-// Per token the sweeps use one FMA of the raw indexer dot product:
-//   u    = (top - s) * log2(e) * 16   sixteenths of an octave below top
-//          (top >= max s: a Cauchy-Schwarz bound, or a rebased one)
-//   mass = 2^(-u/16) as 31-bit fixed point, summed in 64-bit LDS integers
-//          (exact and order-independent: the result is deterministic)
-//   K    = floor(u * 2^16) clamped to 32 bits (the same FMA with both
-//          operands scaled by 2^16, so K >> 16 == floor(u) exactly)
-// Sweep 1 histograms the mass over 256 bins of floor(u) (the last one open-
-// ended) and scans for the bin where the cumulative mass reaches p * Z.
-// Refinement sweeps histogram (mass, count) over the next 8 bits of K inside
-// the chosen range (counting the tokens above it on the first pass) until the
-// crossing range holds at most 128 tokens; a collect sweep then gathers them,
-// they are sorted by (score desc, position asc) and the crossing token gives
-// tau and tie_pos.  Exact ties too large to collect switch the key to the
-// score's bit pattern and then to the position (general path, degenerate
-// inputs only).
+// Per token, with u = (top - s) log2(e) * B the distance below the reference
+// top >= max s in units of 1/B octave (B = kBinsPerOctave; top is a
+// Cauchy-Schwarz bound, rebased when loose):
+//   mass = 2^(31 - (top - s) log2 e) as an integer, one FMA and one exp2 of
+//          the raw dot product, summed in 64-bit LDS integers (exact and
+//          order-independent: the result is deterministic);
+//   K    = floor(u * 2^16) clamped to 32 bits (K >> 16 == floor(u)).
+// Sweep 1 histograms the mass over kNB1 bins of floor(u) (the last one open-
+// ended); 16 threads per row scan it for the bin where the cumulative mass
+// reaches p * Z.  A refinement sweep histograms the mass over the next 8 bits
+// of K inside the chosen range and keeps the crossing digit; a collect sweep
+// then counts the tokens above the range and gathers the range's tokens.  If
+// they are at most 128, they are sorted by (score desc, position asc) and the
+// crossing token gives tau and tie_pos; otherwise the range is refined again.  Exact ties too large to collect switch the key
+// to the score's bit pattern and then to the position (general path,
+// degenerate inputs only).  The refine and collect sweeps touch LDS only for
+// the few tokens inside the range: a wave tests its whole tile first and
+// skips the update code when no lane has a token there.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,10 +41,14 @@ namespace rtp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int kRows = 16;
-constexpr int kNB = 256;
+constexpr int kNB1 = 256;                       // first-sweep bins
+constexpr float kBinsPerOctave = 16.f;          // kNB1 bins span 16 octaves
+constexpr int kNB2 = 256;                       // refinement digits (8 bits)
 constexpr int kCap = 128;
-constexpr float kMaxK = 4294967040.f;      // largest float below 2^32
+constexpr float kMaxK = 4294967040.f;           // largest float below 2^32
+constexpr int kParts = kThreads / kRows;        // threads per row in the scans
 
 enum { PH_HIST1 = 0, PH_REFINE = 1, PH_COLLECT = 2, PH_DONE = 3 };
 
@@ -66,16 +72,16 @@ struct RowCtl {
   int sh;                     // digit shift of the range
   int phase, kind;
   int pos;
-  uint32_t cabove;            // tokens strictly better than the range
-  int counted;                // cabove holds the count above the first-level bin
+  uint32_t cabove;            // tokens strictly better than the range (counted by the collect sweep)
   float tau;
   int tie, count;
 };
 
 // Per-lane constants of a row for one sweep.
 struct RowK {
-  float a20, b20;   // u20 = fma(dot, a20, b20); u16 = fma(dot, a20 / 2^16, b20 / 2^16)
-  float lo_f, hi_f; // float range of u20 for the fast range test
+  float a20, b20;   // K as float = fma(dot, a20, b20)
+  float am, bm;     // mass = 2^fma(dot, am, bm)
+  float lo_f, hi_f; // float range of K for the fast range test
   uint32_t lo;
   int sh, kind, pos;
   uint32_t kfix, dfix;
@@ -83,8 +89,8 @@ struct RowK {
 };
 
 __device__ __forceinline__ uint32_t key20(float u20) { return (uint32_t)__builtin_amdgcn_fmed3f(u20, 0.f, kMaxK); }
-__device__ __forceinline__ uint32_t mass31(float u16) {
-  return (uint32_t)(__builtin_amdgcn_exp2f(u16 * -0.0625f) * 2147483648.f);
+__device__ __forceinline__ uint32_t mass31(float dot, float am, float bm) {
+  return (uint32_t)__builtin_amdgcn_exp2f(fmaf(dot, am, bm));
 }
 
 __global__ void kidx_norm_clear(uint32_t* p, int n) {
@@ -114,8 +120,15 @@ __global__ __launch_bounds__(256) void kidx_norm_max(ProbDev p, const T* __restr
   if ((threadIdx.x & 63) == 0) atomicMax(&out[row], __float_as_uint(mx));
 }
 
+// LDS shared by the sweeps (one at a time).
+constexpr size_t kHist1Bytes = sizeof(unsigned long long) * kNB1 * kRows;
+constexpr size_t kRefineBytes = sizeof(unsigned long long) * kNB2 * kRows;
+constexpr size_t kCandBytes = sizeof(unsigned long long) * kRows * kCap;
+constexpr size_t kUnionBytes = (kHist1Bytes > kRefineBytes ? (kHist1Bytes > kCandBytes ? kHist1Bytes : kCandBytes)
+                                                            : (kRefineBytes > kCandBytes ? kRefineBytes : kCandBytes));
+
 template <typename T>
-__global__ __launch_bounds__(kThreads) void select_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     ProbDev p, const T* __restrict__ q_pre, const float* __restrict__ w_q, const T* __restrict__ k_idx,
     const float* __restrict__ top_p, rtp_selection sel, const uint32_t* __restrict__ kn2) {
   typedef typename IdxFrag<T>::type IF;
@@ -133,34 +146,38 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
 
   __shared__ T qidx_s[kRows][kIdxDim];
   __shared__ RowCtl ctl[kRows];
-  __shared__ unsigned long long hm_s[kNB][kRows];     // masses, or candidates (aliased)
-  __shared__ uint32_t hc_s[kNB][kRows];               // counts
+  __shared__ __attribute__((aligned(16))) unsigned char un_s[kUnionBytes];
   __shared__ int ccount_s[kRows];
   __shared__ uint32_t cbetter_s[kRows];
+  __shared__ unsigned long long psum_s[kRows][kParts];
+  __shared__ int pidx_s[kRows][kParts];
   __shared__ int sweep_s;
-  unsigned long long* cand = &hm_s[0][0];             // [kRows][kCap] during a collect sweep
-  static_assert(kRows * kCap <= kNB * kRows, "candidate buffer must fit in the histogram");
+  auto h1 = reinterpret_cast<unsigned long long(*)[kRows]>(un_s);                      // [kNB1][kRows]
+  auto hm2 = reinterpret_cast<unsigned long long(*)[kRows]>(un_s);                     // [kNB2][kRows]
+  unsigned long long* cand = reinterpret_cast<unsigned long long*>(un_s);              // [kRows][kCap]
 
   // ---- indexer queries of the 16 rows (float64, fixed order, rounded once);
   // rows past the end repeat the last row and are not written back.  The 16
-  // pre-RoPE rows and W^Q are staged in LDS (inside the histogram space) first.
+  // pre-RoPE rows and W^Q are staged in LDS (inside the sweep space) first.
   {
-    float* wl = reinterpret_cast<float*>(&hm_s[0][0]);        // [16][129] (padded rows)
-    T* xl = reinterpret_cast<T*>(wl + kIdxDim * (kHeadDim + 1)); // [16][128]
+    float* wl = reinterpret_cast<float*>(un_s);                     // [16][129] (padded rows)
+    T* xl = reinterpret_cast<T*>(wl + kIdxDim * (kHeadDim + 1));    // [16][128]
     for (int e = tid; e < kIdxDim * kHeadDim; e += kThreads) {
       wl[(e >> 7) * (kHeadDim + 1) + (e & 127)] = w_q[(size_t)r * kIdxDim * kHeadDim + e];
       const int row = min(i0 + (e >> 7), Lq - 1);
       xl[e] = q_pre[((size_t)(q0 + row) * p.R + r) * kHeadDim + (e & 127)];
     }
     __syncthreads();
-    const int rr = tid >> 4, j = tid & 15;
+    const int rr = (tid >> 4) & (kRows - 1), j = tid & 15;
     double acc = 0.0;
     for (int d = 0; d < kHeadDim; ++d)
       acc = fma((double)Elem<T>::to_f(xl[rr * kHeadDim + d]), (double)wl[j * (kHeadDim + 1) + d], acc);
     const T qv = Elem<T>::from_d(acc);
     __syncthreads();
-    qidx_s[rr][j] = qv;
-    if (i0 + rr < Lq) ((T*)sel.q_idx)[((size_t)r * p.Tq + q0 + i0 + rr) * kIdxDim + j] = qv;
+    if (tid < kRows * kIdxDim) {
+      qidx_s[rr][j] = qv;
+      if (i0 + rr < Lq) ((T*)sel.q_idx)[((size_t)r * p.Tq + q0 + i0 + rr) * kIdxDim + j] = qv;
+    }
   }
   __syncthreads();
   if (tid < kRows) {
@@ -177,7 +194,6 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
     c.top = sqrtf(qn * kn) * 0.25f * 1.0009765625f + 1e-30f;
     c.above = 0ull;
     c.cabove = 0u;
-    c.counted = 0;
     c.lo = 0u; c.sh = 16; c.kind = 0; c.kfix = 0u; c.dfix = 0u;
     c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = c.pos + 1;
     c.target = 1.0;
@@ -204,6 +220,19 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
     }
     return idx_dot_tile(kxf, qxf);
   };
+  // two tiles per step over the full tiles, then the diagonal tiles one at a time
+  auto sweep_tiles = [&](auto&& body) {
+    int t = w;
+    for (; t + kWaves < nfull; t += 2 * kWaves) {
+      const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + kWaves);
+      body(d0, t, false);
+      body(d1, t + kWaves, false);
+    }
+    for (; t < ntile; t += kWaves) body(tile_dot(t), t, t >= nfull);
+  };
+
+  // thread (row, part) of the parallel scans
+  const int srow = tid / kParts, spart = tid % kParts;
 
   for (int iter = 0; iter < 64; ++iter) {
     if (tid == 0) {
@@ -219,8 +248,10 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
     {
       const RowCtl& c = ctl[col];
       const bool active = c.phase == sweep;
-      rk.a20 = -kLog2e * 4.f * 65536.f;            // -(log2(e) / 4) * 16 * 2^16
-      rk.b20 = c.top * kLog2e * 16.f * 65536.f;
+      rk.a20 = -kLog2e * 0.25f * kBinsPerOctave * 65536.f;
+      rk.b20 = c.top * kLog2e * kBinsPerOctave * 65536.f;
+      rk.am = kLog2e * 0.25f;
+      rk.bm = 31.f - c.top * kLog2e;
       rk.lo = c.lo;
       rk.sh = c.sh;
       rk.kind = c.kind;
@@ -234,78 +265,80 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
       const double hi = (double)c.lo + (double)(1ull << min(width, 32));
       rk.hi_f = (hi >= 4294967040.0) ? INFINITY : (float)hi;
     }
-    for (int e = tid; e < kNB * kRows; e += kThreads) { (&hm_s[0][0])[e] = 0ull; (&hc_s[0][0])[e] = 0u; }
+    {
+      uint32_t* z = reinterpret_cast<uint32_t*>(un_s);
+      const int nz = (int)(((sweep == PH_HIST1) ? kHist1Bytes : (sweep == PH_REFINE) ? kRefineBytes : 0) / 4);
+      for (int e = tid; e < nz; e += kThreads) z[e] = 0u;
+    }
     if (tid < kRows) { ccount_s[tid] = 0; cbetter_s[tid] = 0u; }
     __syncthreads();
 
     const bool all_fast = __builtin_amdgcn_ballot_w64(!rk.fast) == 0;
-    const float a16 = rk.a20 * (1.f / 65536.f), b16 = rk.b20 * (1.f / 65536.f);
+    const float a1 = rk.a20 * (1.f / 65536.f), b1 = rk.b20 * (1.f / 65536.f);
     uint32_t better = 0u;
 
     if (sweep == PH_HIST1) {
-      auto body = [&](const f32x4& d, int t, bool check) {
+      sweep_tiles([&](const f32x4& d, int t, bool check) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
           if (check && n > rk.pos) continue;
-          const float u16 = fmaf(d[i], a16, b16);
-          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u16, 0.f, (float)(kNB - 1));
-          atomicAdd(&hm_s[bin][col], (unsigned long long)mass31(u16));
+          const float u = fmaf(d[i], a1, b1);
+          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kNB1 - 1));
+          atomicAdd(&h1[bin][col], (unsigned long long)mass31(d[i], rk.am, rk.bm));
         }
-      };
-      int t = w;
-      for (; t + 4 < nfull; t += 8) {
-        const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + 4);
-        body(d0, t, false);
-        body(d1, t + 4, false);
-      }
-      for (; t < ntile; t += 4) body(tile_dot(t), t, t >= nfull);
+      });
     } else if (sweep == PH_REFINE && all_fast) {
-      auto body = [&](const f32x4& d, int t, bool check) {
+      sweep_tiles([&](const f32x4& d, int t, bool check) {
+        float u20[4];
+        bool inr[4];
+        bool any = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
-          if (check && n > rk.pos) continue;
-          const float u20 = fmaf(d[i], rk.a20, rk.b20);
-          better += (u20 < rk.lo_f) ? 1u : 0u;
-          if (u20 >= rk.lo_f && u20 < rk.hi_f) {
-            const uint32_t dig = (key20(u20) - rk.lo) >> rk.sh;
-            atomicAdd(&hm_s[dig][col], (unsigned long long)mass31(u20 * (1.f / 65536.f)));
-            atomicAdd(&hc_s[dig][col], 1u);
+          const bool valid = !check || n <= rk.pos;
+          u20[i] = fmaf(d[i], rk.a20, rk.b20);
+          inr[i] = valid && u20[i] >= rk.lo_f && u20[i] < rk.hi_f;
+          any |= inr[i];
+        }
+        if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (inr[i]) {
+              const uint32_t dig = (key20(u20[i]) - rk.lo) >> rk.sh;
+              atomicAdd(&hm2[dig][col], (unsigned long long)mass31(d[i], rk.am, rk.bm));
+            }
           }
         }
-      };
-      int t = w;
-      for (; t + 4 < nfull; t += 8) {
-        const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + 4);
-        body(d0, t, false);
-        body(d1, t + 4, false);
-      }
-      for (; t < ntile; t += 4) body(tile_dot(t), t, t >= nfull);
+      });
     } else if (sweep == PH_COLLECT && all_fast) {
-      auto body = [&](const f32x4& d, int t, bool check) {
+      sweep_tiles([&](const f32x4& d, int t, bool check) {
+        bool inr[4];
+        bool any = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
-          if (check && n > rk.pos) continue;
+          const bool valid = !check || n <= rk.pos;
           const float u20 = fmaf(d[i], rk.a20, rk.b20);
-          if (u20 >= rk.lo_f && u20 < rk.hi_f) {
-            const int slot = atomicAdd(&ccount_s[col], 1);
-            if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(idx_score(d[i])) << 32) | (uint32_t)n;
+          better += (valid && u20 < rk.lo_f) ? 1u : 0u;
+          inr[i] = valid && u20 >= rk.lo_f && u20 < rk.hi_f;
+          any |= inr[i];
+        }
+        if (__builtin_amdgcn_ballot_w64(any)) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (inr[i]) {
+              const int n = 16 * t + 4 * grp + i;
+              const int slot = atomicAdd(&ccount_s[col], 1);
+              if (slot < kCap)
+                cand[col * kCap + slot] = ((unsigned long long)desc_key(idx_score(d[i])) << 32) | (uint32_t)n;
+            }
           }
         }
-      };
-      int t = w;
-      for (; t + 4 < nfull; t += 8) {
-        const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + 4);
-        body(d0, t, false);
-        body(d1, t + 4, false);
-      }
-      for (; t < ntile; t += 4) body(tile_dot(t), t, t >= nfull);
+      });
     } else {
       // general path: integer keys and the tie key spaces
-      for (int t = w; t < ntile; t += 4) {
-        const f32x4 d = tile_dot(t);
+      sweep_tiles([&](const f32x4& d, int t, bool) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
@@ -333,98 +366,149 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
           const int width = (sweep == PH_REFINE) ? rk.sh + 8 : rk.sh;
           const uint32_t dk2 = key - rk.lo;
           const bool inr = ok && ((width >= 32) ? (key >= rk.lo) : ((dk2 >> width) == 0u));
-          if (sweep == PH_REFINE) better += bt ? 1u : 0u;
+          if (sweep == PH_COLLECT) better += bt ? 1u : 0u;
           if (!inr) continue;
           if (sweep == PH_REFINE) {
             const uint32_t dig = dk2 >> rk.sh;
-            atomicAdd(&hm_s[dig][col], (unsigned long long)mass31(u20 * (1.f / 65536.f)));
-            atomicAdd(&hc_s[dig][col], 1u);
+            atomicAdd(&hm2[dig][col], (unsigned long long)mass31(d[i], rk.am, rk.bm));
           } else {
             const int slot = atomicAdd(&ccount_s[col], 1);
             if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
           }
         }
-      }
+      });
     }
-    if (sweep == PH_REFINE) {
+    if (sweep == PH_COLLECT) {
       better += __shfl_xor(better, 16);
       better += __shfl_xor(better, 32);
       if (grp == 0) atomicAdd(&cbetter_s[col], better);
     }
     __syncthreads();
 
-    // ---- per-row controller
-    if (tid < kRows && ctl[tid].phase == sweep) {
-      RowCtl& rc = ctl[tid];
-      if (rc.phase == PH_HIST1) {
-        unsigned long long Z = 0ull;
-        int blo = -1;
-        for (int bi = 0; bi < kNB; ++bi) {
-          const unsigned long long hv = hm_s[bi][tid];
-          if (blo < 0 && hv != 0ull) blo = bi;
-          Z += hv;
+    // ---- per-row controller.  The histogram scans run on 16 threads per row:
+    // part sums, then the part holding the crossing walks its bins.
+    const bool act = ctl[srow].phase == sweep;
+    if (sweep == PH_HIST1) {
+      constexpr int PB = kNB1 / kParts;
+      unsigned long long sp = 0ull;
+      int first = kNB1;
+      if (act) {
+        for (int j = 0; j < PB; ++j) {
+          const unsigned long long hv = h1[spart * PB + j][srow];
+          if (first == kNB1 && hv != 0ull) first = spart * PB + j;
+          sp += hv;
         }
-        if (blo >= 128 || Z == 0ull) {
+      }
+      psum_s[srow][spart] = sp;
+      pidx_s[srow][spart] = first;
+      __syncthreads();
+      if (act) {
+        RowCtl& rc = ctl[srow];
+        unsigned long long Z = 0ull, pre = 0ull;
+        int blo = kNB1;
+        for (int q = 0; q < kParts; ++q) {
+          if (q < spart) pre += psum_s[srow][q];
+          Z += psum_s[srow][q];
+          blo = min(blo, pidx_s[srow][q]);
+        }
+        if (blo >= kNB1 / 2 || Z == 0ull) {
           // loose bound (the best token sits >= 8 octaves below it): lower the
           // reference to just above the best token and histogram again
-          const int bl = (blo < 0) ? kNB - 1 : blo;
-          rc.top = rc.top - (float)(bl - 1) * 0.0625f / kLog2e;
+          if (spart == 0) {
+            const int bl = (blo >= kNB1) ? kNB1 - 1 : blo;
+            rc.top = rc.top - (float)(bl - 1) / (kBinsPerOctave * kLog2e);
+          }
         } else {
-          rc.target = fmax((double)rc.pval * (double)Z, 1.0);
-          unsigned long long cm = 0ull;
-          int bstar = kNB - 1;
-          for (int bi = 0; bi < kNB; ++bi) {
-            if ((double)(cm + hm_s[bi][tid]) >= rc.target) { bstar = bi; break; }
-            cm += hm_s[bi][tid];
+          const double target = fmax((double)rc.pval * (double)Z, 1.0);
+          if ((double)pre < target && target <= (double)(pre + sp)) {
+            unsigned long long cm = pre;
+            int bstar = spart * PB + PB - 1;
+            for (int j = 0; j < PB; ++j) {
+              const unsigned long long hv = h1[spart * PB + j][srow];
+              if ((double)(cm + hv) >= target) { bstar = spart * PB + j; break; }
+              cm += hv;
+            }
+            rc.target = target;
+            rc.above = cm;
+            rc.lo = (uint32_t)bstar << 16;
+            rc.sh = (bstar < kNB1 - 1) ? 8 : 24;   // the last bin spans the rest of the 32-bit key
+            rc.phase = PH_REFINE;
           }
-          if (bstar == kNB - 1) {
-            cm = 0ull;
-            for (int bi = 0; bi < kNB - 1; ++bi) cm += hm_s[bi][tid];
+        }
+      }
+    } else if (sweep == PH_REFINE) {
+      constexpr int PD = kNB2 / kParts;
+      unsigned long long sp = 0ull;
+      int lastne = -1;
+      if (act) {
+        for (int j = 0; j < PD; ++j) {
+          const unsigned long long hv = hm2[spart * PD + j][srow];
+          sp += hv;
+          if (hv != 0ull) lastne = spart * PD + j;
+        }
+      }
+      psum_s[srow][spart] = sp;
+      pidx_s[srow][spart] = lastne;
+      __syncthreads();
+      // read the row state and the part sums, then (after a barrier every thread
+      // reaches) the part holding the crossing digit updates the row
+      bool mine = false, crosses = true;
+      unsigned long long pre = 0ull;
+      int last = -1;
+      double target = 0.0;
+      if (act) {
+        const RowCtl& rc = ctl[srow];
+        pre = rc.above;
+        unsigned long long tot = rc.above;
+        for (int q = 0; q < kParts; ++q) {
+          if (q < spart) pre += psum_s[srow][q];
+          tot += psum_s[srow][q];
+          last = max(last, pidx_s[srow][q]);
+        }
+        target = rc.target;
+        // the part holding the crossing digit; if rounding left the target just beyond
+        // the range, the part holding the last digit with mass
+        crosses = (double)tot >= target;
+        mine = crosses ? ((double)pre < target && target <= (double)(pre + sp))
+                       : (last < 0 ? spart == 0 : (last >= spart * PD && last < spart * PD + PD));
+      }
+      __syncthreads();
+      if (mine) {
+        RowCtl& rc = ctl[srow];
+        unsigned long long cm = pre;
+        int dstar = crosses ? spart * PD + PD - 1 : max(last, 0);
+        if (crosses) {
+          for (int j = 0; j < PD; ++j) {
+            const int dg = spart * PD + j;
+            const unsigned long long hv = hm2[dg][srow];
+            if ((double)(cm + hv) >= target) { dstar = dg; break; }
+            cm += hv;
           }
-          rc.above = cm;
-          rc.lo = (uint32_t)bstar << 16;
-          rc.sh = (bstar < kNB - 1) ? 8 : 24;   // the last bin spans the rest of the 32-bit key
-          rc.phase = PH_REFINE;
-        }
-      } else if (rc.phase == PH_REFINE) {
-        if (!rc.counted) {   // the first refinement counted the tokens above the first-level bin
-          rc.cabove = cbetter_s[tid];
-          rc.counted = 1;
-        }
-        unsigned long long cm = rc.above;
-        uint32_t cc = rc.cabove;
-        int dstar = -1;
-        uint32_t cnt = 0u;
-        for (int d = 0; d < kNB; ++d) {
-          if (hc_s[d][tid] == 0u) continue;
-          if ((double)(cm + hm_s[d][tid]) >= rc.target) { dstar = d; cnt = hc_s[d][tid]; break; }
-          cm += hm_s[d][tid];
-          cc += hc_s[d][tid];
-        }
-        if (dstar < 0) {  // rounding left the target just beyond the range: take its last digit
-          cm = rc.above;
-          cc = rc.cabove;
-          for (int d = 0; d < kNB; ++d) {
-            if (hc_s[d][tid] == 0u) continue;
-            dstar = d; cnt = hc_s[d][tid];
-          }
-          for (int d = 0; d < dstar; ++d) { cm += hm_s[d][tid]; cc += hc_s[d][tid]; }
+        } else {
+          for (int dg = spart * PD; dg < dstar; ++dg) cm += hm2[dg][srow];
         }
         rc.above = cm;
-        rc.cabove = cc;
         rc.lo = rc.lo + ((uint32_t)dstar << rc.sh);
-        if (cnt <= (uint32_t)kCap) {
-          rc.phase = PH_COLLECT;
-        } else if (rc.sh >= 8) {
+        rc.phase = PH_COLLECT;
+      }
+    } else if (sweep == PH_COLLECT) {
+      if (act && spart == 0 && ccount_s[srow] > kCap) {
+        // too many tokens in the range: refine it further
+        RowCtl& rc = ctl[srow];
+        if (rc.sh >= 8) {
           rc.sh -= 8;
         } else if (rc.kind == 0) {
           rc.kind = 1; rc.kfix = rc.lo; rc.lo = 0u; rc.sh = 24;
         } else {
           rc.kind = 2; rc.dfix = rc.lo; rc.lo = 0u; rc.sh = 23;
         }
-      } else if (rc.phase == PH_COLLECT) {
-        const int nc = min(ccount_s[tid], kCap);
-        unsigned long long* cd = cand + tid * kCap;
+        rc.phase = PH_REFINE;
+      } else if (act && spart == 0) {
+        RowCtl& rc = ctl[srow];
+        rc.cabove = cbetter_s[srow];
+        const int tidr = srow;
+        const int nc = min(ccount_s[tidr], kCap);
+        unsigned long long* cd = cand + tidr * kCap;
         for (int a = 1; a < nc; ++a) {  // insertion sort: (desc_key asc, position asc)
           const unsigned long long x = cd[a];
           int bb = a - 1;
@@ -433,11 +517,10 @@ __global__ __launch_bounds__(kThreads) void select_prefill_kernel(
         }
         unsigned long long cm = rc.above;
         int jstar = nc - 1;
-        const float b16r = rc.top * kLog2e * 16.f * 65536.f * (1.f / 65536.f);
-        const float a16r = -kLog2e * 4.f * 65536.f * (1.f / 65536.f);
+        const float am = kLog2e * 0.25f, bm = 31.f - rc.top * kLog2e;
         for (int a = 0; a < nc; ++a) {
           const float s = undesc_key((uint32_t)(cd[a] >> 32));
-          const uint32_t mf = mass31(fmaf(s * 4.f, a16r, b16r));
+          const uint32_t mf = mass31(s * 4.f, am, bm);
           if ((double)(cm + mf) >= rc.target) { jstar = a; break; }
           cm += mf;
         }
