@@ -29,6 +29,17 @@ if ROOT not in sys.path:
 METRIC = "sparse-attn prefill tokens/s @128K and decode step µs @32K, 1 MI355X, % roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+# v_exp_f32 issues at half the fp32 rate: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz / 2
+EXP_PEAK_TEXPS = 256 * 4 * 16 * 2.4e9 / 2 / 1e12
+# kernel behind each timed call, its source, and the committed HBM counter summary
+KERNELS = {
+    "select_topp": ("rtp::select_prefill_kernel", "long_context_sparse_rtp_amd/csrc/select_prefill.hip",
+                    "profiles/select_prefill_128k_traffic.txt"),
+    "sparse_attn_prefill": ("rtp::attn_prefill_kernel<MODE 0>", "long_context_sparse_rtp_amd/csrc/attn_prefill.hip",
+                            "profiles/attn_prefill_ret_128k_traffic.txt"),
+    "local_attn": ("rtp::attn_prefill_kernel<MODE 1>", "long_context_sparse_rtp_amd/csrc/attn_prefill.hip",
+                   "profiles/attn_prefill_local_128k_traffic.txt"),
+}
 
 
 def _args():
@@ -40,6 +51,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only copy a 1 GiB buffer 4 times (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -60,6 +73,25 @@ class Timer:
 
     def means_ms(self):
         return {k: sum(a.elapsed_time(b) for a, b in v) / len(v) for k, v in self.acc.items()}
+
+
+def _traffic(name):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel's source changed since the counters were taken (or none were)."""
+    import hashlib
+    _, src, summ = KERNELS[name]
+    try:
+        kv = {}
+        for ln in open(os.path.join(ROOT, summ)):
+            if ":" in ln and not ln.startswith("#"):
+                a, b = ln.split(":", 1)
+                kv[a.strip()] = b.strip()
+        sha = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+        if kv.get("kernel_source_sha256") != sha:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def bench_prefill(args, torch, rtp, synth):
@@ -93,19 +125,16 @@ def bench_prefill(args, torch, rtp, synth):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # the timed steps, with an event pair around every call on the launch stream
+    t = Timer(torch, stream)
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for _ in range(args.steps):
-        step()
+        step(t)
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    # per-kernel breakdown in a second, separately bracketed pass
-    t = Timer(torch, stream)
-    for _ in range(max(1, min(args.steps, 3))):
-        step(t)
-    torch.cuda.synchronize()
     per = t.means_ms()
 
     # algorithmic work (sets measured from this run's selection)
@@ -123,8 +152,9 @@ def bench_prefill(args, torch, rtp, synth):
         "select_topp": 2 * r * causal_pairs * cfg.n_ret,
     }
     total_flops = sum(flops.values())
+    exps_select = causal_pairs * cfg.n_ret    # one softmax-mass exponential per causal (row, key) pair
     bytes_ik = inp.total_k * cfg.n_ret * (d * 2 + r * 2)
-    return dict(ms=ms, per_kernel_ms=per, flops=flops, total_flops=total_flops, sum_S=sum_S,
+    return dict(ms=ms, per_kernel_ms=per, flops=flops, total_flops=total_flops, sum_S=sum_S, exps_select=exps_select,
                 mean_frac_selected=sum_S / (cfg.n_ret * causal_pairs), bytes_index_keys=bytes_ik,
                 tokens=L, cfg=cfg, inp=inp, sel=sel)
 
@@ -255,6 +285,14 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes_per_launch": 1 << 30, "launches": 4}))
+        return
     import long_context_sparse_rtp_amd as rtp
     import synth
     rtp.library()  # fail loudly if the HIP library is missing
@@ -276,12 +314,21 @@ def main():
                                       "4 retrieval heads (top-p 0.9, 16-dim indexer), 28 local heads "
                                       "(window 2048 + 4 sinks)",
                           "global_batch": 1, "seq_len": pre["tokens"], "parallelism": "none (1 GPU)"}
-        rt = per[dom]
-        ach = pre["flops"][dom] / (rt * 1e-3) / 1e12
-        line["roofline"] = {"kernel": dom, "bound": "mfma" if dom != "select_topp" else "alu",
-                            "achieved": ach, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": ach / MFMA_BF16_PEAK_TFLOPS, "traffic": None}
+        roofs = {}
+        for k in ("select_topp", "sparse_attn_prefill", "local_attn"):
+            rt = per[k] * 1e-3
+            if k == "select_topp":   # bound by the exponential unit
+                ach = pre["exps_select"] / rt / 1e12
+                roofs[k] = {"kernel": KERNELS[k][0], "bound": "alu", "achieved": ach, "peak": EXP_PEAK_TEXPS,
+                            "unit": "Texp/s", "frac": ach / EXP_PEAK_TEXPS, "traffic": _traffic(k)}
+            else:
+                ach = pre["flops"][k] / rt / 1e12
+                roofs[k] = {"kernel": KERNELS[k][0], "bound": "mfma", "achieved": ach,
+                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                            "traffic": _traffic(k)}
+        line["roofline"] = roofs[dom]
         line["prefill"] = {"ms_per_step": pre["ms"], "per_kernel_ms": per,
+                           "per_kernel_roofline": roofs,
                            "per_kernel_tflops": fl,
                            "algorithmic_tflop": pre["total_flops"] / 1e12,
                            "step_frac_of_mfma_roofline": (pre["total_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e12 * 1e3)

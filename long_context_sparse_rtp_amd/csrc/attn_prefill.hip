@@ -13,7 +13,9 @@
 // dense there); this one is a flash-attention style loop written for gfx950:
 //   - workgroup = 8 wave64s, 256 query rows (32 per wave as two 16-column
 //     MFMA tiles), 64-key tiles: every staged K/V tile feeds 256 queries, which
-//     halves the re-reads of the causal K/V prefix against 128-row tiles;
+//     halves the re-reads of the causal K/V prefix against 128-row tiles
+//     (a 4-wave, 128-row variant needs more than 128 VGPRs per lane and
+//     spills at two workgroups per CU);
 //   - the next tile's K/V is loaded into registers while the current one is
 //     computed and written to the other half of a double-buffered LDS;
 //   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (f32 path: 16x16x4 steps), K
@@ -34,9 +36,12 @@ namespace rtp {
 
 namespace {
 
-constexpr int kThreads = 512;   // 8 wave64s
-constexpr int BQ = 256;         // query rows per workgroup (32 per wave)
+constexpr int kWaves = 8;                 // waves per workgroup, 32 query rows each
+constexpr int kThreads = 64 * kWaves;
+constexpr int BQ = 32 * kWaves;           // query rows per workgroup
 constexpr int KT = 64;          // keys per tile
+static_assert((KT / 2) * (kHeadDim / 8) % kThreads == 0, "V staging splits evenly over the workgroup");
+static_assert(KT * kHeadDim / 8 % kThreads == 0, "K staging splits evenly over the workgroup");
 
 template <typename T> struct Lds;
 template <> struct Lds<bf16_t> { static constexpr int kStr = 128 + 8; static constexpr int vStr = 64 + 4; };
@@ -77,7 +82,8 @@ template <typename T> struct Stage;
 // dims, written transposed as packed key pairs.
 template <> struct Stage<bf16_t> {
   static constexpr int kU = KT * kHeadDim / 8 / kThreads;   // 16-byte K chunks per thread
-  uint4 k[kU], v[2];
+  static constexpr int kVU = (KT / 2) * (kHeadDim / 8) / kThreads;   // (key pair, 8-dim chunk) units per thread
+  uint4 k[kU], v[kVU][2];
   __device__ __forceinline__ void load(const bf16_t* kg, const bf16_t* vg, size_t rstride, int nvalid, int tid) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -86,12 +92,16 @@ template <> struct Stage<bf16_t> {
       k[u] = {0u, 0u, 0u, 0u};
       if (key < nvalid) k[u] = *reinterpret_cast<const uint4*>(kg + (size_t)key * rstride + ch * 8);
     }
-    const int kp = tid & 31, dc = tid >> 5;   // keys 2kp, 2kp+1; dims 8dc..8dc+7
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = 2 * kp + u;
-      v[u] = {0u, 0u, 0u, 0u};
-      if (key < nvalid) v[u] = *reinterpret_cast<const uint4*>(vg + (size_t)key * rstride + dc * 8);
+    for (int w = 0; w < kVU; ++w) {
+      const int e = w * kThreads + tid;
+      const int kp = e & 31, dc = e >> 5;   // keys 2kp, 2kp+1; dims 8dc..8dc+7
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int key = 2 * kp + u;
+        v[w][u] = {0u, 0u, 0u, 0u};
+        if (key < nvalid) v[w][u] = *reinterpret_cast<const uint4*>(vg + (size_t)key * rstride + dc * 8);
+      }
     }
   }
   __device__ __forceinline__ void store(bf16_t* k_s, bf16_t* vt_s, int tid) const {
@@ -102,19 +112,24 @@ template <> struct Stage<bf16_t> {
       const int key = e >> 4, ch = e & 15;
       *reinterpret_cast<uint4*>(k_s + key * KS + ch * 8) = k[u];
     }
-    const int kp = tid & 31, dc = tid >> 5;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t w0 = (&v[0].x)[e >> 1], w1 = (&v[1].x)[e >> 1];
-      const uint32_t pr = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
-      *reinterpret_cast<uint32_t*>(vt_s + (8 * dc + e) * VS + 2 * kp) = pr;
+    for (int w = 0; w < kVU; ++w) {
+      const int e2 = w * kThreads + tid;
+      const int kp = e2 & 31, dc = e2 >> 5;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w0 = (&v[w][0].x)[e >> 1], w1 = (&v[w][1].x)[e >> 1];
+        const uint32_t pr = (e & 1) ? ((w0 >> 16) | (w1 & 0xFFFF0000u)) : ((w0 & 0xFFFFu) | (w1 << 16));
+        *reinterpret_cast<uint32_t*>(vt_s + (8 * dc + e) * VS + 2 * kp) = pr;
+      }
     }
   }
 };
 template <> struct Stage<float> {
   static constexpr int kU = KT * kHeadDim / 4 / kThreads;   // 16-byte K chunks per thread
+  static constexpr int kVU = (KT / 2) * (kHeadDim / 8) / kThreads;
   float4 k[kU];
-  float v[2][8];
+  float v[kVU][2][8];
   __device__ __forceinline__ void load(const float* kg, const float* vg, size_t rstride, int nvalid, int tid) {
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
@@ -123,17 +138,21 @@ template <> struct Stage<float> {
       k[u] = {0.f, 0.f, 0.f, 0.f};
       if (key < nvalid) k[u] = *reinterpret_cast<const float4*>(kg + (size_t)key * rstride + ch * 4);
     }
-    const int kp = tid & 31, dc = tid >> 5;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int key = 2 * kp + u;
+    for (int w = 0; w < kVU; ++w) {
+      const int e = w * kThreads + tid;
+      const int kp = e & 31, dc = e >> 5;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = 0.f;
-      if (key < nvalid) {
-        float4 a = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8);
-        float4 b = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8 + 4);
-        v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
-        v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+      for (int u = 0; u < 2; ++u) {
+        const int key = 2 * kp + u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[w][u][i] = 0.f;
+        if (key < nvalid) {
+          float4 a = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8);
+          float4 b = *reinterpret_cast<const float4*>(vg + (size_t)key * rstride + dc * 8 + 4);
+          v[w][u][0] = a.x; v[w][u][1] = a.y; v[w][u][2] = a.z; v[w][u][3] = a.w;
+          v[w][u][4] = b.x; v[w][u][5] = b.y; v[w][u][6] = b.z; v[w][u][7] = b.w;
+        }
       }
     }
   }
@@ -145,11 +164,15 @@ template <> struct Stage<float> {
       const int key = e >> 5, ch = e & 31;
       *reinterpret_cast<float4*>(k_s + key * KS + ch * 4) = k[u];
     }
-    const int kp = tid & 31, dc = tid >> 5;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float2 o = {v[0][e], v[1][e]};
-      *reinterpret_cast<float2*>(vt_s + (8 * dc + e) * VS + 2 * kp) = o;
+    for (int w = 0; w < kVU; ++w) {
+      const int e2 = w * kThreads + tid;
+      const int kp = e2 & 31, dc = e2 >> 5;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float2 o = {v[w][0][e], v[w][1][e]};
+        *reinterpret_cast<float2*>(vt_s + (8 * dc + e) * VS + 2 * kp) = o;
+      }
     }
   }
 };
@@ -168,24 +191,39 @@ __device__ __forceinline__ void store_out4<float>(float* dst, const float* v) {
   *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// Work order: blockIdx -> (query tile, head).  Consecutive workgroups on one
-// XCD (block ids are dealt round-robin over the 8 XCDs) take the heads of one
-// query tile, so heads that share a KV group reuse that XCD's L2; query tiles
-// go longest-first so the causal tail does not straggle.
+// Work order: blockIdx -> (query tile, head).  Workgroups are dealt round-robin
+// over the 8 XCDs (block id mod 8), and each XCD has its own L2, so the order
+// decides which workgroups share K/V tiles in L2:
+//   - heads that share KV (local heads of one group) run side by side: the
+//     consecutive workgroups of an XCD take all heads of one query tile;
+//   - heads on different KV groups (the retrieval heads, one per group) are
+//     given XCDs of their own when they divide the 8 XCDs evenly, so all the
+//     workgroups resident on an XCD sweep the same head's K/V prefix at about
+//     the same time.
+// Query tiles go longest-first so the causal tail does not straggle.
 struct Work { int b, qt, hidx; bool ok; };
-__device__ __forceinline__ Work work_of(int bid, int nheads, int batch, int tiles_per_b) {
+__device__ __forceinline__ Work work_of(int bid, int nheads, int batch, int tiles_per_b, bool per_head_xcd) {
   Work wk;
-  const int t = bid >> 3, x = bid & 7;
-  const int unit = (t / nheads) * 8 + x;
-  wk.hidx = t % nheads;
-  wk.ok = unit < batch * tiles_per_b;
+  const int units = batch * tiles_per_b;
+  const int k = bid >> 3, x = bid & 7;
+  int unit;
+  if (per_head_xcd) {
+    const int xpg = 8 / nheads;            // XCDs per head
+    wk.hidx = x % nheads;
+    unit = k * xpg + x / nheads;
+  } else {
+    unit = (k / nheads) * 8 + x;
+    wk.hidx = k % nheads;
+  }
+  wk.ok = unit < units;
   wk.b = unit % batch;
   wk.qt = tiles_per_b - 1 - unit / batch;
   return wk;
 }
+__host__ __device__ inline bool per_head_xcd(int mode, int nheads) { return mode == 0 && nheads <= 8 && 8 % nheads == 0; }
 
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
     ProbDev p, int nheads, int tiles_per_b, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ k_idx, const rtp_selection sel, T* __restrict__ out,
     float* __restrict__ lse) {
@@ -195,7 +233,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
   __shared__ __attribute__((aligned(16))) T k_s[2][KT * KS];
   __shared__ __attribute__((aligned(16))) T vt_s[2][kHeadDim * VS];
 
-  const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b);
+  const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b, per_head_xcd(MODE, nheads));
   if (!wk.ok) return;
   const int b = wk.b, hidx = wk.hidx;
   const int h = (MODE == 0) ? p.ret_heads[hidx] : p.local_heads[hidx];
@@ -451,7 +489,9 @@ hipError_t launch_attn_prefill(const ProbDev& p, bool bf16, int mode, const void
   if (nheads == 0 || p.Tq == 0) return hipSuccess;
   const int tiles_per_b = (p.max_q + BQ - 1) / BQ;
   const int units = tiles_per_b * p.batch;
-  dim3 grid((unsigned)(((units + 7) / 8) * 8 * nheads));
+  const unsigned nblk = per_head_xcd(mode, nheads) ? 8u * (unsigned)((units + 8 / nheads - 1) / (8 / nheads))
+                                                  : (unsigned)(((units + 7) / 8) * 8 * nheads);
+  dim3 grid(nblk);
   rtp_selection sl = {};
   if (sel) sl = *sel;
 #define RTP_LAUNCH(TT, MM)                                                                                    \
