@@ -49,6 +49,7 @@ def _args():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-references", action="store_true", help="skip the dense and pages'-prefill references")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -157,6 +158,58 @@ def bench_prefill(args, torch, rtp, synth):
     return dict(ms=ms, per_kernel_ms=per, flops=flops, total_flops=total_flops, sum_S=sum_S, exps_select=exps_select,
                 mean_frac_selected=sum_S / (cfg.n_ret * causal_pairs), bytes_index_keys=bytes_ik,
                 tokens=L, cfg=cfg, inp=inp, sel=sel)
+
+
+def bench_prefill_references(args, torch, rtp, synth, pre):
+    """Two references on the same 128K inputs:
+    - dense: causal attention of all 32 heads (our attention kernel with no
+      retrieval heads and a window covering the whole sequence), the baseline
+      the pages' prefill speedups are quoted against;
+    - pages_prefill: the pages' own prefill, where retrieval heads stay dense
+      (top-p = 1, so the selection keeps every key) and local heads attend to
+      sinks + window; the index cache is still built for the decode steps."""
+    cfg, inp = pre["cfg"], pre["inp"]
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    L = cfg.seqlen
+    dense = rtp.Problem(batch=cfg.batch, n_q_heads=cfg.n_q_heads, n_kv_heads=cfg.n_kv_heads, ret_heads=[],
+                        n_sink=0, window=L, dtype=inp.q.dtype, cu_seqlens_q=inp.cu_q, cu_seqlens_k=inp.cu_k,
+                        max_seqlen_q=L, max_seqlen_k=L, total_q=inp.total_q, total_k=inp.total_k)
+    prob = rtp.Problem.from_inputs(inp)
+    out = torch.empty_like(inp.q)
+    lse = torch.empty((cfg.n_q_heads, inp.total_q), dtype=torch.float32, device=dev)
+    k_idx = torch.empty((cfg.n_ret, inp.total_k, 16), dtype=inp.q.dtype, device=dev)
+    sel = rtp.Selection.empty(prob, rtp.RTP_SEL_THRESHOLD, dev)
+    ws_sel = torch.empty(max(16, rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SELECT, rtp.RTP_SEL_THRESHOLD)),
+                         dtype=torch.uint8, device=dev)
+    p_one = torch.ones_like(inp.top_p)
+
+    def dense_step():
+        rtp.rtp_local_attn(dense, inp.q, inp.k, inp.v, out, lse, stream=stream)
+
+    def pages_step():
+        rtp.rtp_index_keys(prob, inp.k_pre, inp.w, k_idx, stream=stream)
+        rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, p_one, rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream=stream)
+        rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel, out, lse, stream=stream)
+        rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, stream=stream)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    n = max(1, min(args.steps, 3))
+    dense_ms = timed(dense_step, n)
+    pages_ms = timed(pages_step, n)
+    dense_flop = 4 * 128 * cfg.n_q_heads * L * (L + 1) / 2
+    return dict(dense_ms=dense_ms, pages_ms=pages_ms, dense_tflops=dense_flop / (dense_ms * 1e-3) / 1e12)
 
 
 def bench_decode(args, torch, rtp, synth):
@@ -334,6 +387,16 @@ def main():
                            "step_frac_of_mfma_roofline": (pre["total_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e12 * 1e3)
                            / pre["ms"],
                            "mean_selected_fraction": pre["mean_frac_selected"]}
+        if not args.no_references:
+            print("[bench] prefill references (dense, pages' prefill) ...", file=sys.stderr, flush=True)
+            ref = bench_prefill_references(args, torch, rtp, synth, pre)
+            line["prefill"]["references"] = {
+                "dense_causal_ms": ref["dense_ms"], "dense_causal_tflops": ref["dense_tflops"],
+                "pages_prefill_ms": ref["pages_ms"],
+                "speedup_vs_dense": ref["dense_ms"] / pre["ms"],
+                "pages_prefill_speedup_vs_dense": ref["dense_ms"] / ref["pages_ms"],
+                "note": "dense = all 32 heads causal on our attention kernel; pages_prefill = retrieval heads "
+                        "dense (top-p 1) + local heads, as the pages run prefill"}
     if args.only in ("decode", "both"):
         print("[bench] decode 32K x 8 ...", file=sys.stderr, flush=True)
         dec = bench_decode(args, torch, rtp, synth)

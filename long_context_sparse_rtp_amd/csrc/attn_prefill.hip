@@ -232,6 +232,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   constexpr int KS = Lds<T>::kStr, VS = Lds<T>::vStr;
   __shared__ __attribute__((aligned(16))) T k_s[2][KT * KS];
   __shared__ __attribute__((aligned(16))) T vt_s[2][kHeadDim * VS];
+  // retrieval heads: the tile's 16-dim index keys, staged with K/V (one tile ahead)
+  constexpr int KXW = (MODE == 0) ? KT * kIdxDim * (int)sizeof(T) / 4 / kThreads : 0;   // words per thread
+  __shared__ __attribute__((aligned(16))) uint32_t kx_s[2][(MODE == 0) ? KT * kIdxDim * sizeof(T) / 4 : 1];
+  uint32_t kxr[KXW > 0 ? KXW : 1];
 
   const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b, per_head_xcd(MODE, nheads));
   if (!wk.ok) return;
@@ -268,6 +272,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   float tau4[2] = {0.f, 0.f};
   int tie[2] = {0, 0};
   bool exact_ties = false;
+  bool all_keys = false;
   const T* kxb = nullptr;
   if (MODE == 0) {
 #pragma unroll
@@ -280,6 +285,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
     }
     exact_ties = __builtin_amdgcn_ballot_w64(exact_ties) != 0;
     kxb = k_idx + ((size_t)hidx * p.Tk + k0) * kIdxDim;
+    // every row of this wave keeps its whole causal prefix (p >= 1, tau = -inf):
+    // dense causal attention, no indexer work
+    all_keys = __builtin_amdgcn_ballot_w64(!(tau4[0] == -INFINITY && tau4[1] == -INFINITY)) == 0;
   }
 
   const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
@@ -303,12 +311,31 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   const int ntiles = kt_last - kt_first + 1 + (sink_tile ? 1 : 0);
   auto tile_of = [&](int t) { return (sink_tile && t == 0) ? 0 : (kt_first + t - (sink_tile ? 1 : 0)); };
 
+  // index keys of a tile as 4-byte words (keys past the sequence read as 0)
+  auto kx_load = [&](int kb0) {
+    if (MODE != 0) return;
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(kxb + (size_t)kb0 * kIdxDim);
+    constexpr int kWordsPerKey = kIdxDim * (int)sizeof(T) / 4;
+#pragma unroll
+    for (int w = 0; w < KXW; ++w) {
+      const int e = w * kThreads + tid;
+      kxr[w] = (kb0 + e / kWordsPerKey < Lk) ? src[e] : 0u;
+    }
+  };
+  auto kx_store = [&](int b2) {
+    if (MODE != 0) return;
+#pragma unroll
+    for (int w = 0; w < KXW; ++w) kx_s[b2][w * kThreads + tid] = kxr[w];
+  };
+
   Stage<T> st;
   {
     const int fb = tile_of(0) * KT;
     st.load(kg + (size_t)fb * rstride, vg + (size_t)fb * rstride, rstride, min(KT, Lk - fb), tid);
+    kx_load(fb);
   }
   st.store(k_s[0], vt_s[0], tid);
+  kx_store(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
@@ -318,6 +345,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
     if (t + 1 < ntiles) {
       const int nb = tile_of(t + 1) * KT;
       st.load(kg + (size_t)nb * rstride, vg + (size_t)nb * rstride, rstride, min(KT, Lk - nb), tid);
+      kx_load(nb);
     }
 
     // wave-uniform tile classification
@@ -333,17 +361,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
     }
     if (!skip) {
       IF kxf[4];
-      if (MODE == 0) {
+      if (MODE == 0 && !all_keys) {
+        const T* kxt = reinterpret_cast<const T*>(kx_s[buf]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int key = kbase + 16 * ks + col;
-          if (key < Lk) {
-            load_idx_frag(kxf[ks], kxb + (size_t)key * kIdxDim + 4 * grp);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) kxf[ks].v[j] = 0;
-          }
-        }
+        for (int ks = 0; ks < 4; ++ks) load_idx_frag(kxf[ks], kxt + (16 * ks + col) * kIdxDim + 4 * grp);
       }
       // S^T = K Q^T
       f32x4 sacc[2][4];
@@ -385,7 +406,19 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
             }
           }
         };
-        if (exact_ties) {
+        if (all_keys) {
+          if (need_mask) {   // causal mask only
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+              for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int key = kbase + 16 * ks + 4 * grp + i;
+                  sacc[c][ks][i] = (key <= qpos[c]) ? sacc[c][ks][i] : -INFINITY;
+                }
+          }
+        } else if (exact_ties) {
           if (need_mask) apply(std::true_type{}, std::true_type{}); else apply(std::true_type{}, std::false_type{});
         } else {
           if (need_mask) apply(std::false_type{}, std::true_type{}); else apply(std::false_type{}, std::false_type{});
@@ -456,7 +489,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
         }
       }
     }
-    if (t + 1 < ntiles) st.store(k_s[buf ^ 1], vt_s[buf ^ 1], tid);
+    if (t + 1 < ntiles) {
+      st.store(k_s[buf ^ 1], vt_s[buf ^ 1], tid);
+      kx_store(buf ^ 1);
+    }
     __syncthreads();
   }
 

@@ -62,6 +62,40 @@ def test_prefill_dense_limit_p1_window_ge_L():
     assert np.all(g["tau"] == -np.inf)
 
 
+def test_pages_prefill_retrieval_dense_bf16():
+    # the pages' prefill: retrieval heads keep every key (top-p 1), local heads sinks + window
+    cfg = scaled(PREFILL_128K, name="pages_prefill_p1", seqlen=1300, top_p=1.0, window=256)
+    _say(f"[case] {cfg.name}")
+    inp = make_inputs(cfg, DEV)
+    rows = [(0, i) for i in (0, 1, 17, 255, 256, 700, 1023, 1024, 1299)]
+    g = P.to_host(P.run_prefill(inp))
+    assert np.all(g["tau"] == -np.inf)
+    pr = from_inputs(inp)
+    n, fails, stats = P.check_rows(pr, g, rows, list(range(cfg.n_q_heads)), P.TOL[cfg.dtype])
+    _say(f"[result] {cfg.name}: {n} pairs, {len(fails)} failures, {stats}")
+    assert not fails, fails[:5]
+
+
+def test_dense_causal_baseline_all_heads():
+    # every head dense causal: no retrieval heads, window covering the sequence, no sinks
+    import long_context_sparse_rtp_amd as rtp
+    cfg = scaled(PREFILL_128K, name="dense_all_heads", seqlen=1100, ret_heads=(), window=1100, n_sink=0,
+                 needles="none")
+    _say(f"[case] {cfg.name}")
+    inp = make_inputs(cfg, DEV)
+    prob = rtp.Problem.from_inputs(inp)
+    out = torch.full_like(inp.q, float("nan"))
+    lse = torch.full((cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=DEV)
+    rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse)
+    torch.cuda.synchronize()
+    g = P.to_host(dict(out=out, lse=lse))
+    pr = from_inputs(inp)
+    rows = [(0, i) for i in (0, 1, 63, 64, 65, 511, 700, 1099)]
+    n, fails, stats = P.check_rows(pr, g, rows, list(range(cfg.n_q_heads)), P.TOL[cfg.dtype])
+    _say(f"[result] {cfg.name}: {n} pairs, {len(fails)} failures, {stats}")
+    assert not fails, fails[:5]
+
+
 def test_prefill_argmax_limit_and_window_one():
     cfg = scaled(TINY_PREFILL, name="argmax_w1", seqlen=513, top_p=1e-7, window=1, n_sink=0)
     _say(f"[case] {cfg.name}")
