@@ -17,6 +17,9 @@ Transferring Full Attention into Sparse within Hundred Training Steps"
   softmax over the indexer scores of all cached keys, descending order, the
   smallest prefix whose cumulative mass reaches p; then exact softmax
   attention with post-RoPE q, k over the selected set only.
+* Sections "Evaluation Methodology" and "Ablation Studies and Robustness
+  Checks": the static top-k variant (k = 4096) the page measures top-p
+  against - the same scores, a fixed number of keys.
 * "Local Head Attention Pattern": the first n_sink tokens plus a causal
   sliding window.
 
@@ -26,6 +29,8 @@ Readings of points the page leaves open:
   round-to-nearest-even, straight to the stored dtype (float32 or bfloat16);
 * "reaches" means cumulative mass >= p; equal scores are ordered by ascending
   position; p >= 1 selects every candidate; the set is never empty;
+* top-k keeps min(k, candidates) keys, equal scores by ascending position,
+  and reads k < 1 as 1;
 * candidates are the causal prefix including the query's own position;
   sinks and window are not added to the retrieval set;
 * the window holds the W positions ending at and including the query
@@ -34,7 +39,8 @@ Readings of points the page leaves open:
 Pins (tests under ``tests/`` marked ``not gpu``): brute-force minimal subsets,
 dense causal attention from torch's SDPA when p = 1 and W >= L, closed forms
 (v == 1, window 1), exact rational rounding of the projection, the GQA union
-example and the Table 6 sparsity values.  Nothing in this module is "parity
+example and the Table 6 sparsity values; top-k against a pairwise rank count,
+the argmax and the top-p set of the same size.  Nothing in this module is "parity
 unpinned".
 """
 from __future__ import annotations
@@ -152,6 +158,29 @@ def top_p(scores, p: float) -> TopP:
     return TopP(selected=np.sort(order[:k]), count=k, order=order, prob=prob, cum=cum, scores=s)
 
 
+def top_k(scores, k: int) -> TopP:
+    """Fixed top-k, the static-budget variant the page compares top-p against
+    (section "Evaluation Methodology", baselines; section "Ablation Studies and
+    Robustness Checks", static top-k vs. dynamic top-p, k = 4096).
+
+    The k highest scores of the candidates, equal scores taken by ascending
+    position; every candidate when there are at most k; k < 1 reads as 1 so
+    that the set is never empty.  ``prob`` / ``cum`` are the softmax masses of
+    the same scores, for reporting the mass a fixed budget keeps.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.size
+    if n == 0:
+        raise ValueError("no candidates")
+    kk = min(max(int(k), 1), n)
+    order = np.lexsort((np.arange(n), -s))
+    e = np.exp(s - s.max())
+    prob = e / e.sum()
+    cum = np.empty(n)
+    cum[order] = np.cumsum(prob[order])
+    return TopP(selected=np.sort(order[:kk]), count=kk, order=order, prob=prob, cum=cum, scores=s)
+
+
 def near_threshold(t: TopP, p: float, tol: float = 1e-5) -> np.ndarray:
     """Mask of candidates whose cumulative mass lies within ``tol`` of the threshold p."""
     return (t.cum >= p - tol) & (t.cum - t.prob <= p + tol)
@@ -213,16 +242,17 @@ class RowResult:
 
 
 def retrieval_row(q, q_pre, w_q, K, V, k_idx, pos: int, p: float, dtype: str,
-                  keys: Optional[np.ndarray] = None) -> RowResult:
+                  keys: Optional[np.ndarray] = None, k: Optional[int] = None) -> RowResult:
     """A retrieval head for one query: project, score the causal prefix, top-p, attend.
 
     ``k_idx`` holds the (already rounded) index keys of positions 0..pos.
     ``keys`` overrides the attended set (used to re-evaluate the output on a
-    different valid set); the selection is still returned.
+    different valid set); the selection is still returned.  With ``k`` given
+    the set is the fixed top-k instead of top-p.
     """
     q_idx = project(q_pre, w_q, dtype)
     s = indexer_scores(q_idx, k_idx[: pos + 1])
-    t = top_p(s, p)
+    t = top_p(s, p) if k is None else top_k(s, k)
     sel = t.selected if keys is None else np.asarray(keys, dtype=np.int64)
     return RowResult(attn=attend(q, K, V, sel), topp=t, q_idx=q_idx)
 

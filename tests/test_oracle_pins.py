@@ -202,6 +202,59 @@ def test_near_threshold_rule():
     assert O.set_ok(r, 0.5, [0, 1])[0]
 
 
+# ------------------------------------------------------------------ top-k
+def check_topk_rank(trials=200, seed=13):
+    # rank by pairwise counting: token n is in the set iff fewer than k tokens
+    # beat it (a higher score, or an equal score at an earlier position)
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        n = int(rng.integers(1, 40))
+        s = rng.standard_normal(n) * rng.uniform(0.1, 4.0)
+        if t % 3 == 0:
+            s = np.round(s)                    # force ties
+        k = int(rng.integers(-1, n + 3))
+        res = O.top_k(s, k)
+        beaten = np.array([sum(1 for m in range(n) if s[m] > s[a] or (s[m] == s[a] and m < a))
+                           for a in range(n)])
+        expect = np.nonzero(beaten < max(k, 1))[0]
+        assert res.count == min(max(k, 1), n), (n, k, res.count)
+        assert res.selected.tolist() == expect.tolist(), (s, k)
+
+
+def test_topk_pairwise_rank():
+    check_topk_rank()
+
+
+def test_topk_extremes():
+    rng = np.random.default_rng(14)
+    s = np.round(rng.standard_normal(64) * 2)
+    assert O.top_k(s, 1).selected.tolist() == [int(np.argmax(s))]   # argmax: first of the maxima
+    assert O.top_k(s, 0).selected.tolist() == [int(np.argmax(s))]
+    assert O.top_k(s, 64).count == 64 and O.top_k(s, 10 ** 6).selected.tolist() == list(range(64))
+
+
+def test_topk_equals_topp_of_same_size():
+    # the top-p set is a descending-score prefix, so it is the top-k set with k = |S|
+    rng = np.random.default_rng(15)
+    for t in range(50):
+        s = rng.standard_normal(500) * rng.uniform(0.2, 3.0)
+        if t % 4 == 0:
+            s = np.round(s, 1)
+        p = float(rng.uniform(0.05, 0.999))
+        tp = O.top_p(s, p)
+        assert O.top_k(s, tp.count).selected.tolist() == tp.selected.tolist()
+
+
+def test_topk_shift_and_permutation():
+    rng = np.random.default_rng(16)
+    s = rng.standard_normal(300)
+    a = O.top_k(s, 37).selected
+    assert O.top_k(s + 8.0, 37).selected.tolist() == a.tolist()
+    perm = rng.permutation(300)
+    b = O.top_k(s[perm], 37).selected
+    assert sorted(perm[b].tolist()) == a.tolist()
+
+
 # ------------------------------------------------------------------ attention
 def _problem(L, Hq, Hkv, ret, window, n_sink, p, dtype="f32", seed=7, decode=False, B=1):
     rng = np.random.default_rng(seed)
@@ -361,3 +414,23 @@ def test_mutation_attention_scale_caught(monkeypatch):
     monkeypatch.setattr(O, "HEAD_DIM", 64)
     with pytest.raises(AssertionError):
         check_dense_equivalence()
+
+
+def test_mutation_topk_tie_order_caught(monkeypatch):
+    # equal scores taken by descending position instead of ascending
+    real = O.top_k
+
+    def late_ties(scores, k):
+        s = np.asarray(scores, dtype=np.float64)
+        r = real(s[::-1], k)
+        return O.TopP(np.sort(s.size - 1 - r.selected), r.count, r.order, r.prob, r.cum, s)
+    monkeypatch.setattr(O, "top_k", late_ties)
+    with pytest.raises(AssertionError):
+        check_topk_rank(trials=60)
+
+
+def test_mutation_topk_off_by_one_caught(monkeypatch):
+    real = O.top_k
+    monkeypatch.setattr(O, "top_k", lambda s, k: real(s, k + 1))
+    with pytest.raises(AssertionError):
+        check_topk_rank(trials=60)
