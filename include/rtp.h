@@ -146,6 +146,22 @@ RTP_API rtp_status rtp_select_topp(const rtp_problem *prob, const void *q_pre, c
                            const rtp_selection *sel, void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * rtp_select_topk: the same indexer scores with a fixed budget instead of top-p -
+ * the static top-k (k = 4096 on the page) that the page measures dynamic top-p
+ * against (sections "Evaluation Methodology", baselines, and "Ablation Studies
+ * and Robustness Checks", static top-k vs. dynamic top-p).
+ *   S = the min(k, L) keys n <= pos with the highest s_n, equal scores taken by
+ *       ascending position; k = top_k[b], values below 1 read as 1.
+ *   top_k (dev) [batch] int32.  Every other argument, the output (LIST or
+ *   THRESHOLD, same encoding: tau is the k-th highest score, -inf when every
+ *   key is kept) and the workspace (RTP_CALL_SELECT) are those of rtp_select_topp,
+ *   so the sparse attention calls consume either selection unchanged.
+ */
+RTP_API rtp_status rtp_select_topk(const rtp_problem *prob, const void *q_pre, const float *w_q,
+                           const void *k_idx, const int32_t *top_k, rtp_sel_mode mode,
+                           const rtp_selection *sel, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * rtp_sparse_attn_prefill: exact attention of every retrieval-head query over its
  * THRESHOLD set, O = sum_{n in S} softmax_S(q . k_n / sqrt(128)) v_n
  * (section 3.4, equation after Eq. 5), float32 accumulation.  Membership is

@@ -12,7 +12,7 @@ RTP_F32, RTP_BF16 = 0, 1
 RTP_SEL_LIST, RTP_SEL_THRESHOLD = 0, 1
 RTP_CALL_SELECT, RTP_CALL_SPARSE_PREFILL, RTP_CALL_SPARSE_DECODE, RTP_CALL_LOCAL = 1, 2, 3, 4
 
-EXPORTED = ("rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_sparse_attn_prefill",
+EXPORTED = ("rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_select_topk", "rtp_sparse_attn_prefill",
             "rtp_sparse_attn_decode", "rtp_local_attn", "rtp_status_str", "rtp_last_hip_error")
 
 
@@ -67,6 +67,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtp_index_keys.restype = i32
     lib.rtp_select_topp.argtypes = [P, vp, vp, vp, vp, i32, S, vp, sz, vp]
     lib.rtp_select_topp.restype = i32
+    lib.rtp_select_topk.argtypes = [P, vp, vp, vp, vp, i32, S, vp, sz, vp]
+    lib.rtp_select_topk.restype = i32
     lib.rtp_sparse_attn_prefill.argtypes = [P, vp, vp, vp, vp, S, vp, vp, vp, sz, vp]
     lib.rtp_sparse_attn_prefill.restype = i32
     lib.rtp_sparse_attn_decode.argtypes = [P, vp, vp, vp, S, vp, vp, vp, sz, vp]

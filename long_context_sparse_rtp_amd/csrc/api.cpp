@@ -112,6 +112,35 @@ rtp_status check_ws(const ProbDev& p, rtp_call call, rtp_sel_mode mode, const vo
   return RTP_OK;
 }
 
+// Shared by rtp_select_topp (top_k == nullptr) and rtp_select_topk (top_p == nullptr).
+rtp_status select_common(const rtp_problem* prob, const void* q_pre, const float* w_q, const void* k_idx,
+                         const float* top_p, const int32_t* top_k, rtp_sel_mode mode, const rtp_selection* sel,
+                         void* ws, size_t ws_bytes, void* stream) {
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  if (mode != RTP_SEL_LIST && mode != RTP_SEL_THRESHOLD) return RTP_ERR_INVALID_ARG;
+  if (p.R == 0) return RTP_OK;
+  if (!sel || !aligned16(q_pre) || !aligned16(w_q) || !aligned16(k_idx) || !aligned4(top_k ? (const void*)top_k : top_p))
+    return RTP_ERR_INVALID_ARG;
+  if (!aligned16(sel->q_idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
+  if (mode == RTP_SEL_LIST) {
+    if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
+    if (p.max_k > rtp::select_decode_max_keys()) return RTP_ERR_UNSUPPORTED;
+    if (!aligned4(sel->idx)) return RTP_ERR_INVALID_ARG;
+    if ((sel->tau && !aligned4(sel->tau)) || (sel->tie_pos && !aligned4(sel->tie_pos))) return RTP_ERR_INVALID_ARG;
+  } else {
+    if (!aligned4(sel->tau) || !aligned4(sel->tie_pos)) return RTP_ERR_INVALID_ARG;
+  }
+  st = check_ws(p, RTP_CALL_SELECT, mode, ws, ws_bytes);
+  if (st != RTP_OK) return st;
+  const bool bf16 = prob->dtype == RTP_BF16;
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == RTP_SEL_LIST)
+    return finish(rtp::launch_select_decode(p, bf16, q_pre, w_q, k_idx, top_p, top_k, *sel, ws, s));
+  return finish(rtp::launch_select_prefill(p, bf16, q_pre, w_q, k_idx, top_p, top_k, *sel, ws, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,29 +164,13 @@ rtp_status rtp_index_keys(const rtp_problem* prob, const void* k_pre, const floa
 rtp_status rtp_select_topp(const rtp_problem* prob, const void* q_pre, const float* w_q, const void* k_idx,
                            const float* top_p, rtp_sel_mode mode, const rtp_selection* sel, void* ws,
                            size_t ws_bytes, void* stream) {
-  ProbDev p;
-  rtp_status st = check_problem(prob, &p);
-  if (st != RTP_OK) return st;
-  if (mode != RTP_SEL_LIST && mode != RTP_SEL_THRESHOLD) return RTP_ERR_INVALID_ARG;
-  if (p.R == 0) return RTP_OK;
-  if (!sel || !aligned16(q_pre) || !aligned16(w_q) || !aligned16(k_idx) || !aligned4(top_p))
-    return RTP_ERR_INVALID_ARG;
-  if (!aligned16(sel->q_idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
-  if (mode == RTP_SEL_LIST) {
-    if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
-    if (p.max_k > rtp::select_decode_max_keys()) return RTP_ERR_UNSUPPORTED;
-    if (!aligned4(sel->idx)) return RTP_ERR_INVALID_ARG;
-    if ((sel->tau && !aligned4(sel->tau)) || (sel->tie_pos && !aligned4(sel->tie_pos))) return RTP_ERR_INVALID_ARG;
-  } else {
-    if (!aligned4(sel->tau) || !aligned4(sel->tie_pos)) return RTP_ERR_INVALID_ARG;
-  }
-  st = check_ws(p, RTP_CALL_SELECT, mode, ws, ws_bytes);
-  if (st != RTP_OK) return st;
-  const bool bf16 = prob->dtype == RTP_BF16;
-  hipStream_t s = (hipStream_t)stream;
-  if (mode == RTP_SEL_LIST)
-    return finish(rtp::launch_select_decode(p, bf16, q_pre, w_q, k_idx, top_p, *sel, ws, s));
-  return finish(rtp::launch_select_prefill(p, bf16, q_pre, w_q, k_idx, top_p, *sel, ws, s));
+  return select_common(prob, q_pre, w_q, k_idx, top_p, nullptr, mode, sel, ws, ws_bytes, stream);
+}
+
+rtp_status rtp_select_topk(const rtp_problem* prob, const void* q_pre, const float* w_q, const void* k_idx,
+                           const int32_t* top_k, rtp_sel_mode mode, const rtp_selection* sel, void* ws,
+                           size_t ws_bytes, void* stream) {
+  return select_common(prob, q_pre, w_q, k_idx, nullptr, top_k, mode, sel, ws, ws_bytes, stream);
 }
 
 rtp_status rtp_sparse_attn_prefill(const rtp_problem* prob, const void* q, const void* k, const void* v,

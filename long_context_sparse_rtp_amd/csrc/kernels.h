@@ -36,12 +36,13 @@ int attn_decode_tile_heads(); // local heads of one KV group handled together in
 
 hipError_t launch_index_keys(const ProbDev& p, bool bf16, const void* k_pre, const float* w_k,
                              void* k_idx, hipStream_t s);
+// top_k == nullptr: dynamic top-p over top_p[batch]; otherwise fixed top-k over top_k[batch]
 hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
-                                const void* k_idx, const float* top_p, const rtp_selection& sel,
-                                void* ws, hipStream_t s);
+                                const void* k_idx, const float* top_p, const int32_t* top_k,
+                                const rtp_selection& sel, void* ws, hipStream_t s);
 hipError_t launch_select_prefill(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
-                                 const void* k_idx, const float* top_p, const rtp_selection& sel,
-                                 void* ws, hipStream_t s);
+                                 const void* k_idx, const float* top_p, const int32_t* top_k,
+                                 const rtp_selection& sel, void* ws, hipStream_t s);
 // mode 0: retrieval heads over sel LIST; mode 1: local heads over window + sinks
 hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
                               const void* v, const rtp_selection* sel, void* out, float* lse,

@@ -7,7 +7,10 @@
 // reaches p.  Token-exact; the pages' own kernel ("Hardware-Aware Fast Top-p
 // Decoding Kernel") approximates with 64-token blocks and a 256-bin histogram
 // finished by the last CTA - kept here as the idea of a sort-free histogram
-// threshold.
+// threshold.  With a top-k budget instead of p (the static top-k the page
+// ablates against, sections "Evaluation Methodology" and "Ablation Studies and
+// Robustness Checks") the same kernels walk token counts instead of masses:
+// the histogram already carries both.
 //
 // A row (retrieval slot, sequence) is cut into units of 4096 keys and every
 // kernel runs one workgroup per unit, so the whole device works on each step.
@@ -71,7 +74,7 @@ struct RowState {
   int jstar;
   uint32_t cabove;            // tokens before the crossing bin
   uint32_t bincnt;            // tokens in the crossing bin
-  int pad;
+  int count_mode;             // top-k: every token weighs 1 and the target is k
 };
 
 struct DecodeWs {
@@ -422,15 +425,18 @@ __device__ Merge row_merge(const DecodeWs& ws, const RowGeom& g, int* A_s, int* 
 
 // ======================================================================= 2. collect
 __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const float* __restrict__ top_p,
-                                                            DecodeWs ws) {
+                                                            const int32_t* __restrict__ top_k, DecodeWs ws) {
   const RowGeom g = row_geom(p, blockIdx.y);
   const int c = blockIdx.x;
   if (c >= g.U || g.U > kMaxUnits) return;
   const int tid = threadIdx.x;
   const int64_t slot = g.slot0 + c;
-  const float pp = top_p[g.b];
+  const bool count_mode = top_k != nullptr;
+  const int kk = count_mode ? max(top_k[g.b], 1) : 0;
+  const float pp = count_mode ? 0.f : top_p[g.b];
 
-  if (g.L == 0 || !(pp < 1.f)) {   // nothing to choose: empty row, or every key
+  // nothing to choose: empty row, or every key (p >= 1 or NaN; k >= L)
+  if (g.L == 0 || (count_mode ? kk >= g.L : !(pp < 1.f))) {
     if (c == 0 && tid == 0) {
       RowState rs = {};
       rs.mode = (g.L == 0) ? ROW_EMPTY : ROW_ALL;
@@ -461,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
 
   const Merge mg = row_merge(ws, g, A_s, used_s, f_s, itmp, dtmp);
   const int A = mg.A;
-  const double target = fmax((double)pp * mg.Z, 1.0);
+  const double target = count_mode ? (double)kk : fmax((double)pp * mg.Z, 1.0);
 
   // ---- row bins, kBinsPerPass at a time (8 consecutive per thread): the first bin
   // whose cumulative mass reaches the target.  A bin's mass above is computed by
@@ -511,6 +517,10 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
           cb[i] += (uint32_t)(e[k][i] >> kCountShift);
         }
       }
+    }
+    if (count_mode) {
+#pragma unroll
+      for (int i = 0; i < BT; ++i) mb[i] = (double)cb[i];
     }
     double tm = 0.0;
     uint32_t tc = 0u;
@@ -588,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
       rs.jstar = jstar;
       rs.cabove = cabove_s;
       rs.bincnt = bincnt_s;
-      rs.pad = 0;
+      rs.count_mode = count_mode ? 1 : 0;
       ws.rows[g.row] = rs;
     }
   }
@@ -644,6 +654,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
   } else {
     const int A = rs.A;
     const double target = rs.target;
+    const bool cmode = rs.count_mode != 0;
     // per unit: reference bin and scale of the row merge, candidate count
     constexpr int PU = kMaxUnits / kThreads;
     uint32_t nin = 0u, cmax = 0u;
@@ -705,7 +716,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
           const float sv = undesc_key((uint32_t)(kv >> 32));
           const uint32_t n = (uint32_t)(kv & 0xFFFFFFFFull);
           const int u = (int)min(n / (uint32_t)kChunk, (uint32_t)(g.U - 1));
-          ms[t] = (double)mass38(sv, A_s[u]) * f_s[u];
+          ms[t] = cmode ? 1.0 : (double)mass38(sv, A_s[u]) * f_s[u];
         }
         loc += ms[t];
       }
@@ -768,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
           const uint32_t key = desc_key(sv);
           if (shift < 32 && (key >> shift) != prefix) continue;
           const uint32_t dg = (key >> nshift) & ((1u << nbits) - 1u);
-          atomicAdd(&hm2[dg], mass38(sv, A));
+          atomicAdd(&hm2[dg], cmode ? 1ull : mass38(sv, A));
           atomicAdd(&hc2[dg], 1u);
         }
         __syncthreads();
@@ -798,7 +809,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
       if (cnt_s > (uint32_t)kCap) {
         // exact ties: the tied value is the key `prefix`; admit them by ascending position
         const float tv = undesc_key(prefix);
-        const double mt = (double)mass38(tv, A);
+        const double mt = cmode ? 1.0 : (double)mass38(tv, A);
         const double need = target - ab_s;
         long long kneed = (mt > 0.0) ? (long long)ceil(need / mt) : (long long)cnt_s;
         kneed = max(1ll, min(kneed, (long long)cnt_s));
@@ -845,7 +856,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
           int js = max(nc - 1, 0);
           for (int i = 0; i < nc; ++i) {
             const float sv = undesc_key((uint32_t)(cand_s[order_s[i]] >> 32));
-            const double mi = (double)mass38(sv, A);
+            const double mi = cmode ? 1.0 : (double)mass38(sv, A);
             if (cm + mi >= target) { js = i; break; }
             cm += mi;
           }
@@ -898,8 +909,8 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
 size_t ws_select_decode(const ProbDev& p) { return ws_layout(p, nullptr, nullptr); }
 
 hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
-                                const void* k_idx, const float* top_p, const rtp_selection& sel,
-                                void* ws, hipStream_t s) {
+                                const void* k_idx, const float* top_p, const int32_t* top_k,
+                                const rtp_selection& sel, void* ws, hipStream_t s) {
   if (p.R == 0) return hipSuccess;
   DecodeWs w;
   ws_layout(p, ws, &w);
@@ -911,7 +922,7 @@ hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, 
   else
     hipLaunchKernelGGL(sel_dec_score<float>, grid, dim3(kThreads), 0, s, p, (const float*)q_pre, w_q,
                        (const float*)k_idx, sel, w);
-  hipLaunchKernelGGL(sel_dec_collect, grid, dim3(kThreads), 0, s, p, top_p, w);
+  hipLaunchKernelGGL(sel_dec_collect, grid, dim3(kThreads), 0, s, p, top_p, top_k, w);
   hipLaunchKernelGGL(sel_dec_emit, grid, dim3(kThreads), 0, s, p, sel, w);
   return hipGetLastError();
 }

@@ -4,6 +4,10 @@
 // section 3.4 "Dynamic Top-p Selection Mechanism", Eq. 5): over the causal
 // prefix n <= pos, softmax of s_n = q_idx . k_idx_n / 4, keys by descending
 // score (ties: ascending position), the smallest prefix whose mass reaches p.
+// The same kernel with COUNT = true gives the fixed top-k the page ablates
+// against (sections "Evaluation Methodology" and "Ablation Studies and
+// Robustness Checks"): every token then weighs 1 instead of its mass and the
+// target is k instead of p * Z.
 // The result of a row is (tau, tie_pos, count): S = {s > tau} U {s == tau,
 // n <= tie_pos}; tie_pos = INT_MAX when no token scoring exactly tau is left
 // out, so that S = {s >= tau}.  Lists are never materialised (a 128K prefill
@@ -67,6 +71,7 @@ struct RowCtl {
   unsigned long long above;   // fixed-point mass of tokens strictly better than the range
   float top;                  // reference score (>= row max)
   float pval;
+  int kval;                   // top-k budget (COUNT)
   uint32_t lo;                // range start in the current key space
   uint32_t kfix, dfix;        // fixed K / desc_key for the tie key spaces
   int sh;                     // digit shift of the range
@@ -127,10 +132,11 @@ constexpr size_t kCandBytes = sizeof(unsigned long long) * kRows * kCap;
 constexpr size_t kUnionBytes = (kHist1Bytes > kRefineBytes ? (kHist1Bytes > kCandBytes ? kHist1Bytes : kCandBytes)
                                                             : (kRefineBytes > kCandBytes ? kRefineBytes : kCandBytes));
 
-template <typename T>
+template <typename T, bool COUNT>
 __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     ProbDev p, const T* __restrict__ q_pre, const float* __restrict__ w_q, const T* __restrict__ k_idx,
-    const float* __restrict__ top_p, rtp_selection sel, const uint32_t* __restrict__ kn2) {
+    const float* __restrict__ top_p, const int32_t* __restrict__ top_k, rtp_selection sel,
+    const uint32_t* __restrict__ kn2) {
   typedef typename IdxFrag<T>::type IF;
   const int tiles_per_b = (p.max_q + kRows - 1) / kRows;
   const int b = blockIdx.x % p.batch;
@@ -183,7 +189,6 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
   if (tid < kRows) {
     RowCtl& c = ctl[tid];
     c.pos = off + min(i0 + tid, Lq - 1);
-    c.pval = top_p[b];
     float qn = 0.f;
 #pragma unroll
     for (int j = 0; j < kIdxDim; ++j) {
@@ -197,7 +202,15 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     c.lo = 0u; c.sh = 16; c.kind = 0; c.kfix = 0u; c.dfix = 0u;
     c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = c.pos + 1;
     c.target = 1.0;
-    c.phase = (c.pval < 1.f) ? PH_HIST1 : PH_DONE;   // p >= 1 (or NaN): every key
+    if (COUNT) {
+      c.pval = 0.f;
+      c.kval = max(top_k[b], 1);
+      c.phase = (c.kval <= c.pos) ? PH_HIST1 : PH_DONE;   // k >= pos + 1: every key
+    } else {
+      c.pval = top_p[b];
+      c.kval = 0;
+      c.phase = (c.pval < 1.f) ? PH_HIST1 : PH_DONE;     // p >= 1 (or NaN): every key
+    }
   }
   __syncthreads();
 
@@ -285,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           if (check && n > rk.pos) continue;
           const float u = fmaf(d[i], a1, b1);
           const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kNB1 - 1));
-          atomicAdd(&h1[bin][col], (unsigned long long)mass31(d[i], rk.am, rk.bm));
+          atomicAdd(&h1[bin][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
         }
       });
     } else if (sweep == PH_REFINE && all_fast) {
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           for (int i = 0; i < 4; ++i) {
             if (inr[i]) {
               const uint32_t dig = (key20(u20[i]) - rk.lo) >> rk.sh;
-              atomicAdd(&hm2[dig][col], (unsigned long long)mass31(d[i], rk.am, rk.bm));
+              atomicAdd(&hm2[dig][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
             }
           }
         }
@@ -370,7 +383,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           if (!inr) continue;
           if (sweep == PH_REFINE) {
             const uint32_t dig = dk2 >> rk.sh;
-            atomicAdd(&hm2[dig][col], (unsigned long long)mass31(d[i], rk.am, rk.bm));
+            atomicAdd(&hm2[dig][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
           } else {
             const int slot = atomicAdd(&ccount_s[col], 1);
             if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
@@ -419,7 +432,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
             rc.top = rc.top - (float)(bl - 1) / (kBinsPerOctave * kLog2e);
           }
         } else {
-          const double target = fmax((double)rc.pval * (double)Z, 1.0);
+          const double target = COUNT ? (double)rc.kval : fmax((double)rc.pval * (double)Z, 1.0);
           if ((double)pre < target && target <= (double)(pre + sp)) {
             unsigned long long cm = pre;
             int bstar = spart * PB + PB - 1;
@@ -520,7 +533,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         const float am = kLog2e * 0.25f, bm = 31.f - rc.top * kLog2e;
         for (int a = 0; a < nc; ++a) {
           const float s = undesc_key((uint32_t)(cd[a] >> 32));
-          const uint32_t mf = mass31(s * 4.f, am, bm);
+          const uint32_t mf = COUNT ? 1u : mass31(s * 4.f, am, bm);
           if ((double)(cm + mf) >= rc.target) { jstar = a; break; }
           cm += mf;
         }
@@ -553,8 +566,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
 size_t ws_select_prefill(const ProbDev& p) { return (sizeof(uint32_t) * (size_t)p.R * p.batch + 255) & ~(size_t)255; }
 
 hipError_t launch_select_prefill(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
-                                 const void* k_idx, const float* top_p, const rtp_selection& sel, void* ws,
-                                 hipStream_t s) {
+                                 const void* k_idx, const float* top_p, const int32_t* top_k,
+                                 const rtp_selection& sel, void* ws, hipStream_t s) {
   if (p.R == 0 || p.Tq == 0) return hipSuccess;
   uint32_t* kn2 = (uint32_t*)ws;
   const int nrows = p.R * p.batch;
@@ -566,12 +579,18 @@ hipError_t launch_select_prefill(const ProbDev& p, bool bf16, const void* q_pre,
     hipLaunchKernelGGL(kidx_norm_max<float>, dim3(nb, nrows), dim3(256), 0, s, p, (const float*)k_idx, kn2);
   const int tiles_per_b = (p.max_q + kRows - 1) / kRows;
   dim3 grid(tiles_per_b * p.batch, p.R);
-  if (bf16)
-    hipLaunchKernelGGL(select_prefill_kernel<bf16_t>, grid, dim3(kThreads), 0, s, p, (const bf16_t*)q_pre, w_q,
-                       (const bf16_t*)k_idx, top_p, sel, (const uint32_t*)kn2);
+  if (bf16 && top_k)
+    hipLaunchKernelGGL((select_prefill_kernel<bf16_t, true>), grid, dim3(kThreads), 0, s, p, (const bf16_t*)q_pre,
+                       w_q, (const bf16_t*)k_idx, top_p, top_k, sel, (const uint32_t*)kn2);
+  else if (bf16)
+    hipLaunchKernelGGL((select_prefill_kernel<bf16_t, false>), grid, dim3(kThreads), 0, s, p, (const bf16_t*)q_pre,
+                       w_q, (const bf16_t*)k_idx, top_p, top_k, sel, (const uint32_t*)kn2);
+  else if (top_k)
+    hipLaunchKernelGGL((select_prefill_kernel<float, true>), grid, dim3(kThreads), 0, s, p, (const float*)q_pre,
+                       w_q, (const float*)k_idx, top_p, top_k, sel, (const uint32_t*)kn2);
   else
-    hipLaunchKernelGGL(select_prefill_kernel<float>, grid, dim3(kThreads), 0, s, p, (const float*)q_pre, w_q,
-                       (const float*)k_idx, top_p, sel, (const uint32_t*)kn2);
+    hipLaunchKernelGGL((select_prefill_kernel<float, false>), grid, dim3(kThreads), 0, s, p, (const float*)q_pre,
+                       w_q, (const float*)k_idx, top_p, top_k, sel, (const uint32_t*)kn2);
   return hipGetLastError();
 }
 

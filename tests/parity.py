@@ -20,12 +20,20 @@ def sync():
     torch.cuda.synchronize()
 
 
-def run_prefill(inp) -> Dict[str, torch.Tensor]:
-    """Prefill path: index keys -> THRESHOLD select -> sparse attention + local attention."""
+def _select(rtp, prob, inp, k_idx, mode, top_k):
+    if top_k is None:
+        return rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, mode)
+    kt = torch.as_tensor(list(top_k), dtype=torch.int32, device=inp.q.device)
+    return rtp.rtp_select_topk(prob, inp.q_pre, inp.w, k_idx, kt, mode)
+
+
+def run_prefill(inp, top_k: Optional[Sequence[int]] = None) -> Dict[str, torch.Tensor]:
+    """Prefill path: index keys -> THRESHOLD select (top-p, or top-k per sequence when
+    ``top_k`` is given) -> sparse attention + local attention."""
     import long_context_sparse_rtp_amd as rtp
     prob = rtp.Problem.from_inputs(inp)
     k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w)
-    sel = rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_THRESHOLD)
+    sel = _select(rtp, prob, inp, k_idx, rtp.RTP_SEL_THRESHOLD, top_k)
     out = torch.full_like(inp.q, float("nan"))
     lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=inp.q.device)
     rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel, out, lse)
@@ -34,11 +42,12 @@ def run_prefill(inp) -> Dict[str, torch.Tensor]:
     return dict(k_idx=k_idx, q_idx=sel.q_idx, tau=sel.tau, tie=sel.tie_pos, count=sel.count, out=out, lse=lse)
 
 
-def run_decode(inp, k_idx: torch.Tensor) -> Dict[str, torch.Tensor]:
-    """Decode path with a precomputed index cache: LIST select -> sparse decode + local decode."""
+def run_decode(inp, k_idx: torch.Tensor, top_k: Optional[Sequence[int]] = None) -> Dict[str, torch.Tensor]:
+    """Decode path with a precomputed index cache: LIST select (top-p, or top-k) ->
+    sparse decode + local decode."""
     import long_context_sparse_rtp_amd as rtp
     prob = rtp.Problem.from_inputs(inp)
-    sel = rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_LIST)
+    sel = _select(rtp, prob, inp, k_idx, rtp.RTP_SEL_LIST, top_k)
     out = torch.full_like(inp.q, float("nan"))
     lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=inp.q.device)
     rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse)
@@ -105,6 +114,40 @@ def _amb_eps(q_idx: np.ndarray, k_idx: np.ndarray) -> np.ndarray:
     return 2.0 ** -19 * (np.abs(k_idx) @ np.abs(q_idx)) * O.IDX_SCALE + 1e-30
 
 
+def topk_set_ok(t: O.TopP, got, eps: np.ndarray):
+    """Is ``got`` the oracle's top-k set, up to keys whose float64 score lies within the
+    float32 scoring error of the k-th score (where the two precisions may order them
+    differently)?  Returns (ok, n_differing)."""
+    n = t.scores.size
+    G = np.asarray(got, dtype=np.int64)
+    if G.size != t.count or (G.size and (G.min() < 0 or G.max() >= n or np.unique(G).size != G.size)):
+        return False, -1
+    gm = np.zeros(n, dtype=bool)
+    gm[G] = True
+    sm = np.zeros(n, dtype=bool)
+    sm[t.selected] = True
+    diff = gm ^ sm
+    if not diff.any():
+        return True, 0
+    kth = t.order[t.count - 1]
+    ok = np.all(np.abs(t.scores[diff] - t.scores[kth]) <= eps[diff] + eps[kth])
+    return bool(ok), int(diff.sum())
+
+
+def _set_check(pr: Problem, b: int, t: O.TopP, eps: np.ndarray):
+    """The set rule of the row: near-threshold mass for top-p, score ambiguity for top-k."""
+    if pr.top_k is None:
+        p = float(pr.top_p[b])
+        return lambda G: O.set_ok(t, p, G)
+    return lambda G: topk_set_ok(t, G, eps)
+
+
+def _keeps_all(pr: Problem, b: int, pos: int) -> bool:
+    if pr.top_k is None:
+        return float(pr.top_p[b]) >= 1.0
+    return int(pr.top_k[b]) >= pos + 1
+
+
 def check_retrieval_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.ndarray], tol: float):
     """Compare one retrieval-head row (THRESHOLD output).  Returns (ok, info)."""
     r = pr.slot_of(h)
@@ -113,19 +156,19 @@ def check_retrieval_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.nda
     info = {}
     if not np.array_equal(g["q_idx"][r, qi], res.q_idx):
         return False, {"why": "q_idx mismatch"}
-    p = float(pr.top_p[b])
     tau = g["tau"][r, qi]
     count = int(g["count"][r, qi])
     t = res.topp
     pos = pr.pos_of(b, i)
     tie = int(g["tie"][r, qi])
     INT_MAX = 2 ** 31 - 1
-    if p >= 1.0:
+    eps = _amb_eps(res.q_idx, pr.index_keys(b, r)[: pos + 1])
+    set_check = _set_check(pr, b, t, eps)
+    if _keeps_all(pr, b, pos):
         G_list = [np.arange(pos + 1)]
     else:
         if not (0 <= tie <= pos or tie == INT_MAX):
             return False, {"why": f"tie_pos {tie} outside [0, {pos}]"}
-        eps = _amb_eps(res.q_idx, pr.index_keys(b, r)[: pos + 1])
         s = t.scores
         n = np.arange(s.size)
         if tie != INT_MAX:
@@ -155,7 +198,7 @@ def check_retrieval_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.nda
     qv = pr.q_row(qi, h)
     best = None
     for G in G_list:
-        ok_set, ndiff = O.set_ok(t, p, G)
+        ok_set, ndiff = set_check(G)
         if not ok_set:
             continue
         a = O.attend(qv, pr_k, pr_v, G)
@@ -179,8 +222,8 @@ def check_list_row(pr: Problem, b: int, h: int, g: Dict[str, np.ndarray], tol: f
     G = g["idx"][r, k0:k0 + count].astype(np.int64)
     if count < 1 or np.any(np.diff(G) <= 0) or G.min() < 0 or G.max() >= k1 - k0:
         return False, {"why": "list not ascending / out of range", "count": count}
-    p = float(pr.top_p[b])
-    ok_set, ndiff = O.set_ok(res.topp, p, G)
+    eps = _amb_eps(res.q_idx, pr.index_keys(b, r))
+    ok_set, ndiff = _set_check(pr, b, res.topp, eps)(G)
     if not ok_set:
         return False, {"why": "set differs beyond near-threshold tokens", "count": count,
                        "oracle_count": res.topp.count, "ndiff": ndiff}

@@ -1,0 +1,130 @@
+"""GPU parity of the fixed top-k selection (rtp_select_topk) against the oracle's
+top-k, in both output forms, and of the attention calls fed with its sets.
+
+Top-k is the static-budget variant the page compares dynamic top-p with
+(k = 4096 there).  Sets must equal the oracle's except for keys whose float64
+score lies within the float32 scoring error of the k-th score; count is exact."""
+import numpy as np
+import pytest
+import torch
+
+from synth import DECODE_32K, PREFILL_128K, TINY_PREFILL, make_inputs, sample_rows, scaled
+from synth.configs import forced_edge_rows
+from oracle.problem import from_inputs
+
+from . import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _prefill(cfg, top_k, rows=None, heads=None):
+    _say(f"[case] top-k prefill {cfg.name} L={cfg.seqlens or cfg.seqlen} dtype={cfg.dtype} k={top_k}")
+    inp = make_inputs(cfg, DEV)
+    g = P.to_host(P.run_prefill(inp, top_k=top_k))
+    pr = from_inputs(inp)
+    pr.top_k = list(top_k)
+    if rows is None:
+        rows = [(b, i) for b in range(cfg.batch) for i in range(inp.seqlens_q[b])]
+    heads = list(range(cfg.n_q_heads)) if heads is None else heads
+    n, fails, stats = P.check_rows(pr, g, rows, heads, P.TOL[cfg.dtype])
+    _say(f"[result] {cfg.name}: {n} pairs, {len(fails)} failures, {stats}")
+    assert not fails, fails[:5]
+    # count is exactly min(k, pos + 1) on every row, checked or not
+    for r in range(cfg.n_ret):
+        for b in range(cfg.batch):
+            q0, lq = int(inp.cu_q[b]), inp.seqlens_q[b]
+            pos = np.arange(lq)
+            assert np.array_equal(g["count"][r, q0:q0 + lq], np.minimum(max(top_k[b], 1), pos + 1))
+    return g
+
+
+def _decode(cfg, top_k):
+    _say(f"[case] top-k decode {cfg.name} B={cfg.batch} k={top_k}")
+    inp = make_inputs(cfg, DEV)
+    pr = from_inputs(inp)
+    pr.top_k = list(top_k)
+    k_idx = P.oracle_index_keys(pr, inp.q.dtype, DEV)
+    pr.k_idx = k_idx.cpu()
+    g = P.to_host(P.run_decode(inp, k_idx, top_k=top_k))
+    rows = [(b, 0) for b in range(cfg.batch)]
+    n, fails, stats = P.check_rows(pr, g, rows, list(range(cfg.n_q_heads)), P.TOL[cfg.dtype], decode=True)
+    _say(f"[result] {cfg.name}: {n} pairs, {len(fails)} failures, {stats}")
+    assert not fails, fails[:5]
+    for r in range(cfg.n_ret):
+        for b in range(cfg.batch):
+            assert int(g["count"][r, b]) == min(max(top_k[b], 1), inp.seqlens_k[b])
+    return g
+
+
+def test_topk_prefill_tiny_f32_all_rows():
+    # rows 0..255 keep every key, later rows exactly 256
+    _prefill(TINY_PREFILL, [256])
+
+
+def test_topk_prefill_bf16_k4096_sampled():
+    cfg = scaled(PREFILL_128K, name="topk_prefill_9k_bf16", seqlen=9000, window=512)
+    rows = [(0, i) for i in sample_rows(cfg, 96, forced_edge_rows(cfg) + [4094, 4095, 4096, 4097])]
+    _prefill(cfg, [4096], rows=rows)
+
+
+def test_topk_prefill_ragged_batch_extremes():
+    # k = 1 (the argmax), k < 1 (read as 1), a mid budget, and k beyond the length
+    cfg = scaled(TINY_PREFILL, name="topk_ragged", batch=4, seqlens=(37, 300, 1, 1000), dtype="bf16",
+                 n_q_heads=8, n_kv_heads=2, ret_heads=(0, 5), window=64, needles="none")
+    _prefill(cfg, [1, 0, 5, 123])
+    _prefill(cfg, [2000, 64, 1, 999])
+
+
+def test_topk_prefill_exact_ties():
+    # many identical index keys: the k-th score is shared by hundreds of keys, so the
+    # tie key spaces (score bits, then positions) decide the set
+    cfg = scaled(TINY_PREFILL, name="topk_ties", seqlen=1500, n_q_heads=2, n_kv_heads=1, ret_heads=(0,),
+                 window=32, needles="none")
+    inp = make_inputs(cfg, DEV)
+    kp = inp.k_pre.view(-1, 128)
+    kp[:] = kp[torch.arange(kp.shape[0], device=kp.device) % 7]   # seven distinct keys
+    _say("[case] top-k prefill exact ties")
+    g = P.to_host(P.run_prefill(inp, top_k=[300]))
+    pr = from_inputs(inp)
+    pr.top_k = [300]
+    rows = [(0, i) for i in (0, 6, 7, 299, 300, 301, 700, 1024, 1499)]
+    n, fails, stats = P.check_rows(pr, g, rows, [0, 1], P.TOL[cfg.dtype])
+    _say(f"[result] topk ties: {n} pairs, {len(fails)} failures, {stats}")
+    assert not fails, fails[:5]
+
+
+def test_topk_decode_k4096():
+    _decode(scaled(DECODE_32K, name="topk_decode_16k_b2", batch=2, seqlen=16384), [4096, 4096])
+
+
+def test_topk_decode_ragged_extremes():
+    cfg = scaled(DECODE_32K, name="topk_ragged_decode", batch=6, seqlens=(4096, 5000, 300, 70000, 1, 9000),
+                 needles="query", needles_per_seq=16)
+    _decode(cfg, [4096, 1, 300, 4096, 4096, 0])
+
+
+def test_topk_decode_exact_ties_all_equal():
+    # every index key equal: the first k positions win
+    cfg = scaled(DECODE_32K, name="topk_decode_ties", batch=2, seqlen=9000, needles="none")
+    inp = make_inputs(cfg, DEV)
+    pr = from_inputs(inp)
+    pr.top_k = [4096, 5000]
+    k_idx = P.oracle_index_keys(pr, inp.q.dtype, DEV)
+    k_idx[:] = k_idx[:, :1]
+    pr.k_idx = k_idx.cpu()
+    _say("[case] top-k decode all-equal keys")
+    g = P.to_host(P.run_decode(inp, k_idx, top_k=pr.top_k))
+    for r in range(cfg.n_ret):
+        for b in range(cfg.batch):
+            k0 = int(inp.cu_k[b])
+            cnt = int(g["count"][r, b])
+            assert cnt == pr.top_k[b]
+            assert np.array_equal(g["idx"][r, k0:k0 + cnt], np.arange(cnt))
+    n, fails, stats = P.check_rows(pr, g, [(b, 0) for b in range(cfg.batch)], list(range(cfg.n_q_heads)),
+                                   P.TOL[cfg.dtype], decode=True)
+    assert not fails, fails[:5]
