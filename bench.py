@@ -11,7 +11,8 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts.
 
 Prints one JSON line: ``value`` is prefill tokens/s; the decode step time, the
 per-kernel times, the roofline of the dominant kernel and the CPU oracle
-baseline ride along in the same line.
+baseline ride along in the same line, and so do the same steps with the fixed top-k
+selection (k = 4096, the pages' static-budget ablation) under ``topk_4096``.
 """
 from __future__ import annotations
 
@@ -50,6 +51,7 @@ def _args():
     ap.add_argument("--decode-steps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-references", action="store_true", help="skip the dense and pages'-prefill references")
+    ap.add_argument("--no-variants", action="store_true", help="skip the fixed top-k (k = 4096) steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -95,10 +97,18 @@ def _traffic(name):
         return None
 
 
-def bench_prefill(args, torch, rtp, synth):
+def _select_call(rtp, prob, inp, k_idx, mode, sel, ws, stream, top_k):
+    if top_k is None:
+        return lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, mode, sel, ws, stream=stream)
+    return lambda: rtp.rtp_select_topk(prob, inp.q_pre, inp.w, k_idx, top_k, mode, sel, ws, stream=stream)
+
+
+def bench_prefill(args, torch, rtp, synth, inp=None, top_k=None):
+    """The prefill step; with ``top_k`` (int32 [batch]) the selection is the fixed top-k."""
     cfg = synth.PREFILL_128K
     dev = "cuda"
-    inp = synth.make_inputs(cfg, dev)
+    if inp is None:
+        inp = synth.make_inputs(cfg, dev)
     prob = rtp.Problem.from_inputs(inp)
     stream = torch.cuda.current_stream()
     k_idx = torch.empty((cfg.n_ret, inp.total_k, 16), dtype=inp.q.dtype, device=dev)
@@ -111,8 +121,8 @@ def bench_prefill(args, torch, rtp, synth):
     def step(t: Timer = None):
         calls = [
             ("index_keys", lambda: rtp.rtp_index_keys(prob, inp.k_pre, inp.w, k_idx, stream=stream)),
-            ("select_topp", lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p,
-                                                        rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream=stream)),
+            ("select_topp" if top_k is None else "select_topk",
+             _select_call(rtp, prob, inp, k_idx, rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream, top_k)),
             ("sparse_attn_prefill", lambda: rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel,
                                                                         out, lse, stream=stream)),
             ("local_attn", lambda: rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, stream=stream)),
@@ -212,10 +222,12 @@ def bench_prefill_references(args, torch, rtp, synth, pre):
     return dict(dense_ms=dense_ms, pages_ms=pages_ms, dense_tflops=dense_flop / (dense_ms * 1e-3) / 1e12)
 
 
-def bench_decode(args, torch, rtp, synth):
+def bench_decode(args, torch, rtp, synth, inp=None, top_k=None):
+    """The decode step; with ``top_k`` (int32 [batch]) the selection is the fixed top-k."""
     cfg = synth.DECODE_32K
     dev = "cuda"
-    inp = synth.make_inputs(cfg, dev)
+    if inp is None:
+        inp = synth.make_inputs(cfg, dev)
     prob = rtp.Problem.from_inputs(inp)
     stream = torch.cuda.current_stream()
     k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w, stream=stream)   # cache built before timing
@@ -231,8 +243,8 @@ def bench_decode(args, torch, rtp, synth):
 
     def step(t: Timer = None):
         calls = [
-            ("select_topp", lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_LIST,
-                                                        sel, ws_sel, stream=stream)),
+            ("select_topp" if top_k is None else "select_topk",
+             _select_call(rtp, prob, inp, k_idx, rtp.RTP_SEL_LIST, sel, ws_sel, stream, top_k)),
             ("sparse_attn_decode", lambda: rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse,
                                                                       ws_dec, stream=stream)),
             ("local_attn", lambda: rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, ws_loc, stream=stream)),
@@ -281,7 +293,7 @@ def bench_decode(args, torch, rtp, synth):
     return dict(ms=ms, per_kernel_ms=per, bytes=dict(sparse_attn_decode=sparse_bytes, local_attn=local_bytes,
                                                      select_topp=idx_bytes, q_out=qo_bytes),
                 total_bytes=sparse_bytes + local_bytes + idx_bytes + qo_bytes,
-                mean_frac_selected=float(counts.mean().item()) / L)
+                mean_frac_selected=float(counts.mean().item()) / L, inp=inp)
 
 
 def cpu_baseline(args, pre):
@@ -410,6 +422,27 @@ def main():
                           "mean_selected_fraction": dec["mean_frac_selected"]}
         if pre is None:
             line.update(value=dec["ms"] * 1e3, unit="us", higher_is_better=False, ms_per_step=dec["ms"])
+    if not args.no_variants:
+        # the pages' static-budget ablation: the same steps with the fixed top-k selection
+        var = {"note": "fixed top-k, k = 4096 (the pages' top-k ablation) in place of top-p; same inputs"}
+        if pre is not None:
+            print("[bench] prefill 128K, top-k 4096 ...", file=sys.stderr, flush=True)
+            kt = torch.full((pre["cfg"].batch,), 4096, dtype=torch.int32, device="cuda")
+            pk = bench_prefill(args, torch, rtp, synth, inp=pre["inp"], top_k=kt)
+            var["prefill_128k"] = {"ms_per_step": pk["ms"], "tokens_per_s": pk["tokens"] / (pk["ms"] * 1e-3),
+                                   "per_kernel_ms": pk["per_kernel_ms"],
+                                   "mean_selected_fraction": pk["mean_frac_selected"]}
+        if dec is not None:
+            print("[bench] decode 32K x 8, top-k 4096 ...", file=sys.stderr, flush=True)
+            kt = torch.full((synth.DECODE_32K.batch,), 4096, dtype=torch.int32, device="cuda")
+            dk = bench_decode(args, torch, rtp, synth, inp=dec["inp"], top_k=kt)
+            var["decode_32k_b8"] = {"step_us": dk["ms"] * 1e3,
+                                    "per_kernel_us": {k: v * 1e3 for k, v in dk["per_kernel_ms"].items()},
+                                    "algorithmic_bytes": dk["total_bytes"],
+                                    "step_frac_of_hbm_roofline": dk["total_bytes"] / (HBM_PEAK_GBS * 1e9)
+                                    / (dk["ms"] * 1e-3),
+                                    "mean_selected_fraction": dk["mean_frac_selected"]}
+        line["topk_4096"] = var
     if pre is not None and not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args, pre)
