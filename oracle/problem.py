@@ -44,6 +44,7 @@ class Problem:
     dtype: str               # "f32" | "bf16"
     k_idx: Any = None        # [R, T_k, 16] stored index keys (decode inputs), optional
     top_k: Optional[Sequence[int]] = None   # per sequence: fixed top-k instead of top-p
+    blocks: bool = False     # the pages' block-granular top-p instead of the token-exact one
     _cache: Dict[Tuple, np.ndarray] = dataclasses.field(default_factory=dict)
 
     @property
@@ -117,7 +118,7 @@ class Problem:
         if r >= 0:
             return O.retrieval_row(self.q_row(qi, h), self.q_pre_row(qi, r), self.w("w_q", r), K, V,
                                    self.index_keys(b, r), pos, float(self.top_p[b]), self.dtype, keys=keys,
-                                   k=None if self.top_k is None else int(self.top_k[b]))
+                                   k=None if self.top_k is None else int(self.top_k[b]), blocks=self.blocks)
         return O.local_row(self.q_row(qi, h), K, V, pos, self.window, self.n_sink)
 
 

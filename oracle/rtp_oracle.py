@@ -20,6 +20,9 @@ Transferring Full Attention into Sparse within Hundred Training Steps"
 * Sections "Evaluation Methodology" and "Ablation Studies and Robustness
   Checks": the static top-k variant (k = 4096) the page measures top-p
   against - the same scores, a fixed number of keys.
+* Section "Hardware-Aware Fast Top-p Decoding Kernel": the page's own
+  block-granular approximation of top-p (64-token blocks, 256-bin histogram
+  of block masses over block maxima), ``block_top_p``.
 * "Local Head Attention Pattern": the first n_sink tokens plus a causal
   sliding window.
 
@@ -40,7 +43,9 @@ Pins (tests under ``tests/`` marked ``not gpu``): brute-force minimal subsets,
 dense causal attention from torch's SDPA when p = 1 and W >= L, closed forms
 (v == 1, window 1), exact rational rounding of the projection, the GQA union
 example and the Table 6 sparsity values; top-k against a pairwise rank count,
-the argmax and the top-p set of the same size.  Nothing in this module is "parity
+the argmax and the top-p set of the same size; block top-p against a worked
+example, the token-exact top-p it reduces to with one-token blocks and fine
+bins, and a brute-force scan over the cut bin.  Nothing in this module is "parity
 unpinned".
 """
 from __future__ import annotations
@@ -181,6 +186,77 @@ def top_k(scores, k: int) -> TopP:
     return TopP(selected=np.sort(order[:kk]), count=kk, order=order, prob=prob, cum=cum, scores=s)
 
 
+@dataclasses.dataclass
+class BlockTopP:
+    selected: np.ndarray     # ascending token positions of the kept blocks
+    count: int
+    blocks: np.ndarray       # kept block indices (ascending)
+    j_star: int              # crossing bin
+    block_max: np.ndarray    # m_b per block
+    block_mass: np.ndarray   # sum over the block of exp(s - max s)
+    pos: np.ndarray          # fractional bin coordinate of m_b: 256 (m_b - lo) / (hi - lo)
+    bins: np.ndarray         # bin of each block
+    lo: float
+    hi: float
+    Z: float
+
+
+def block_top_p(scores, p: float, block: int = 64, nbins: int = 256) -> BlockTopP:
+    """Block-granular top-p of the page's decode kernel (section "Hardware-Aware
+    Fast Top-p Decoding Kernel", steps 1-5 of the sort-free histogram).
+
+    1. positions are cut into blocks of ``block`` consecutive tokens (the last
+       one may be short);
+    2. each block keeps its maximum score m_b and its log-sum-exp; the mass it
+       carries is exp(logsumexp_b - M) = sum over the block of exp(s - M), with
+       M the row maximum (a common factor that cancels in the fractions);
+    3. the range [min m_b, max m_b] of the row is cut into ``nbins`` equal bins
+       and every block's mass goes to the bin of its m_b (the top value falls
+       in the last bin; a row whose blocks all share one m_b uses the last bin);
+    4. bins are scanned from the highest down, accumulating mass, to the first
+       bin where the cumulative fraction reaches p (p >= 1: every block);
+    5. every block in that bin or above is kept, whole.
+    Readings: the histogram sums block masses (the page calls the deposited
+    value the block's log-sum-exp; adding logs would not be a mass); the
+    crossing bin is kept whole, since a bin cannot be split without ordering
+    its blocks.
+    """
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.size
+    if n == 0:
+        raise ValueError("no candidates")
+    nb = -(-n // block)
+    M = s.max()
+    m = np.array([s[b * block:(b + 1) * block].max() for b in range(nb)])
+    mass = np.array([np.exp(s[b * block:(b + 1) * block] - M).sum() for b in range(nb)])
+    lo, hi = float(m.min()), float(m.max())
+    if hi > lo:
+        pos = (m - lo) / (hi - lo) * nbins
+        bins = np.minimum(np.floor(pos), nbins - 1).astype(np.int64)
+    else:
+        pos = np.full(nb, float(nbins))
+        bins = np.full(nb, nbins - 1, dtype=np.int64)
+    Z = float(mass.sum())
+    if p >= 1.0:
+        j_star = 0
+    else:
+        # the non-empty bins, highest first (empty bins add nothing to the scan)
+        occupied, inv = np.unique(bins, return_inverse=True)
+        hist = np.zeros(occupied.size)
+        np.add.at(hist, inv, mass)
+        cum = 0.0
+        j_star = int(occupied[0])
+        for j in range(occupied.size - 1, -1, -1):
+            cum += hist[j]
+            if cum >= p * Z:
+                j_star = int(occupied[j])
+                break
+    kept = np.nonzero(bins >= j_star)[0]
+    sel = np.concatenate([np.arange(b * block, min((b + 1) * block, n)) for b in kept])
+    return BlockTopP(selected=sel, count=int(sel.size), blocks=kept, j_star=j_star, block_max=m, block_mass=mass,
+                     pos=pos, bins=bins, lo=lo, hi=hi, Z=Z)
+
+
 def near_threshold(t: TopP, p: float, tol: float = 1e-5) -> np.ndarray:
     """Mask of candidates whose cumulative mass lies within ``tol`` of the threshold p."""
     return (t.cum >= p - tol) & (t.cum - t.prob <= p + tol)
@@ -242,17 +318,21 @@ class RowResult:
 
 
 def retrieval_row(q, q_pre, w_q, K, V, k_idx, pos: int, p: float, dtype: str,
-                  keys: Optional[np.ndarray] = None, k: Optional[int] = None) -> RowResult:
+                  keys: Optional[np.ndarray] = None, k: Optional[int] = None, blocks: bool = False) -> RowResult:
     """A retrieval head for one query: project, score the causal prefix, top-p, attend.
 
     ``k_idx`` holds the (already rounded) index keys of positions 0..pos.
     ``keys`` overrides the attended set (used to re-evaluate the output on a
     different valid set); the selection is still returned.  With ``k`` given
-    the set is the fixed top-k instead of top-p.
+    the set is the fixed top-k instead of top-p; with ``blocks`` it is the
+    page's block-granular top-p.
     """
     q_idx = project(q_pre, w_q, dtype)
     s = indexer_scores(q_idx, k_idx[: pos + 1])
-    t = top_p(s, p) if k is None else top_k(s, k)
+    if blocks:
+        t = block_top_p(s, p)
+    else:
+        t = top_p(s, p) if k is None else top_k(s, k)
     sel = t.selected if keys is None else np.asarray(keys, dtype=np.int64)
     return RowResult(attn=attend(q, K, V, sel), topp=t, q_idx=q_idx)
 

@@ -255,6 +255,85 @@ def test_topk_shift_and_permutation():
     assert sorted(perm[b].tolist()) == a.tolist()
 
 
+# ------------------------------------------------------------------ block top-p
+def check_block_worked_example():
+    # three full blocks with constant scores 0, 5, 1: block maxima 0, 5, 1 give
+    # bins 0, 255 (the top value) and floor(256 / 5) = 51; the block masses are
+    # 64 e^0, 64 e^5, 64 e^1, so block 1 alone holds e^5 / (1 + e + e^5) = 0.9756
+    # and blocks 1 + 2 hold (e^5 + e) / (1 + e + e^5) = 0.9934
+    s = np.concatenate([np.zeros(64), np.full(64, 5.0), np.ones(64)])
+    r = O.block_top_p(s, 0.9)
+    assert r.bins.tolist() == [0, 255, 51]
+    assert r.blocks.tolist() == [1] and r.selected.tolist() == list(range(64, 128))
+    r = O.block_top_p(s, 0.99)
+    assert r.blocks.tolist() == [1, 2] and r.j_star == 51 and r.count == 128
+    r = O.block_top_p(s, 0.995)
+    assert r.blocks.tolist() == [0, 1, 2] and r.j_star == 0
+    e = math.e
+    assert abs(r.block_mass[1] / r.Z - e ** 5 / (1 + e + e ** 5)) < 1e-12
+    # a block's mass is the sum over its tokens: one token at 3 and 63 at 0 carry
+    # e^3 + 63 = 83.1 against 64 e^2.9 = 1162.3 for a flat block at 2.9, so at
+    # p = 1/2 the top bin (block 0, 6.7 % of the mass) does not suffice
+    s2 = np.concatenate([[3.0], np.zeros(63), np.full(64, 2.9)])
+    r = O.block_top_p(s2, 0.5)
+    assert r.bins.tolist() == [255, 0] and r.blocks.tolist() == [0, 1]
+    assert abs(r.block_mass[0] / r.Z - (e ** 3 + 63) / (e ** 3 + 63 + 64 * e ** 2.9)) < 1e-12
+
+
+def check_block_reduces_to_token_exact(trials=40, seed=21):
+    # one-token blocks and bins far finer than the gaps between scores: the
+    # histogram scan walks the tokens in descending score order, i.e. Eq. 5
+    rng = np.random.default_rng(seed)
+    for _ in range(trials):
+        n = int(rng.integers(1, 400))
+        sc = rng.standard_normal(n) * rng.uniform(0.3, 3.0)
+        p = float(rng.uniform(0.05, 0.999))
+        b = O.block_top_p(sc, p, block=1, nbins=2 ** 40)
+        assert b.selected.tolist() == O.top_p(sc, p).selected.tolist(), (n, p)
+
+
+def test_block_topp_worked_example():
+    check_block_worked_example()
+
+
+def test_block_topp_reduces_to_token_exact():
+    check_block_reduces_to_token_exact()
+
+
+def test_block_topp_cut_is_the_highest_reaching_bin():
+    # brute force over every cut: the kept blocks are those at or above the
+    # highest bin whose upper-tail mass reaches p, whole blocks, the tail short
+    rng = np.random.default_rng(22)
+    for t in range(60):
+        n = int(rng.integers(1, 1500))
+        sc = rng.standard_normal(n) * rng.uniform(0.3, 3.0)
+        if t % 5 == 0:
+            sc = np.round(sc)
+        p = float(rng.choice([0.5, 0.8, 0.9, 0.95, rng.uniform(0.01, 0.999)]))
+        r = O.block_top_p(sc, p)
+        tail = [r.block_mass[r.bins >= j].sum() for j in range(257)]
+        reach = [j for j in range(256) if tail[j] >= p * r.Z]
+        assert r.j_star == max(reach)
+        assert r.blocks.tolist() == np.nonzero(r.bins >= r.j_star)[0].tolist()
+        expect = [x for bb in r.blocks for x in range(64 * bb, min(64 * bb + 64, n))]
+        assert r.selected.tolist() == expect
+        assert r.selected.size == r.count
+
+
+def test_block_topp_extremes():
+    rng = np.random.default_rng(23)
+    sc = rng.standard_normal(1000)
+    assert O.block_top_p(sc, 1.0).count == 1000
+    r = O.block_top_p(sc, 1e-9)
+    assert r.blocks.tolist() == np.nonzero(r.bins == 255)[0].tolist()
+    assert int(np.argmax(sc)) // 64 in r.blocks.tolist()
+    flat = np.concatenate([np.full(64, 2.0)] * 5 + [np.full(10, 2.0)])
+    assert O.block_top_p(flat, 0.3).count == flat.size      # one shared block max: every block
+    a = O.block_top_p(sc, 0.6).count
+    b = O.block_top_p(sc, 0.9).count
+    assert a <= b
+
+
 # ------------------------------------------------------------------ attention
 def _problem(L, Hq, Hkv, ret, window, n_sink, p, dtype="f32", seed=7, decode=False, B=1):
     rng = np.random.default_rng(seed)
@@ -434,3 +513,49 @@ def test_mutation_topk_off_by_one_caught(monkeypatch):
     monkeypatch.setattr(O, "top_k", lambda s, k: real(s, k + 1))
     with pytest.raises(AssertionError):
         check_topk_rank(trials=60)
+
+
+def test_mutation_block_scan_from_bottom_caught(monkeypatch):
+    # the scan walks the bins from the lowest up instead of from the highest down
+    real = O.block_top_p
+
+    def from_bottom(scores, p, block=64, nbins=256):
+        neg = -np.asarray(scores, dtype=np.float64)
+        r = real(neg, p, block, nbins)
+        return r
+    monkeypatch.setattr(O, "block_top_p", from_bottom)
+    with pytest.raises(AssertionError):
+        check_block_worked_example()
+
+
+def test_mutation_block_crossing_bin_dropped_caught(monkeypatch):
+    real = O.block_top_p
+
+    def drop_crossing(scores, p, block=64, nbins=256):
+        r = real(scores, p, block, nbins)
+        if p >= 1.0:
+            return r
+        keep = r.blocks[r.bins[r.blocks] > r.j_star]
+        n = np.asarray(scores).size
+        sel = np.concatenate([np.arange(b * block, min((b + 1) * block, n)) for b in keep]) if keep.size \
+            else np.zeros(0, dtype=np.int64)
+        return O.BlockTopP(sel, int(sel.size), keep, r.j_star, r.block_max, r.block_mass, r.pos, r.bins, r.lo, r.hi, r.Z)
+    monkeypatch.setattr(O, "block_top_p", drop_crossing)
+    with pytest.raises(AssertionError):
+        check_block_worked_example()
+
+
+def test_mutation_block_mass_from_max_caught(monkeypatch):
+    # a block's mass taken as its length times exp(its maximum) instead of the
+    # sum of its tokens' masses
+    real = O.block_top_p
+
+    def mass_from_max(scores, p, block=64, nbins=256):
+        sc = np.asarray(scores, dtype=np.float64)
+        flat = np.concatenate([np.full(min(block, sc.size - b), sc[b:b + block].max())
+                               for b in range(0, sc.size, block)])
+        r = real(flat, p, block, nbins)
+        return r
+    monkeypatch.setattr(O, "block_top_p", mass_from_max)
+    with pytest.raises(AssertionError):
+        check_block_worked_example()
