@@ -12,7 +12,8 @@ Inputs are seeded synthetic tensors resident in HBM before timing starts.
 Prints one JSON line: ``value`` is prefill tokens/s; the decode step time, the
 per-kernel times, the roofline of the dominant kernel and the CPU oracle
 baseline ride along in the same line, and so do the same steps with the fixed top-k
-selection (k = 4096, the pages' static-budget ablation) under ``topk_4096``.
+selection (k = 4096, the pages' static-budget ablation) under ``topk_4096`` and the
+decode step with the pages' block-granular top-p under ``topp_blocks64``.
 """
 from __future__ import annotations
 
@@ -222,8 +223,9 @@ def bench_prefill_references(args, torch, rtp, synth, pre):
     return dict(dense_ms=dense_ms, pages_ms=pages_ms, dense_tflops=dense_flop / (dense_ms * 1e-3) / 1e12)
 
 
-def bench_decode(args, torch, rtp, synth, inp=None, top_k=None):
-    """The decode step; with ``top_k`` (int32 [batch]) the selection is the fixed top-k."""
+def bench_decode(args, torch, rtp, synth, inp=None, top_k=None, blocks=False):
+    """The decode step; with ``top_k`` (int32 [batch]) the selection is the fixed top-k,
+    with ``blocks`` the pages' block-granular top-p."""
     cfg = synth.DECODE_32K
     dev = "cuda"
     if inp is None:
@@ -232,8 +234,8 @@ def bench_decode(args, torch, rtp, synth, inp=None, top_k=None):
     stream = torch.cuda.current_stream()
     k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w, stream=stream)   # cache built before timing
     sel = rtp.Selection.empty(prob, rtp.RTP_SEL_LIST, dev)
-    ws_sel = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SELECT, rtp.RTP_SEL_LIST), dtype=torch.uint8,
-                         device=dev)
+    ws_sel = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SELECT_BLOCKS if blocks else rtp.RTP_CALL_SELECT,
+                                                 rtp.RTP_SEL_LIST), dtype=torch.uint8, device=dev)
     ws_dec = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SPARSE_DECODE), dtype=torch.uint8, device=dev)
     ws_loc = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_LOCAL), dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp.q)
@@ -243,7 +245,9 @@ def bench_decode(args, torch, rtp, synth, inp=None, top_k=None):
 
     def step(t: Timer = None):
         calls = [
-            ("select_topp" if top_k is None else "select_topk",
+            ("select_topp_blocks" if blocks else "select_topp" if top_k is None else "select_topk",
+             (lambda: rtp.rtp_select_topp_blocks(prob, inp.q_pre, inp.w, k_idx, inp.top_p, sel, ws_sel,
+                                                 stream=stream)) if blocks else
              _select_call(rtp, prob, inp, k_idx, rtp.RTP_SEL_LIST, sel, ws_sel, stream, top_k)),
             ("sparse_attn_decode", lambda: rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse,
                                                                       ws_dec, stream=stream)),
@@ -443,6 +447,19 @@ def main():
                                     / (dk["ms"] * 1e-3),
                                     "mean_selected_fraction": dk["mean_frac_selected"]}
         line["topk_4096"] = var
+        if dec is not None:
+            print("[bench] decode 32K x 8, block top-p ...", file=sys.stderr, flush=True)
+            db = bench_decode(args, torch, rtp, synth, inp=dec["inp"], blocks=True)
+            line["topp_blocks64"] = {
+                "note": "the pages' block-granular top-p (64-token blocks, 256-bin histogram of block masses "
+                        "over block maxima) in place of the token-exact selection; same inputs and p",
+                "decode_32k_b8": {"step_us": db["ms"] * 1e3,
+                                  "per_kernel_us": {k: v * 1e3 for k, v in db["per_kernel_ms"].items()},
+                                  "algorithmic_bytes": db["total_bytes"],
+                                  "step_frac_of_hbm_roofline": db["total_bytes"] / (HBM_PEAK_GBS * 1e9)
+                                  / (db["ms"] * 1e-3),
+                                  "mean_selected_fraction": db["mean_frac_selected"],
+                                  "token_exact_mean_selected_fraction": dec["mean_frac_selected"]}}
     if pre is not None and not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(args, pre)

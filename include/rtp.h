@@ -71,7 +71,8 @@ typedef enum {
   RTP_CALL_SELECT = 1,
   RTP_CALL_SPARSE_PREFILL = 2,
   RTP_CALL_SPARSE_DECODE = 3,
-  RTP_CALL_LOCAL = 4
+  RTP_CALL_LOCAL = 4,
+  RTP_CALL_SELECT_BLOCKS = 5
 } rtp_call;
 
 #define RTP_MAX_HEADS 128
@@ -160,6 +161,28 @@ RTP_API rtp_status rtp_select_topp(const rtp_problem *prob, const void *q_pre, c
 RTP_API rtp_status rtp_select_topk(const rtp_problem *prob, const void *q_pre, const float *w_q,
                            const void *k_idx, const int32_t *top_k, rtp_sel_mode mode,
                            const rtp_selection *sel, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rtp_select_topp_blocks: the pages' own block-granular approximation of top-p
+ * for decode (section "Hardware-Aware Fast Top-p Decoding Kernel", the
+ * sort-free histogram, steps 1-5).  The same indexer scores as rtp_select_topp;
+ * then, per (retrieval head, sequence):
+ *   - keys are cut into 64-token blocks from position 0 (the last may be short);
+ *     block b keeps m_b = max score and its mass sum_{n in b} exp(s_n - max s);
+ *   - [min m_b, max m_b] is cut into 256 equal bins, each block's mass goes to
+ *     the bin of its m_b (all blocks in the top bin when every m_b is equal);
+ *   - bins are scanned from the top to the first where the cumulative mass
+ *     reaches top_p[b] of the total (p >= 1: every block);
+ *   - every block in that bin or above is kept whole.
+ * Output is LIST only (requires max_seqlen_q == 1, else RTP_ERR_UNSUPPORTED):
+ * sel->idx holds the kept blocks' positions ascending, sel->count their number;
+ * sel->tau (optional) the lower edge of the crossing bin in score units (-inf
+ * when every block is kept), sel->tie_pos (optional) INT32_MAX.  sel->q_idx is
+ * written.  ws: rtp_workspace_size(prob, RTP_CALL_SELECT_BLOCKS, RTP_SEL_LIST).
+ */
+RTP_API rtp_status rtp_select_topp_blocks(const rtp_problem *prob, const void *q_pre, const float *w_q,
+                                  const void *k_idx, const float *top_p, const rtp_selection *sel,
+                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
  * rtp_sparse_attn_prefill: exact attention of every retrieval-head query over its

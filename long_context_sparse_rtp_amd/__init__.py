@@ -15,13 +15,13 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import (RTP_BF16, RTP_CALL_LOCAL, RTP_CALL_SELECT, RTP_CALL_SPARSE_DECODE,
+from ._lib import (RTP_BF16, RTP_CALL_LOCAL, RTP_CALL_SELECT, RTP_CALL_SELECT_BLOCKS, RTP_CALL_SPARSE_DECODE,
                    RTP_CALL_SPARSE_PREFILL, RTP_F32, RTP_SEL_LIST, RTP_SEL_THRESHOLD)
 
-__all__ = ["Problem", "Selection", "rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_select_topk",
+__all__ = ["Problem", "Selection", "rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
            "rtp_sparse_attn_prefill", "rtp_sparse_attn_decode", "rtp_local_attn", "RtpError",
            "RTP_SEL_LIST", "RTP_SEL_THRESHOLD", "RTP_CALL_SELECT", "RTP_CALL_SPARSE_PREFILL",
-           "RTP_CALL_SPARSE_DECODE", "RTP_CALL_LOCAL", "library"]
+           "RTP_CALL_SPARSE_DECODE", "RTP_CALL_LOCAL", "RTP_CALL_SELECT_BLOCKS", "library"]
 
 
 class RtpError(RuntimeError):
@@ -186,6 +186,21 @@ def rtp_select_topk(prob: Problem, q_pre: torch.Tensor, w_q: torch.Tensor, k_idx
     st = _lib.load().rtp_select_topk(prob.ref, _ptr(q_pre), _ptr(w_q), _ptr(k_idx), _ptr(top_k), mode,
                                      ctypes.byref(cs), _ptr(ws), nws, _stream(stream))
     _check(st, "rtp_select_topk")
+    sel._ws = ws
+    return sel
+
+
+def rtp_select_topp_blocks(prob: Problem, q_pre: torch.Tensor, w_q: torch.Tensor, k_idx: torch.Tensor,
+                           top_p: torch.Tensor, sel: Optional[Selection] = None,
+                           ws: Optional[torch.Tensor] = None, stream=None) -> Selection:
+    """The pages' block-granular top-p (decode, LIST output)."""
+    if sel is None:
+        sel = Selection.empty(prob, RTP_SEL_LIST, q_pre.device)
+    ws, nws = _workspace(prob, RTP_CALL_SELECT_BLOCKS, RTP_SEL_LIST, ws, q_pre.device)
+    cs = sel.c()
+    st = _lib.load().rtp_select_topp_blocks(prob.ref, _ptr(q_pre), _ptr(w_q), _ptr(k_idx), _ptr(top_p),
+                                            ctypes.byref(cs), _ptr(ws), nws, _stream(stream))
+    _check(st, "rtp_select_topp_blocks")
     sel._ws = ws
     return sel
 

@@ -10,9 +10,10 @@ LIB_PATH = os.path.join(PKG, "librtp.so")
 RTP_OK, RTP_ERR_INVALID_ARG, RTP_ERR_UNSUPPORTED, RTP_ERR_WORKSPACE_TOO_SMALL, RTP_ERR_HIP = range(5)
 RTP_F32, RTP_BF16 = 0, 1
 RTP_SEL_LIST, RTP_SEL_THRESHOLD = 0, 1
-RTP_CALL_SELECT, RTP_CALL_SPARSE_PREFILL, RTP_CALL_SPARSE_DECODE, RTP_CALL_LOCAL = 1, 2, 3, 4
+RTP_CALL_SELECT, RTP_CALL_SPARSE_PREFILL, RTP_CALL_SPARSE_DECODE, RTP_CALL_LOCAL, RTP_CALL_SELECT_BLOCKS = 1, 2, 3, 4, 5
 
-EXPORTED = ("rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_select_topk", "rtp_sparse_attn_prefill",
+EXPORTED = ("rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
+            "rtp_sparse_attn_prefill",
             "rtp_sparse_attn_decode", "rtp_local_attn", "rtp_status_str", "rtp_last_hip_error")
 
 
@@ -69,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtp_select_topp.restype = i32
     lib.rtp_select_topk.argtypes = [P, vp, vp, vp, vp, i32, S, vp, sz, vp]
     lib.rtp_select_topk.restype = i32
+    lib.rtp_select_topp_blocks.argtypes = [P, vp, vp, vp, vp, S, vp, sz, vp]
+    lib.rtp_select_topp_blocks.restype = i32
     lib.rtp_sparse_attn_prefill.argtypes = [P, vp, vp, vp, vp, S, vp, vp, vp, sz, vp]
     lib.rtp_sparse_attn_prefill.restype = i32
     lib.rtp_sparse_attn_decode.argtypes = [P, vp, vp, vp, S, vp, vp, vp, sz, vp]

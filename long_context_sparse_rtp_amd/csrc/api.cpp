@@ -100,6 +100,8 @@ size_t ws_need(const ProbDev& p, rtp_call call, rtp_sel_mode mode) {
       return rtp::ws_attn_decode(p, 0);
     case RTP_CALL_LOCAL:
       return p.max_q == 1 ? rtp::ws_attn_decode(p, 1) : 0;
+    case RTP_CALL_SELECT_BLOCKS:
+      return rtp::ws_select_blocks(p);
   }
   return 0;
 }
@@ -171,6 +173,25 @@ rtp_status rtp_select_topk(const rtp_problem* prob, const void* q_pre, const flo
                            const int32_t* top_k, rtp_sel_mode mode, const rtp_selection* sel, void* ws,
                            size_t ws_bytes, void* stream) {
   return select_common(prob, q_pre, w_q, k_idx, nullptr, top_k, mode, sel, ws, ws_bytes, stream);
+}
+
+rtp_status rtp_select_topp_blocks(const rtp_problem* prob, const void* q_pre, const float* w_q, const void* k_idx,
+                                  const float* top_p, const rtp_selection* sel, void* ws, size_t ws_bytes,
+                                  void* stream) {
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  if (p.R == 0) return RTP_OK;
+  if (!sel || !aligned16(q_pre) || !aligned16(w_q) || !aligned16(k_idx) || !aligned4(top_p))
+    return RTP_ERR_INVALID_ARG;
+  if (!aligned16(sel->q_idx) || !aligned4(sel->count) || !aligned4(sel->idx)) return RTP_ERR_INVALID_ARG;
+  if ((sel->tau && !aligned4(sel->tau)) || (sel->tie_pos && !aligned4(sel->tie_pos))) return RTP_ERR_INVALID_ARG;
+  if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
+  if (p.max_k > rtp::select_decode_max_keys()) return RTP_ERR_UNSUPPORTED;
+  st = check_ws(p, RTP_CALL_SELECT_BLOCKS, RTP_SEL_LIST, ws, ws_bytes);
+  if (st != RTP_OK) return st;
+  return finish(rtp::launch_select_blocks(p, prob->dtype == RTP_BF16, q_pre, w_q, k_idx, top_p, *sel, ws,
+                                          (hipStream_t)stream));
 }
 
 rtp_status rtp_sparse_attn_prefill(const rtp_problem* prob, const void* q, const void* k, const void* v,

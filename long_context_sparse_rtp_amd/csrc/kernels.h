@@ -43,6 +43,11 @@ hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, 
 hipError_t launch_select_prefill(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
                                  const void* k_idx, const float* top_p, const int32_t* top_k,
                                  const rtp_selection& sel, void* ws, hipStream_t s);
+// the pages' block-granular top-p (decode, LIST output)
+size_t ws_select_blocks(const ProbDev& p);
+hipError_t launch_select_blocks(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
+                                const void* k_idx, const float* top_p, const rtp_selection& sel, void* ws,
+                                hipStream_t s);
 // mode 0: retrieval heads over sel LIST; mode 1: local heads over window + sinks
 hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
                               const void* v, const rtp_selection* sel, void* out, float* lse,

@@ -271,6 +271,30 @@ __device__ __forceinline__ void load8(const float* p, float* x) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
+// The rounded indexer query of a decode row: 16 threads per output dim, 8
+// products each in float64, combined by a fixed shuffle tree and rounded once.
+// Needs all 256 threads; q_s gets the 16 values (visible after a barrier),
+// q_out (if not null) too.
+template <typename T>
+__device__ __forceinline__ void project_query(const ProbDev& p, const RowGeom& g, const T* __restrict__ q_pre,
+                                              const float* __restrict__ w_q, T* q_s, T* q_out) {
+  const int tid = threadIdx.x;
+  const int dim = tid >> 4, part = tid & 15;
+  float x[8], wv[8];
+  load8(q_pre + ((size_t)g.qrow * p.R + g.r) * kHeadDim + part * 8, x);
+  load8(w_q + ((size_t)g.r * kIdxDim + dim) * kHeadDim + part * 8, wv);
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = fma((double)x[i], (double)wv[i], acc);
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+  if (part == 0) {
+    const T qv = Elem<T>::from_d(acc);
+    q_s[dim] = qv;
+    if (q_out) q_out[dim] = qv;
+  }
+}
+
 // ======================================================================= 1. score
 template <typename T>
 __global__ __launch_bounds__(kThreads) void sel_dec_score(ProbDev p, const T* __restrict__ q_pre,
@@ -304,24 +328,8 @@ __global__ __launch_bounds__(kThreads) void sel_dec_score(ProbDev p, const T* __
   };
   if (g.L > 0) load_batch(0);
 
-  // ---- the rounded indexer query: 16 threads per output dim, 8 products each in
-  // float64, combined by a fixed shuffle tree and rounded once
-  {
-    const int dim = tid >> 4, part = tid & 15;
-    float x[8], wv[8];
-    load8(q_pre + ((size_t)g.qrow * p.R + g.r) * kHeadDim + part * 8, x);
-    load8(w_q + ((size_t)g.r * kIdxDim + dim) * kHeadDim + part * 8, wv);
-    double acc = 0.0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fma((double)x[i], (double)wv[i], acc);
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
-    if (part == 0) {
-      const T qv = Elem<T>::from_d(acc);
-      q_s[dim] = qv;
-      if (c == 0) ((T*)sel.q_idx)[((size_t)g.r * p.Tq + g.qrow) * kIdxDim + dim] = qv;
-    }
-  }
+  // ---- the rounded indexer query
+  project_query<T>(p, g, q_pre, w_q, q_s, c == 0 ? (T*)sel.q_idx + ((size_t)g.r * p.Tq + g.qrow) * kIdxDim : nullptr);
   for (int e = tid; e < kNB; e += kThreads) hist_s[e] = 0ull;
   __syncthreads();
   float q[kIdxDim];
@@ -904,6 +912,151 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
     if ((fl & (1u << j)) && o < (uint32_t)g.L) out[o++] = nb + j;
 }
 
+// ======================================================================= block top-p
+// The pages' own decode selection ("Hardware-Aware Fast Top-p Decoding
+// Kernel", steps 1-5): 64-token blocks reduced to (max score m_b, block mass),
+// block masses binned by m_b over 256 equal bins of the row's [min m_b,
+// max m_b], bins scanned from the top to the first where the cumulative
+// fraction reaches p, every block in that bin or above kept whole.  The
+// selection is written as a LIST of the kept blocks' positions, so the decode
+// attention consumes it unchanged.  Two kernels: block statistics with one
+// workgroup per unit of 4096 keys (the pages use one CTA per block; a wave
+// per block keeps the whole device busy with 256-thread workgroups), then one
+// workgroup per row for the histogram, the scan and the list.
+constexpr int kBlk = 64;
+constexpr int kBlkBins = 256;
+
+// Block statistics of sequence b, slot r start here: room for ceil(L_b / 64) blocks.
+__host__ __device__ inline int64_t blk_slots_per_r(const ProbDev& p) { return p.Tk / kBlk + p.batch + 1; }
+__device__ __forceinline__ int64_t blk_slot0(const ProbDev& p, const RowGeom& g) {
+  return (int64_t)g.r * blk_slots_per_r(p) + g.k0 / kBlk + g.b;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void sel_blk_score(ProbDev p, const T* __restrict__ q_pre,
+                                                          const float* __restrict__ w_q,
+                                                          const T* __restrict__ k_idx, rtp_selection sel,
+                                                          float2* __restrict__ bstat) {
+  const RowGeom g = row_geom(p, blockIdx.y);
+  const int c = blockIdx.x;
+  if (c >= g.U || g.U > kMaxUnits || g.L == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ T q_s[kIdxDim];
+
+  // keys n = c*kChunk + tid + 256 j: wave w of step j holds block c*64 + 4 j + w
+  const T* kb = k_idx + ((size_t)g.r * p.Tk + g.k0) * kIdxDim;
+  const int n0 = c * kChunk + tid;
+  KeyRaw<T> raw[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) raw[j].load(kb + (size_t)min(n0 + j * kThreads, g.L - 1) * kIdxDim);
+  project_query<T>(p, g, q_pre, w_q, q_s, c == 0 ? (T*)sel.q_idx + ((size_t)g.r * p.Tq + g.qrow) * kIdxDim : nullptr);
+  __syncthreads();
+  float q[kIdxDim];
+#pragma unroll
+  for (int d = 0; d < kIdxDim; ++d) q[d] = Elem<T>::to_f(q_s[d]);
+
+  float2* bs = bstat + blk_slot0(p, g);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    const bool valid = n < g.L;
+    const float sc = valid ? idx_score(raw[j].dot(q)) : -INFINITY;
+    const float m = wave_max(sc);
+    const float e = valid ? __builtin_amdgcn_exp2f((sc - m) * kLog2e) : 0.f;
+    const float l = wave_sum(e);
+    const int blk = c * (kChunk / kBlk) + 4 * j + w;
+    if (lane == 0 && blk * kBlk < g.L) bs[blk] = make_float2(m, l);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void sel_blk_choose(ProbDev p, const float* __restrict__ top_p,
+                                                           rtp_selection sel, const float2* __restrict__ bstat) {
+  const RowGeom g = row_geom(p, blockIdx.x);
+  const int tid = threadIdx.x;
+  const size_t qo = (size_t)g.r * p.Tq + g.qrow;
+  if (g.L == 0) {
+    if (tid == 0) {
+      sel.count[qo] = 0;
+      if (sel.tau) sel.tau[qo] = INFINITY;
+      if (sel.tie_pos) sel.tie_pos[qo] = 0x7FFFFFFF;
+    }
+    return;
+  }
+  __shared__ unsigned long long hist_s[kBlkBins];
+  __shared__ unsigned long long red_u[kThreads / 64];
+  __shared__ int red_i[kThreads / 64];
+  __shared__ uint32_t utmp[kThreads / 64];
+  __shared__ uint32_t offs_s[kThreads];
+  __shared__ int jstar_s;
+  const int nb = (g.L + kBlk - 1) / kBlk;
+  const float2* bs = bstat + blk_slot0(p, g);
+
+  // ---- range of the block maxima (order-preserving integer images of the floats)
+  auto ord = [](float f) { const int i = __float_as_int(f); return i ^ ((i >> 31) & 0x7FFFFFFF); };
+  auto unord = [](int i) { return __int_as_float(i ^ ((i >> 31) & 0x7FFFFFFF)); };
+  float hi = -INFINITY, nlo = -INFINITY;
+  for (int i = tid; i < nb; i += kThreads) {
+    const float m = bs[i].x;
+    hi = fmaxf(hi, m);
+    nlo = fmaxf(nlo, -m);
+  }
+  hi = unord(block_max<int>(ord(hi), red_i));
+  const float lo = -unord(block_max<int>(ord(nlo), red_i));
+  const bool spread = hi > lo;
+  const float scale = spread ? (float)kBlkBins / (hi - lo) : 0.f;
+  auto bin_of = [&](float m) { return spread ? min(kBlkBins - 1, (int)((m - lo) * scale)) : kBlkBins - 1; };
+
+  // ---- block masses relative to the row maximum, 2^32 fixed point (a block holds at most 2^38)
+  for (int e = tid; e < kBlkBins; e += kThreads) hist_s[e] = 0ull;
+  __syncthreads();
+  for (int i = tid; i < nb; i += kThreads) {
+    const float2 v = bs[i];
+    const float mf = v.y * __builtin_amdgcn_exp2f((v.x - hi) * kLog2e) * 4294967296.f;
+    atomicAdd(&hist_s[bin_of(v.x)], (unsigned long long)mf);
+  }
+  __syncthreads();
+
+  // ---- the crossing bin: thread t holds bin 255 - t, so the exclusive scan is the mass above it
+  const float pp = top_p[g.b];
+  const bool all = !(pp < 1.f);
+  if (tid == 0) jstar_s = 0;
+  const unsigned long long h = hist_s[kBlkBins - 1 - tid];
+  unsigned long long tot;
+  const unsigned long long pre = block_exscan<unsigned long long>(h, red_u, tot);
+  if (!all) {
+    const unsigned long long tgt = (unsigned long long)ceil((double)pp * (double)tot);
+    const unsigned long long need = tgt > 0ull ? tgt : 1ull;
+    if (pre < need && need <= pre + h) jstar_s = kBlkBins - 1 - tid;
+  }
+  __syncthreads();
+  const int jstar = jstar_s;
+
+  // ---- the kept blocks' positions, ascending: 256 blocks at a time, one per thread
+  int* out = sel.idx + (size_t)g.r * p.Tk + g.k0;
+  uint32_t base = 0u;
+  for (int c0 = 0; c0 < nb; c0 += kThreads) {
+    const int i = c0 + tid;
+    const bool keep = i < nb && bin_of(bs[i].x) >= jstar;
+    const uint32_t len = keep ? (uint32_t)min(kBlk, g.L - i * kBlk) : 0u;
+    uint32_t ctot;
+    const uint32_t off = block_exscan<uint32_t>(len, utmp, ctot);
+    offs_s[tid] = keep ? base + off : 0xFFFFFFFFu;
+    __syncthreads();
+    for (int e = tid; e < kThreads * kBlk; e += kThreads) {
+      const uint32_t o = offs_s[e / kBlk];
+      const int n = (c0 + e / kBlk) * kBlk + (e % kBlk);
+      if (o != 0xFFFFFFFFu && n < g.L) out[o + (e % kBlk)] = n;
+    }
+    base += ctot;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    sel.count[qo] = (int)base;
+    if (sel.tau) sel.tau[qo] = all ? -INFINITY : (spread ? lo + (float)jstar / scale : lo);
+    if (sel.tie_pos) sel.tie_pos[qo] = 0x7FFFFFFF;
+  }
+}
+
 }  // namespace
 
 size_t ws_select_decode(const ProbDev& p) { return ws_layout(p, nullptr, nullptr); }
@@ -928,5 +1081,24 @@ hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, 
 }
 
 int select_decode_max_keys() { return kMaxUnits * kChunk; }
+
+size_t ws_select_blocks(const ProbDev& p) { return align256(sizeof(float2) * (size_t)p.R * blk_slots_per_r(p)); }
+
+hipError_t launch_select_blocks(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
+                                const void* k_idx, const float* top_p, const rtp_selection& sel, void* ws,
+                                hipStream_t s) {
+  if (p.R == 0) return hipSuccess;
+  const int nrows = p.R * p.batch;
+  float2* bstat = (float2*)ws;
+  dim3 grid(max(1, max_units(p)), nrows);
+  if (bf16)
+    hipLaunchKernelGGL(sel_blk_score<bf16_t>, grid, dim3(kThreads), 0, s, p, (const bf16_t*)q_pre, w_q,
+                       (const bf16_t*)k_idx, sel, bstat);
+  else
+    hipLaunchKernelGGL(sel_blk_score<float>, grid, dim3(kThreads), 0, s, p, (const float*)q_pre, w_q,
+                       (const float*)k_idx, sel, bstat);
+  hipLaunchKernelGGL(sel_blk_choose, dim3(nrows), dim3(kThreads), 0, s, p, top_p, sel, (const float2*)bstat);
+  return hipGetLastError();
+}
 
 }  // namespace rtp

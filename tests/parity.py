@@ -234,6 +234,79 @@ def check_list_row(pr: Problem, b: int, h: int, g: Dict[str, np.ndarray], tol: f
     return ok, dict(err=err, lerr=lerr, ndiff=ndiff, count=count)
 
 
+def run_decode_blocks(inp, k_idx: torch.Tensor) -> Dict[str, torch.Tensor]:
+    """Decode path with the pages' block-granular top-p: block LIST select -> sparse decode + local decode."""
+    import long_context_sparse_rtp_amd as rtp
+    prob = rtp.Problem.from_inputs(inp)
+    sel = rtp.rtp_select_topp_blocks(prob, inp.q_pre, inp.w, k_idx, inp.top_p)
+    out = torch.full_like(inp.q, float("nan"))
+    lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=inp.q.device)
+    rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse)
+    rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse)
+    sync()
+    return dict(q_idx=sel.q_idx, idx=sel.idx, count=sel.count, tau=sel.tau, tie=sel.tie_pos, out=out, lse=lse)
+
+
+def block_set_ok(bt: O.BlockTopP, p: float, got_blocks: np.ndarray, eps_max: float, tol: float = 1e-5):
+    """Is ``got_blocks`` a valid block top-p set?  The kernel bins float32 block maxima
+    in float32, so a block whose oracle bin coordinate lies within the scoring error of
+    a bin edge may land on either side; the kept mass must reach p (within tol) and the
+    blocks surely above the cut must not.  Returns (ok, n_blocks_differing)."""
+    nb = bt.block_max.size
+    gm = np.zeros(nb, dtype=bool)
+    gm[got_blocks] = True
+    sm = np.zeros(nb, dtype=bool)
+    sm[bt.blocks] = True
+    ndiff = int((gm ^ sm).sum())
+    if p >= 1.0:
+        return bool(gm.all()), ndiff
+    if ndiff == 0:
+        return True, 0
+    span = bt.hi - bt.lo
+    delta = (256.0 * 4.0 * eps_max / span if span > 0 else 0.0) + 1e-3
+    mass = bt.block_mass
+    if mass[gm].sum() < (p - tol) * bt.Z:
+        return False, ndiff
+    for j in range(256):
+        certain = bt.pos - delta >= j
+        possible = bt.pos + delta >= j
+        if np.any(certain & ~gm) or np.any(gm & ~possible):
+            continue
+        above = bt.pos - delta >= j + 1
+        if mass[above].sum() < (p + tol) * bt.Z:
+            return True, ndiff
+    return False, ndiff
+
+
+def check_block_list_row(pr: Problem, b: int, h: int, g: Dict[str, np.ndarray], tol: float):
+    """Compare one retrieval-head decode row under the block-granular top-p."""
+    r = pr.slot_of(h)
+    qi = int(pr.cu_q[b])
+    res = pr.row(b, 0, h)
+    if not np.array_equal(g["q_idx"][r, qi], res.q_idx):
+        return False, {"why": "q_idx mismatch"}
+    k0, k1 = pr.seq_range_k(b)
+    L = k1 - k0
+    count = int(g["count"][r, qi])
+    G = g["idx"][r, k0:k0 + count].astype(np.int64)
+    if count < 1 or np.any(np.diff(G) <= 0) or G.min() < 0 or G.max() >= L:
+        return False, {"why": "list not ascending / out of range", "count": count}
+    blocks = np.unique(G // 64)
+    whole = np.concatenate([np.arange(64 * bb, min(64 * bb + 64, L)) for bb in blocks])
+    if not np.array_equal(whole, G):
+        return False, {"why": "list is not a union of whole 64-token blocks", "count": count}
+    bt = res.topp
+    eps = _amb_eps(res.q_idx, pr.index_keys(b, r))
+    ok_set, ndiff = block_set_ok(bt, float(pr.top_p[b]), blocks, float(eps.max()))
+    if not ok_set:
+        return False, {"why": "block set invalid", "count": count, "oracle_count": bt.count, "ndiff": ndiff}
+    a = O.attend(pr.q_row(qi, h), pr._kv("k", b, pr.kv_of(h)), pr._kv("v", b, pr.kv_of(h)), G)
+    err = float(np.max(np.abs(g["out"][qi, h] - a.out)))
+    lerr = abs(float(g["lse"][h, qi]) - a.lse)
+    ok = err <= tol and lerr <= max(tol, 1e-4)
+    return ok, dict(err=err, lerr=lerr, ndiff=ndiff, count=count)
+
+
 def check_local_row(pr: Problem, b: int, i: int, h: int, g: Dict[str, np.ndarray], tol: float):
     qi = int(pr.cu_q[b]) + i
     a = pr.row(b, i, h).attn
@@ -276,6 +349,8 @@ _SHARED = {}
 def _check_task(args):
     pr, g, (b, i, h), tol, decode = args
     if pr.slot_of(h) >= 0:
+        if decode and pr.blocks:
+            return check_block_list_row(pr, b, h, g, tol)
         if decode:
             return check_list_row(pr, b, h, g, tol)
         return check_retrieval_row(pr, b, i, h, g, tol)
