@@ -14,10 +14,12 @@
 //   - a row is (retrieval slot, sequence), or (tile of local heads of one KV
 //     group, sequence); tiles hold one head at present: holding several lets
 //     a K/V row feed all of them, but costs more in cross-lane reductions;
-//   - every row's key set is cut into splits of 512 entries; the splits of all
-//     rows form one flat work list (prefix sums of the per-row split counts,
-//     computed by every workgroup) that a fixed grid walks round-robin, so
-//     ragged rows and sparse sets leave no idle workgroups;
+//   - every row's key set is cut into equal splits of at most 512 entries,
+//     sized from the total entry count so that the splits of all rows fill the
+//     resident grid about once (a fixed 512 left the last round of workgroups
+//     half empty); the splits form one flat work list (prefix sums of the
+//     per-row split counts, computed by every workgroup) that the grid walks
+//     round-robin, so ragged rows and sparse sets leave no idle workgroups;
 //   - a split's key positions are staged in LDS with one coalesced read, so
 //     the K/V gathers never wait on the list;
 //   - 16 lanes share a token, each lane holding 8 of the 128 dims, so one K
@@ -35,9 +37,8 @@ namespace rtp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSplit = 512;              // entries per split (retrieval rows)
-constexpr int kSplitTile = 512;          // entries per split (local-head rows)
-__host__ __device__ constexpr int split_of(int mode) { return mode == 0 ? kSplit : kSplitTile; }
+constexpr int kSplit = 512;              // most entries per split
+constexpr int kMinSplit = 64;            // fewest entries per split (unless a row holds fewer)
 constexpr int kGroups = kThreads / 16;   // 16-lane groups per workgroup
 constexpr int kUnroll = 4;               // tokens per group per batch
 constexpr int kStep = kGroups * kUnroll; // tokens per workgroup per batch
@@ -85,6 +86,13 @@ __device__ __forceinline__ int local_token(const ProbDev& p, int L, int j) {
   return (j < ns) ? j : (L - W + (j - ns));
 }
 
+// A row of `count` entries is cut into nsplit equal splits of at most `target` entries.
+__device__ __forceinline__ int nsplit_of(int count, int target) { return (count + target - 1) / target; }
+__device__ __forceinline__ int split_size(int count, int target) {
+  const int ns = nsplit_of(count, target);
+  return ns > 0 ? (count + ns - 1) / ns : 0;
+}
+
 template <typename T> struct RowVec;  // 8 elements of a row
 template <> struct RowVec<bf16_t> {
   uint4 raw;
@@ -114,23 +122,40 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
   extern __shared__ int pre_s[];   // [rows + 1], sized at launch
   __shared__ int idx_s[kSplit];
   __shared__ int wsum_s[kThreads / 64];
+  __shared__ int target_s;
   __shared__ float gm_s[kGroups], gl_s[kGroups];
   __shared__ float go_s[kGroups][kHeadDim];
   const int tid = threadIdx.x;
   // split prefix over the rows (every workgroup computes it; block 0 publishes it
-  // for the combine kernel): pre[r] = sum of ceil(count / split) over rows before r.
+  // for the combine kernel): pre[r] = sum of nsplit(count) over rows before r.
   // Rows are dealt to threads round-robin so all their counts load at once.
   {
     constexpr int PR = kMaxRowsLds / kThreads;
     const int nchunks = rows / kThreads + 1;   // chunks holding rows 0..rows
+    const int lane = tid & 63, wid = tid >> 6;
     int vv[PR];
+    long long tot_entries = 0;
 #pragma unroll
     for (int t = 0; t < PR; ++t) {
       const int r = t * kThreads + tid;
       vv[t] = 0;
-      if (r < rows) vv[t] = (row_info(p, mode, r, sel).count + split_of(mode) - 1) / split_of(mode);
+      if (r < rows) vv[t] = row_info(p, mode, r, sel).count;
+      tot_entries += vv[t];
     }
-    const int lane = tid & 63, wid = tid >> 6;
+    // target split size: the entries spread over the grid once, within [kMinSplit, kSplit]
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) tot_entries += __shfl_xor(tot_entries, o);
+    if (lane == 0) wsum_s[wid] = (int)min(tot_entries, (long long)0x7FFFFFFF);
+    __syncthreads();
+    if (tid == 0) {
+      long long te = 0;
+      for (int w2 = 0; w2 < kThreads / 64; ++w2) te += wsum_s[w2];
+      target_s = (int)min((long long)kSplit, max((long long)kMinSplit, (te + gridDim.x - 1) / gridDim.x));
+    }
+    __syncthreads();
+    const int target = target_s;
+#pragma unroll
+    for (int t = 0; t < PR; ++t) vv[t] = nsplit_of(vv[t], target);
     int carry = 0;
 #pragma unroll
     for (int t = 0; t < PR; ++t) {
@@ -157,6 +182,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
       for (int r = tid; r <= rows; r += kThreads) pre[r] = pre_s[r];
   }
   const int total = pre_s[rows];
+  const int target = target_s;
   const int grp = tid >> 4, gl = tid & 15;
   const int d0 = gl * 8;
   const size_t kstride = (size_t)p.Hkv * kHeadDim;
@@ -173,8 +199,9 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
     const int split = wi - pre_s[row];
     const RowInfo ri = row_info(p, mode, row, sel);
     const int nh = min(ri.nh, H);
-    const int j0 = split * split_of(mode);
-    const int j1 = min(ri.count, j0 + split_of(mode));
+    const int sz = split_size(ri.count, target);
+    const int j0 = split * sz;
+    const int j1 = min(ri.count, j0 + sz);
     const T* kb = k + ((size_t)ri.k0 * p.Hkv + ri.g) * kHeadDim + d0;
     const T* vb = v + ((size_t)ri.k0 * p.Hkv + ri.g) * kHeadDim + d0;
     // the split's key positions, staged once (coalesced)
@@ -286,7 +313,7 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int m
                                                                 T* __restrict__ out, float* __restrict__ lse) {
   constexpr int kMaxS = 256;
   __shared__ float wgt_s[kMaxS];
-  __shared__ float red_s[2];
+  __shared__ float red_s[2], red2_s[2];
   __shared__ float sum_s;
   const int row = blockIdx.x / H, h = blockIdx.x % H;
   const int tid = threadIdx.x;
@@ -311,13 +338,17 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int m
     acc *= scale;
     sum *= scale;
     M = Mn;
-    for (int s = tid; s < cn; s += kHeadDim) wgt_s[s] = __builtin_amdgcn_exp2f(rec_of(c0 + s)[0] - M);
-    __syncthreads();
-    if (tid == 0) {
-      float sl = 0.f;
-      for (int s = 0; s < cn; ++s) sl = fmaf(rec_of(c0 + s)[1], wgt_s[s], sl);
-      sum_s = sl;
+    float sl = 0.f;
+    for (int s = tid; s < cn; s += kHeadDim) {
+      const float* r = rec_of(c0 + s);
+      const float wv = __builtin_amdgcn_exp2f(r[0] - M);
+      wgt_s[s] = wv;
+      sl = fmaf(r[1], wv, sl);
     }
+    sl = wave_sum(sl);
+    if ((tid & 63) == 0) red2_s[tid >> 6] = sl;
+    __syncthreads();
+    if (tid == 0) sum_s = red2_s[0] + red2_s[1];
     int s = 0;
     for (; s + 8 <= cn; s += 8) {
       float v8[8];
@@ -340,15 +371,30 @@ __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size
 inline int rows_of(const ProbDev& p, int mode) { return ((mode == 0) ? p.R : p.n_ltiles) * p.batch; }
 inline int heads_per_row(int mode) { return (mode == 0) ? 1 : kMaxTileHeads; }
 
-// upper bound on the number of splits (every row's set holds at most L_b entries)
+// Resident workgroups of one launch (the grid), from the device's CU count.
+inline int resident_grid() {
+  int n_cu = 256, dev = 0, cu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
+    n_cu = cu;
+  return n_cu * kWgPerCu;
+}
+
+// Upper bound on the number of splits.  While the target is ceil(total / grid)
+// (or is raised to kMinSplit), sum_r ceil(count_r / target) <= total / target +
+// rows <= grid + rows.  When it is capped at kSplit, a row has ceil(count /
+// kSplit) splits, bounded through count <= L_b.
 inline size_t max_work(const ProbDev& p, int mode, int rows) {
+  size_t capped;
   if (mode == 1) {
     const int cnt = min(p.window, p.max_k) + p.n_sink;
-    return (size_t)rows * ((cnt + kSplitTile - 1) / kSplitTile);
+    capped = (size_t)rows * ((cnt + kSplit - 1) / kSplit);
+  } else {
+    const size_t per_row = (size_t)(p.max_k + kSplit - 1) / kSplit;
+    const size_t by_total = (size_t)((p.Tk + kSplit - 1) / kSplit) + (size_t)p.batch;  // sum over sequences
+    capped = (size_t)(rows / max(1, p.batch)) * min(per_row * p.batch, by_total);
   }
-  const size_t per_row = (size_t)(p.max_k + kSplit - 1) / kSplit;
-  const size_t by_total = (size_t)((p.Tk + kSplit - 1) / kSplit) + (size_t)p.batch;  // sum over sequences
-  return (size_t)(rows / max(1, p.batch)) * min(per_row * p.batch, by_total);
+  return max(capped, (size_t)resident_grid() + (size_t)rows);
 }
 
 }  // namespace
@@ -371,14 +417,9 @@ hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void*
   if (sel) sl = *sel;
   int* pre = (int*)ws;
   float* part = (float*)((char*)ws + align256(sizeof(int) * (size_t)(rows + 1)));
-  const size_t mw = max_work(p, mode, rows);
-  // a resident grid: every workgroup walks several work items, so the row prefix is
+  // a resident grid: every workgroup walks its work items, so the row prefix is
   // computed once per workgroup and no launch round waits on the previous one
-  int n_cu = 256, dev = 0, cu = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cu > 0)
-    n_cu = cu;
-  const unsigned grid = (unsigned)max((size_t)1, min((size_t)n_cu * kWgPerCu, mw));
+  const unsigned grid = (unsigned)resident_grid();
   const size_t lds = sizeof(int) * (size_t)(rows + 1);
   const unsigned cgrid = (unsigned)(rows * heads_per_row(mode));
 #define RTP_LAUNCH(TT, HH)                                                                                        \
