@@ -94,7 +94,16 @@ typedef struct {
   int32_t max_seqlen_q;          /* host: max_b L_q(b) (grid sizing; L_q(b) <= L_k(b)) */
   int32_t max_seqlen_k;          /* host: max_b L_k(b) */
   int64_t total_q;               /* host: T_q = cu_seqlens_q[batch] */
-  int64_t total_k;               /* host: T_k = cu_seqlens_k[batch] */
+  int64_t total_k;               /* host: rows of the key arrays: cu_seqlens_k[batch] when packed,
+                                    batch * k_capacity otherwise */
+  int64_t k_capacity;            /* 0: packed keys (sequence b at rows cu_seqlens_k[b] ..);
+                                    > 0: sequence b at rows [b * k_capacity, b * k_capacity + L_k(b)),
+                                    so a cache grows in place (L_k(b) <= k_capacity) */
+  int32_t ring;                  /* 1: the key rows of a sequence are a ring that keeps only what
+                                    local heads read: position n < n_sink at row n, any later
+                                    position at row n_sink + (n - n_sink) % window; requires
+                                    k_capacity = n_sink + window, n_ret = 0 and one query per
+                                    sequence (rtp_local_attn, rtp_append_kv).  0: plain rows. */
 } rtp_problem;
 
 /* Output of rtp_select_topp, input of the sparse attention calls (device pointers). */
@@ -106,6 +115,16 @@ typedef struct {
   int32_t *count;    /* (dev) [R, T_q] size of the selected set */
   int32_t *idx;      /* (dev) LIST: [R, T_k]; slot (r, b) starts at r*T_k + cu_seqlens_k[b] */
 } rtp_selection;
+
+/*
+ * Key layouts.  k, v, k_pre and k_idx rows of sequence b start at cu_seqlens_k[b]
+ * (packed) or at b * k_capacity (capacity layout); the LIST slice (r, b) of
+ * sel->idx starts at r * total_k + that row.  Lengths always come from
+ * cu_seqlens_k[b + 1] - cu_seqlens_k[b].  A ring (ring = 1) holds the n_sink
+ * sinks and the last `window` positions of each sequence in n_sink + window
+ * rows: the storage local heads need, since they never read anything else (page
+ * "Full Attention Strikes Back ...", section 3.4 "Local Head Attention Pattern").
+ */
 
 /* Bytes of workspace a call needs for this problem (0 = none).  Pure host function. */
 RTP_API size_t rtp_workspace_size(const rtp_problem *prob, rtp_call call, rtp_sel_mode mode);
@@ -123,6 +142,27 @@ RTP_API size_t rtp_workspace_size(const rtp_problem *prob, rtp_call call, rtp_se
  */
 RTP_API rtp_status rtp_index_keys(const rtp_problem *prob, const void *k_pre, const float *w_k,
                           void *k_idx, void *stream);
+
+/*
+ * rtp_append_kv: append new tokens to the caches of every sequence (one per
+ * sequence in a decode step; a whole prompt to fill a ring after prefill).
+ * New token t of sequence b (t = 0 .. n_b - 1, n_b = cu_seqlens_new[b+1] -
+ * cu_seqlens_new[b]) takes position L_k(b) - n_b + t, where L_k(b) from prob is
+ * the length after the append; its K and V rows (all KV heads) go to that
+ * position's row of k and v, and every retrieval slot r gets
+ *   k_idx[r, row, :] = RNE_dtype(W^K_r . k_pre_new[t, kv(ret_heads[r]), :])
+ * computed exactly as rtp_index_keys computes it (the index keys are kept
+ * once computed, section 3.4, paragraph on the 16-dimensional scoring cost).
+ * In a ring, new tokens that are neither sinks nor among the last `window`
+ * positions are skipped.
+ *   cu_seqlens_new (dev) [batch+1]; total_new (host) = cu_seqlens_new[batch];
+ *   k_new, v_new, k_pre_new (dev) [total_new, Hkv, 128] dtype; w_k (dev) [R,16,128];
+ *   k, v (dev, in/out) key arrays in the layout of prob; k_idx (dev, in/out)
+ *   [R, total_k, 16].  k_pre_new, w_k and k_idx may be NULL when n_ret = 0.
+ */
+RTP_API rtp_status rtp_append_kv(const rtp_problem *prob, const int32_t *cu_seqlens_new, int64_t total_new,
+                         const void *k_new, const void *v_new, const void *k_pre_new, const float *w_k,
+                         void *k, void *v, void *k_idx, void *stream);
 
 /*
  * rtp_select_topp: indexer scores and dynamic top-p per (retrieval head, query).

@@ -18,7 +18,7 @@ from . import _lib
 from ._lib import (RTP_BF16, RTP_CALL_LOCAL, RTP_CALL_SELECT, RTP_CALL_SELECT_BLOCKS, RTP_CALL_SPARSE_DECODE,
                    RTP_CALL_SPARSE_PREFILL, RTP_F32, RTP_SEL_LIST, RTP_SEL_THRESHOLD)
 
-__all__ = ["Problem", "Selection", "rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
+__all__ = ["Problem", "Selection", "rtp_workspace_size", "rtp_index_keys", "rtp_append_kv", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
            "rtp_sparse_attn_prefill", "rtp_sparse_attn_decode", "rtp_local_attn", "RtpError",
            "RTP_SEL_LIST", "RTP_SEL_THRESHOLD", "RTP_CALL_SELECT", "RTP_CALL_SPARSE_PREFILL",
            "RTP_CALL_SPARSE_DECODE", "RTP_CALL_LOCAL", "RTP_CALL_SELECT_BLOCKS", "library"]
@@ -63,7 +63,7 @@ class Problem:
     def __init__(self, *, batch: int, n_q_heads: int, n_kv_heads: int, ret_heads: Sequence[int],
                  n_sink: int, window: int, dtype: torch.dtype, cu_seqlens_q: torch.Tensor,
                  cu_seqlens_k: torch.Tensor, max_seqlen_q: int, max_seqlen_k: int, total_q: int,
-                 total_k: int):
+                 total_k: int, k_capacity: int = 0, ring: bool = False):
         self.ret_heads = list(int(h) for h in ret_heads)
         self._ret = (ctypes.c_int32 * max(1, len(self.ret_heads)))(*self.ret_heads)
         self.cu_q = cu_seqlens_q
@@ -81,7 +81,8 @@ class Problem:
             n_sink=n_sink, window=window, dtype=dt,
             cu_seqlens_q=cu_seqlens_q.data_ptr() if cu_seqlens_q is not None else 0,
             cu_seqlens_k=cu_seqlens_k.data_ptr() if cu_seqlens_k is not None else 0,
-            max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, total_q=total_q, total_k=total_k)
+            max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k, total_q=total_q, total_k=total_k,
+            k_capacity=k_capacity, ring=1 if ring else 0)
 
     @property
     def n_ret(self) -> int:
@@ -158,6 +159,15 @@ def rtp_index_keys(prob: Problem, k_pre: torch.Tensor, w_k: torch.Tensor,
     st = _lib.load().rtp_index_keys(prob.ref, _ptr(k_pre), _ptr(w_k), _ptr(k_idx), _stream(stream))
     _check(st, "rtp_index_keys")
     return k_idx
+
+
+def rtp_append_kv(prob: Problem, cu_seqlens_new: torch.Tensor, total_new: int, k_new: torch.Tensor,
+                  v_new: torch.Tensor, k: torch.Tensor, v: torch.Tensor, k_pre_new: Optional[torch.Tensor] = None,
+                  w_k: Optional[torch.Tensor] = None, k_idx: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Write new tokens (the last positions of every sequence) into the caches k, v (and k_idx)."""
+    st = _lib.load().rtp_append_kv(prob.ref, _ptr(cu_seqlens_new), int(total_new), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_pre_new), _ptr(w_k), _ptr(k), _ptr(v), _ptr(k_idx), _stream(stream))
+    _check(st, "rtp_append_kv")
 
 
 def rtp_select_topp(prob: Problem, q_pre: torch.Tensor, w_q: torch.Tensor, k_idx: torch.Tensor,

@@ -12,7 +12,7 @@ RTP_F32, RTP_BF16 = 0, 1
 RTP_SEL_LIST, RTP_SEL_THRESHOLD = 0, 1
 RTP_CALL_SELECT, RTP_CALL_SPARSE_PREFILL, RTP_CALL_SPARSE_DECODE, RTP_CALL_LOCAL, RTP_CALL_SELECT_BLOCKS = 1, 2, 3, 4, 5
 
-EXPORTED = ("rtp_workspace_size", "rtp_index_keys", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
+EXPORTED = ("rtp_workspace_size", "rtp_index_keys", "rtp_append_kv", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
             "rtp_sparse_attn_prefill",
             "rtp_sparse_attn_decode", "rtp_local_attn", "rtp_status_str", "rtp_last_hip_error")
 
@@ -35,6 +35,8 @@ class RtpProblem(ctypes.Structure):
         ("max_seqlen_k", ctypes.c_int32),
         ("total_q", ctypes.c_int64),
         ("total_k", ctypes.c_int64),
+        ("k_capacity", ctypes.c_int64),
+        ("ring", ctypes.c_int32),
     ]
 
 
@@ -66,6 +68,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtp_workspace_size.restype = sz
     lib.rtp_index_keys.argtypes = [P, vp, vp, vp, vp]
     lib.rtp_index_keys.restype = i32
+    lib.rtp_append_kv.argtypes = [P, vp, ctypes.c_int64, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.rtp_append_kv.restype = i32
     lib.rtp_select_topp.argtypes = [P, vp, vp, vp, vp, i32, S, vp, sz, vp]
     lib.rtp_select_topp.restype = i32
     lib.rtp_select_topk.argtypes = [P, vp, vp, vp, vp, i32, S, vp, sz, vp]

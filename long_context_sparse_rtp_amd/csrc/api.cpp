@@ -41,8 +41,16 @@ rtp_status check_problem(const rtp_problem* pr, ProbDev* out) {
   if (pr->max_seqlen_q > pr->max_seqlen_k) return RTP_ERR_INVALID_ARG;
   if (pr->total_q < 1 || pr->total_k < 1) return RTP_ERR_INVALID_ARG;
   if (pr->total_q > (int64_t)pr->batch * pr->max_seqlen_q) return RTP_ERR_INVALID_ARG;
-  if (pr->total_k > (int64_t)pr->batch * pr->max_seqlen_k) return RTP_ERR_INVALID_ARG;
+  if (pr->k_capacity == 0 && pr->total_k > (int64_t)pr->batch * pr->max_seqlen_k) return RTP_ERR_INVALID_ARG;
   if (pr->total_q >= INT32_MAX || pr->total_k >= INT32_MAX) return RTP_ERR_UNSUPPORTED;
+  // key layout: packed, per-sequence capacity, or a ring of sinks + window
+  if (pr->k_capacity < 0 || (pr->ring != 0 && pr->ring != 1)) return RTP_ERR_INVALID_ARG;
+  if (pr->ring && pr->k_capacity != (int64_t)pr->n_sink + pr->window) return RTP_ERR_INVALID_ARG;
+  if (pr->k_capacity > 0) {
+    if (pr->total_k != (int64_t)pr->batch * pr->k_capacity) return RTP_ERR_INVALID_ARG;
+    if (!pr->ring && pr->max_seqlen_k > pr->k_capacity) return RTP_ERR_INVALID_ARG;
+  }
+  if (pr->ring && (pr->n_ret != 0 || pr->max_seqlen_q != 1)) return RTP_ERR_UNSUPPORTED;
   if (out) {
     ProbDev& p = *out;
     memset(&p, 0, sizeof(p));
@@ -58,6 +66,8 @@ rtp_status check_problem(const rtp_problem* pr, ProbDev* out) {
     p.Tk = pr->total_k;
     p.cu_q = pr->cu_seqlens_q;
     p.cu_k = pr->cu_seqlens_k;
+    p.kcap = pr->k_capacity;
+    p.ring = pr->ring;
     bool is_ret[RTP_MAX_HEADS] = {false};
     for (int r = 0; r < p.R; ++r) {
       p.ret_heads[r] = pr->ret_heads[r];
@@ -151,6 +161,22 @@ size_t rtp_workspace_size(const rtp_problem* prob, rtp_call call, rtp_sel_mode m
   ProbDev p;
   if (check_problem(prob, &p) != RTP_OK) return 0;
   return ws_need(p, call, mode);
+}
+
+rtp_status rtp_append_kv(const rtp_problem* prob, const int32_t* cu_seqlens_new, int64_t total_new,
+                         const void* k_new, const void* v_new, const void* k_pre_new, const float* w_k, void* k,
+                         void* v, void* k_idx, void* stream) {
+  ProbDev p;
+  rtp_status st = check_problem(prob, &p);
+  if (st != RTP_OK) return st;
+  // a ring takes a whole prompt (most of it skipped); other layouts have a row per new token
+  if (total_new < 0 || total_new >= INT32_MAX || (!p.ring && total_new > p.Tk)) return RTP_ERR_INVALID_ARG;
+  if (total_new == 0) return RTP_OK;
+  if (!aligned4(cu_seqlens_new) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k) || !aligned16(v))
+    return RTP_ERR_INVALID_ARG;
+  if (p.R > 0 && (!aligned16(k_pre_new) || !aligned16(w_k) || !aligned16(k_idx))) return RTP_ERR_INVALID_ARG;
+  return finish(rtp::launch_append_kv(p, prob->dtype == RTP_BF16, cu_seqlens_new, total_new, k_new, v_new,
+                                      k_pre_new, w_k, k, v, k_idx, (hipStream_t)stream));
 }
 
 rtp_status rtp_index_keys(const rtp_problem* prob, const void* k_pre, const float* w_k, void* k_idx,
@@ -247,6 +273,7 @@ rtp_status rtp_local_attn(const rtp_problem* prob, const void* q, const void* k,
     if (st != RTP_OK) return st;
     return finish(rtp::launch_attn_decode(p, bf16, 1, q, k, v, nullptr, out, lse, ws, s));
   }
+  if (p.ring) return RTP_ERR_UNSUPPORTED;
   return finish(rtp::launch_attn_prefill(p, bf16, 1, q, k, v, nullptr, nullptr, out, lse, s));
 }
 

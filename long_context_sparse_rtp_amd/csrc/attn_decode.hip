@@ -57,8 +57,8 @@ __device__ __forceinline__ RowInfo row_info(const ProbDev& p, int mode, int row,
   RowInfo ri;
   ri.b = row % p.batch;
   const int hi = row / p.batch;
-  ri.k0 = p.cu_k[ri.b];
-  ri.L = p.cu_k[ri.b + 1] - ri.k0;
+  ri.k0 = key_row0(p, ri.b);
+  ri.L = p.cu_k[ri.b + 1] - p.cu_k[ri.b];
   ri.qrow = p.cu_q[ri.b];
   if (mode == 0) {
     ri.hfirst = p.ret_heads[hi];
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
       const int* list = sel.idx + (size_t)(row / p.batch) * p.Tk + ri.k0;
       for (int j = j0 + tid; j < j1; j += kThreads) idx_s[j - j0] = list[j];
     } else {
-      for (int j = j0 + tid; j < j1; j += kThreads) idx_s[j - j0] = local_token(p, ri.L, j);
+      for (int j = j0 + tid; j < j1; j += kThreads) idx_s[j - j0] = key_slot(p, local_token(p, ri.L, j));
     }
 
     float qv[H][8];

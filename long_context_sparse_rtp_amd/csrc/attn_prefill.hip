@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   const int h = (MODE == 0) ? p.ret_heads[hidx] : p.local_heads[hidx];
   const int g = kv_of(p, h);
   const int q0 = p.cu_q[b], Lq = p.cu_q[b + 1] - q0;
-  const int k0 = p.cu_k[b], Lk = p.cu_k[b + 1] - k0;
+  const int k0 = key_row0(p, b), Lk = p.cu_k[b + 1] - p.cu_k[b];
   const int i0 = wk.qt * BQ;
   if (i0 >= Lq) return;
   const int off = Lk - Lq;

@@ -62,7 +62,77 @@ __global__ __launch_bounds__(kThreads) void index_keys_kernel(ProbDev p, const T
   for (int i = 0; i < (int)(kIdxDim * sizeof(T) / 16); ++i) dst[i] = src[i];
 }
 
+// ---------------------------------------------------------------- append
+// New tokens at the end of every sequence (a decode step appends one): token t
+// of sequence b (t = 0 .. n_b - 1) takes position L_b - n_b + t, with L_b the
+// length after the append.  Its K and V rows (all KV heads) are copied into the
+// cache row of that position - the position itself, or its ring slot when the
+// cache keeps only sinks and window - and every retrieval slot gets the index
+// key of the new pre-RoPE key, computed exactly as index_keys_kernel does
+// (float64 FMA chain over the 128 dims in order, one rounding), so an appended
+// cache is bit-identical to one projected in a single pass.  In a ring, tokens
+// that no later query can see (neither sinks nor among the last `window`
+// positions) are not written, so no two tokens of one call share a slot.
+// One workgroup of 128 threads per new token.
+template <typename T>
+__global__ __launch_bounds__(kHeadDim) void append_kv_kernel(ProbDev p, const int32_t* __restrict__ cu_new,
+                                                             int64_t total_new, const T* __restrict__ k_new,
+                                                             const T* __restrict__ v_new,
+                                                             const T* __restrict__ k_pre_new,
+                                                             const float* __restrict__ w_k, T* __restrict__ k,
+                                                             T* __restrict__ v, T* __restrict__ k_idx) {
+  const int64_t t = blockIdx.x;
+  if (t >= total_new) return;
+  // sequence of token t: last b with cu_new[b] <= t
+  int lo = 0, hi = p.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu_new[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int b = lo;
+  const int nb = cu_new[b + 1] - cu_new[b];
+  const int L = p.cu_k[b + 1] - p.cu_k[b];
+  const int pos = L - nb + (int)(t - cu_new[b]);
+  if (pos < 0 || pos >= L) return;
+  if (p.ring && pos >= p.n_sink && pos < L - p.window) return;   // outside every later window
+  const int slot = key_slot(p, pos);
+  if (p.kcap > 0 && slot >= p.kcap) return;
+  const int64_t row = (int64_t)key_row0(p, b) + slot;
+  if (row < 0 || row >= p.Tk) return;
+  const int d = threadIdx.x;
+  for (int g = 0; g < p.Hkv; ++g) {
+    k[((size_t)row * p.Hkv + g) * kHeadDim + d] = k_new[((size_t)t * p.Hkv + g) * kHeadDim + d];
+    v[((size_t)row * p.Hkv + g) * kHeadDim + d] = v_new[((size_t)t * p.Hkv + g) * kHeadDim + d];
+  }
+  // index keys: thread (r, j) over the R * 16 outputs
+  for (int o = d; o < p.R * kIdxDim; o += kHeadDim) {
+    const int r = o / kIdxDim, j = o % kIdxDim;
+    const int g = kv_of(p, p.ret_heads[r]);
+    const T* x = k_pre_new + ((size_t)t * p.Hkv + g) * kHeadDim;
+    const float* w = w_k + ((size_t)r * kIdxDim + j) * kHeadDim;
+    double acc = 0.0;
+    for (int e = 0; e < kHeadDim; ++e) acc = fma((double)Elem<T>::to_f(x[e]), (double)w[e], acc);
+    k_idx[((size_t)r * p.Tk + row) * kIdxDim + j] = Elem<T>::from_d(acc);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append_kv(const ProbDev& p, bool bf16, const int32_t* cu_new, int64_t total_new,
+                            const void* k_new, const void* v_new, const void* k_pre_new, const float* w_k,
+                            void* k, void* v, void* k_idx, hipStream_t s) {
+  if (total_new == 0) return hipSuccess;
+  dim3 grid((unsigned)total_new);
+  if (bf16)
+    hipLaunchKernelGGL(append_kv_kernel<bf16_t>, grid, dim3(kHeadDim), 0, s, p, cu_new, total_new,
+                       (const bf16_t*)k_new, (const bf16_t*)v_new, (const bf16_t*)k_pre_new, w_k, (bf16_t*)k,
+                       (bf16_t*)v, (bf16_t*)k_idx);
+  else
+    hipLaunchKernelGGL(append_kv_kernel<float>, grid, dim3(kHeadDim), 0, s, p, cu_new, total_new,
+                       (const float*)k_new, (const float*)v_new, (const float*)k_pre_new, w_k, (float*)k,
+                       (float*)v, (float*)k_idx);
+  return hipGetLastError();
+}
 
 hipError_t launch_index_keys(const ProbDev& p, bool bf16, const void* k_pre, const float* w_k,
                              void* k_idx, hipStream_t s) {

@@ -15,6 +15,8 @@ struct ProbDev {
   int64_t Tq, Tk;
   const int32_t* cu_q;
   const int32_t* cu_k;
+  int64_t kcap;                    // rows per sequence in the key arrays (0: packed at cu_k offsets)
+  int ring;                        // key rows of a sequence form a ring of n_sink + window slots
   int ret_heads[RTP_MAX_HEADS];    // slot -> query head
   int local_heads[RTP_MAX_HEADS];  // local index -> query head
   // local heads grouped by KV head, at most attn_decode_tile_heads() per tile: tile t covers
@@ -26,6 +28,18 @@ struct ProbDev {
 
 __host__ __device__ inline int kv_of(const ProbDev& p, int h) { return (h * p.Hkv) / p.Hq; }
 
+// First row of sequence b in k, v, k_pre, k_idx and the LIST idx: the packed
+// offset cu_k[b], or b * capacity in the per-sequence capacity layout.
+__device__ __forceinline__ int key_row0(const ProbDev& p, int b) {
+  return p.kcap > 0 ? (int)((int64_t)b * p.kcap) : p.cu_k[b];
+}
+// Row of position n within its sequence: n itself, or its slot in a ring that
+// keeps the n_sink sinks and the last `window` positions.
+__device__ __forceinline__ int key_slot(const ProbDev& p, int n) {
+  if (!p.ring || n < p.n_sink) return n;
+  return p.n_sink + (n - p.n_sink) % p.window;
+}
+
 // Workspace layouts (bytes), shared by rtp_workspace_size and the launchers.
 size_t ws_select_decode(const ProbDev& p);
 int select_decode_max_keys();   // longest sequence LIST selection accepts
@@ -36,6 +50,10 @@ int attn_decode_tile_heads(); // local heads of one KV group handled together in
 
 hipError_t launch_index_keys(const ProbDev& p, bool bf16, const void* k_pre, const float* w_k,
                              void* k_idx, hipStream_t s);
+// new tokens [total_new] at the end of every sequence: K/V rows and their index keys
+hipError_t launch_append_kv(const ProbDev& p, bool bf16, const int32_t* cu_new, int64_t total_new,
+                            const void* k_new, const void* v_new, const void* k_pre_new, const float* w_k,
+                            void* k, void* v, void* k_idx, hipStream_t s);
 // top_k == nullptr: dynamic top-p over top_p[batch]; otherwise fixed top-k over top_k[batch]
 hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, const float* w_q,
                                 const void* k_idx, const float* top_p, const int32_t* top_k,

@@ -146,8 +146,8 @@ __device__ __forceinline__ RowGeom row_geom(const ProbDev& p, int row) {
   g.row = row;
   g.r = row / p.batch;
   g.b = row % p.batch;
-  g.k0 = p.cu_k[g.b];
-  g.L = p.cu_k[g.b + 1] - g.k0;
+  g.k0 = key_row0(p, g.b);
+  g.L = p.cu_k[g.b + 1] - p.cu_k[g.b];
   g.U = max(1, (g.L + kChunk - 1) / kChunk);
   g.qrow = p.cu_q[g.b];
   g.slot0 = (int64_t)g.r * slots_per_r(p) + g.k0 / kChunk + g.b;

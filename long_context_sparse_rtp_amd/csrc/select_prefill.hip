@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void kidx_norm_max(ProbDev p, const T* __restr
                                                      uint32_t* __restrict__ out) {
   const int row = blockIdx.y;  // r * batch + b
   const int r = row / p.batch, b = row % p.batch;
-  const int k0 = p.cu_k[b], L = p.cu_k[b + 1] - k0;
+  const int k0 = key_row0(p, b), L = p.cu_k[b + 1] - p.cu_k[b];
   float mx = 0.f;
   for (int n = blockIdx.x * 256 + threadIdx.x; n < L; n += gridDim.x * 256) {
     const T* x = k_idx + ((size_t)r * p.Tk + k0 + n) * kIdxDim;
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
   const int qt = tiles_per_b - 1 - (int)(blockIdx.x / p.batch);  // longest rows first
   const int r = blockIdx.y;
   const int q0 = p.cu_q[b], Lq = p.cu_q[b + 1] - q0;
-  const int k0 = p.cu_k[b], Lk = p.cu_k[b + 1] - k0;
+  const int k0 = key_row0(p, b), Lk = p.cu_k[b + 1] - p.cu_k[b];
   const int i0 = qt * kRows;
   if (i0 >= Lq) return;
   const int off = Lk - Lq;

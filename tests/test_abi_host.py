@@ -100,3 +100,48 @@ def test_status_strings():
     assert lib.rtp_status_str(0) == b"ok"
     assert lib.rtp_status_str(3) == b"workspace too small"
     assert lib.rtp_last_hip_error() == b""
+
+
+def _decode_problem(L, **kw):
+    base = dict(max_seqlen_q=1, total_q=1, max_seqlen_k=1000, total_k=1024)
+    base.update(kw)
+    return _problem(L, **base)
+
+
+def test_capacity_layout_validation():
+    L, lib = _lib()
+    size = lambda p: lib.rtp_workspace_size(ctypes.byref(p), L.RTP_CALL_SELECT, L.RTP_SEL_LIST)
+    # capacity 1024 rows per sequence holding up to 1000 keys: valid
+    assert size(_decode_problem(L, k_capacity=1024)) > 0
+    # rows must be batch * capacity, the longest sequence must fit, capacity >= 0
+    assert size(_decode_problem(L, k_capacity=1024, total_k=1000)) == 0
+    assert size(_decode_problem(L, k_capacity=512, total_k=512)) == 0
+    assert size(_decode_problem(L, k_capacity=-1)) == 0
+
+
+def test_ring_layout_validation():
+    L, lib = _lib()
+    none = ctypes.cast((ctypes.c_int32 * 1)(0), ctypes.POINTER(ctypes.c_int32))
+    # ring of 4 sinks + 256 window rows, local heads only, one query per sequence
+    ok = dict(n_ret=0, ret_heads=none, ring=1, k_capacity=260, total_k=260, max_seqlen_k=100000)
+    assert lib.rtp_workspace_size(ctypes.byref(_decode_problem(L, **ok)), L.RTP_CALL_LOCAL, 0) > 0
+    bad_cap = dict(ok, k_capacity=256, total_k=256)
+    assert lib.rtp_workspace_size(ctypes.byref(_decode_problem(L, **bad_cap)), L.RTP_CALL_LOCAL, 0) == 0
+    p = _decode_problem(L, **dict(ok, ring=2))
+    assert lib.rtp_local_attn(ctypes.byref(p), 16, 16, 16, 16, None, None, 0, None) == L.RTP_ERR_INVALID_ARG
+    # retrieval heads need the whole cache, and a ring serves one query per sequence
+    p = _decode_problem(L, ring=1, k_capacity=260, total_k=260)
+    assert lib.rtp_local_attn(ctypes.byref(p), 16, 16, 16, 16, None, None, 0, None) == L.RTP_ERR_UNSUPPORTED
+    p = _problem(L, n_ret=0, ret_heads=none, ring=1, k_capacity=260, total_k=260, max_seqlen_q=2, total_q=2)
+    assert lib.rtp_local_attn(ctypes.byref(p), 16, 16, 16, 16, None, None, 0, None) == L.RTP_ERR_UNSUPPORTED
+
+
+def test_append_kv_validation():
+    L, lib = _lib()
+    p = _decode_problem(L, k_capacity=1024)
+    call = lambda p, total_new, *ptrs: lib.rtp_append_kv(ctypes.byref(p), 16, total_new, *ptrs, None)
+    assert call(p, 1, 16, 16, 16, 16, 16, 16, None) == L.RTP_ERR_INVALID_ARG      # k_idx missing with n_ret > 0
+    assert call(p, 1, 16, 8, 16, 16, 16, 16, 16) == L.RTP_ERR_INVALID_ARG         # misaligned v_new
+    assert call(p, 2048, 16, 16, 16, 16, 16, 16, 16) == L.RTP_ERR_INVALID_ARG     # more new tokens than rows
+    assert call(p, -1, 16, 16, 16, 16, 16, 16, 16) == L.RTP_ERR_INVALID_ARG
+    assert call(p, 0, None, None, None, None, None, None, None) == L.RTP_OK        # nothing to append
