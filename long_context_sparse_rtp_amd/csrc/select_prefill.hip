@@ -233,13 +233,40 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     }
     return idx_dot_tile(kxf, qxf);
   };
-  // two tiles per step over the full tiles, then the diagonal tiles one at a time
+  // Two tiles per step over the full tiles (every key exists and lies below every
+  // row's position), their index keys loaded one step ahead with unconditional
+  // loads (a prefetch past the last pair re-reads the last full tile) into two
+  // register sets that alternate, so a step never waits on the loads it issues;
+  // then the diagonal tiles one at a time.
+  auto load_full = [&](IF& f, int t) {
+    load_idx_frag(f, kxb + (size_t)(16 * min(t, nfull - 1) + col) * kIdxDim + 4 * grp);
+  };
   auto sweep_tiles = [&](auto&& body) {
     int t = w;
-    for (; t + kWaves < nfull; t += 2 * kWaves) {
-      const f32x4 d0 = tile_dot(t), d1 = tile_dot(t + kWaves);
-      body(d0, t, false);
-      body(d1, t + kWaves, false);
+    if (t + kWaves < nfull) {
+      IF a0, a1, b0, b1;
+      load_full(a0, t);
+      load_full(a1, t + kWaves);
+      while (true) {
+        load_full(b0, t + 2 * kWaves);
+        load_full(b1, t + 3 * kWaves);
+        {
+          const f32x4 d0 = idx_dot_tile(a0, qxf), d1 = idx_dot_tile(a1, qxf);
+          body(d0, t, false);
+          body(d1, t + kWaves, false);
+        }
+        t += 2 * kWaves;
+        if (!(t + kWaves < nfull)) break;
+        load_full(a0, t + 2 * kWaves);
+        load_full(a1, t + 3 * kWaves);
+        {
+          const f32x4 d0 = idx_dot_tile(b0, qxf), d1 = idx_dot_tile(b1, qxf);
+          body(d0, t, false);
+          body(d1, t + kWaves, false);
+        }
+        t += 2 * kWaves;
+        if (!(t + kWaves < nfull)) break;
+      }
     }
     for (; t < ntile; t += kWaves) body(tile_dot(t), t, t >= nfull);
   };
