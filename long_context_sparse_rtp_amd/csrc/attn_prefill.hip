@@ -384,7 +384,17 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
         }
       }
       // membership: branch-free masks; the variant (exact ties, boundary tile)
-      // is fixed per tile so each inner loop is straight-line code
+      // is fixed per tile so each inner loop is straight-line code.  Element
+      // (ks, i) of a lane is key kb4 + 16 ks + i: the tests compare that
+      // compile-time offset with per-row differences computed once per tile
+      // (per-element key counters would cost a register and an add each).
+      const int kb4 = kbase + 4 * grp;
+      int relq[2], relt[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        relq[c] = opaque_int(qpos[c] - kb4);   // key <= qpos  <=>  16 ks + i <= relq
+        relt[c] = opaque_int(tie[c] - kb4);    // key <= tie   <=>  16 ks + i <= relt
+      }
       if (MODE == 0) {
         auto apply = [&](auto exact_t, auto mask_t) {
           constexpr bool kExact = decltype(exact_t)::value;
@@ -396,11 +406,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
               const f32x4 dx = idx_dot_tile(kxf[ks], qxf[c]);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
-                const int key = kbase + 16 * ks + 4 * grp + i;
+                const int ko = 16 * ks + i;
                 bool ok;
-                if (kExact) ok = (dx[i] > tau4[c]) | ((dx[i] == tau4[c]) & (key <= tie[c]));
+                if (kExact) ok = (dx[i] > tau4[c]) | ((dx[i] == tau4[c]) & (ko <= relt[c]));
                 else ok = dx[i] >= tau4[c];
-                if (kMask) ok = ok & (key <= qpos[c]);
+                if (kMask) ok = ok & (ko <= relq[c]);
                 sacc[c][ks][i] = ok ? sacc[c][ks][i] : -INFINITY;
               }
             }
@@ -413,10 +423,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
 #pragma unroll
               for (int c = 0; c < 2; ++c)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                  const int key = kbase + 16 * ks + 4 * grp + i;
-                  sacc[c][ks][i] = (key <= qpos[c]) ? sacc[c][ks][i] : -INFINITY;
-                }
+                for (int i = 0; i < 4; ++i)
+                  sacc[c][ks][i] = (16 * ks + i <= relq[c]) ? sacc[c][ks][i] : -INFINITY;
           }
         } else if (exact_ties) {
           if (need_mask) apply(std::true_type{}, std::true_type{}); else apply(std::true_type{}, std::false_type{});
@@ -424,16 +432,17 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
           if (need_mask) apply(std::false_type{}, std::true_type{}); else apply(std::false_type{}, std::false_type{});
         }
       } else if (need_mask) {
+        const int sink_rel = opaque_int(p.n_sink - kb4);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int key = kbase + 16 * ks + 4 * grp + i;
-              const bool is_sink = key < p.n_sink;
-              const bool in_win = (qpos[c] - key) < p.window;
-              const bool ok = (key <= qpos[c]) & (sink_only ? is_sink : (in_win | is_sink));
+              const int ko = 16 * ks + i;
+              const bool is_sink = ko < sink_rel;                 // key < n_sink
+              const bool in_win = ko > relq[c] - p.window;         // qpos - key < window
+              const bool ok = (ko <= relq[c]) & (sink_only ? is_sink : (in_win | is_sink));
               sacc[c][ks][i] = ok ? sacc[c][ks][i] : -INFINITY;
             }
       }
@@ -474,18 +483,20 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
         make_pfrag(pf[c][1], x[2], x[3]);
       }
 
-      // O^T += V^T P^T
+      // O^T += V^T P^T; the eight V^T fragments of a 32-key step are read before
+      // its products, so the LDS reads overlap instead of each waiting alone
       if (__builtin_amdgcn_ballot_w64(live)) {
         const T* vtt = vt_s[buf];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
+          F vf[8];
 #pragma unroll
-          for (int dt = 0; dt < 8; ++dt) {
-            F vf;
-            load_vfrag(vf, vtt + (16 * dt + col) * VS + 32 * kk + 4 * grp);
+          for (int dt = 0; dt < 8; ++dt) load_vfrag(vf[dt], vtt + (16 * dt + col) * VS + 32 * kk + 4 * grp);
+          __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the products
 #pragma unroll
-            for (int c = 0; c < 2; ++c) oacc[c][dt] = mma_k32(vf, pf[c][kk], oacc[c][dt]);
-          }
+          for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) oacc[c][dt] = mma_k32(vf[dt], pf[c][kk], oacc[c][dt]);
         }
       }
     }

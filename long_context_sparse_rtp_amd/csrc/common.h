@@ -127,6 +127,14 @@ __device__ __forceinline__ f32x4 idx_dot_tile(const IdxFragF32& kf, const IdxFra
   return c;
 }
 
+// A value the optimiser must treat as unknown (an empty asm statement that
+// claims to modify the register): keeps it from turning per-tile expressions
+// into per-element loop counters that each cost a register and an add.
+__device__ __forceinline__ int opaque_int(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 // The indexer score s = (q_idx . k_idx) / sqrt(16); the scale is exact.
 __device__ __forceinline__ float idx_score(float dot) { return dot * 0.25f; }
 
