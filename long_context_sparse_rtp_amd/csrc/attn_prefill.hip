@@ -461,13 +461,19 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const float mnew = fmaxf(m_[c], tmax * sl2);
         live |= (mnew != -INFINITY);
-        const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-        const float alpha = __builtin_amdgcn_exp2f(m_[c] - muse);
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+        // The reference m_ moves (and O, l are rescaled) only when the row maximum
+        // exceeds it by more than 8: until then exp2(s - m_) <= 2^8, and O and l
+        // keep sharing one reference, so the result is the same.
+        const bool up = mnew > m_[c] + 8.f;   // also the first finite maximum
+        if (__builtin_amdgcn_ballot_w64(up)) {
+          const float mref = up ? mnew : m_[c];
+          const float alpha = up ? __builtin_amdgcn_exp2f(m_[c] - mref) : 1.f;
           l_[c] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) oacc[c][dt] *= alpha;
+          m_[c] = mref;
         }
+        const float muse = (m_[c] == -INFINITY) ? 0.f : m_[c];
         float ps = 0.f;
         float x[4][4];
 #pragma unroll
@@ -478,7 +484,6 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
             ps += x[ks][i];
           }
         l_[c] += ps;
-        m_[c] = mnew;
         make_pfrag(pf[c][0], x[0], x[1]);
         make_pfrag(pf[c][1], x[2], x[3]);
       }
