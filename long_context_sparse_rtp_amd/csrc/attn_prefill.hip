@@ -61,6 +61,21 @@ __device__ __forceinline__ void make_pfrag(FragF32& f, const float* a, const flo
   for (int i = 0; i < 4; ++i) { f.v[i] = a[i]; f.v[4 + i] = b[i]; }
 }
 
+// ---- an operand fragment of ones
+template <typename F> __device__ __forceinline__ F ones_frag();
+template <> __device__ __forceinline__ FragBF16 ones_frag<FragBF16>() {
+  FragBF16 f;
+  const uint4 u = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};   // bfloat16 1.0 pairs
+  f.v = __builtin_bit_cast(bf16x8, u);
+  return f;
+}
+template <> __device__ __forceinline__ FragF32 ones_frag<FragF32>() {
+  FragF32 f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = 1.f;
+  return f;
+}
+
 // ---- A operand of O^T += V^T P^T: row d of V^T, keys (4g..4g+3) and (16+4g..16+4g+3)
 __device__ __forceinline__ void load_vfrag(FragBF16& f, const bf16_t* rowp) {
   uint2 a = *reinterpret_cast<const uint2*>(rowp);
@@ -291,7 +306,12 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   }
 
   const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
-  float m_[2] = {-INFINITY, -INFINITY}, l_[2] = {0.f, 0.f};
+  float m_[2] = {-INFINITY, -INFINITY};
+  // row sums of P on the matrix cores: a constant all-ones A operand turns
+  // O^T += V^T P^T into sum_k P[k][row] in every output row (and sums exactly
+  // the rounded P that multiplies V)
+  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const F onesf = ones_frag<F>();
   f32x4 oacc[2][8];
 #pragma unroll
   for (int c = 0; c < 2; ++c)
@@ -468,22 +488,17 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
         if (__builtin_amdgcn_ballot_w64(up)) {
           const float mref = up ? mnew : m_[c];
           const float alpha = up ? __builtin_amdgcn_exp2f(m_[c] - mref) : 1.f;
-          l_[c] *= alpha;
+          lacc[c] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) oacc[c][dt] *= alpha;
           m_[c] = mref;
         }
         const float muse = (m_[c] == -INFINITY) ? 0.f : m_[c];
-        float ps = 0.f;
         float x[4][4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[c][ks][i], sl2, -muse));
-            ps += x[ks][i];
-          }
-        l_[c] += ps;
+          for (int i = 0; i < 4; ++i) x[ks][i] = __builtin_amdgcn_exp2f(fmaf(sacc[c][ks][i], sl2, -muse));
         make_pfrag(pf[c][0], x[0], x[1]);
         make_pfrag(pf[c][1], x[2], x[3]);
       }
@@ -502,6 +517,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
           for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
             for (int c = 0; c < 2; ++c) oacc[c][dt] = mma_k32(vf[dt], pf[c][kk], oacc[c][dt]);
+#pragma unroll
+          for (int c = 0; c < 2; ++c) lacc[c] = mma_k32(onesf, pf[c][kk], lacc[c]);
         }
       }
     }
@@ -515,9 +532,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   // ---- normalise and store
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
-    float lt = l_[c];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = lacc[c][0];   // every output row of the ones tile holds the row sum
     if (!qok[c]) continue;
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
     T* op = out + ((size_t)(q0 + qi[c]) * p.Hq + h) * kHeadDim;
