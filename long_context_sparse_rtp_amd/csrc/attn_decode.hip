@@ -15,9 +15,8 @@
 //     group, sequence); tiles hold one head at present: holding several lets
 //     a K/V row feed all of them, but costs more in cross-lane reductions;
 //   - every row's key set is cut into equal splits of at most 512 entries,
-//     sized from the total entry count so that the splits of all rows fill the
-//     resident grid about once (a fixed 512 left the last round of workgroups
-//     half empty); the splits form one flat work list (prefix sums of the
+//     sized from the total entry count so that the splits of all rows fit the
+//     resident grid once; the splits form one flat work list (prefix sums of the
 //     per-row split counts, computed by every workgroup) that the grid walks
 //     round-robin, so ragged rows and sparse sets leave no idle workgroups;
 //   - a split's key positions are staged in LDS with one coalesced read, so
@@ -39,6 +38,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kSplit = 512;              // most entries per split
 constexpr int kMinSplit = 64;            // fewest entries per split (unless a row holds fewer)
+constexpr int kBalance = 1;              // 1: size splits so that every row fits the grid once; 0: kSplit
 constexpr int kGroups = kThreads / 16;   // 16-lane groups per workgroup
 constexpr int kUnroll = 4;               // tokens per group per batch
 constexpr int kStep = kGroups * kUnroll; // tokens per workgroup per batch
@@ -113,12 +113,14 @@ template <> struct RowVec<float> {
   }
 };
 
-// H: heads per row this instantiation holds (1: retrieval slots, 8: local tiles)
-template <typename T, int H>
-__global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mode, int rows, const T* __restrict__ q,
+// MODE 0: retrieval slots over the LIST; MODE 1: tiles of local heads over sinks + window
+template <typename T, int MODE>
+__global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int rows, const T* __restrict__ q,
                                                                const T* __restrict__ k, const T* __restrict__ v,
                                                                const rtp_selection sel, int* __restrict__ pre,
                                                                float* __restrict__ part) {
+  constexpr int mode = MODE;
+  constexpr int H = (MODE == 0) ? 1 : kMaxTileHeads;   // heads per row
   extern __shared__ int pre_s[];   // [rows + 1], sized at launch
   __shared__ int idx_s[kSplit];
   __shared__ int wsum_s[kThreads / 64];
@@ -148,9 +150,14 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
     if (lane == 0) wsum_s[wid] = (int)min(tot_entries, (long long)0x7FFFFFFF);
     __syncthreads();
     if (tid == 0) {
+      // sum_r ceil(count_r / t) <= total / t + rows, so t >= total / (grid - rows)
+      // puts every split of every row in one round of the grid
       long long te = 0;
       for (int w2 = 0; w2 < kThreads / 64; ++w2) te += wsum_s[w2];
-      target_s = (int)min((long long)kSplit, max((long long)kMinSplit, (te + gridDim.x - 1) / gridDim.x));
+      const long long slots = (long long)gridDim.x - rows;
+      long long t = kSplit;
+      if (kBalance && slots > 0) t = (te + slots - 1) / slots;
+      target_s = (int)min((long long)kSplit, max((long long)kMinSplit, t));
     }
     __syncthreads();
     const int target = target_s;
@@ -306,11 +313,13 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int mo
 // Log-sum-exp merge of a (row, head)'s split partials: split weights first (one
 // load per thread), then every thread sums its head dim over the splits with
 // independent loads.
-template <typename T, int H>
-__global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, int mode, const rtp_selection sel,
+template <typename T, int MODE>
+__global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, const rtp_selection sel,
                                                                 const int* __restrict__ pre,
                                                                 const float* __restrict__ part,
                                                                 T* __restrict__ out, float* __restrict__ lse) {
+  constexpr int mode = MODE;
+  constexpr int H = (MODE == 0) ? 1 : kMaxTileHeads;
   constexpr int kMaxS = 256;
   __shared__ float wgt_s[kMaxS];
   __shared__ float red_s[2], red2_s[2];
@@ -380,9 +389,9 @@ inline int resident_grid() {
   return n_cu * kWgPerCu;
 }
 
-// Upper bound on the number of splits.  While the target is ceil(total / grid)
-// (or is raised to kMinSplit), sum_r ceil(count_r / target) <= total / target +
-// rows <= grid + rows.  When it is capped at kSplit, a row has ceil(count /
+// Upper bound on the number of splits.  While the target is ceil(total / (grid -
+// rows)) (or is raised to kMinSplit), sum_r ceil(count_r / target) <= total /
+// target + rows <= grid.  When it is capped at kSplit, a row has ceil(count /
 // kSplit) splits, bounded through count <= L_b.
 inline size_t max_work(const ProbDev& p, int mode, int rows) {
   size_t capped;
@@ -394,7 +403,7 @@ inline size_t max_work(const ProbDev& p, int mode, int rows) {
     const size_t by_total = (size_t)((p.Tk + kSplit - 1) / kSplit) + (size_t)p.batch;  // sum over sequences
     capped = (size_t)(rows / max(1, p.batch)) * min(per_row * p.batch, by_total);
   }
-  return max(capped, (size_t)resident_grid() + (size_t)rows);
+  return max(capped, (size_t)resident_grid());
 }
 
 }  // namespace
@@ -422,17 +431,17 @@ hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void*
   const unsigned grid = (unsigned)resident_grid();
   const size_t lds = sizeof(int) * (size_t)(rows + 1);
   const unsigned cgrid = (unsigned)(rows * heads_per_row(mode));
-#define RTP_LAUNCH(TT, HH)                                                                                        \
+#define RTP_LAUNCH(TT, MM)                                                                                        \
   do {                                                                                                            \
-    hipLaunchKernelGGL((attn_decode_kernel<TT, HH>), dim3(grid), dim3(kThreads), lds, s, p, mode, rows,             \
-                       (const TT*)q, (const TT*)k, (const TT*)v, sl, pre, part);                                  \
-    hipLaunchKernelGGL((attn_decode_combine<TT, HH>), dim3(cgrid), dim3(kHeadDim), 0, s, p, mode, sl,             \
-                       (const int*)pre, part, (TT*)out, lse);                                                     \
+    hipLaunchKernelGGL((attn_decode_kernel<TT, MM>), dim3(grid), dim3(kThreads), lds, s, p, rows, (const TT*)q,     \
+                       (const TT*)k, (const TT*)v, sl, pre, part);                                                \
+    hipLaunchKernelGGL((attn_decode_combine<TT, MM>), dim3(cgrid), dim3(kHeadDim), 0, s, p, sl, (const int*)pre,  \
+                       part, (TT*)out, lse);                                                                      \
   } while (0)
   if (bf16) {
-    if (mode == 0) RTP_LAUNCH(bf16_t, 1); else RTP_LAUNCH(bf16_t, kMaxTileHeads);
+    if (mode == 0) RTP_LAUNCH(bf16_t, 0); else RTP_LAUNCH(bf16_t, 1);
   } else {
-    if (mode == 0) RTP_LAUNCH(float, 1); else RTP_LAUNCH(float, kMaxTileHeads);
+    if (mode == 0) RTP_LAUNCH(float, 0); else RTP_LAUNCH(float, 1);
   }
 #undef RTP_LAUNCH
   return hipGetLastError();
