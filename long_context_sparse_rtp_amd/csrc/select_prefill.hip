@@ -87,6 +87,7 @@ struct RowK {
   float a20, b20;   // K as float = fma(dot, a20, b20)
   float am, bm;     // mass = 2^fma(dot, am, bm)
   float lo_f, hi_f; // float range of K for the fast range test
+  float dA, dB;     // the same tests on the raw dot: K >= lo <=> d <= dA, K < hi <=> d > dB
   uint32_t lo;
   int sh, kind, pos;
   uint32_t kfix, dfix;
@@ -94,6 +95,23 @@ struct RowK {
 };
 
 __device__ __forceinline__ uint32_t key20(float u20) { return (uint32_t)__builtin_amdgcn_fmed3f(u20, 0.f, kMaxK); }
+
+// The largest dot product d with fmaf(d, a, b) >= t, for a < 0 (the map is then
+// non-increasing in d, so {d : fmaf(d, a, b) >= t} = {d <= result}): bisection
+// over the order-preserving integer image of the floats.  Comparing the raw dot
+// with it is exactly the float test on fmaf(d, a, b), one FMA cheaper per pair.
+__device__ __forceinline__ float dot_bound(float a, float b, float t) {
+  if (t == -INFINITY) return INFINITY;
+  if (t == INFINITY) return -INFINITY;
+  auto ord = [](float f) { const int i = __float_as_int(f); return (long long)(i ^ ((i >> 31) & 0x7FFFFFFF)); };
+  auto unord = [](long long v) { const int i = (int)v; return __int_as_float(i ^ ((i >> 31) & 0x7FFFFFFF)); };
+  long long lo = ord(-INFINITY), hi = ord(INFINITY);   // fmaf(-inf, a, b) = +inf >= t; fmaf(+inf, a, b) = -inf < t
+  while (hi - lo > 1) {
+    const long long mid = lo + (hi - lo) / 2;
+    if (fmaf(unord(mid), a, b) >= t) lo = mid; else hi = mid;
+  }
+  return unord(lo);
+}
 __device__ __forceinline__ uint32_t mass31(float dot, float am, float bm) {
   return (uint32_t)__builtin_amdgcn_exp2f(fmaf(dot, am, bm));
 }
@@ -304,6 +322,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       rk.lo_f = (c.lo == 0u) ? -INFINITY : (float)c.lo;
       const double hi = (double)c.lo + (double)(1ull << min(width, 32));
       rk.hi_f = (hi >= 4294967040.0) ? INFINITY : (float)hi;
+      rk.dA = dot_bound(rk.a20, rk.b20, rk.lo_f);
+      rk.dB = dot_bound(rk.a20, rk.b20, rk.hi_f);
     }
     {
       uint32_t* z = reinterpret_cast<uint32_t*>(un_s);
@@ -330,22 +350,20 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       });
     } else if (sweep == PH_REFINE && all_fast) {
       sweep_tiles([&](const f32x4& d, int t, bool check) {
-        float u20[4];
         bool inr[4];
         bool any = false;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
           const bool valid = !check || n <= rk.pos;
-          u20[i] = fmaf(d[i], rk.a20, rk.b20);
-          inr[i] = valid && u20[i] >= rk.lo_f && u20[i] < rk.hi_f;
+          inr[i] = valid && d[i] <= rk.dA && d[i] > rk.dB;
           any |= inr[i];
         }
         if (__builtin_amdgcn_ballot_w64(any)) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (inr[i]) {
-              const uint32_t dig = (key20(u20[i]) - rk.lo) >> rk.sh;
+              const uint32_t dig = (key20(fmaf(d[i], rk.a20, rk.b20)) - rk.lo) >> rk.sh;
               atomicAdd(&hm2[dig][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
             }
           }
@@ -359,9 +377,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
           const bool valid = !check || n <= rk.pos;
-          const float u20 = fmaf(d[i], rk.a20, rk.b20);
-          better += (valid && u20 < rk.lo_f) ? 1u : 0u;
-          inr[i] = valid && u20 >= rk.lo_f && u20 < rk.hi_f;
+          better += (valid && d[i] > rk.dA) ? 1u : 0u;
+          inr[i] = valid && d[i] <= rk.dA && d[i] > rk.dB;
           any |= inr[i];
         }
         if (__builtin_amdgcn_ballot_w64(any)) {
