@@ -23,8 +23,10 @@
 //     of one query column) is already the B-operand layout of O^T = V^T P^T,
 //     so P goes from registers into the second product without a shuffle;
 //     V is staged transposed in LDS (rows = head dims) for the A operand;
-//   - online softmax in the log2 domain, row sums kept per lane and reduced
-//     once at the end; masked tiles of a wave skip both products.
+//   - online softmax in the log2 domain with a reference that moves only when
+//     a row maximum exceeds it by more than 8; row sums from the matrix cores
+//     (an all-ones operand in the PV product); masked tiles of a wave skip
+//     both products.
 // LDS strides are padded so the fragment reads of one 8- or 16-lane phase hit
 // distinct banks.
 #include <type_traits>
