@@ -26,17 +26,25 @@
 //          the raw dot product, summed in 64-bit LDS integers (exact and
 //          order-independent: the result is deterministic);
 //   K    = floor(u * 2^16) clamped to 32 bits (K >> 16 == floor(u)).
-// Sweep 1 histograms the mass over kNB1 bins of floor(u) (the last one open-
-// ended); 16 threads per row scan it for the bin where the cumulative mass
-// reaches p * Z.  A refinement sweep histograms the mass over the next 8 bits
-// of K inside the chosen range and keeps the crossing digit; a collect sweep
-// then counts the tokens above the range and gathers the range's tokens.  If
-// they are at most 128, they are sorted by (score desc, position asc) and the
-// crossing token gives tau and tie_pos; otherwise the range is refined again.  Exact ties too large to collect switch the key
-// to the score's bit pattern and then to the position (general path,
-// degenerate inputs only).  The refine and collect sweeps touch LDS only for
-// the few tokens inside the range: a wave tests its whole tile first and
-// skips the update code when no lane has a token there.
+// A first sweep reads every 8th full tile (and the diagonal tiles) and
+// histograms the mass over kNB1 bins of floor(u) (the last one open-ended);
+// 16 threads per row scan it for the bin where the cumulative mass reaches p
+// times the sampled total (top-k: k times the sampled share of the keys), an
+// estimate of the crossing.  The windowed sweep
+// then histograms every key's mass over 254 bins of 1/256 octave centred on
+// that estimate, plus one bin above and one below the window; the scan finds
+// the crossing bin exactly.  A collect sweep counts the tokens above the bin
+// and gathers the bin's tokens; if they are at most kCap, they are sorted by
+// (score desc, position asc) (ranks: every candidate against all, 16 threads
+// per row) and the crossing token gives tau and tie_pos.  A crossing outside
+// the window, a loose reference (the best sampled key far below it) or a bin
+// with more than kCap tokens fall back to refinement sweeps that histogram
+// the mass over the next 8 bits of K inside the chosen range; exact ties too
+// large to collect switch the key to the score's bit pattern and then to the
+// position (degenerate inputs only).  The refine and collect sweeps compare
+// the raw dot product with per-row bounds (exactly the float tests on K) and
+// touch LDS only for the few tokens inside the range: a wave tests its whole
+// tile first and skips the update code when no lane has a token there.
 #include "common.h"
 #include "kernels.h"
 
@@ -50,11 +58,15 @@ constexpr int kRows = 16;
 constexpr int kNB1 = 256;                       // first-sweep bins
 constexpr float kBinsPerOctave = 16.f;          // kNB1 bins span 16 octaves
 constexpr int kNB2 = 256;                       // refinement digits (8 bits)
-constexpr int kCap = 128;
+constexpr int kCap = 192;
 constexpr float kMaxK = 4294967040.f;           // largest float below 2^32
 constexpr int kParts = kThreads / kRows;        // threads per row in the scans
 
-enum { PH_HIST1 = 0, PH_REFINE = 1, PH_COLLECT = 2, PH_DONE = 3 };
+// Sweeps in the order a row can need them; a workgroup runs the lowest phase any
+// of its rows is in.
+enum { PH_P0 = 0, PH_HIST1 = 1, PH_HISTW = 2, PH_REFINE = 3, PH_COLLECT = 4, PH_DONE = 5 };
+constexpr int kFineShift = 12;                  // window bins: 1/256 octave = 2^12 units of K
+constexpr int kSample = 8;                      // the first sweep reads every 8th full tile
 
 __device__ __forceinline__ uint32_t desc_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -77,6 +89,7 @@ struct RowCtl {
   int sh;                     // digit shift of the range
   int phase, kind;
   int pos;
+  int g0;                     // first fine bin (1/256 octave) of the window of the windowed sweep
   uint32_t cabove;            // tokens strictly better than the range (counted by the collect sweep)
   float tau;
   int tie, count;
@@ -88,6 +101,8 @@ struct RowK {
   float am, bm;     // mass = 2^fma(dot, am, bm)
   float lo_f, hi_f; // float range of K for the fast range test
   float dA, dB;     // the same tests on the raw dot: K >= lo <=> d <= dA, K < hi <=> d > dB
+  float a12, b12;   // fine bin coordinate (1/256 octave) = fma(dot, a12, b12) = K / 2^12 exactly
+  float c12;        // g0 - 1: window bin = clamp(coordinate - c12, 0, 255)
   uint32_t lo;
   int sh, kind, pos;
   uint32_t kfix, dfix;
@@ -149,6 +164,8 @@ constexpr size_t kRefineBytes = sizeof(unsigned long long) * kNB2 * kRows;
 constexpr size_t kCandBytes = sizeof(unsigned long long) * kRows * kCap;
 constexpr size_t kUnionBytes = (kHist1Bytes > kRefineBytes ? (kHist1Bytes > kCandBytes ? kHist1Bytes : kCandBytes)
                                                             : (kRefineBytes > kCandBytes ? kRefineBytes : kCandBytes));
+static_assert(kCap <= 256, "the sort's permutation is stored in bytes");
+static_assert(kCandBytes + kRows * kCap <= kUnionBytes, "candidates and their permutation share the sweep space");
 
 template <typename T, bool COUNT>
 __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
@@ -220,14 +237,15 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     c.lo = 0u; c.sh = 16; c.kind = 0; c.kfix = 0u; c.dfix = 0u;
     c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = c.pos + 1;
     c.target = 1.0;
+    c.g0 = 1;
     if (COUNT) {
       c.pval = 0.f;
       c.kval = max(top_k[b], 1);
-      c.phase = (c.kval <= c.pos) ? PH_HIST1 : PH_DONE;   // k >= pos + 1: every key
+      c.phase = (c.kval <= c.pos) ? PH_P0 : PH_DONE;      // k >= pos + 1: every key
     } else {
       c.pval = top_p[b];
       c.kval = 0;
-      c.phase = (c.pval < 1.f) ? PH_HIST1 : PH_DONE;     // p >= 1 (or NaN): every key
+      c.phase = (c.pval < 1.f) ? PH_P0 : PH_DONE;        // p >= 1 (or NaN): every key
     }
   }
   __syncthreads();
@@ -288,6 +306,26 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     }
     for (; t < ntile; t += kWaves) body(tile_dot(t), t, t >= nfull);
   };
+  // every kSample-th full tile (same prefetch scheme), then every diagonal tile
+  auto sweep_sample = [&](auto&& body) {
+    constexpr int kStride = kSample * kWaves;
+    int t = kSample * w;
+    if (t < nfull) {
+      IF a, bb;
+      load_full(a, t);
+      while (true) {
+        load_full(bb, t + kStride);
+        body(idx_dot_tile(a, qxf), t, false);
+        t += kStride;
+        if (t >= nfull) break;
+        load_full(a, t + kStride);
+        body(idx_dot_tile(bb, qxf), t, false);
+        t += kStride;
+        if (t >= nfull) break;
+      }
+    }
+    for (int td = nfull + w; td < ntile; td += kWaves) body(tile_dot(td), td, true);
+  };
 
   // thread (row, part) of the parallel scans
   const int srow = tid / kParts, spart = tid % kParts;
@@ -317,17 +355,23 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       rk.dfix = c.dfix;
       rk.pos = active ? c.pos : -1;
       const int width = (sweep == PH_REFINE) ? c.sh + 8 : c.sh;
-      // the float test of K's range is exact when both ends are multiples of 256 below 2^32
-      rk.fast = (c.kind == 0) && (width >= 8);
-      rk.lo_f = (c.lo == 0u) ? -INFINITY : (float)c.lo;
+      // the float test of K's range is exact when both ends are exact floats
       const double hi = (double)c.lo + (double)(1ull << min(width, 32));
+      const bool lo_exact = (double)(float)c.lo == (double)c.lo;
+      const bool hi_exact = hi >= 4294967040.0 || (double)(float)hi == hi;
+      rk.fast = (c.kind == 0) && lo_exact && hi_exact;
+      rk.lo_f = (c.lo == 0u) ? -INFINITY : (float)c.lo;
       rk.hi_f = (hi >= 4294967040.0) ? INFINITY : (float)hi;
       rk.dA = dot_bound(rk.a20, rk.b20, rk.lo_f);
       rk.dB = dot_bound(rk.a20, rk.b20, rk.hi_f);
+      rk.a12 = rk.a20 * (1.f / 4096.f);
+      rk.b12 = rk.b20 * (1.f / 4096.f);
+      rk.c12 = (float)(c.g0 - 1);
     }
     {
       uint32_t* z = reinterpret_cast<uint32_t*>(un_s);
-      const int nz = (int)(((sweep == PH_HIST1) ? kHist1Bytes : (sweep == PH_REFINE) ? kRefineBytes : 0) / 4);
+      const int nz = (int)(((sweep == PH_P0 || sweep == PH_HIST1 || sweep == PH_HISTW) ? kHist1Bytes
+                            : (sweep == PH_REFINE) ? kRefineBytes : 0) / 4);
       for (int e = tid; e < nz; e += kThreads) z[e] = 0u;
     }
     if (tid < kRows) { ccount_s[tid] = 0; cbetter_s[tid] = 0u; }
@@ -337,14 +381,32 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     const float a1 = rk.a20 * (1.f / 65536.f), b1 = rk.b20 * (1.f / 65536.f);
     uint32_t better = 0u;
 
-    if (sweep == PH_HIST1) {
+    // coarse histogram: bins of 1/16 octave below the reference, the last open-ended
+    auto hist_coarse = [&](const f32x4& d, int t, bool check) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * t + 4 * grp + i;
+        if (check && n > rk.pos) continue;
+        const float u = fmaf(d[i], a1, b1);
+        const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kNB1 - 1));
+        atomicAdd(&h1[bin][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+      }
+    };
+    if (sweep == PH_P0) {
+      sweep_sample(hist_coarse);
+    } else if (sweep == PH_HIST1) {
+      sweep_tiles(hist_coarse);
+    } else if (sweep == PH_HISTW) {
+      // window of 254 bins of 1/256 octave; bin 0 holds everything above it, bin 255 everything below.
+      // The coordinate is K / 2^12 exactly (a power-of-two scaling of the key's FMA) and
+      // subtracting the integer c12 from it is exact, so bin j holds K in [(g0+j-1) << 12, (g0+j) << 12).
       sweep_tiles([&](const f32x4& d, int t, bool check) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
           if (check && n > rk.pos) continue;
-          const float u = fmaf(d[i], a1, b1);
-          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kNB1 - 1));
+          const float u12 = fmaf(d[i], rk.a12, rk.b12);
+          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u12 - rk.c12, 0.f, 255.f);
           atomicAdd(&h1[bin][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
         }
       });
@@ -445,7 +507,99 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     // ---- per-row controller.  The histogram scans run on 16 threads per row:
     // part sums, then the part holding the crossing walks its bins.
     const bool act = ctl[srow].phase == sweep;
-    if (sweep == PH_HIST1) {
+    if (sweep == PH_P0) {
+      // estimate the crossing from the sample; the windowed sweep then bins finely
+      // around it.  A loose reference (best sampled key >= 8 octaves below it) or a
+      // crossing the scan does not find takes the full coarse sweep instead.
+      constexpr int PB = kNB1 / kParts;
+      unsigned long long sp = 0ull;
+      int first = kNB1;
+      if (act) {
+        for (int j = 0; j < PB; ++j) {
+          const unsigned long long hv = h1[spart * PB + j][srow];
+          if (first == kNB1 && hv != 0ull) first = spart * PB + j;
+          sp += hv;
+        }
+      }
+      psum_s[srow][spart] = sp;
+      pidx_s[srow][spart] = first;
+      __syncthreads();
+      if (act && spart == 0) ctl[srow].phase = PH_HIST1;   // default: the full coarse sweep
+      __syncthreads();
+      if (act) {
+        RowCtl& rc = ctl[srow];
+        unsigned long long Z = 0ull, pre = 0ull;
+        int blo = kNB1;
+        for (int q = 0; q < kParts; ++q) {
+          if (q < spart) pre += psum_s[srow][q];
+          Z += psum_s[srow][q];
+          blo = min(blo, pidx_s[srow][q]);
+        }
+        if (blo < kNB1 / 2 && Z != 0ull) {
+          // the sample holds a share Z / (pos + 1) of the keys: scale a count target by it
+          const double target = COUNT ? fmax((double)rc.kval * (double)Z / (double)(rc.pos + 1), 1.0)
+                                      : fmax((double)rc.pval * (double)Z, 1.0);
+          if ((double)pre < target && target <= (double)(pre + sp)) {
+            unsigned long long cm = pre;
+            int bstar = spart * PB + PB - 1;
+            for (int j = 0; j < PB; ++j) {
+              const unsigned long long hv = h1[spart * PB + j][srow];
+              if ((double)(cm + hv) >= target) { bstar = spart * PB + j; break; }
+              cm += hv;
+            }
+            // window of 254 fine bins (just under an octave) centred on the estimated bin
+            rc.g0 = max(1, bstar * 16 + 8 - 127);
+            rc.phase = PH_HISTW;
+          }
+        }
+      }
+    } else if (sweep == PH_HISTW) {
+      constexpr int PB = kNB1 / kParts;
+      unsigned long long sp = 0ull;
+      if (act) {
+        for (int j = 0; j < PB; ++j) sp += h1[spart * PB + j][srow];
+      }
+      psum_s[srow][spart] = sp;
+      __syncthreads();
+      if (act && spart == 0) ctl[srow].phase = PH_HIST1;   // default (the scan below always claims)
+      __syncthreads();
+      if (act) {
+        RowCtl& rc = ctl[srow];
+        unsigned long long Z = 0ull, pre = 0ull;
+        for (int q = 0; q < kParts; ++q) {
+          if (q < spart) pre += psum_s[srow][q];
+          Z += psum_s[srow][q];
+        }
+        const double target = COUNT ? (double)rc.kval : fmax((double)rc.pval * (double)Z, 1.0);
+        if ((double)pre < target && target <= (double)(pre + sp)) {
+          unsigned long long cm = pre;
+          int jstar = spart * PB + PB - 1;
+          for (int j = 0; j < PB; ++j) {
+            const unsigned long long hv = h1[spart * PB + j][srow];
+            if ((double)(cm + hv) >= target) { jstar = spart * PB + j; break; }
+            cm += hv;
+          }
+          rc.target = target;
+          rc.above = cm;
+          const int g0 = rc.g0;
+          if (jstar >= 1 && jstar <= 254) {        // inside the window: gather the bin's keys
+            rc.lo = (uint32_t)(g0 + jstar - 1) << kFineShift;
+            rc.sh = kFineShift;
+            rc.phase = PH_COLLECT;
+          } else if (jstar == 0) {                 // above the window: refine [0, g0 << 12)
+            const uint32_t span = ((uint32_t)g0 << kFineShift) - 1u;
+            const int wdt = 32 - __clz(span);
+            rc.lo = 0u;
+            rc.sh = max(wdt, 8) - 8;
+            rc.phase = PH_REFINE;
+          } else {                                 // below the window: refine the rest
+            rc.lo = (uint32_t)(g0 + 254) << kFineShift;
+            rc.sh = 24;
+            rc.phase = PH_REFINE;
+          }
+        }
+      }
+    } else if (sweep == PH_HIST1) {
       constexpr int PB = kNB1 / kParts;
       unsigned long long sp = 0ull;
       int first = kNB1;
@@ -549,48 +703,100 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         rc.phase = PH_COLLECT;
       }
     } else if (sweep == PH_COLLECT) {
-      if (act && spart == 0 && ccount_s[srow] > kCap) {
+      const int ncr = act ? ccount_s[srow] : 0;
+      const bool over = ncr > kCap;
+      if (over && spart == 0) {
         // too many tokens in the range: refine it further
         RowCtl& rc = ctl[srow];
         if (rc.sh >= 8) {
           rc.sh -= 8;
+        } else if (rc.sh > 0) {
+          rc.sh = 0;   // a narrower range: refine to single key values first (the digits cover a superset)
         } else if (rc.kind == 0) {
           rc.kind = 1; rc.kfix = rc.lo; rc.lo = 0u; rc.sh = 24;
         } else {
           rc.kind = 2; rc.dfix = rc.lo; rc.lo = 0u; rc.sh = 23;
         }
         rc.phase = PH_REFINE;
-      } else if (act && spart == 0) {
+      }
+      // Sort the candidates by (desc_key, position), both ascending, with ranks: the
+      // keys are distinct, so a candidate's rank is the number of smaller ones.  Each
+      // of the row's 16 threads ranks kCap / 16 of them against all, a few at a time,
+      // and records the permutation (candidate index by rank) in LDS.
+      constexpr int E = kCap / kParts;
+      constexpr int EC = 4;
+      const int nc = over ? 0 : ncr;
+      const unsigned long long* cd = cand + srow * kCap;
+      unsigned char* perm = un_s + kCandBytes + srow * kCap;
+#pragma unroll 1
+      for (int c0 = 0; c0 < E; c0 += EC) {
+        if (spart + c0 * kParts >= nc) break;
+        unsigned long long xv[EC];
+        int rank[EC];
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          const int a = spart + (c0 + e) * kParts;
+          xv[e] = (a < nc) ? cd[a] : ~0ull;
+          rank[e] = 0;
+        }
+        for (int jj = 0; jj < nc; ++jj) {
+          const unsigned long long v = cd[jj];
+#pragma unroll
+          for (int e = 0; e < EC; ++e) rank[e] += (v < xv[e]) ? 1 : 0;
+        }
+#pragma unroll
+        for (int e = 0; e < EC; ++e) {
+          const int a = spart + (c0 + e) * kParts;
+          if (a < nc) perm[rank[e]] = (unsigned char)a;
+        }
+      }
+      __syncthreads();
+      // The crossing in sorted order: the first candidate at which the mass above
+      // the range plus the candidates' cumulative mass reaches the target (the last
+      // candidate if none does).  Thread q sums ranks [q E, q E + E); the part where
+      // the cumulative mass crosses walks its ranks.
+      const float am = kLog2e * 0.25f, bm = 31.f - ctl[srow].top * kLog2e;
+      auto cmass = [&](int k) -> uint32_t {
+        return COUNT ? 1u : mass31(undesc_key((uint32_t)(cd[perm[k]] >> 32)) * 4.f, am, bm);
+      };
+      const int a0 = spart * E;
+      unsigned long long sp = 0ull;
+      for (int k = a0; k < min(a0 + E, nc); ++k) sp += cmass(k);
+      psum_s[srow][spart] = sp;
+      __syncthreads();
+      if (act && !over) {
         RowCtl& rc = ctl[srow];
-        rc.cabove = cbetter_s[srow];
-        const int tidr = srow;
-        const int nc = min(ccount_s[tidr], kCap);
-        unsigned long long* cd = cand + tidr * kCap;
-        for (int a = 1; a < nc; ++a) {  // insertion sort: (desc_key asc, position asc)
-          const unsigned long long x = cd[a];
-          int bb = a - 1;
-          while (bb >= 0 && cd[bb] > x) { cd[bb + 1] = cd[bb]; --bb; }
-          cd[bb + 1] = x;
+        unsigned long long pre = rc.above, tot = rc.above;
+        for (int q = 0; q < kParts; ++q) {
+          if (q < spart) pre += psum_s[srow][q];
+          tot += psum_s[srow][q];
         }
-        unsigned long long cm = rc.above;
-        int jstar = nc - 1;
-        const float am = kLog2e * 0.25f, bm = 31.f - rc.top * kLog2e;
-        for (int a = 0; a < nc; ++a) {
-          const float s = undesc_key((uint32_t)(cd[a] >> 32));
-          const uint32_t mf = COUNT ? 1u : mass31(s * 4.f, am, bm);
-          if ((double)(cm + mf) >= rc.target) { jstar = a; break; }
-          cm += mf;
-        }
-        if (nc > 0) {
-          rc.tau = undesc_key((uint32_t)(cd[jstar] >> 32));
-          rc.tie = (int)(uint32_t)(cd[jstar] & 0xFFFFFFFFull);
-          rc.count = (int)rc.cabove + jstar + 1;
+        const double target = rc.target;
+        const bool crosses = (double)tot >= target;
+        const bool mine = nc > 0 && (crosses ? ((spart == 0 && (double)pre >= target) ||
+                                                ((double)pre < target && target <= (double)(pre + sp)))
+                                             : (a0 <= nc - 1 && nc - 1 < a0 + E));
+        if (mine) {
+          int js = min(a0 + E, nc) - 1;
+          unsigned long long cm = pre;
+          for (int k = a0; k < min(a0 + E, nc); ++k) {
+            const uint32_t m = cmass(k);
+            if ((double)(cm + m) >= target) { js = k; break; }
+            cm += m;
+          }
+          const unsigned long long xs = cd[perm[js]];
+          rc.tau = undesc_key((uint32_t)(xs >> 32));
+          rc.tie = (int)(uint32_t)(xs & 0xFFFFFFFFull);
+          rc.count = (int)cbetter_s[srow] + js + 1;
           // every token scoring exactly tau is a candidate unless the position key was needed;
           // if none of them is left out, the set is simply {s >= tau}
-          const bool excluded = (jstar + 1 < nc) && ((uint32_t)(cd[jstar + 1] >> 32) == (uint32_t)(cd[jstar] >> 32));
+          const bool excluded = (js + 1 < nc) && ((uint32_t)(cd[perm[js + 1]] >> 32) == (uint32_t)(xs >> 32));
           if (rc.kind < 2 && !excluded) rc.tie = 0x7FFFFFFF;
         }
-        rc.phase = PH_DONE;
+        if (spart == 0) {
+          rc.cabove = cbetter_s[srow];
+          rc.phase = PH_DONE;
+        }
       }
     }
     __syncthreads();
