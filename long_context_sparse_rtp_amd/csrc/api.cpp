@@ -76,18 +76,23 @@ rtp_status check_problem(const rtp_problem* pr, ProbDev* out) {
     p.n_local = 0;
     for (int h = 0; h < p.Hq; ++h)
       if (!is_ret[h]) p.local_heads[p.n_local++] = h;
-    p.n_ltiles = 0;
-    for (int i = 0; i < p.n_local; ++i) {
-      const int t = p.n_ltiles - 1;
-      if (t >= 0 && p.ltile_cnt[t] < rtp::attn_decode_tile_heads() &&
-          rtp::kv_of(p, p.local_heads[p.ltile_start[t]]) == rtp::kv_of(p, p.local_heads[i])) {
-        ++p.ltile_cnt[t];
-      } else {
-        p.ltile_start[p.n_ltiles] = i;
-        p.ltile_cnt[p.n_ltiles] = 1;
-        ++p.n_ltiles;
+    // local heads in runs of one KV group, at most `cap` per tile (heads ascend, so a
+    // group's local heads are consecutive)
+    auto tiles = [&](int cap, int& n, int* start, int* cnt) {
+      n = 0;
+      for (int i = 0; i < p.n_local; ++i) {
+        const int t = n - 1;
+        if (t >= 0 && cnt[t] < cap && rtp::kv_of(p, p.local_heads[start[t]]) == rtp::kv_of(p, p.local_heads[i])) {
+          ++cnt[t];
+        } else {
+          start[n] = i;
+          cnt[n] = 1;
+          ++n;
+        }
       }
-    }
+    };
+    tiles(rtp::attn_decode_tile_heads(), p.n_ltiles, p.ltile_start, p.ltile_cnt);
+    tiles(rtp::attn_decode_group_heads(), p.n_gtiles, p.gtile_start, p.gtile_cnt);
   }
   return RTP_OK;
 }

@@ -375,6 +375,204 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, const
   if (lse && tid == 0) lse[(size_t)head * p.Tq + ri.qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
 }
 
+// ---- bfloat16 local heads: a KV group's heads together on the matrix cores.
+// A row is (tile of up to kGH local heads of one KV group, sequence); its key
+// list (sinks, then window) is cut into chunks of 64 keys and a row's chunks are
+// dealt round-robin to nsplit one-wave workgroups.  Per chunk the wave
+//   - scores 64 keys against the tile's heads with 16x16x32 MFMAs (A = K rows
+//     read straight from HBM in operand layout, B = the heads' queries; each K
+//     row is read once for every head of the group),
+//   - updates every head's running max and sum (16-lane groups of the output
+//     layout hold one head's scores) and stores the chunk's weights in LDS,
+//   - accumulates P V on the vector ALUs: lane (dims 8c..8c+7, heads 2j, 2j+1)
+//     reads each V row segment once and the two weights from LDS.
+// Splits write (max, sum, o) partials that a second kernel merges by
+// log-sum-exp, as for the other decode rows.
+constexpr int kGH = 8;           // local heads per tile
+constexpr int kGChunk = 64;      // keys per chunk
+constexpr int kGMaxSplit = 64;   // splits per row at most
+constexpr int kGTargetWaves = 2048;
+
+__global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, const bf16_t* __restrict__ q,
+                                                       const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                       float* __restrict__ part) {
+  const int split = blockIdx.x, row = blockIdx.y;
+  const int b = row % p.batch, tile = row / p.batch;
+  const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
+  const int L = p.cu_k[b + 1] - p.cu_k[b];
+  const int W = min(p.window, L);
+  const int ns = min(p.n_sink, L - W);
+  const int count = ns + W;
+  const int nchunk = (count + kGChunk - 1) / kGChunk;
+  if (split >= min(nsplit, nchunk)) return;
+  const int nh = p.gtile_cnt[tile];
+  const int hl0 = p.gtile_start[tile];
+  const int kvg = kv_of(p, p.local_heads[hl0]);
+  const int qrow = p.cu_q[b];
+  const size_t kstride = (size_t)p.Hkv * kHeadDim;
+  const bf16_t* kb = k + ((size_t)key_row0(p, b) * p.Hkv + kvg) * kHeadDim;
+  const bf16_t* vb = v + ((size_t)key_row0(p, b) * p.Hkv + kvg) * kHeadDim;
+  const float qscale = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
+
+  __shared__ int slot_s[kGChunk];
+  __shared__ __attribute__((aligned(16))) float p_s[kGChunk][kGH];
+  __shared__ float scale_s[kGH];
+
+  // B operand: column = head slot col (zero past the tile), k = dims 32 kc + 8 g .. + 8
+  FragBF16 qf[4];
+#pragma unroll
+  for (int kc = 0; kc < 4; ++kc) {
+    if (col < nh) {
+      load_frag(qf[kc], q + ((size_t)qrow * p.Hq + p.local_heads[hl0 + col]) * kHeadDim + 32 * kc + 8 * g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kc].v[e] = (__bf16)0.f;
+    }
+  }
+  float m_run = -INFINITY, l_run = 0.f;   // head col (output layout)
+  const int dc = lane & 15, hg = lane >> 4;
+  float o[2][8];                           // heads 2 hg, 2 hg + 1; dims 8 dc .. + 8
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[u][e] = 0.f;
+
+  for (int c = split; c < nchunk; c += nsplit) {
+    const int j0 = c * kGChunk;
+    const int nv = min(kGChunk, count - j0);   // valid keys of the chunk (>= 1)
+    slot_s[lane] = key_slot(p, local_token(p, L, j0 + min(lane, nv - 1)));
+    __syncthreads();
+    // scores: tile t holds keys 16 t .. 16 t + 15 (rows) x heads (columns)
+    FragBF16 kf[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16_t* kr = kb + (size_t)slot_s[16 * t + col] * kstride + 8 * g;
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) load_frag(kf[t][kc], kr + 32 * kc);
+    }
+    f32x4 sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < 4; ++kc) sc[t] = mma_k32(kf[t][kc], qf[kc], sc[t]);
+    }
+    // lane (col, g) holds keys 16 t + 4 g + i of head col
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 16 * t + 4 * g + i;
+        sc[t][i] = (j < nv) ? sc[t][i] * qscale : -INFINITY;
+        mx = fmaxf(mx, sc[t][i]);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m_run, mx);
+    const float rs = __builtin_amdgcn_exp2f(m_run - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float pe = __builtin_amdgcn_exp2f(sc[t][i] - mn);
+        ls += pe;
+        if (col < kGH) p_s[16 * t + 4 * g + i][col] = pe;
+      }
+    ls += __shfl_xor(ls, 16);
+    ls += __shfl_xor(ls, 32);
+    l_run = l_run * rs + ls;
+    m_run = mn;
+    if (g == 0 && col < kGH) scale_s[col] = rs;
+    __syncthreads();
+    // P V: lane (dc, hg) over the chunk's valid keys, 8 V segments in flight
+    {
+      const float r0 = scale_s[2 * hg], r1 = scale_s[2 * hg + 1];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { o[0][e] *= r0; o[1][e] *= r1; }
+    }
+    for (int jb = 0; jb < nv; jb += 8) {
+      uint4 vr[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int j = min(jb + u, nv - 1);
+        vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)slot_s[j] * kstride + 8 * dc);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (jb + u < nv) {
+          const float2 pw = *reinterpret_cast<const float2*>(&p_s[jb + u][2 * hg]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wd = (&vr[u].x)[e >> 1];
+            const float ve = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+            o[0][e] = fmaf(pw.x, ve, o[0][e]);
+            o[1][e] = fmaf(pw.y, ve, o[1][e]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+  float* rec0 = part + ((size_t)row * nsplit + split) * kGH * kPart;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int h = 2 * hg + u;
+    if (h < nh) {
+      float* rec = rec0 + (size_t)h * kPart + 2 + 8 * dc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rec[e] = o[u][e];
+    }
+  }
+  if (g == 0 && col < nh) {
+    rec0[(size_t)col * kPart] = m_run;
+    rec0[(size_t)col * kPart + 1] = l_run;
+  }
+}
+
+// Log-sum-exp merge of one (row, head)'s split partials; one thread per head dim.
+__global__ __launch_bounds__(kHeadDim) void local_decode_gqa_combine(ProbDev p, int nsplit,
+                                                                     const float* __restrict__ part,
+                                                                     bf16_t* __restrict__ out,
+                                                                     float* __restrict__ lse) {
+  const int row = blockIdx.x / kGH, h = blockIdx.x % kGH;
+  const int b = row % p.batch, tile = row / p.batch;
+  if (h >= p.gtile_cnt[tile]) return;
+  const int tid = threadIdx.x;
+  const int head = p.local_heads[p.gtile_start[tile] + h];
+  const int L = p.cu_k[b + 1] - p.cu_k[b];
+  const int W = min(p.window, L);
+  const int count = min(p.n_sink, L - W) + W;
+  const int S = min(nsplit, (count + kGChunk - 1) / kGChunk);
+  const int qrow = p.cu_q[b];
+  const float* rec0 = part + (size_t)row * nsplit * kGH * kPart + (size_t)h * kPart;
+  const size_t sstride = (size_t)kGH * kPart;
+  float M = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, rec0[sp * sstride]);
+  float acc = 0.f, sum = 0.f;
+  for (int sp = 0; sp < S; ++sp) {
+    const float* r = rec0 + sp * sstride;
+    const float wv = __builtin_amdgcn_exp2f(r[0] - M);
+    sum = fmaf(r[1], wv, sum);
+    acc = fmaf(r[2 + tid], wv, acc);
+  }
+  out[((size_t)qrow * p.Hq + head) * kHeadDim + tid] = Elem<bf16_t>::from_f(acc / sum);
+  if (lse && tid == 0) lse[(size_t)head * p.Tq + qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
+}
+
+// splits per row of the bfloat16 local path: about kGTargetWaves waves in all
+inline int gqa_nsplit(const ProbDev& p) {
+  const int rows = p.n_gtiles * p.batch;
+  const int cnt = min(p.window, p.max_k) + p.n_sink;
+  const int nchunk = max(1, (cnt + kGChunk - 1) / kGChunk);
+  const int want = (kGTargetWaves + max(rows, 1) - 1) / max(rows, 1);
+  return max(1, min(min(nchunk, kGMaxSplit), want));
+}
+inline size_t ws_gqa(const ProbDev& p) {
+  return sizeof(float) * (size_t)p.n_gtiles * p.batch * gqa_nsplit(p) * kGH * kPart;
+}
+
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline int rows_of(const ProbDev& p, int mode) { return ((mode == 0) ? p.R : p.n_ltiles) * p.batch; }
@@ -410,11 +608,14 @@ inline size_t max_work(const ProbDev& p, int mode, int rows) {
 
 int attn_decode_max_rows() { return kMaxRowsLds - 1; }
 int attn_decode_tile_heads() { return kMaxTileHeads; }
+int attn_decode_group_heads() { return kGH; }
 
 size_t ws_attn_decode(const ProbDev& p, int mode) {
   const int rows = rows_of(p, mode);
-  return align256(sizeof(int) * (size_t)(rows + 1)) +
-         sizeof(float) * max_work(p, mode, rows) * heads_per_row(mode) * kPart;
+  const size_t split_list = align256(sizeof(int) * (size_t)(rows + 1)) +
+                            sizeof(float) * max_work(p, mode, rows) * heads_per_row(mode) * kPart;
+  // local heads: float32 takes the split-list kernel, bfloat16 the group kernel
+  return mode == 1 ? max(split_list, ws_gqa(p)) : split_list;
 }
 
 hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
@@ -422,6 +623,16 @@ hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void*
                               hipStream_t s) {
   const int rows = rows_of(p, mode);
   if (rows == 0) return hipSuccess;
+  if (mode == 1 && bf16) {
+    const int grows = p.n_gtiles * p.batch;
+    const int nsplit = gqa_nsplit(p);
+    float* part = (float*)ws;
+    hipLaunchKernelGGL(local_decode_gqa, dim3(nsplit, grows), dim3(64), 0, s, p, nsplit, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, part);
+    hipLaunchKernelGGL(local_decode_gqa_combine, dim3(grows * kGH), dim3(kHeadDim), 0, s, p, nsplit,
+                       (const float*)part, (bf16_t*)out, lse);
+    return hipGetLastError();
+  }
   rtp_selection sl = {};
   if (sel) sl = *sel;
   int* pre = (int*)ws;

@@ -24,6 +24,11 @@ struct ProbDev {
   int n_ltiles;
   int ltile_start[RTP_MAX_HEADS];
   int ltile_cnt[RTP_MAX_HEADS];
+  // the same grouping with up to attn_decode_group_heads() heads per tile (the
+  // bfloat16 decode path scores a tile's heads together on the matrix cores)
+  int n_gtiles;
+  int gtile_start[RTP_MAX_HEADS];
+  int gtile_cnt[RTP_MAX_HEADS];
 };
 
 __host__ __device__ inline int kv_of(const ProbDev& p, int h) { return (h * p.Hkv) / p.Hq; }
@@ -47,6 +52,7 @@ size_t ws_select_prefill(const ProbDev& p);
 size_t ws_attn_decode(const ProbDev& p, int mode);  // mode 0: retrieval heads, 1: local heads
 int attn_decode_max_rows();   // (head, sequence) rows one decode attention call accepts
 int attn_decode_tile_heads(); // local heads of one KV group handled together in decode
+int attn_decode_group_heads(); // local heads of one KV group per tile of the bfloat16 decode path
 
 hipError_t launch_index_keys(const ProbDev& p, bool bf16, const void* k_pre, const float* w_k,
                              void* k_idx, hipStream_t s);

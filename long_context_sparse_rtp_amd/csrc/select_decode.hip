@@ -24,15 +24,17 @@
 //     j = A_u - a(s) counts down from the bin A_u of its own maximum, and a
 //     token's mass is 38-bit fixed point of 2^(s log2 e - (A_u + 1) / 128).
 //     Mass and count share one 64-bit LDS integer per bin (count << 51), so
-//     one atomic per token keeps the sums exact and order-independent.
-//  2. collect: every unit merges the row's unit histograms (unit u shifted by
-//     A - A_u bins and scaled by 2^((A_u - A) / 128) in float64, in a fixed
-//     order, so all workgroups of the row reach bit-identical sums), finds the
-//     row bin where the cumulative mass reaches p * Z, counts its own tokens
-//     above that bin and stores its tokens inside the bin as candidates.
+//     one atomic per token keeps the sums exact and order-independent.  The
+//     fine bins are stored, and so are coarse bins of 16 absolute bins each.
+//  2. collect: every unit finds the row's crossing bin from the units'
+//     histograms (unit u's sums scaled by 2^((A_u - A) / 128) in float64, in
+//     a fixed order, so all workgroups of the row reach bit-identical sums):
+//     first the coarse bin where the cumulative mass reaches p * Z, then the
+//     fine bin inside it.  It then counts its own tokens above that bin and
+//     stores its tokens inside the bin as candidates.
 //  3. emit: every unit ranks the row's candidates by (score desc, position
 //     asc), walks their masses to the crossing token (tau, tie_pos, count),
-//     derives its output offset from the per-unit counts and writes its
+//     derives its first output slot from the per-unit counts and writes its
 //     members in ascending order.  A crossing bin too crowded for the
 //     candidate lists (mass piled on near-identical scores) is resolved from
 //     the row's stored scores, with radix digits of the score's bit pattern
@@ -48,9 +50,9 @@ constexpr int kThreads = 256;
 constexpr int kChunk = 4096;                  // keys per unit
 constexpr int kPer = kChunk / kThreads;       // keys per thread
 constexpr int kNB = 4096;                     // bins per unit / row histogram
-constexpr int kBinsPerPass = 2048;            // row bins merged per pass (8 per thread)
-constexpr int kCapUnit = 1024;                // candidates stored per unit
+constexpr int kNC = kNB / 16 + 1;             // coarse bins per unit (16 absolute bins each)
 constexpr int kCap = 4096;                    // candidates per row (ranked in LDS)
+constexpr int kCapUnit = 1024;                // candidates stored per unit
 constexpr int kMaxUnits = 1024;               // units per row (4M keys)
 constexpr float kBinScale = 128.f * kLog2e;   // bins per unit of score
 constexpr int kCountShift = 51;
@@ -60,31 +62,30 @@ struct UnitMeta {
   int A;                      // absolute bin of the unit maximum
   int used;                   // highest non-empty unit bin (-1: empty unit)
   unsigned long long Z;       // sum of the unit's fixed-point masses
+  int cused;                  // highest non-empty coarse bin
 };
+enum { ROW_NORMAL = 0, ROW_ALL = 1, ROW_EMPTY = 2 };
 struct UnitCnt {
   uint32_t above;             // unit tokens in row bins before the crossing bin
   uint32_t inbin;             // unit tokens in the crossing bin
 };
-enum { ROW_NORMAL = 0, ROW_ALL = 1, ROW_EMPTY = 2 };
 struct RowState {
-  double above;               // merged mass of the row bins before the crossing bin
-  double target;              // p * Z
+  double above;               // mass of the row bins before the crossing bin
+  double target;              // p * Z (top-k: k)
   int mode;
-  int A;
-  int jstar;
+  int A, Ap;                  // row reference bin, and A | 15 (the row bin grid J = Ap - a)
+  int jstar;                  // crossing row bin
   uint32_t cabove;            // tokens before the crossing bin
   uint32_t bincnt;            // tokens in the crossing bin
-  int count_mode;             // top-k: every token weighs 1 and the target is k
 };
-
 struct DecodeWs {
   float* scores;               // [R * Tk]
   UnitMeta* meta;              // [nslots]
   unsigned long long* hist;    // [nslots * kNB]
+  unsigned long long* chist;   // [nslots * kNC]: 16 absolute bins per coarse bin
   UnitCnt* ucnt;               // [nslots]
-  double* fu;                  // [nslots]: 2^((A_u - A) / 128) of the row merge
   unsigned long long* cand;    // [nslots * kCapUnit]: (desc_key << 32) | position
-  RowState* rows;              // [nrows]
+  RowState* rows;              // [R * batch]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -95,20 +96,20 @@ __host__ __device__ inline int64_t slots_per_r(const ProbDev& p) { return p.Tk /
 
 inline size_t ws_layout(const ProbDev& p, void* base, DecodeWs* w) {
   const int64_t nslots = (int64_t)p.R * slots_per_r(p);
-  const int64_t nrows = (int64_t)p.R * p.batch;
   char* b = (char*)base;
   size_t o = 0;
   auto take = [&](size_t bytes) { char* q = b ? b + o : nullptr; o = align256(o + bytes); return q; };
   char* s = take(sizeof(float) * (size_t)p.R * p.Tk);
   char* m = take(sizeof(UnitMeta) * nslots);
   char* h = take(sizeof(unsigned long long) * nslots * kNB);
+  char* ch = take(sizeof(unsigned long long) * nslots * kNC);
   char* uc = take(sizeof(UnitCnt) * nslots);
-  char* fu = take(sizeof(double) * nslots);
   char* cd = take(sizeof(unsigned long long) * nslots * kCapUnit);
-  char* rs = take(sizeof(RowState) * nrows);
+  char* ro = take(sizeof(RowState) * (size_t)p.R * p.batch);
   if (w) {
     w->scores = (float*)s; w->meta = (UnitMeta*)m; w->hist = (unsigned long long*)h;
-    w->ucnt = (UnitCnt*)uc; w->fu = (double*)fu; w->cand = (unsigned long long*)cd; w->rows = (RowState*)rs;
+    w->chist = (unsigned long long*)ch; w->ucnt = (UnitCnt*)uc; w->cand = (unsigned long long*)cd;
+    w->rows = (RowState*)ro;
   }
   return o;
 }
@@ -217,6 +218,27 @@ __device__ double block_exscan_f64(double x, double* tmp, double& total) {
   double off = 0.0;
   for (int w = 0; w < wid; ++w) off += tmp[w];
   total = ((tmp[0] + tmp[1]) + tmp[2]) + tmp[3];
+  __syncthreads();
+  return off + (inc - x);
+}
+
+// the same with NW waves (fixed order)
+template <int NW>
+__device__ double block_exscan_f64_n(double x, double* tmp, double& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  double inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const double y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[wid] = inc;
+  __syncthreads();
+  double off = 0.0;
+  for (int w = 0; w < wid; ++w) off += tmp[w];
+  total = 0.0;
+  for (int w = 0; w < NW; ++w) total += tmp[w];
   __syncthreads();
   return off + (inc - x);
 }
@@ -382,26 +404,91 @@ __global__ __launch_bounds__(kThreads) void sel_dec_score(ProbDev p, const T* __
   used = block_max<int>(used, red_i);   // its barriers also order the histogram atomics before the copy
   unsigned long long* hg = ws.hist + slot * kNB;
   for (int e = tid; e <= used; e += kThreads) hg[e] = hist_s[e];
+  // coarse bins on the absolute grid: coarse bin cj holds the absolute bins a with
+  // a >> 4 == (A_u >> 4) - cj, i.e. unit bins A_u - a
+  const int cused = (A_u >> 4) - ((A_u - used) >> 4);
+  for (int cj = tid; cj <= cused; cj += kThreads) {
+    const int a0 = ((A_u >> 4) - cj) * 16;
+    const int jlo = max(A_u - a0 - 15, 0), jhi = min(A_u - a0, used);
+    unsigned long long acc = 0ull;
+    for (int j = jlo; j <= jhi; ++j) acc += hist_s[j];
+    ws.chist[slot * kNC + cj] = acc;
+  }
   if (tid == 0) {
     UnitMeta mt;
     mt.A = A_u;
     mt.used = empty ? -1 : used;
     mt.Z = Z;
+    mt.cused = empty ? -1 : cused;
     ws.meta[slot] = mt;
   }
 }
 
-// Row merge shared by the collect and emit kernels: reference bin A and the
-// per-unit scale factors (identical in every workgroup of the row).
-struct Merge {
-  int A;
-  double Z;
-};
-__device__ Merge row_merge(const DecodeWs& ws, const RowGeom& g, int* A_s, int* used_s, double* f_s, int* itmp,
-                           double* dtmp) {
-  const int tid = threadIdx.x;
-  int amax = -2147483647 - 1;
+// ======================================================================= 2. collect
+// Every unit finds the row's crossing bin (the same in every workgroup of the
+// row: fixed-order sums of the same data), then counts its own tokens above
+// it and stores its tokens inside it as candidates.  Row bins sit on the grid
+// J = Ap - a(s) with Ap = A | 15, A the highest unit bin, so that 16 row bins
+// form one coarse bin of the units' coarse histograms; the coarse crossing
+// is found first (one coarse bin per thread), then the fine bins inside it.
+// The last row bin (coarse and fine) is open-ended: its count is the row's
+// remainder and its mass what the others leave of Z.
+constexpr int kRowCoarse = kNB / 16;   // 256: one per thread
+static_assert(kRowCoarse == kThreads, "one coarse bin per thread");
+
+__device__ __forceinline__ double bin_mass(unsigned long long e, double f, bool cmode) {
+  return cmode ? (double)(uint32_t)(e >> kCountShift) : (double)(e & kMassMask) * f;
+}
+
+__global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const float* __restrict__ top_p,
+                                                            const int32_t* __restrict__ top_k, rtp_selection sel,
+                                                            DecodeWs ws) {
+  const RowGeom g = row_geom(p, blockIdx.y);
+  const int c = blockIdx.x;
+  if (c >= g.U || g.U > kMaxUnits) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const bool cmode = top_k != nullptr;
+  const int kk = cmode ? max(top_k[g.b], 1) : 0;
+  const float pp = cmode ? 0.f : top_p[g.b];
+  if (g.L == 0 || (cmode ? kk >= g.L : !(pp < 1.f))) {   // empty row; every key (p >= 1 or NaN; k >= L)
+    if (c == 0 && tid == 0) {
+      const bool empty = g.L == 0;
+      const size_t ro = (size_t)g.r * p.Tq + g.qrow;
+      sel.count[ro] = empty ? 0 : g.L;
+      if (sel.tau) sel.tau[ro] = empty ? INFINITY : -INFINITY;
+      if (sel.tie_pos) sel.tie_pos[ro] = 0x7FFFFFFF;
+      RowState rs = {};
+      rs.mode = empty ? ROW_EMPTY : ROW_ALL;
+      ws.rows[g.row] = rs;
+    }
+    return;
+  }
+  // this unit's scores, requested first so the loads overlap the merge
+  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
+  const int n0 = c * kChunk + tid;
+  float s[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    s[j] = (n < g.L) ? sb[n] : 0.f;
+  }
+
+  __shared__ int A_s[kMaxUnits];
+  __shared__ int used_s[kMaxUnits];
+  __shared__ int cused_s[kMaxUnits];
+  __shared__ double f_s[kMaxUnits];
+  __shared__ double fm_s[kThreads / 64][16];
+  __shared__ uint32_t fc_s[kThreads / 64][16];
+  __shared__ double dtmp[kThreads / 64];
+  __shared__ int itmp[kThreads / 64];
+  __shared__ uint32_t utmp[kThreads / 64];
+  __shared__ int cstar_s, clast_s, jstar_s, nc_s;
+  __shared__ double cab_m_s, cbin_m_s, above_s;
+  __shared__ uint32_t cab_c_s, cbin_c_s, cabove_s, bincnt_s;
+
+  // ---- merge: reference bin A and per-unit scales 2^((A_u - A) / 128)
   constexpr int PU = kMaxUnits / kThreads;
+  int amax = -2147483647 - 1;
   unsigned long long zu[PU];
 #pragma unroll
   for (int t = 0; t < PU; ++t) {
@@ -411,160 +498,129 @@ __device__ Merge row_merge(const DecodeWs& ws, const RowGeom& g, int* A_s, int* 
       const UnitMeta mt = ws.meta[g.slot0 + u];
       A_s[u] = mt.A;
       used_s[u] = mt.used;
+      cused_s[u] = mt.cused;
       zu[t] = mt.Z;
       if (mt.used >= 0) amax = max(amax, mt.A);
     }
   }
-  Merge m;
-  m.A = block_max<int>(amax, itmp);
+  const int A = block_max<int>(amax, itmp);
+  const int Ap = A | 15;
   double zl = 0.0;
 #pragma unroll
   for (int t = 0; t < PU; ++t) {
     const int u = tid + t * kThreads;
     if (u < g.U) {
-      const double f = (used_s[u] >= 0) ? unit_scale(A_s[u], m.A) : 0.0;
+      const double f = (used_s[u] >= 0) ? unit_scale(A_s[u], A) : 0.0;
       f_s[u] = f;
       zl += (double)zu[t] * f;
     }
   }
-  m.Z = block_sum_f64(zl, dtmp);   // its barriers also publish f_s
-  return m;
-}
+  double Z;
+  (void)block_exscan_f64_n<kThreads / 64>(zl, dtmp, Z);   // its barriers also publish f_s
+  const double target = cmode ? (double)kk : fmax((double)pp * Z, 1.0);
 
-// ======================================================================= 2. collect
-__global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const float* __restrict__ top_p,
-                                                            const int32_t* __restrict__ top_k, DecodeWs ws) {
-  const RowGeom g = row_geom(p, blockIdx.y);
-  const int c = blockIdx.x;
-  if (c >= g.U || g.U > kMaxUnits) return;
-  const int tid = threadIdx.x;
-  const int64_t slot = g.slot0 + c;
-  const bool count_mode = top_k != nullptr;
-  const int kk = count_mode ? max(top_k[g.b], 1) : 0;
-  const float pp = count_mode ? 0.f : top_p[g.b];
-
-  // nothing to choose: empty row, or every key (p >= 1 or NaN; k >= L)
-  if (g.L == 0 || (count_mode ? kk >= g.L : !(pp < 1.f))) {
-    if (c == 0 && tid == 0) {
-      RowState rs = {};
-      rs.mode = (g.L == 0) ? ROW_EMPTY : ROW_ALL;
-      ws.rows[g.row] = rs;
-    }
-    return;
-  }
-
-  // this unit's scores, requested before the merge so the loads overlap it
-  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
-  const int n0 = c * kChunk + tid;
-  float s[kPer];
+  // ---- coarse row bin tid: unit u's coarse bin tid - ((Ap >> 4) - (A_u >> 4)), eight units' loads at a time
+  double cm = 0.0;
+  uint32_t cc = 0u;
+  if (tid < kRowCoarse - 1) {
+    for (int u0 = 0; u0 < g.U; u0 += 8) {
+      unsigned long long e[8];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int n = n0 + j * kThreads;
-    s[j] = (n < g.L) ? sb[n] : -INFINITY;
-  }
-
-  __shared__ int A_s[kMaxUnits];
-  __shared__ int used_s[kMaxUnits];
-  __shared__ double f_s[kMaxUnits];
-  __shared__ double dtmp[kThreads / 64];
-  __shared__ int itmp[kThreads / 64];
-  __shared__ uint32_t utmp[kThreads / 64];
-  __shared__ int jstar_s, lastne_s;
-  __shared__ double above_s;
-  __shared__ uint32_t cabove_s, bincnt_s;
-
-  const Merge mg = row_merge(ws, g, A_s, used_s, f_s, itmp, dtmp);
-  const int A = mg.A;
-  const double target = count_mode ? (double)kk : fmax((double)pp * mg.Z, 1.0);
-
-  // ---- row bins, kBinsPerPass at a time (8 consecutive per thread): the first bin
-  // whose cumulative mass reaches the target.  A bin's mass above is computed by
-  // exactly one thread, so every bin has one well-defined value.
-  constexpr int BT = kBinsPerPass / kThreads;
-  if (tid == 0) { jstar_s = kNB; lastne_s = -1; }
-  __syncthreads();
-  double carry = 0.0;
-  uint32_t ccarry = 0u;
-  int my_last = -1;
-  double my_last_above = 0.0;
-  uint32_t my_last_cab = 0u, my_last_cnt = 0u;
-  for (int base = 0; base < kNB; base += kBinsPerPass) {
-    const int J0 = base + tid * BT;
-    double mb[BT];
-    uint32_t cb[BT];
-#pragma unroll
-    for (int i = 0; i < BT; ++i) { mb[i] = 0.0; cb[i] = 0u; }
-    // four units' bins in flight at once
-    for (int u0 = 0; u0 < g.U; u0 += 4) {
-      unsigned long long e[4][BT];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
+      for (int k = 0; k < 8; ++k) {
         const int u = u0 + k;
-        const int used = (u < g.U) ? used_s[u] : -1;
-        const int d = (u < g.U) ? A - A_s[u] : 0;
-        const unsigned long long* hu = ws.hist + (g.slot0 + min(u, g.U - 1)) * kNB;
-#pragma unroll
-        for (int i = 0; i < BT; ++i) {
-          const int jl = J0 + i - d;
-          e[k][i] = (jl >= 0 && jl <= used && J0 + i < kNB - 1) ? hu[jl] : 0ull;
+        e[k] = 0ull;
+        if (u < g.U && used_s[u] >= 0) {
+          const int cj = tid - ((Ap >> 4) - (A_s[u] >> 4));
+          if (cj >= 0 && cj <= cused_s[u]) e[k] = ws.chist[(g.slot0 + u) * kNC + cj];
         }
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int u = u0 + k;
-        if (u >= g.U) continue;
-        const int used = used_s[u];
-        if (J0 + BT - 1 == kNB - 1 && used >= 0) {   // the last row bin also takes every deeper unit bin
-          const unsigned long long* hu = ws.hist + (g.slot0 + u) * kNB;
-          for (int j = max(kNB - 1 - (A - A_s[u]), 0); j <= used; ++j) e[k][BT - 1] += hu[j];
-        }
-        const double f = f_s[u];
-#pragma unroll
-        for (int i = 0; i < BT; ++i) {
-          mb[i] += (double)(e[k][i] & kMassMask) * f;
-          cb[i] += (uint32_t)(e[k][i] >> kCountShift);
+      for (int k = 0; k < 8; ++k) {
+        if (u0 + k < g.U) {
+          cm += bin_mass(e[k], f_s[u0 + k], cmode);
+          cc += (uint32_t)(e[k] >> kCountShift);
         }
       }
     }
-    if (count_mode) {
-#pragma unroll
-      for (int i = 0; i < BT; ++i) mb[i] = (double)cb[i];
-    }
-    double tm = 0.0;
-    uint32_t tc = 0u;
-#pragma unroll
-    for (int i = 0; i < BT; ++i) { tm += mb[i]; tc += cb[i]; }
-    double ptot;
-    uint32_t ctot;
-    double pre = carry + block_exscan_f64(tm, dtmp, ptot);
-    uint32_t cpre = ccarry + block_exscan<uint32_t>(tc, utmp, ctot);
-    int mine = -1;
-    double mine_above = 0.0;
-    uint32_t mine_cab = 0u, mine_cnt = 0u;
-#pragma unroll
-    for (int i = 0; i < BT; ++i) {
-      if (cb[i] > 0u) {
-        if (mine < 0 && pre + mb[i] >= target) { mine = J0 + i; mine_above = pre; mine_cab = cpre; mine_cnt = cb[i]; }
-        my_last = J0 + i; my_last_above = pre; my_last_cab = cpre; my_last_cnt = cb[i];
-      }
-      pre += mb[i];
-      cpre += cb[i];
-    }
-    if (mine >= 0) atomicMin(&jstar_s, mine);
-    __syncthreads();
-    if (jstar_s < kNB) {
-      if (mine == jstar_s) { above_s = mine_above; cabove_s = mine_cab; bincnt_s = mine_cnt; }
-      __syncthreads();
-      break;
-    }
-    carry += ptot;
-    ccarry += ctot;
   }
-  if (jstar_s == kNB) {   // rounding left the target just out of reach: the last non-empty bin
-    atomicMax(&lastne_s, my_last);
+  {
+    double part, rest;
+    uint32_t partc, restc;
+    (void)block_exscan_f64_n<kThreads / 64>(cm, dtmp, part);
+    (void)block_exscan<uint32_t>(cc, utmp, partc);
+    // the open-ended last bin: the row's remainder
+    rest = fmax((cmode ? (double)g.L : Z) - part, 0.0);
+    restc = (uint32_t)g.L - partc;
+    if (tid == kRowCoarse - 1) { cm = rest; cc = restc; }
+  }
+  if (tid == 0) { cstar_s = kRowCoarse; clast_s = -1; nc_s = 0; }
+  {
+    double ctot;
+    uint32_t ctotc;
+    const double pre = block_exscan_f64_n<kThreads / 64>(cm, dtmp, ctot);
+    const uint32_t cpre = block_exscan<uint32_t>(cc, utmp, ctotc);
+    if (cc > 0u && pre < target && pre + cm >= target) atomicMin(&cstar_s, tid);
+    if (cc > 0u) atomicMax(&clast_s, tid);
     __syncthreads();
-    if (my_last >= 0 && my_last == lastne_s) {
-      jstar_s = my_last; above_s = my_last_above; cabove_s = my_last_cab; bincnt_s = my_last_cnt;
+    // rounding left the target just out of reach: the last non-empty coarse bin
+    const int cs = (cstar_s < kRowCoarse) ? cstar_s : clast_s;
+    if (tid == cs) { cab_m_s = pre; cab_c_s = cpre; cbin_m_s = cm; cbin_c_s = cc; }
+    __syncthreads();
+    if (tid == 0) cstar_s = cs;
+    __syncthreads();
+  }
+  const int cstar = cstar_s;
+
+  // ---- fine bins of the crossing coarse bin: lane group (i, q) sums units q, q + 16, ...
+  {
+    const int i = tid & 15, q = tid >> 4;
+    const int J = cstar * 16 + i;
+    double fm = 0.0;
+    uint32_t fc = 0u;
+    if (J < kNB - 1) {
+      for (int u = q; u < g.U; u += kThreads / 16) {
+        if (used_s[u] < 0) continue;
+        const int j = J - (Ap - A_s[u]);
+        if (j >= 0 && j <= used_s[u]) {
+          const unsigned long long e = ws.hist[(g.slot0 + u) * kNB + j];
+          fm += bin_mass(e, f_s[u], cmode);
+          fc += (uint32_t)(e >> kCountShift);
+        }
+      }
+    }
+    // lanes i, i + 16, i + 32, i + 48 of a wave hold four groups of bin i
+    fm += __shfl_xor(fm, 16);
+    fc += __shfl_xor(fc, 16);
+    fm += __shfl_xor(fm, 32);
+    fc += __shfl_xor(fc, 32);
+    if (lane < 16) { fm_s[wid][i] = fm; fc_s[wid][i] = fc; }
+    __syncthreads();
+    if (tid == 0) {
+      double m = cab_m_s, rm = cbin_m_s;
+      uint32_t cnt = cab_c_s, rc = cbin_c_s;
+      int js = -1, jl = -1;
+      double ml = 0.0;
+      uint32_t cl = 0u, nl = 0u, nb = 0u;
+      for (int b2 = 0; b2 < 16; ++b2) {
+        double bm = 0.0;
+        uint32_t bc = 0u;
+        if (cstar * 16 + b2 < kNB - 1) {
+          for (int w2 = 0; w2 < kThreads / 64; ++w2) { bm += fm_s[w2][b2]; bc += fc_s[w2][b2]; }
+          rm -= bm;
+          rc -= bc;
+        } else {   // the open-ended last bin: what the coarse bin leaves
+          bm = fmax(rm, 0.0);
+          bc = rc;
+        }
+        if (bc == 0u) continue;
+        if (js < 0 && m + bm >= target) { js = b2; above_s = m; cabove_s = cnt; nb = bc; }
+        jl = b2; ml = m; cl = cnt; nl = bc;
+        m += bm;
+        cnt += bc;
+      }
+      if (js < 0) { js = jl; above_s = ml; cabove_s = cl; nb = nl; }
+      jstar_s = cstar * 16 + js;
+      bincnt_s = nb;
     }
     __syncthreads();
   }
@@ -572,138 +628,283 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
 
   // ---- this unit: tokens above the crossing bin, and the bin's tokens as candidates
   uint32_t nabove = 0u, nbin = 0u;
+  unsigned long long* cd = ws.cand + (g.slot0 + c) * kCapUnit;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int n = n0 + j * kThreads;
     if (n < g.L) {
-      const int J = min(kNB - 1, A - abs_bin(s[j]));
+      const int J = min(kNB - 1, Ap - abs_bin(s[j]));
       nabove += (J < jstar) ? 1u : 0u;
-      nbin += (J == jstar) ? 1u : 0u;
+      if (J == jstar) {
+        ++nbin;
+        const int sl = atomicAdd(&nc_s, 1);
+        if (sl < kCapUnit) cd[sl] = ((unsigned long long)desc_key(s[j]) << 32) | (uint32_t)n;
+      }
     }
   }
   uint32_t tot_above, tot_bin;
   (void)block_exscan<uint32_t>(nabove, utmp, tot_above);
-  uint32_t o = block_exscan<uint32_t>(nbin, utmp, tot_bin);
-  unsigned long long* cd = ws.cand + slot * kCapUnit;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int n = n0 + j * kThreads;
-    if (n < g.L && min(kNB - 1, A - abs_bin(s[j])) == jstar) {
-      if (o < (uint32_t)kCapUnit) cd[o] = ((unsigned long long)desc_key(s[j]) << 32) | (uint32_t)n;
-      ++o;
-    }
-  }
+  (void)block_exscan<uint32_t>(nbin, utmp, tot_bin);
   if (tid == 0) {
     UnitCnt uc = {tot_above, tot_bin};
-    ws.ucnt[slot] = uc;
-    ws.fu[slot] = f_s[c];
+    ws.ucnt[g.slot0 + c] = uc;
     if (c == 0) {
       RowState rs;
       rs.above = above_s;
       rs.target = target;
       rs.mode = ROW_NORMAL;
       rs.A = A;
+      rs.Ap = Ap;
       rs.jstar = jstar;
       rs.cabove = cabove_s;
       rs.bincnt = bincnt_s;
-      rs.count_mode = count_mode ? 1 : 0;
       ws.rows[g.row] = rs;
     }
   }
 }
 
 // ======================================================================= 3. emit
-__global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selection sel, DecodeWs ws) {
+// Every unit ranks the row's candidates by (score desc, position asc), walks
+// their masses to the crossing token (tau, tie_pos, count), derives its first
+// output slot from the per-unit counts and writes its members in ascending
+// order: within a wave's 1024 keys by ballots (keys j * 64 + lane in order j,
+// then lane), across the four waves by their counts.  A crossing bin too
+// crowded for the candidate lists (mass piled on near-identical scores) is
+// resolved from the row's stored scores, with radix digits of the score's bit
+// pattern and then positions.
+__global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_t* __restrict__ top_k,
+                                                         rtp_selection sel, DecodeWs ws) {
   const RowGeom g = row_geom(p, blockIdx.y);
   const int c = blockIdx.x;
-  if (c >= g.U || g.U > kMaxUnits) return;
-  const int tid = threadIdx.x;
+  if (c >= g.U || g.U > kMaxUnits || g.L == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const RowState rs = ws.rows[g.row];
-  if (rs.mode == ROW_EMPTY) {
-    if (c == 0 && tid == 0) {
-      sel.count[(size_t)g.r * p.Tq + g.qrow] = 0;
-      if (sel.tau) sel.tau[(size_t)g.r * p.Tq + g.qrow] = INFINITY;
-      if (sel.tie_pos) sel.tie_pos[(size_t)g.r * p.Tq + g.qrow] = 0x7FFFFFFF;
+  int* out = sel.idx + (size_t)g.r * p.Tk + g.k0;
+  constexpr int kSeg = kChunk / kThreads;
+  const int nw = c * kChunk + wid * (64 * kSeg);
+  if (rs.mode == ROW_ALL) {
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) {
+      const int n = nw + j * 64 + lane;
+      if (n < g.L) out[n] = n;
     }
     return;
   }
+  if (rs.mode != ROW_NORMAL) return;
+  const bool cmode = top_k != nullptr;
   const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
-  int* out = sel.idx + (size_t)g.r * p.Tk + g.k0;
-  // kPer consecutive keys per thread, so the unit's members come out ascending
-  const int nb = c * kChunk + tid * kPer;
-  float s[kPer];
+  float sv[kSeg];
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) s[j] = (nb + j < g.L) ? sb[nb + j] : -INFINITY;
+  for (int j = 0; j < kSeg; ++j) {
+    const int n = nw + j * 64 + lane;
+    sv[j] = (n < g.L) ? sb[n] : 0.f;
+  }
 
   __shared__ int A_s[kMaxUnits];
   __shared__ double f_s[kMaxUnits];
   __shared__ uint32_t cmem_s[kMaxUnits];     // members per unit among the candidates
   __shared__ uint32_t cbase_s[kMaxUnits];
+  __shared__ uint32_t cab_s[kMaxUnits];
   __shared__ unsigned long long cand_s[kCap];
-  __shared__ short order_s[kCap];            // candidate index by rank
+  __shared__ short order_s[kCap];
   __shared__ double dtmp[kThreads / 64];
-  __shared__ int itmp[kThreads / 64];
   __shared__ uint32_t utmp[kThreads / 64];
   __shared__ float tau_s;
   __shared__ int tie_s, count_s, js_s;
   __shared__ uint32_t off_s;
+  __shared__ uint32_t wcnt_s[kThreads / 64];
 
-  float tau = -INFINITY;
-  int tie = 0x7FFFFFFF;
-  uint32_t off = 0u;
-  const bool all = (rs.mode == ROW_ALL);
-  if (all) {
-    off = (uint32_t)(c * kChunk);
-    if (c == 0 && tid == 0) {
-      sel.count[(size_t)g.r * p.Tq + g.qrow] = g.L;
-      if (sel.tau) sel.tau[(size_t)g.r * p.Tq + g.qrow] = -INFINITY;
-      if (sel.tie_pos) sel.tie_pos[(size_t)g.r * p.Tq + g.qrow] = 0x7FFFFFFF;
-    }
-  } else {
-    const int A = rs.A;
-    const double target = rs.target;
-    const bool cmode = rs.count_mode != 0;
-    // per unit: reference bin and scale of the row merge, candidate count
-    constexpr int PU = kMaxUnits / kThreads;
-    uint32_t nin = 0u, cmax = 0u;
-    uint32_t vin[PU];
+  const int A = rs.A, Ap = rs.Ap;
+  const double target = rs.target;
+  auto bin_of = [&](float v) { return min(kNB - 1, Ap - abs_bin(v)); };
+  // per unit: reference bin, scale, candidate count and base
+  constexpr int PU = kMaxUnits / kThreads;
+  uint32_t nin = 0u, cmax = 0u;
+  uint32_t vin[PU];
 #pragma unroll
-    for (int t = 0; t < PU; ++t) {
-      const int u = tid * PU + t;
-      vin[t] = 0u;
-      if (u < g.U) {
-        A_s[u] = ws.meta[g.slot0 + u].A;
-        f_s[u] = ws.fu[g.slot0 + u];
-        vin[t] = ws.ucnt[g.slot0 + u].inbin;
-        cmem_s[u] = 0u;
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid * PU + t;
+    vin[t] = 0u;
+    if (u < g.U) {
+      const UnitMeta mt = ws.meta[g.slot0 + u];
+      const UnitCnt uc = ws.ucnt[g.slot0 + u];
+      A_s[u] = mt.A;
+      f_s[u] = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
+      vin[t] = uc.inbin;
+      cab_s[u] = uc.above;
+      cmem_s[u] = 0u;
+    }
+    nin += vin[t];
+    cmax = max(cmax, vin[t]);
+  }
+  uint32_t ntot;
+  uint32_t run = block_exscan<uint32_t>(nin, utmp, ntot);
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid * PU + t;
+    if (u < g.U) cbase_s[u] = run;
+    run += vin[t];
+  }
+  cmax = block_max<uint32_t>(cmax, utmp);
+  const bool fits = (ntot == rs.bincnt) && (ntot <= (uint32_t)kCap) && (cmax <= (uint32_t)kCapUnit) && ntot > 0u;
+
+  if (fits) {
+    const int nc = (int)ntot;
+    // gather: candidate k belongs to the last unit whose base is <= k
+    for (int kq = tid; kq < nc; kq += kThreads) {
+      int lo = 0, hi = g.U - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cbase_s[mid] <= (uint32_t)kq) lo = mid; else hi = mid - 1;
       }
-      nin += vin[t];
-      cmax = max(cmax, vin[t]);
+      cand_s[kq] = ws.cand[(g.slot0 + lo) * kCapUnit + (kq - (int)cbase_s[lo])];
     }
-    uint32_t ntot;
-    uint32_t run = block_exscan<uint32_t>(nin, utmp, ntot);
+    __syncthreads();
+    // rank of every candidate in (desc_key, position) order: keys are distinct
+    for (int i = tid; i < nc; i += kThreads) {
+      const unsigned long long ki = cand_s[i];
+      int rank = 0;
+      for (int j = 0; j < nc; ++j) rank += (cand_s[j] < ki) ? 1 : 0;
+      order_s[rank] = (short)i;
+    }
+    __syncthreads();
+    // cumulative masses in rank order: G consecutive ranks per thread, fixed order
+    constexpr int G = kCap / kThreads;
+    double ms[G];
+    double loc = 0.0;
 #pragma unroll
-    for (int t = 0; t < PU; ++t) {
-      const int u = tid * PU + t;
-      if (u < g.U) cbase_s[u] = run;
-      run += vin[t];
+    for (int t = 0; t < G; ++t) {
+      const int rk = tid * G + t;
+      ms[t] = 0.0;
+      if (rk < nc) {
+        const unsigned long long kv = cand_s[order_s[rk]];
+        const float v = undesc_key((uint32_t)(kv >> 32));
+        const int u = min((int)(uint32_t)(kv & 0xFFFFFFFFull) / kChunk, g.U - 1);
+        ms[t] = cmode ? 1.0 : (double)mass38(v, A_s[u]) * f_s[u];
+      }
+      loc += ms[t];
     }
-    cmax = block_max<uint32_t>(cmax, utmp);
-    const bool fits = (ntot == rs.bincnt) && (ntot <= (uint32_t)kCap) && (cmax <= (uint32_t)kCapUnit) && ntot > 0u;
-
-    if (fits) {
-      const int nc = (int)ntot;
-      // gather: candidate k belongs to the last unit whose base is <= k
-      for (int kk = tid; kk < nc; kk += kThreads) {
-        int lo = 0, hi = g.U - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (cbase_s[mid] <= (uint32_t)kk) lo = mid; else hi = mid - 1;
-        }
-        cand_s[kk] = ws.cand[(g.slot0 + lo) * kCapUnit + (kk - (int)cbase_s[lo])];
+    double tt;
+    double pre = block_exscan_f64_n<kThreads / 64>(loc, dtmp, tt) + rs.above;
+    if (tid == 0) js_s = nc - 1;   // if rounding hides the crossing: the last candidate
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < G; ++t) {
+      const int rk = tid * G + t;
+      pre += ms[t];
+      if (rk < nc && pre >= target) { atomicMin(&js_s, rk); break; }
+    }
+    __syncthreads();
+    const int js = js_s;
+    if (tid == 0) {
+      const unsigned long long kv = cand_s[order_s[js]];
+      tau_s = undesc_key((uint32_t)(kv >> 32));
+      tie_s = (int)(uint32_t)(kv & 0xFFFFFFFFull);
+      // every token scoring exactly tau is a candidate: if none is left out, S = {s >= tau}
+      if (!(js + 1 < nc && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
+      count_s = (int)rs.cabove + js + 1;
+    }
+    for (int rk = tid; rk <= js; rk += kThreads) {
+      const uint32_t n = (uint32_t)(cand_s[order_s[rk]] & 0xFFFFFFFFull);
+      atomicAdd(&cmem_s[min(n / (uint32_t)kChunk, (uint32_t)(g.U - 1))], 1u);
+    }
+    __syncthreads();
+    // first output slot of this unit: members of the units before it
+    uint32_t ol = 0u;
+    for (int u = tid; u < c; u += kThreads) ol += cab_s[u] + cmem_s[u];
+    uint32_t otot;
+    (void)block_exscan<uint32_t>(ol, utmp, otot);
+    if (tid == 0) off_s = otot;
+    __syncthreads();
+  } else {
+    // ---- crowded crossing bin: radix digits of desc_key inside the bin (11 + 11 + 10
+    // bits) with masses relative to the row reference, then exact ties by position;
+    // the digit histograms share the candidate buffer
+    unsigned long long* hm2 = cand_s;
+    uint32_t* hc2 = reinterpret_cast<uint32_t*>(cand_s + 2048);
+    __shared__ int dig_s, nc_s;
+    __shared__ double ab_s;
+    __shared__ uint32_t cb_s, cnt_s;
+    const int jstar = rs.jstar;
+    if (tid == 0) { ab_s = rs.above; cb_s = rs.cabove; cnt_s = rs.bincnt; }
+    __syncthreads();
+    uint32_t prefix = 0u;
+    int shift = 32;
+    while (cnt_s > (uint32_t)kCap && shift > 0) {
+      const int nbits = (shift >= 11) ? 11 : shift;
+      const int nshift = shift - nbits;
+      for (int i = tid; i < 2048; i += kThreads) { hm2[i] = 0ull; hc2[i] = 0u; }
+      __syncthreads();
+      for (int n = tid; n < g.L; n += kThreads) {
+        const float v = sb[n];
+        if (bin_of(v) != jstar) continue;
+        const uint32_t key = desc_key(v);
+        if (shift < 32 && (key >> shift) != prefix) continue;
+        const uint32_t dg = (key >> nshift) & ((1u << nbits) - 1u);
+        atomicAdd(&hm2[dg], cmode ? 1ull : mass38(v, A));
+        atomicAdd(&hc2[dg], 1u);
       }
       __syncthreads();
-      // rank of every candidate in (desc_key, position) order: keys are distinct
+      if (tid == 0) {
+        double cm = ab_s;
+        uint32_t cc = cb_s;
+        int dsel = -1;
+        bool found = false;
+        for (int d = 0; d < (1 << nbits); ++d) {
+          if (hc2[d] == 0u) continue;
+          dsel = d;
+          if (cm + (double)hm2[d] >= target) { found = true; break; }
+          cm += (double)hm2[d];
+          cc += hc2[d];
+        }
+        if (dsel < 0) dsel = 0;
+        if (!found) {  // rounding hid the crossing: the last non-empty digit
+          cm = ab_s; cc = cb_s;
+          for (int d = 0; d < dsel; ++d) { cm += (double)hm2[d]; cc += hc2[d]; }
+        }
+        ab_s = cm; cb_s = cc; cnt_s = hc2[dsel]; dig_s = dsel;
+      }
+      __syncthreads();
+      prefix = (shift < 32 ? (prefix << nbits) : 0u) | (uint32_t)dig_s;
+      shift = nshift;
+    }
+    if (cnt_s > (uint32_t)kCap) {
+      // exact ties: the tied value is the key `prefix`; admit them by ascending position
+      const float tv = undesc_key(prefix);
+      const double mt = cmode ? 1.0 : (double)mass38(tv, A);
+      const double need = target - ab_s;
+      long long kneed = (mt > 0.0) ? (long long)ceil(need / mt) : (long long)cnt_s;
+      kneed = max(1ll, min(kneed, (long long)cnt_s));
+      __shared__ int runt_s, tiepos_s;
+      if (tid == 0) { runt_s = 0; tiepos_s = -1; }
+      __syncthreads();
+      for (int base = 0; base < g.L; base += kThreads) {
+        const int n = base + tid;
+        const uint32_t f = (n < g.L && sb[n] == tv) ? 1u : 0u;
+        uint32_t tt;
+        const uint32_t ex = block_exscan<uint32_t>(f, utmp, tt);
+        const int before = runt_s;
+        if (f && (long long)(before + (int)ex + 1) == kneed) tiepos_s = n;
+        __syncthreads();
+        if (tid == 0) runt_s = before + (int)tt;
+        __syncthreads();
+        if ((long long)runt_s >= kneed) break;
+      }
+      if (tid == 0) { tau_s = tv; tie_s = tiepos_s; count_s = (int)cb_s + (int)kneed; }
+      __syncthreads();
+    } else {
+      // the remaining range fits: collect it, rank it and walk it
+      if (tid == 0) nc_s = 0;
+      __syncthreads();
+      for (int n = tid; n < g.L; n += kThreads) {
+        const float v = sb[n];
+        if (bin_of(v) != jstar) continue;
+        if (shift < 32 && (desc_key(v) >> shift) != prefix) continue;
+        const int sl = atomicAdd(&nc_s, 1);
+        if (sl < kCap) cand_s[sl] = ((unsigned long long)desc_key(v) << 32) | (uint32_t)n;
+      }
+      __syncthreads();
+      const int nc = min(nc_s, kCap);
       for (int i = tid; i < nc; i += kThreads) {
         const unsigned long long ki = cand_s[i];
         int rank = 0;
@@ -711,205 +912,62 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, rtp_selectio
         order_s[rank] = (short)i;
       }
       __syncthreads();
-      // cumulative masses in rank order: G consecutive ranks per thread, fixed order
-      constexpr int G = kCap / kThreads;
-      double ms[G];
-      double loc = 0.0;
-#pragma unroll
-      for (int t = 0; t < G; ++t) {
-        const int rk = tid * G + t;
-        ms[t] = 0.0;
-        if (rk < nc) {
-          const unsigned long long kv = cand_s[order_s[rk]];
-          const float sv = undesc_key((uint32_t)(kv >> 32));
-          const uint32_t n = (uint32_t)(kv & 0xFFFFFFFFull);
-          const int u = (int)min(n / (uint32_t)kChunk, (uint32_t)(g.U - 1));
-          ms[t] = cmode ? 1.0 : (double)mass38(sv, A_s[u]) * f_s[u];
-        }
-        loc += ms[t];
-      }
-      double tt;
-      double pre = block_exscan_f64(loc, dtmp, tt) + rs.above;
-      if (tid == 0) js_s = nc - 1;   // if rounding hides the crossing: the last candidate
-      __syncthreads();
-#pragma unroll
-      for (int t = 0; t < G; ++t) {
-        const int rk = tid * G + t;
-        pre += ms[t];
-        if (rk < nc && pre >= target) { atomicMin(&js_s, rk); break; }
-      }
-      __syncthreads();
-      const int js = js_s;
       if (tid == 0) {
+        double cm = ab_s;
+        int js = max(nc - 1, 0);
+        for (int i = 0; i < nc; ++i) {
+          const float v = undesc_key((uint32_t)(cand_s[order_s[i]] >> 32));
+          const double mi = cmode ? 1.0 : (double)mass38(v, A);
+          if (cm + mi >= target) { js = i; break; }
+          cm += mi;
+        }
         const unsigned long long kv = cand_s[order_s[js]];
         tau_s = undesc_key((uint32_t)(kv >> 32));
         tie_s = (int)(uint32_t)(kv & 0xFFFFFFFFull);
-        // every token scoring exactly tau is a candidate: if none is left out, S = {s >= tau}
         if (!(js + 1 < nc && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
-        count_s = (int)rs.cabove + js + 1;
+        count_s = (int)cb_s + js + 1;
       }
-      for (int rk = tid; rk <= js; rk += kThreads) {
-        const uint32_t n = (uint32_t)(cand_s[order_s[rk]] & 0xFFFFFFFFull);
-        atomicAdd(&cmem_s[min(n / (uint32_t)kChunk, (uint32_t)(g.U - 1))], 1u);
-      }
-      __syncthreads();
-      // offset of this unit: members of the units before it
-      uint32_t ol = 0u;
-      for (int u = tid; u < c; u += kThreads) ol += ws.ucnt[g.slot0 + u].above + cmem_s[u];
-      uint32_t otot;
-      (void)block_exscan<uint32_t>(ol, utmp, otot);
-      if (tid == 0) off_s = otot;
-      __syncthreads();
-    } else {
-      // ---- crowded crossing bin: resolve it from the row's scores, radix digits of
-      // desc_key inside the bin (11 + 11 + 10 bits), then exact ties by position
-      // digit histograms share the candidate buffer (used only once the range fits)
-      unsigned long long* hm2 = cand_s;
-      uint32_t* hc2 = reinterpret_cast<uint32_t*>(cand_s + 2048);
-      __shared__ int dig_s;
-      __shared__ double ab_s;
-      __shared__ uint32_t cab_s, cnt_s;
-      const int jstar = rs.jstar;
-      if (tid == 0) { ab_s = rs.above; cab_s = rs.cabove; cnt_s = rs.bincnt; }
-      __syncthreads();
-      auto in_bin = [&](float sv) { return min(kNB - 1, A - abs_bin(sv)) == jstar; };
-      uint32_t prefix = 0u;
-      int shift = 32;
-      while (cnt_s > (uint32_t)kCap && shift > 0) {
-        const int nbits = (shift >= 11) ? 11 : shift;
-        const int nshift = shift - nbits;
-        for (int i = tid; i < 2048; i += kThreads) { hm2[i] = 0ull; hc2[i] = 0u; }
-        __syncthreads();
-        // digit masses in fixed point relative to the row reference (exact sums)
-        for (int n = tid; n < g.L; n += kThreads) {
-          const float sv = sb[n];
-          if (!in_bin(sv)) continue;
-          const uint32_t key = desc_key(sv);
-          if (shift < 32 && (key >> shift) != prefix) continue;
-          const uint32_t dg = (key >> nshift) & ((1u << nbits) - 1u);
-          atomicAdd(&hm2[dg], cmode ? 1ull : mass38(sv, A));
-          atomicAdd(&hc2[dg], 1u);
-        }
-        __syncthreads();
-        if (tid == 0) {
-          double cm = ab_s;
-          uint32_t cc = cab_s;
-          int dsel = -1;
-          bool found = false;
-          for (int d = 0; d < (1 << nbits); ++d) {
-            if (hc2[d] == 0u) continue;
-            dsel = d;
-            if (cm + (double)hm2[d] >= target) { found = true; break; }
-            cm += (double)hm2[d];
-            cc += hc2[d];
-          }
-          if (dsel < 0) dsel = 0;
-          if (!found) {  // rounding hid the crossing: the last non-empty digit
-            cm = ab_s; cc = cab_s;
-            for (int d = 0; d < dsel; ++d) { cm += (double)hm2[d]; cc += hc2[d]; }
-          }
-          ab_s = cm; cab_s = cc; cnt_s = hc2[dsel]; dig_s = dsel;
-        }
-        __syncthreads();
-        prefix = (shift < 32 ? (prefix << nbits) : 0u) | (uint32_t)dig_s;
-        shift = nshift;
-      }
-      if (cnt_s > (uint32_t)kCap) {
-        // exact ties: the tied value is the key `prefix`; admit them by ascending position
-        const float tv = undesc_key(prefix);
-        const double mt = cmode ? 1.0 : (double)mass38(tv, A);
-        const double need = target - ab_s;
-        long long kneed = (mt > 0.0) ? (long long)ceil(need / mt) : (long long)cnt_s;
-        kneed = max(1ll, min(kneed, (long long)cnt_s));
-        __shared__ int runt_s, tiepos_s;
-        if (tid == 0) { runt_s = 0; tiepos_s = -1; }
-        __syncthreads();
-        for (int base = 0; base < g.L; base += kThreads) {
-          const int n = base + tid;
-          const uint32_t f = (n < g.L && sb[n] == tv) ? 1u : 0u;
-          uint32_t tt;
-          const uint32_t ex = block_exscan<uint32_t>(f, utmp, tt);
-          const int before = runt_s;
-          if (f && (long long)(before + (int)ex + 1) == kneed) tiepos_s = n;
-          __syncthreads();
-          if (tid == 0) runt_s = before + (int)tt;
-          __syncthreads();
-          if ((long long)runt_s >= kneed) break;
-        }
-        if (tid == 0) { tau_s = tv; tie_s = tiepos_s; count_s = (int)cab_s + (int)kneed; }
-        __syncthreads();
-      } else {
-        // the remaining range fits: collect it, rank it and walk it
-        __shared__ int nc_s;
-        if (tid == 0) nc_s = 0;
-        __syncthreads();
-        for (int n = tid; n < g.L; n += kThreads) {
-          const float sv = sb[n];
-          if (!in_bin(sv)) continue;
-          if (shift < 32 && (desc_key(sv) >> shift) != prefix) continue;
-          const int sl = atomicAdd(&nc_s, 1);
-          if (sl < kCap) cand_s[sl] = ((unsigned long long)desc_key(sv) << 32) | (uint32_t)n;
-        }
-        __syncthreads();
-        const int nc = min(nc_s, kCap);
-        for (int i = tid; i < nc; i += kThreads) {
-          const unsigned long long ki = cand_s[i];
-          int rank = 0;
-          for (int j = 0; j < nc; ++j) rank += (cand_s[j] < ki) ? 1 : 0;
-          order_s[rank] = (short)i;
-        }
-        __syncthreads();
-        if (tid == 0) {
-          double cm = ab_s;
-          int js = max(nc - 1, 0);
-          for (int i = 0; i < nc; ++i) {
-            const float sv = undesc_key((uint32_t)(cand_s[order_s[i]] >> 32));
-            const double mi = cmode ? 1.0 : (double)mass38(sv, A);
-            if (cm + mi >= target) { js = i; break; }
-            cm += mi;
-          }
-          const unsigned long long kv = cand_s[order_s[js]];
-          tau_s = undesc_key((uint32_t)(kv >> 32));
-          tie_s = (int)(uint32_t)(kv & 0xFFFFFFFFull);
-          if (!(js + 1 < nc && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
-          count_s = (int)cab_s + js + 1;
-        }
-        __syncthreads();
-      }
-      // offset of this unit: members among the keys before it
-      const float tv = tau_s;
-      const int tp = tie_s;
-      uint32_t ol = 0u;
-      for (int n = tid; n < c * kChunk && n < g.L; n += kThreads) ol += is_member(sb[n], n, tv, tp) ? 1u : 0u;
-      uint32_t otot;
-      (void)block_exscan<uint32_t>(ol, utmp, otot);
-      if (tid == 0) off_s = otot;
       __syncthreads();
     }
-    tau = tau_s;
-    tie = tie_s;
-    off = off_s;
-    if (c == 0 && tid == 0) {
-      sel.count[(size_t)g.r * p.Tq + g.qrow] = count_s;
-      if (sel.tau) sel.tau[(size_t)g.r * p.Tq + g.qrow] = tau;
-      if (sel.tie_pos) sel.tie_pos[(size_t)g.r * p.Tq + g.qrow] = tie;
-    }
+    // first output slot of this unit: members among the keys before it
+    const float tv = tau_s;
+    const int tp = tie_s;
+    uint32_t ol = 0u;
+    for (int n = tid; n < c * kChunk && n < g.L; n += kThreads) ol += is_member(sb[n], n, tv, tp) ? 1u : 0u;
+    uint32_t otot;
+    (void)block_exscan<uint32_t>(ol, utmp, otot);
+    if (tid == 0) off_s = otot;
+    __syncthreads();
+  }
+  const float tau = tau_s;
+  const int tie = tie_s;
+  if (c == 0 && tid == 0) {
+    const size_t ro = (size_t)g.r * p.Tq + g.qrow;
+    sel.count[ro] = count_s;
+    if (sel.tau) sel.tau[ro] = tau;
+    if (sel.tie_pos) sel.tie_pos[ro] = tie;
   }
 
   // ---- this unit's members, ascending
-  uint32_t fl = 0u, cnt = 0u;
+  auto member_mask = [&](int j) {
+    const int n = nw + j * 64 + lane;
+    return __builtin_amdgcn_ballot_w64(n < g.L && is_member(sv[j], n, tau, tie));
+  };
+  uint32_t wc = 0u;
 #pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int n = nb + j;
-    const bool m = (n < g.L) && (all || is_member(s[j], n, tau, tie));
-    fl |= (m ? 1u : 0u) << j;
-    cnt += m ? 1u : 0u;
+  for (int j = 0; j < kSeg; ++j) wc += (uint32_t)__popcll(member_mask(j));
+  if (lane == 0) wcnt_s[wid] = wc;
+  __syncthreads();
+  uint32_t o = off_s;
+  for (int w2 = 0; w2 < wid; ++w2) o += wcnt_s[w2];
+  const unsigned long long below = (1ull << lane) - 1ull;
+#pragma unroll
+  for (int j = 0; j < kSeg; ++j) {
+    const unsigned long long mk = member_mask(j);
+    const uint32_t at = o + (uint32_t)__popcll(mk & below);
+    if (((mk >> lane) & 1ull) && at < (uint32_t)g.L) out[at] = nw + j * 64 + lane;
+    o += (uint32_t)__popcll(mk);
   }
-  uint32_t tt;
-  uint32_t o = off + block_exscan<uint32_t>(cnt, utmp, tt);
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if ((fl & (1u << j)) && o < (uint32_t)g.L) out[o++] = nb + j;
 }
 
 // ======================================================================= block top-p
@@ -1075,8 +1133,8 @@ hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, 
   else
     hipLaunchKernelGGL(sel_dec_score<float>, grid, dim3(kThreads), 0, s, p, (const float*)q_pre, w_q,
                        (const float*)k_idx, sel, w);
-  hipLaunchKernelGGL(sel_dec_collect, grid, dim3(kThreads), 0, s, p, top_p, top_k, w);
-  hipLaunchKernelGGL(sel_dec_emit, grid, dim3(kThreads), 0, s, p, sel, w);
+  hipLaunchKernelGGL(sel_dec_collect, grid, dim3(kThreads), 0, s, p, top_p, top_k, sel, w);
+  hipLaunchKernelGGL(sel_dec_emit, grid, dim3(kThreads), 0, s, p, top_k, sel, w);
   return hipGetLastError();
 }
 
