@@ -27,8 +27,12 @@
 //     a row maximum exceeds it by more than 8; row sums from the matrix cores
 //     (an all-ones operand in the PV product); masked tiles of a wave skip
 //     both products.
-// LDS strides are padded so the fragment reads of one 8- or 16-lane phase hit
-// distinct banks.
+//   - the two products run at wave priority 0 and the mask/softmax ALU work
+//     at 2, so when two waves of a SIMD are ready the one in its ALU phase
+//     issues first and the other's matrix-core work overlaps it.
+// LDS strides are padded (chosen by measurement) so that fragment reads of one
+// phase mostly hit distinct banks; the 16-bit index-key rows are padded to 10
+// words, which removed most of the bank conflicts of their 8-byte reads.
 #include <type_traits>
 
 #include "common.h"
@@ -46,7 +50,7 @@ static_assert((KT / 2) * (kHeadDim / 8) % kThreads == 0, "V staging splits evenl
 static_assert(KT * kHeadDim / 8 % kThreads == 0, "K staging splits evenly over the workgroup");
 
 template <typename T> struct Lds;
-template <> struct Lds<bf16_t> { static constexpr int kStr = 128 + 8; static constexpr int vStr = 64 + 4; };
+template <> struct Lds<bf16_t> { static constexpr int kStr = 128 + 16; static constexpr int vStr = 64 + 4; };
 template <> struct Lds<float> { static constexpr int kStr = 128 + 4; static constexpr int vStr = 64 + 4; };
 
 // ---- B operand of O^T += V^T P^T from the four P values of two key subtiles
@@ -251,7 +255,11 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   __shared__ __attribute__((aligned(16))) T vt_s[2][kHeadDim * VS];
   // retrieval heads: the tile's 16-dim index keys, staged with K/V (one tile ahead)
   constexpr int KXW = (MODE == 0) ? KT * kIdxDim * (int)sizeof(T) / 4 / kThreads : 0;   // words per thread
-  __shared__ __attribute__((aligned(16))) uint32_t kx_s[2][(MODE == 0) ? KT * kIdxDim * sizeof(T) / 4 : 1];
+  // rows of 16-bit index keys padded to 10 words, so the 16 rows a fragment read
+  // touches fall in distinct banks
+  constexpr int KXWK = kIdxDim * (int)sizeof(T) / 4;                     // words per key
+  constexpr int KXS = (sizeof(T) == 2) ? KXWK + 2 : KXWK;                 // row stride in words
+  __shared__ __attribute__((aligned(16))) uint32_t kx_s[2][(MODE == 0) ? KT * KXS : 1];
   uint32_t kxr[KXW > 0 ? KXW : 1];
 
   const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b, per_head_xcd(MODE, nheads));
@@ -347,7 +355,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   auto kx_store = [&](int b2) {
     if (MODE != 0) return;
 #pragma unroll
-    for (int w = 0; w < KXW; ++w) kx_s[b2][w * kThreads + tid] = kxr[w];
+    for (int w = 0; w < KXW; ++w) {
+      const int e = w * kThreads + tid;
+      kx_s[b2][(e / KXWK) * KXS + e % KXWK] = kxr[w];
+    }
   };
 
   Stage<T> st;
@@ -386,8 +397,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
       if (MODE == 0 && !all_keys) {
         const T* kxt = reinterpret_cast<const T*>(kx_s[buf]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) load_idx_frag(kxf[ks], kxt + (16 * ks + col) * kIdxDim + 4 * grp);
+        for (int ks = 0; ks < 4; ++ks) load_idx_frag(kxf[ks], kxt + (16 * ks + col) * (KXS * 4 / (int)sizeof(T)) + 4 * grp);
       }
+      __builtin_amdgcn_s_setprio(0);   // matrix-core phase: waves in their ALU phase issue first
       // S^T = K Q^T
       f32x4 sacc[2][4];
 #pragma unroll
@@ -405,6 +417,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
           for (int c = 0; c < 2; ++c) sacc[c][ks] = mma_k32(kf, qf[c][kc], sacc[c][ks]);
         }
       }
+      __builtin_amdgcn_s_setprio(2);
       // membership: branch-free masks; the variant (exact ties, boundary tile)
       // is fixed per tile so each inner loop is straight-line code.  Element
       // (ks, i) of a lane is key kb4 + 16 ks + i: the tests compare that
@@ -507,6 +520,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
 
       // O^T += V^T P^T; the eight V^T fragments of a 32-key step are read before
       // its products, so the LDS reads overlap instead of each waiting alone
+      __builtin_amdgcn_s_setprio(0);
       if (__builtin_amdgcn_ballot_w64(live)) {
         const T* vtt = vt_s[buf];
 #pragma unroll
@@ -524,6 +538,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
         }
       }
     }
+    __builtin_amdgcn_s_setprio(2);
     if (t + 1 < ntiles) {
       st.store(k_s[buf ^ 1], vt_s[buf ^ 1], tid);
       kx_store(buf ^ 1);
