@@ -102,7 +102,7 @@ struct RowK {
   float lo_f, hi_f; // float range of K for the fast range test
   float dA, dB;     // the same tests on the raw dot: K >= lo <=> d <= dA, K < hi <=> d > dB
   float a12, b12;   // fine bin coordinate (1/256 octave) = fma(dot, a12, b12) = K / 2^12 exactly
-  float c12;        // g0 - 1: window bin = clamp(coordinate - c12, 0, 255)
+  float c12;        // g0 - 1: window bin = clamp(floor(coordinate), c12, c12 + 255) - c12
   uint32_t lo;
   int sh, kind, pos;
   uint32_t kfix, dfix;
@@ -182,7 +182,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
   const int i0 = qt * kRows;
   if (i0 >= Lq) return;
   const int off = Lk - Lq;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: tile loops run on scalars
   const int col = lane & 15, grp = lane >> 4;
 
   __shared__ T qidx_s[kRows][kIdxDim];
@@ -274,8 +275,13 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
   // loads (a prefetch past the last pair re-reads the last full tile) into two
   // register sets that alternate, so a step never waits on the loads it issues;
   // then the diagonal tiles one at a time.
+  // byte offsets from the row block's first index key: a scalar base plus one
+  // 32-bit lane offset (the keys of one retrieval head span well under 4 GB)
+  const char* kxc = reinterpret_cast<const char*>(kxb);
+  const uint32_t lane_off = (uint32_t)(col * kIdxDim + 4 * grp) * (uint32_t)sizeof(T);
   auto load_full = [&](IF& f, int t) {
-    load_idx_frag(f, kxb + (size_t)(16 * min(t, nfull - 1) + col) * kIdxDim + 4 * grp);
+    const uint32_t tt = (uint32_t)__builtin_amdgcn_readfirstlane(min(t, nfull - 1));
+    load_idx_frag(f, reinterpret_cast<const T*>(kxc + (tt * (16u * kIdxDim * (uint32_t)sizeof(T)) + lane_off)));
   };
   auto sweep_tiles = [&](auto&& body) {
     int t = w;
@@ -400,14 +406,20 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       // window of 254 bins of 1/256 octave; bin 0 holds everything above it, bin 255 everything below.
       // The coordinate is K / 2^12 exactly (a power-of-two scaling of the key's FMA) and
       // subtracting the integer c12 from it is exact, so bin j holds K in [(g0+j-1) << 12, (g0+j) << 12).
+      static_assert(kRows * sizeof(unsigned long long) == 128, "a window bin row is 128 bytes");
+      // floor(coordinate) clamped to [c12, c12 + 255] is c12 + the bin, so the lane's
+      // LDS base absorbs -c12 and the bin costs a clamp, a conversion and a shift-add
+      const float c12hi = rk.c12 + 255.f;
+      char* hbase = reinterpret_cast<char*>(&h1[0][col]) - (ptrdiff_t)(int)rk.c12 * (kRows * 8);
       sweep_tiles([&](const f32x4& d, int t, bool check) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
           if (check && n > rk.pos) continue;
           const float u12 = fmaf(d[i], rk.a12, rk.b12);
-          const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u12 - rk.c12, 0.f, 255.f);
-          atomicAdd(&h1[bin][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+          const uint32_t gb = (uint32_t)__builtin_amdgcn_fmed3f(u12, rk.c12, c12hi);
+          atomicAdd(reinterpret_cast<unsigned long long*>(hbase + (gb << 7)),
+                    COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
         }
       });
     } else if (sweep == PH_REFINE && all_fast) {
