@@ -136,6 +136,31 @@ def test_decode_ragged_short_sequences():
     _check_decode(make_inputs(cfg, DEV))
 
 
+def test_decode_f32():
+    # float32 decode: the split-list kernel for the local heads, float32 selection
+    cfg = scaled(DECODE_32K, name="decode_f32", batch=3, seqlens=(700, 5000, 9000), dtype="f32",
+                 n_q_heads=8, n_kv_heads=2, ret_heads=(0, 5), window=256, needles="query", needles_per_seq=8)
+    _say(f"[case] {cfg.name}")
+    _check_decode(make_inputs(cfg, DEV))
+
+
+def test_decode_mqa_many_local_heads_per_group():
+    # one KV group holding 20 local heads: the bfloat16 local kernel takes them as
+    # tiles of 8, 8 and 4 heads that share every K/V row
+    cfg = scaled(DECODE_32K, name="decode_mqa", batch=2, seqlens=(3000, 1100), n_q_heads=22, n_kv_heads=1,
+                 ret_heads=(3, 17), window=512, needles="query", needles_per_seq=8)
+    _say(f"[case] {cfg.name}")
+    _check_decode(make_inputs(cfg, DEV))
+
+
+def test_decode_groups_without_local_heads():
+    # KV groups 0 and 2 hold only retrieval heads; groups 1 and 3 only local heads
+    cfg = scaled(DECODE_32K, name="decode_mixed_groups", batch=2, seqlens=(2000, 4500), n_q_heads=8,
+                 n_kv_heads=4, ret_heads=(0, 1, 4, 5), window=300, needles="none")
+    _say(f"[case] {cfg.name}")
+    _check_decode(make_inputs(cfg, DEV))
+
+
 def test_v_one_gives_one():
     cfg = scaled(PREFILL_128K, name="v_one", seqlen=800, window=64)
     _say(f"[case] {cfg.name}")
