@@ -377,19 +377,24 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, const
 
 // ---- bfloat16 local heads: a KV group's heads together on the matrix cores.
 // A row is (tile of up to kGH local heads of one KV group, sequence); its key
-// list (sinks, then window) is cut into chunks of 64 keys and a row's chunks are
-// dealt round-robin to nsplit one-wave workgroups.  Per chunk the wave
-//   - scores 64 keys against the tile's heads with 16x16x32 MFMAs (A = K rows
-//     read straight from HBM in operand layout, B = the heads' queries; each K
-//     row is read once for every head of the group),
+// list (sinks, then window) is cut into chunks of kGChunk keys and a row's
+// chunks are dealt round-robin to nsplit one-wave workgroups.  Per chunk the
+// wave
+//   - issues every load first: K rows straight into MFMA operand layout and
+//     the V rows (16 lanes per row), so it waits on memory once;
+//   - scores the keys against the tile's heads with 16x16x32 MFMAs (A = K,
+//     B = the heads' queries; each K row is read once for every head of the
+//     group),
 //   - updates every head's running max and sum (16-lane groups of the output
-//     layout hold one head's scores) and stores the chunk's weights in LDS,
+//     layout hold one head's scores) and stores the chunk's weights and V rows
+//     in LDS,
 //   - accumulates P V on the vector ALUs: lane (dims 8c..8c+7, heads 2j, 2j+1)
-//     reads each V row segment once and the two weights from LDS.
+//     reads each V row segment and the two weights from LDS.
 // Splits write (max, sum, o) partials that a second kernel merges by
 // log-sum-exp, as for the other decode rows.
 constexpr int kGH = 8;           // local heads per tile
-constexpr int kGChunk = 64;      // keys per chunk
+constexpr int kGChunk = 32;      // keys per chunk
+static_assert(kGChunk % 16 == 0 && kGChunk <= 64, "16-key MFMA tiles; one slot per lane");
 constexpr int kGMaxSplit = 64;   // splits per row at most
 constexpr int kGTargetWaves = 2048;
 
@@ -417,6 +422,7 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
   __shared__ int slot_s[kGChunk];
   __shared__ __attribute__((aligned(16))) float p_s[kGChunk][kGH];
   __shared__ float scale_s[kGH];
+  __shared__ __attribute__((aligned(16))) bf16_t v_s[kGChunk][kHeadDim + 8];   // the chunk's V rows
 
   // B operand: column = head slot col (zero past the tile), k = dims 32 kc + 8 g .. + 8
   FragBF16 qf[4];
@@ -440,19 +446,26 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
   for (int c = split; c < nchunk; c += nsplit) {
     const int j0 = c * kGChunk;
     const int nv = min(kGChunk, count - j0);   // valid keys of the chunk (>= 1)
-    slot_s[lane] = key_slot(p, local_token(p, L, j0 + min(lane, nv - 1)));
+    if (lane < kGChunk) slot_s[lane] = key_slot(p, local_token(p, L, j0 + min(lane, nv - 1)));
     __syncthreads();
-    // scores: tile t holds keys 16 t .. 16 t + 15 (rows) x heads (columns)
-    FragBF16 kf[4][4];
+    // every load of the chunk first: K in operand layout, V rows (16 lanes per row,
+    // key (lane >> 4) + 4 u), so the chunk waits on memory once
+    constexpr int NT = kGChunk / 16;   // 16-key tiles of a chunk
+    FragBF16 kf[NT][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const bf16_t* kr = kb + (size_t)slot_s[16 * t + col] * kstride + 8 * g;
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) load_frag(kf[t][kc], kr + 32 * kc);
     }
-    f32x4 sc[4];
+    uint4 vr[kGChunk / 4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int u = 0; u < kGChunk / 4; ++u)
+      vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)slot_s[g + 4 * u] * kstride + 8 * col);
+    // scores: tile t holds keys 16 t .. 16 t + 15 (rows) x heads (columns)
+    f32x4 sc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
       sc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) sc[t] = mma_k32(kf[t][kc], qf[kc], sc[t]);
@@ -460,7 +473,7 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
     // lane (col, g) holds keys 16 t + 4 g + i of head col
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * t + 4 * g + i;
@@ -473,7 +486,7 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
     const float rs = __builtin_amdgcn_exp2f(m_run - mn);
     float ls = 0.f;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float pe = __builtin_amdgcn_exp2f(sc[t][i] - mn);
@@ -485,32 +498,25 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
     l_run = l_run * rs + ls;
     m_run = mn;
     if (g == 0 && col < kGH) scale_s[col] = rs;
+#pragma unroll
+    for (int u = 0; u < kGChunk / 4; ++u) *reinterpret_cast<uint4*>(&v_s[g + 4 * u][8 * col]) = vr[u];
     __syncthreads();
-    // P V: lane (dc, hg) over the chunk's valid keys, 8 V segments in flight
+    // P V: lane (dc, hg) over the chunk's valid keys (weights of keys past nv are 0)
     {
       const float r0 = scale_s[2 * hg], r1 = scale_s[2 * hg + 1];
 #pragma unroll
       for (int e = 0; e < 8; ++e) { o[0][e] *= r0; o[1][e] *= r1; }
     }
-    for (int jb = 0; jb < nv; jb += 8) {
-      uint4 vr[8];
+#pragma unroll 4
+    for (int j = 0; j < nv; ++j) {
+      const uint4 vv = *reinterpret_cast<const uint4*>(&v_s[j][8 * dc]);
+      const float2 pw = *reinterpret_cast<const float2*>(&p_s[j][2 * hg]);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int j = min(jb + u, nv - 1);
-        vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)slot_s[j] * kstride + 8 * dc);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        if (jb + u < nv) {
-          const float2 pw = *reinterpret_cast<const float2*>(&p_s[jb + u][2 * hg]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t wd = (&vr[u].x)[e >> 1];
-            const float ve = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
-            o[0][e] = fmaf(pw.x, ve, o[0][e]);
-            o[1][e] = fmaf(pw.y, ve, o[1][e]);
-          }
-        }
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wd = (&vv.x)[e >> 1];
+        const float ve = __uint_as_float((e & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+        o[0][e] = fmaf(pw.x, ve, o[0][e]);
+        o[1][e] = fmaf(pw.y, ve, o[1][e]);
       }
     }
     __syncthreads();
@@ -531,11 +537,14 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
   }
 }
 
-// Log-sum-exp merge of one (row, head)'s split partials; one thread per head dim.
+// Log-sum-exp merge of one (row, head)'s split partials: thread s < S reads split
+// s's (max, sum), the block forms the weights, then every thread (one head dim)
+// sums its dim over the splits, eight independent loads at a time.
 __global__ __launch_bounds__(kHeadDim) void local_decode_gqa_combine(ProbDev p, int nsplit,
                                                                      const float* __restrict__ part,
                                                                      bf16_t* __restrict__ out,
                                                                      float* __restrict__ lse) {
+  static_assert(kGMaxSplit <= kHeadDim, "one thread per split");
   const int row = blockIdx.x / kGH, h = blockIdx.x % kGH;
   const int b = row % p.batch, tile = row / p.batch;
   if (h >= p.gtile_cnt[tile]) return;
@@ -548,14 +557,33 @@ __global__ __launch_bounds__(kHeadDim) void local_decode_gqa_combine(ProbDev p, 
   const int qrow = p.cu_q[b];
   const float* rec0 = part + (size_t)row * nsplit * kGH * kPart + (size_t)h * kPart;
   const size_t sstride = (size_t)kGH * kPart;
-  float M = -INFINITY;
-  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, rec0[sp * sstride]);
-  float acc = 0.f, sum = 0.f;
-  for (int sp = 0; sp < S; ++sp) {
-    const float* r = rec0 + sp * sstride;
-    const float wv = __builtin_amdgcn_exp2f(r[0] - M);
-    sum = fmaf(r[1], wv, sum);
-    acc = fmaf(r[2 + tid], wv, acc);
+  __shared__ float w_s[kGMaxSplit];
+  __shared__ float red_s[kHeadDim / 64];
+  __shared__ float red2_s[kHeadDim / 64];
+  const float ms = (tid < S) ? rec0[tid * sstride] : -INFINITY;
+  const float ls = (tid < S) ? rec0[tid * sstride + 1] : 0.f;
+  float mx = wave_max(ms);
+  if ((tid & 63) == 0) red_s[tid >> 6] = mx;
+  __syncthreads();
+  float M = red_s[0];
+#pragma unroll
+  for (int w2 = 1; w2 < kHeadDim / 64; ++w2) M = fmaxf(M, red_s[w2]);
+  const float wv = (tid < S) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+  if (tid < kGMaxSplit) w_s[tid] = wv;
+  float sl = wave_sum(ls * wv);
+  if ((tid & 63) == 0) red2_s[tid >> 6] = sl;
+  __syncthreads();
+  float sum = 0.f;
+#pragma unroll
+  for (int w2 = 0; w2 < kHeadDim / 64; ++w2) sum += red2_s[w2];
+  float acc = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float v8[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v8[u] = (s0 + u < S) ? rec0[(s0 + u) * sstride + 2 + tid] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (s0 + u < S) acc = fmaf(v8[u], w_s[s0 + u], acc);
   }
   out[((size_t)qrow * p.Hq + head) * kHeadDim + tid] = Elem<bf16_t>::from_f(acc / sum);
   if (lse && tid == 0) lse[(size_t)head * p.Tq + qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
