@@ -451,8 +451,9 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
           const bool valid = !check || n <= rk.pos;
-          better += (valid && d[i] > rk.dA) ? 1u : 0u;
-          inr[i] = valid && d[i] <= rk.dA && d[i] > rk.dB;
+          const bool above = d[i] > rk.dA;   // scores are finite: not above <=> d <= dA
+          better += (valid && above) ? 1u : 0u;
+          inr[i] = valid && !above && d[i] > rk.dB;
           any |= inr[i];
         }
         if (__builtin_amdgcn_ballot_w64(any)) {
