@@ -93,6 +93,21 @@ rtp_status check_problem(const rtp_problem* pr, ProbDev* out) {
     };
     tiles(rtp::attn_decode_tile_heads(), p.n_ltiles, p.ltile_start, p.ltile_cnt);
     tiles(rtp::attn_decode_group_heads(), p.n_gtiles, p.gtile_start, p.gtile_cnt);
+    // retrieval slots (ascending heads: a group's slots are consecutive)
+    p.n_rtiles = 0;
+    p.max_rtile = 0;
+    for (int r = 0; r < p.R; ++r) {
+      const int t = p.n_rtiles - 1;
+      if (t >= 0 && p.rtile_cnt[t] < rtp::attn_decode_group_heads() &&
+          rtp::kv_of(p, p.ret_heads[p.rtile_start[t]]) == rtp::kv_of(p, p.ret_heads[r])) {
+        ++p.rtile_cnt[t];
+      } else {
+        p.rtile_start[p.n_rtiles] = (uint8_t)r;
+        p.rtile_cnt[p.n_rtiles] = 1;
+        ++p.n_rtiles;
+      }
+    }
+    for (int t = 0; t < p.n_rtiles; ++t) p.max_rtile = p.max_rtile > p.rtile_cnt[t] ? p.max_rtile : p.rtile_cnt[t];
   }
   return RTP_OK;
 }

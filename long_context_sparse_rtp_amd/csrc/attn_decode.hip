@@ -375,16 +375,23 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, const
   if (lse && tid == 0) lse[(size_t)head * p.Tq + ri.qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
 }
 
-// ---- bfloat16 local heads: a KV group's heads together on the matrix cores.
-// A row is (tile of up to kGH local heads of one KV group, sequence); its key
-// list (sinks, then window) is cut into chunks of kGChunk keys and a row's
-// chunks are dealt round-robin to nsplit one-wave workgroups.  Per chunk the
-// wave
+// ---- bfloat16, a KV group's heads together on the matrix cores (group_decode):
+//   local heads: a row is (tile of up to kGH local heads of one KV group,
+//     sequence) over the sinks + window list, in chunks of kGChunk keys;
+//   retrieval heads, when a group holds two or more of them: a row is (tile of
+//     the group's retrieval heads, sequence) over the union of their LISTs
+//     (each K/V row of the group is read once for all heads that selected it,
+//     the group-wise loading of "Full Attention Strikes Back ...", paper-graph-ui
+//     summary, Table 6), in ranges of kUR positions: the range's entries of each
+//     head's LIST (located through a boundary table) mark the positions in LDS,
+//     the marked positions form the chunk and a (head, key) pair outside the
+//     head's LIST is masked out.
+// A row's chunks are dealt round-robin to nsplit one-wave workgroups.  Per chunk
+// the wave
 //   - issues every load first: K rows straight into MFMA operand layout and
 //     the V rows (16 lanes per row), so it waits on memory once;
 //   - scores the keys against the tile's heads with 16x16x32 MFMAs (A = K,
-//     B = the heads' queries; each K row is read once for every head of the
-//     group),
+//     B = the heads' queries),
 //   - updates every head's running max and sum (16-lane groups of the output
 //     layout hold one head's scores) and stores the chunk's weights and V rows
 //     in LDS,
@@ -398,38 +405,76 @@ static_assert(kGChunk % 16 == 0 && kGChunk <= 64, "16-key MFMA tiles; one slot p
 constexpr int kGMaxSplit = 64;   // splits per row at most
 constexpr int kGTargetWaves = 2048;
 
-__global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, const bf16_t* __restrict__ q,
-                                                       const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
-                                                       float* __restrict__ part) {
+constexpr int kUR = 64;          // positions per range of the retrieval union path
+
+// Boundaries of every retrieval slot's LIST in ranges of kUR positions:
+// bnd[(r * batch + b) * (nr + 1) + s] = the first list entry at a position >= s * kUR
+// (the list is ascending), for s = 0 .. ceil(L / kUR).
+__global__ __launch_bounds__(256) void ret_union_bounds(ProbDev p, rtp_selection sel, int nr,
+                                                        int* __restrict__ bnd) {
+  const int row = blockIdx.y;
+  const int r = row / p.batch, b = row % p.batch;
+  const int L = p.cu_k[b + 1] - p.cu_k[b];
+  const int nrng = (L + kUR - 1) / kUR;
+  const int count = min(sel.count[(size_t)r * p.Tq + p.cu_q[b]], L);
+  const int* list = sel.idx + (size_t)r * p.Tk + key_row0(p, b);
+  int* B = bnd + (size_t)row * (nr + 1);
+  auto range_of = [&](int i) { return min(max(list[i], 0) / kUR, max(nrng - 1, 0)); };
+  if (count <= 0) {
+    for (int t = blockIdx.x * 256 + threadIdx.x; t <= nrng; t += gridDim.x * 256) B[t] = 0;
+    return;
+  }
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < count; i += gridDim.x * 256) {
+    const int s = range_of(i);
+    const int sp = (i == 0) ? -1 : range_of(i - 1);
+    for (int t = sp + 1; t <= s; ++t) B[t] = i;
+    if (i == count - 1)
+      for (int t = s + 1; t <= nrng; ++t) B[t] = count;
+  }
+}
+
+// RET = false: a tile of local heads over sinks + window, chunks of kGChunk keys.
+// RET = true: a tile of retrieval heads of one KV group over the union of their
+// LISTs, chunks = ranges of kUR positions; a (head, key) pair outside the head's
+// LIST is masked out.
+template <bool RET>
+__global__ __launch_bounds__(64) void group_decode(ProbDev p, int nsplit, int nr, const bf16_t* __restrict__ q,
+                                                   const bf16_t* __restrict__ k, const bf16_t* __restrict__ v,
+                                                   const rtp_selection sel, const int* __restrict__ bnd,
+                                                   float* __restrict__ part) {
+  constexpr int CH = RET ? kUR : kGChunk;   // keys (positions) per chunk
   const int split = blockIdx.x, row = blockIdx.y;
   const int b = row % p.batch, tile = row / p.batch;
   const int lane = threadIdx.x, col = lane & 15, g = lane >> 4;
   const int L = p.cu_k[b + 1] - p.cu_k[b];
   const int W = min(p.window, L);
   const int ns = min(p.n_sink, L - W);
-  const int count = ns + W;
-  const int nchunk = (count + kGChunk - 1) / kGChunk;
+  const int count = RET ? L : ns + W;       // positions walked
+  const int nchunk = (count + CH - 1) / CH;
   if (split >= min(nsplit, nchunk)) return;
-  const int nh = p.gtile_cnt[tile];
-  const int hl0 = p.gtile_start[tile];
-  const int kvg = kv_of(p, p.local_heads[hl0]);
+  const int nh = RET ? p.rtile_cnt[tile] : p.gtile_cnt[tile];
+  const int h0 = RET ? p.rtile_start[tile] : p.gtile_start[tile];
+  auto head_at = [&](int i) { return RET ? p.ret_heads[h0 + i] : p.local_heads[h0 + i]; };
+  const int kvg = kv_of(p, head_at(0));
   const int qrow = p.cu_q[b];
   const size_t kstride = (size_t)p.Hkv * kHeadDim;
   const bf16_t* kb = k + ((size_t)key_row0(p, b) * p.Hkv + kvg) * kHeadDim;
   const bf16_t* vb = v + ((size_t)key_row0(p, b) * p.Hkv + kvg) * kHeadDim;
   const float qscale = 0.08838834764831845f * kLog2e;   // log2(e) / sqrt(128)
 
-  __shared__ int slot_s[kGChunk];
-  __shared__ __attribute__((aligned(16))) float p_s[kGChunk][kGH];
+  __shared__ int slot_s[CH];
+  __shared__ uint32_t hm_s[RET ? CH : 1];    // union: heads selecting position c * CH + i
+  __shared__ uint32_t um_s[RET ? CH : 1];    // union: heads selecting the chunk's key j
+  __shared__ __attribute__((aligned(16))) float p_s[CH][kGH];
   __shared__ float scale_s[kGH];
-  __shared__ __attribute__((aligned(16))) bf16_t v_s[kGChunk][kHeadDim + 8];   // the chunk's V rows
+  __shared__ __attribute__((aligned(16))) bf16_t v_s[CH][kHeadDim + 8];   // the chunk's V rows
 
   // B operand: column = head slot col (zero past the tile), k = dims 32 kc + 8 g .. + 8
   FragBF16 qf[4];
 #pragma unroll
   for (int kc = 0; kc < 4; ++kc) {
     if (col < nh) {
-      load_frag(qf[kc], q + ((size_t)qrow * p.Hq + p.local_heads[hl0 + col]) * kHeadDim + 32 * kc + 8 * g);
+      load_frag(qf[kc], q + ((size_t)qrow * p.Hq + head_at(col)) * kHeadDim + 32 * kc + 8 * g);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[kc].v[e] = (__bf16)0.f;
@@ -444,13 +489,42 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
     for (int e = 0; e < 8; ++e) o[u][e] = 0.f;
 
   for (int c = split; c < nchunk; c += nsplit) {
-    const int j0 = c * kGChunk;
-    const int nv = min(kGChunk, count - j0);   // valid keys of the chunk (>= 1)
-    if (lane < kGChunk) slot_s[lane] = key_slot(p, local_token(p, L, j0 + min(lane, nv - 1)));
-    __syncthreads();
+    int nv;
+    if (RET) {
+      // the range's entries of every head's LIST mark the positions they select
+      if (lane < CH) hm_s[lane] = 0u;
+      __syncthreads();
+      for (int hh = 0; hh < nh; ++hh) {
+        const int* Bh = bnd + (size_t)((h0 + hh) * p.batch + b) * (nr + 1);
+        const int* list = sel.idx + (size_t)(h0 + hh) * p.Tk + key_row0(p, b);
+        const int e1 = Bh[c + 1];
+        for (int i = Bh[c] + lane; i < e1; i += 64) {
+          const int d = list[i] - c * CH;
+          if (d >= 0 && d < CH) atomicOr(&hm_s[d], 1u << hh);
+        }
+      }
+      __syncthreads();
+      const uint32_t mk = (lane < CH) ? hm_s[lane] : 0u;
+      const unsigned long long bal = __builtin_amdgcn_ballot_w64(mk != 0u);
+      nv = __popcll(bal);
+      if (mk) {
+        const int at = __popcll(bal & ((1ull << lane) - 1ull));
+        slot_s[at] = c * CH + lane;
+        um_s[at] = mk;
+      }
+      __syncthreads();
+      if (nv == 0) continue;   // no head selects a key of this range
+      if (lane < CH && lane >= nv) slot_s[lane] = slot_s[nv - 1];
+      __syncthreads();
+    } else {
+      const int j0 = c * CH;
+      nv = min(CH, count - j0);   // valid keys of the chunk (>= 1)
+      if (lane < CH) slot_s[lane] = key_slot(p, local_token(p, L, j0 + min(lane, nv - 1)));
+      __syncthreads();
+    }
     // every load of the chunk first: K in operand layout, V rows (16 lanes per row,
     // key (lane >> 4) + 4 u), so the chunk waits on memory once
-    constexpr int NT = kGChunk / 16;   // 16-key tiles of a chunk
+    constexpr int NT = CH / 16;   // 16-key tiles of a chunk
     FragBF16 kf[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -458,9 +532,9 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
 #pragma unroll
       for (int kc = 0; kc < 4; ++kc) load_frag(kf[t][kc], kr + 32 * kc);
     }
-    uint4 vr[kGChunk / 4];
+    uint4 vr[CH / 4];
 #pragma unroll
-    for (int u = 0; u < kGChunk / 4; ++u)
+    for (int u = 0; u < CH / 4; ++u)
       vr[u] = *reinterpret_cast<const uint4*>(vb + (size_t)slot_s[g + 4 * u] * kstride + 8 * col);
     // scores: tile t holds keys 16 t .. 16 t + 15 (rows) x heads (columns)
     f32x4 sc[NT];
@@ -477,19 +551,22 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = 16 * t + 4 * g + i;
-        sc[t][i] = (j < nv) ? sc[t][i] * qscale : -INFINITY;
+        bool ok = j < nv;
+        if (RET) ok = ok && ((um_s[j] >> col) & 1u);
+        sc[t][i] = ok ? sc[t][i] * qscale : -INFINITY;
         mx = fmaxf(mx, sc[t][i]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mn = fmaxf(m_run, mx);
-    const float rs = __builtin_amdgcn_exp2f(m_run - mn);
+    const float mref = (mn == -INFINITY) ? 0.f : mn;   // a head with no key yet keeps l = 0
+    const float rs = __builtin_amdgcn_exp2f(m_run - mref);
     float ls = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float pe = __builtin_amdgcn_exp2f(sc[t][i] - mn);
+        const float pe = __builtin_amdgcn_exp2f(sc[t][i] - mref);
         ls += pe;
         if (col < kGH) p_s[16 * t + 4 * g + i][col] = pe;
       }
@@ -499,9 +576,9 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
     m_run = mn;
     if (g == 0 && col < kGH) scale_s[col] = rs;
 #pragma unroll
-    for (int u = 0; u < kGChunk / 4; ++u) *reinterpret_cast<uint4*>(&v_s[g + 4 * u][8 * col]) = vr[u];
+    for (int u = 0; u < CH / 4; ++u) *reinterpret_cast<uint4*>(&v_s[g + 4 * u][8 * col]) = vr[u];
     __syncthreads();
-    // P V: lane (dc, hg) over the chunk's valid keys (weights of keys past nv are 0)
+    // P V: lane (dc, hg) over the chunk's valid keys (weights of masked keys are 0)
     {
       const float r0 = scale_s[2 * hg], r1 = scale_s[2 * hg + 1];
 #pragma unroll
@@ -540,20 +617,22 @@ __global__ __launch_bounds__(64) void local_decode_gqa(ProbDev p, int nsplit, co
 // Log-sum-exp merge of one (row, head)'s split partials: thread s < S reads split
 // s's (max, sum), the block forms the weights, then every thread (one head dim)
 // sums its dim over the splits, eight independent loads at a time.
-__global__ __launch_bounds__(kHeadDim) void local_decode_gqa_combine(ProbDev p, int nsplit,
-                                                                     const float* __restrict__ part,
-                                                                     bf16_t* __restrict__ out,
-                                                                     float* __restrict__ lse) {
+template <bool RET>
+__global__ __launch_bounds__(kHeadDim) void group_decode_combine(ProbDev p, int nsplit,
+                                                                 const float* __restrict__ part,
+                                                                 bf16_t* __restrict__ out,
+                                                                 float* __restrict__ lse) {
   static_assert(kGMaxSplit <= kHeadDim, "one thread per split");
   const int row = blockIdx.x / kGH, h = blockIdx.x % kGH;
   const int b = row % p.batch, tile = row / p.batch;
-  if (h >= p.gtile_cnt[tile]) return;
+  if (h >= (RET ? p.rtile_cnt[tile] : p.gtile_cnt[tile])) return;
   const int tid = threadIdx.x;
-  const int head = p.local_heads[p.gtile_start[tile] + h];
+  const int head = RET ? p.ret_heads[p.rtile_start[tile] + h] : p.local_heads[p.gtile_start[tile] + h];
   const int L = p.cu_k[b + 1] - p.cu_k[b];
   const int W = min(p.window, L);
-  const int count = min(p.n_sink, L - W) + W;
-  const int S = min(nsplit, (count + kGChunk - 1) / kGChunk);
+  const int count = RET ? L : min(p.n_sink, L - W) + W;
+  const int CH = RET ? kUR : kGChunk;
+  const int S = min(nsplit, (count + CH - 1) / CH);
   const int qrow = p.cu_q[b];
   const float* rec0 = part + (size_t)row * nsplit * kGH * kPart + (size_t)h * kPart;
   const size_t sstride = (size_t)kGH * kPart;
@@ -568,7 +647,7 @@ __global__ __launch_bounds__(kHeadDim) void local_decode_gqa_combine(ProbDev p, 
   float M = red_s[0];
 #pragma unroll
   for (int w2 = 1; w2 < kHeadDim / 64; ++w2) M = fmaxf(M, red_s[w2]);
-  const float wv = (tid < S) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
+  const float wv = (tid < S && ms != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.f;
   if (tid < kGMaxSplit) w_s[tid] = wv;
   float sl = wave_sum(ls * wv);
   if ((tid & 63) == 0) red2_s[tid >> 6] = sl;
@@ -585,8 +664,9 @@ __global__ __launch_bounds__(kHeadDim) void local_decode_gqa_combine(ProbDev p, 
     for (int u = 0; u < 8; ++u)
       if (s0 + u < S) acc = fmaf(v8[u], w_s[s0 + u], acc);
   }
-  out[((size_t)qrow * p.Hq + head) * kHeadDim + tid] = Elem<bf16_t>::from_f(acc / sum);
-  if (lse && tid == 0) lse[(size_t)head * p.Tq + qrow] = (M + __log2f(sum)) * 0.6931471805599453f;
+  const bool none = !(sum > 0.f);   // no key at all (an empty set): zeros, lse = -inf
+  out[((size_t)qrow * p.Hq + head) * kHeadDim + tid] = Elem<bf16_t>::from_f(none ? 0.f : acc / sum);
+  if (lse && tid == 0) lse[(size_t)head * p.Tq + qrow] = none ? -INFINITY : (M + __log2f(sum)) * 0.6931471805599453f;
 }
 
 // splits per row of the bfloat16 local path: about kGTargetWaves waves in all
@@ -600,8 +680,23 @@ inline int gqa_nsplit(const ProbDev& p) {
 inline size_t ws_gqa(const ProbDev& p) {
   return sizeof(float) * (size_t)p.n_gtiles * p.batch * gqa_nsplit(p) * kGH * kPart;
 }
-
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// the retrieval union path: groups holding two or more retrieval heads (bfloat16)
+inline bool use_union(const ProbDev& p, bool bf16) { return bf16 && p.max_rtile >= 2; }
+inline int union_nr(const ProbDev& p) { return max(1, (p.max_k + kUR - 1) / kUR); }
+inline int union_nsplit(const ProbDev& p) {
+  const int rows = p.n_rtiles * p.batch;
+  const int want = (kGTargetWaves + max(rows, 1) - 1) / max(rows, 1);
+  return max(1, min(min(union_nr(p), kGMaxSplit), want));
+}
+inline size_t ws_union_bnd(const ProbDev& p) {
+  return align256(sizeof(int) * (size_t)p.R * p.batch * (union_nr(p) + 1));
+}
+inline size_t ws_union(const ProbDev& p) {
+  return ws_union_bnd(p) + sizeof(float) * (size_t)p.n_rtiles * p.batch * union_nsplit(p) * kGH * kPart;
+}
+
 
 inline int rows_of(const ProbDev& p, int mode) { return ((mode == 0) ? p.R : p.n_ltiles) * p.batch; }
 inline int heads_per_row(int mode) { return (mode == 0) ? 1 : kMaxTileHeads; }
@@ -642,8 +737,10 @@ size_t ws_attn_decode(const ProbDev& p, int mode) {
   const int rows = rows_of(p, mode);
   const size_t split_list = align256(sizeof(int) * (size_t)(rows + 1)) +
                             sizeof(float) * max_work(p, mode, rows) * heads_per_row(mode) * kPart;
-  // local heads: float32 takes the split-list kernel, bfloat16 the group kernel
-  return mode == 1 ? max(split_list, ws_gqa(p)) : split_list;
+  // local heads: float32 takes the split-list kernel, bfloat16 the group kernel; retrieval
+  // heads: the split-list kernel, or the union kernel when a group holds two or more (bfloat16)
+  if (mode == 1) return max(split_list, ws_gqa(p));
+  return p.max_rtile >= 2 ? max(split_list, ws_union(p)) : split_list;
 }
 
 hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
@@ -655,9 +752,23 @@ hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void*
     const int grows = p.n_gtiles * p.batch;
     const int nsplit = gqa_nsplit(p);
     float* part = (float*)ws;
-    hipLaunchKernelGGL(local_decode_gqa, dim3(nsplit, grows), dim3(64), 0, s, p, nsplit, (const bf16_t*)q,
-                       (const bf16_t*)k, (const bf16_t*)v, part);
-    hipLaunchKernelGGL(local_decode_gqa_combine, dim3(grows * kGH), dim3(kHeadDim), 0, s, p, nsplit,
+    const rtp_selection none = {};
+    hipLaunchKernelGGL(group_decode<false>, dim3(nsplit, grows), dim3(64), 0, s, p, nsplit, 0, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, none, (const int*)nullptr, part);
+    hipLaunchKernelGGL(group_decode_combine<false>, dim3(grows * kGH), dim3(kHeadDim), 0, s, p, nsplit,
+                       (const float*)part, (bf16_t*)out, lse);
+    return hipGetLastError();
+  }
+  if (mode == 0 && use_union(p, bf16)) {
+    const int rrows = p.n_rtiles * p.batch;
+    const int nsplit = union_nsplit(p), nr = union_nr(p);
+    int* bnd = (int*)ws;
+    float* part = (float*)((char*)ws + ws_union_bnd(p));
+    const unsigned bgrid = (unsigned)max(1, (p.max_k + 255) / 256);
+    hipLaunchKernelGGL(ret_union_bounds, dim3(bgrid, p.R * p.batch), dim3(256), 0, s, p, *sel, nr, bnd);
+    hipLaunchKernelGGL(group_decode<true>, dim3(nsplit, rrows), dim3(64), 0, s, p, nsplit, nr, (const bf16_t*)q,
+                       (const bf16_t*)k, (const bf16_t*)v, *sel, (const int*)bnd, part);
+    hipLaunchKernelGGL(group_decode_combine<true>, dim3(rrows * kGH), dim3(kHeadDim), 0, s, p, nsplit,
                        (const float*)part, (bf16_t*)out, lse);
     return hipGetLastError();
   }

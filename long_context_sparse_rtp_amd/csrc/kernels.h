@@ -29,7 +29,13 @@ struct ProbDev {
   int n_gtiles;
   int gtile_start[RTP_MAX_HEADS];
   int gtile_cnt[RTP_MAX_HEADS];
+  // retrieval slots grouped by KV head the same way (slots r .. r + cnt - 1 of one
+  // group); max_rtile = the largest tile
+  int n_rtiles, max_rtile;
+  uint8_t rtile_start[RTP_MAX_HEADS];
+  uint8_t rtile_cnt[RTP_MAX_HEADS];
 };
+static_assert(sizeof(ProbDev) <= 3584, "ProbDev travels as a kernel argument (4 KB in all)");
 
 __host__ __device__ inline int kv_of(const ProbDev& p, int h) { return (h * p.Hkv) / p.Hq; }
 

@@ -161,6 +161,15 @@ def test_decode_groups_without_local_heads():
     _check_decode(make_inputs(cfg, DEV))
 
 
+def test_decode_union_three_retrieval_heads_ragged():
+    # KV group 0 holds retrieval heads 0, 1, 2 (their K/V rows are read once for the
+    # union of the three LISTs), group 1 one retrieval head; ragged lengths down to 1
+    cfg = scaled(DECODE_32K, name="decode_union3", batch=5, seqlens=(1, 63, 64, 65, 3000), n_q_heads=8,
+                 n_kv_heads=2, ret_heads=(0, 1, 2, 5), window=96, needles="query", needles_per_seq=4)
+    _say(f"[case] {cfg.name}")
+    _check_decode(make_inputs(cfg, DEV))
+
+
 def test_v_one_gives_one():
     cfg = scaled(PREFILL_128K, name="v_one", seqlen=800, window=64)
     _say(f"[case] {cfg.name}")

@@ -108,6 +108,14 @@ def test_topk_decode_ragged_extremes():
     _decode(cfg, [4096, 1, 300, 4096, 4096, 0])
 
 
+def test_topk_decode_union_of_group_heads():
+    # two retrieval heads per KV group: the attention reads each group's rows once
+    # for the union of the two top-k LISTs
+    cfg = scaled(DECODE_32K, name="topk_union_decode", batch=3, seqlens=(5000, 300, 9000), n_q_heads=8,
+                 n_kv_heads=2, ret_heads=(0, 1, 4, 7), window=128, needles="query", needles_per_seq=8)
+    _decode(cfg, [1024, 4096, 700])
+
+
 def test_topk_decode_exact_ties_all_equal():
     # every index key equal: the first k positions win
     cfg = scaled(DECODE_32K, name="topk_decode_ties", batch=2, seqlen=9000, needles="none")
