@@ -80,10 +80,16 @@ DEC = scaled(DECODE_32K, name="cache_decode", batch=3, seqlens=(5000, 300, 7000)
              needles_per_seq=16)
 
 
-def test_capacity_layout_decode_matches_oracle_and_packed():
+# two retrieval heads per KV group: the decode attention takes the union path
+DEC_UNION = scaled(DECODE_32K, name="cache_decode_union", batch=3, seqlens=(5000, 300, 7000), n_q_heads=8,
+                   n_kv_heads=2, ret_heads=(0, 2, 4, 5), window=200, needles="query", needles_per_seq=16)
+
+
+@pytest.mark.parametrize("cfg", [DEC, DEC_UNION], ids=["one_retrieval_head_per_group", "union"])
+def test_capacity_layout_decode_matches_oracle_and_packed(cfg):
     rtp = _rtp()
-    _say("[case] capacity layout decode")
-    inp = make_inputs(DEC, DEV)
+    _say(f"[case] capacity layout decode {cfg.name}")
+    inp = make_inputs(cfg, DEV)
     cu = inp.cu_k.cpu().tolist()
     cap = 8192
     prob = _problem(inp, cap)
