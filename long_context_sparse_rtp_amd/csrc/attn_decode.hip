@@ -358,15 +358,15 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, const
     if ((tid & 63) == 0) red2_s[tid >> 6] = sl;
     __syncthreads();
     if (tid == 0) sum_s = red2_s[0] + red2_s[1];
-    int s = 0;
-    for (; s + 8 <= cn; s += 8) {
-      float v8[8];
+    // 32 independent loads in flight, summed in split order
+    for (int s = 0; s < cn; s += 32) {
+      float v32[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v8[u] = rec_of(c0 + s + u)[2 + tid];
+      for (int u = 0; u < 32; ++u) v32[u] = (s + u < cn) ? rec_of(c0 + s + u)[2 + tid] : 0.f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(v8[u], wgt_s[s + u], acc);
+      for (int u = 0; u < 32; ++u)
+        if (s + u < cn) acc = fmaf(v32[u], wgt_s[s + u], acc);
     }
-    for (; s < cn; ++s) acc = fmaf(rec_of(c0 + s)[2 + tid], wgt_s[s], acc);
     __syncthreads();
     sum += sum_s;
     __syncthreads();
@@ -616,7 +616,7 @@ __global__ __launch_bounds__(64) void group_decode(ProbDev p, int nsplit, int nr
 
 // Log-sum-exp merge of one (row, head)'s split partials: thread s < S reads split
 // s's (max, sum), the block forms the weights, then every thread (one head dim)
-// sums its dim over the splits, eight independent loads at a time.
+// sums its dim over the splits, 32 independent loads at a time.
 template <bool RET>
 __global__ __launch_bounds__(kHeadDim) void group_decode_combine(ProbDev p, int nsplit,
                                                                  const float* __restrict__ part,
@@ -656,13 +656,13 @@ __global__ __launch_bounds__(kHeadDim) void group_decode_combine(ProbDev p, int 
 #pragma unroll
   for (int w2 = 0; w2 < kHeadDim / 64; ++w2) sum += red2_s[w2];
   float acc = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float v8[8];
+  for (int s0 = 0; s0 < S; s0 += 32) {
+    float v32[32];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v8[u] = (s0 + u < S) ? rec0[(s0 + u) * sstride + 2 + tid] : 0.f;
+    for (int u = 0; u < 32; ++u) v32[u] = (s0 + u < S) ? rec0[(s0 + u) * sstride + 2 + tid] : 0.f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
-      if (s0 + u < S) acc = fmaf(v8[u], w_s[s0 + u], acc);
+    for (int u = 0; u < 32; ++u)
+      if (s0 + u < S) acc = fmaf(v32[u], w_s[s0 + u], acc);
   }
   const bool none = !(sum > 0.f);   // no key at all (an empty set): zeros, lse = -inf
   out[((size_t)qrow * p.Hq + head) * kHeadDim + tid] = Elem<bf16_t>::from_f(none ? 0.f : acc / sum);
