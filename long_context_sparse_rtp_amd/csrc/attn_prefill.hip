@@ -42,9 +42,11 @@ namespace rtp {
 
 namespace {
 
-constexpr int kWaves = 8;                 // waves per workgroup, 32 query rows each
+constexpr int NC = 2;                     // 16-row MFMA column tiles per wave
+constexpr int kWaves = 8;                 // waves per workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int BQ = 32 * kWaves;           // query rows per workgroup
+constexpr int RW = 16 * NC;               // query rows per wave
+constexpr int BQ = RW * kWaves;           // query rows per workgroup
 constexpr int KT = 64;          // keys per tile
 static_assert((KT / 2) * (kHeadDim / 8) % kThreads == 0, "V staging splits evenly over the workgroup");
 static_assert(KT * kHeadDim / 8 % kThreads == 0, "K staging splits evenly over the workgroup");
@@ -244,7 +246,7 @@ __device__ __forceinline__ Work work_of(int bid, int nheads, int batch, int tile
 __host__ __device__ inline bool per_head_xcd(int mode, int nheads) { return mode == 0 && nheads <= 8 && 8 % nheads == 0; }
 
 template <typename T, int MODE>
-__global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     ProbDev p, int nheads, int tiles_per_b, const T* __restrict__ q, const T* __restrict__ k,
     const T* __restrict__ v, const T* __restrict__ k_idx, const rtp_selection sel, T* __restrict__ out,
     float* __restrict__ lse) {
@@ -279,29 +281,31 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
   const T* vg = v + ((size_t)k0 * p.Hkv + g) * kHeadDim;
 
   // ---- this wave's query rows: i0 + 32w + 16c + col
-  F qf[2][4];
-  int qi[2], qpos[2];
-  bool qok[2];
+  F qf[NC][4];
+  int qi[NC], qpos[NC];
+  bool qok[NC];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    qi[c] = i0 + 32 * w + 16 * c + col;
+  for (int c = 0; c < NC; ++c) {
+    qi[c] = i0 + RW * w + 16 * c + col;
     qok[c] = qi[c] < Lq;
     qpos[c] = off + (qok[c] ? qi[c] : (Lq - 1));
     const T* qp = q + ((size_t)(q0 + (qok[c] ? qi[c] : Lq - 1)) * p.Hq + h) * kHeadDim + 8 * grp;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) load_frag(qf[c][kc], qp + 32 * kc);
   }
-  const int wpos_lo = off + min(i0 + 32 * w, Lq - 1);
-  const int wpos_hi = off + min(i0 + 32 * w + 31, Lq - 1);
-  IF qxf[2];
-  float tau4[2] = {0.f, 0.f};
-  int tie[2] = {0, 0};
+  const int wpos_lo = off + min(i0 + RW * w, Lq - 1);
+  const int wpos_hi = off + min(i0 + RW * w + RW - 1, Lq - 1);
+  IF qxf[NC];
+  float tau4[NC];
+  int tie[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) { tau4[c] = 0.f; tie[c] = 0; }
   bool exact_ties = false;
   bool all_keys = false;
   const T* kxb = nullptr;
   if (MODE == 0) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < NC; ++c) {
       const size_t qr = (size_t)hidx * p.Tq + q0 + (qok[c] ? qi[c] : Lq - 1);
       load_idx_frag(qxf[c], (const T*)sel.q_idx + qr * kIdxDim + 4 * grp);
       tau4[c] = sel.tau[qr] * 4.f;   // compare raw dot products: dot / 4 vs tau is exact
@@ -312,21 +316,27 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
     kxb = k_idx + ((size_t)hidx * p.Tk + k0) * kIdxDim;
     // every row of this wave keeps its whole causal prefix (p >= 1, tau = -inf):
     // dense causal attention, no indexer work
-    all_keys = __builtin_amdgcn_ballot_w64(!(tau4[0] == -INFINITY && tau4[1] == -INFINITY)) == 0;
+    bool rows_all = true;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) rows_all &= (tau4[c] == -INFINITY);
+    all_keys = __builtin_amdgcn_ballot_w64(!rows_all) == 0;
   }
 
   const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
-  float m_[2] = {-INFINITY, -INFINITY};
+  float m_[NC];
   // row sums of P on the matrix cores: a constant all-ones A operand turns
   // O^T += V^T P^T into sum_k P[k][row] in every output row (and sums exactly
   // the rounded P that multiplies V)
-  f32x4 lacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  f32x4 lacc[NC];
   const F onesf = ones_frag<F>();
-  f32x4 oacc[2][8];
+  f32x4 oacc[NC][8];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int c = 0; c < NC; ++c) {
+    m_[c] = -INFINITY;
+    lacc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) oacc[c][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- key tiles of the workgroup
   const int pos_lo = off + i0;
@@ -401,9 +411,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
       }
       __builtin_amdgcn_s_setprio(0);   // matrix-core phase: waves in their ALU phase issue first
       // S^T = K Q^T
-      f32x4 sacc[2][4];
+      f32x4 sacc[NC][4];
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+      for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sacc[c][ks] = f32x4{0.f, 0.f, 0.f, 0.f};
       const T* kt_s = k_s[buf];
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
           F kf;
           load_frag(kf, kt_s + (16 * ks + col) * KS + 32 * kc + 8 * grp);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) sacc[c][ks] = mma_k32(kf, qf[c][kc], sacc[c][ks]);
+          for (int c = 0; c < NC; ++c) sacc[c][ks] = mma_k32(kf, qf[c][kc], sacc[c][ks]);
         }
       }
       __builtin_amdgcn_s_setprio(2);
@@ -424,9 +434,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
       // compile-time offset with per-row differences computed once per tile
       // (per-element key counters would cost a register and an add each).
       const int kb4 = kbase + 4 * grp;
-      int relq[2], relt[2];
+      int relq[NC], relt[NC];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NC; ++c) {
         relq[c] = opaque_int(qpos[c] - kb4);   // key <= qpos  <=>  16 ks + i <= relq
         relt[c] = opaque_int(tie[c] - kb4);    // key <= tie   <=>  16 ks + i <= relt
       }
@@ -437,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
 #pragma unroll
           for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
+            for (int c = 0; c < NC; ++c) {
               const f32x4 dx = idx_dot_tile(kxf[ks], qxf[c]);
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
@@ -456,7 +466,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-              for (int c = 0; c < 2; ++c)
+              for (int c = 0; c < NC; ++c)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                   sacc[c][ks][i] = (16 * ks + i <= relq[c]) ? sacc[c][ks][i] : -INFINITY;
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-          for (int c = 0; c < 2; ++c)
+          for (int c = 0; c < NC; ++c)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int ko = 16 * ks + i;
@@ -483,10 +493,10 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
       }
 
       // online softmax (log2 domain)
-      F pf[2][2];
+      F pf[NC][2];
       bool live = false;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+      for (int c = 0; c < NC; ++c) {
         float tmax = -INFINITY;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -532,9 +542,9 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-            for (int c = 0; c < 2; ++c) oacc[c][dt] = mma_k32(vf[dt], pf[c][kk], oacc[c][dt]);
+            for (int c = 0; c < NC; ++c) oacc[c][dt] = mma_k32(vf[dt], pf[c][kk], oacc[c][dt]);
 #pragma unroll
-          for (int c = 0; c < 2; ++c) lacc[c] = mma_k32(onesf, pf[c][kk], lacc[c]);
+          for (int c = 0; c < NC; ++c) lacc[c] = mma_k32(onesf, pf[c][kk], lacc[c]);
         }
       }
     }
@@ -548,7 +558,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void attn_prefill_kernel(
 
   // ---- normalise and store
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const float lt = lacc[c][0];   // every output row of the ones tile holds the row sum
     if (!qok[c]) continue;
     const float inv = (lt > 0.f) ? 1.f / lt : 0.f;
