@@ -14,7 +14,7 @@
 //   - a row is (retrieval slot, sequence), or (tile of local heads of one KV
 //     group, sequence); tiles hold one head at present: holding several lets
 //     a K/V row feed all of them, but costs more in cross-lane reductions;
-//   - every row's key set is cut into equal splits of at most 512 entries,
+//   - every row's key set is cut into equal splits of at most 1024 entries,
 //     sized from the total entry count so that the splits of all rows fit the
 //     resident grid once; the splits form one flat work list (prefix sums of the
 //     per-row split counts, computed by every workgroup) that the grid walks
@@ -36,7 +36,7 @@ namespace rtp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kSplit = 512;              // most entries per split
+constexpr int kSplit = 1024;             // most entries per split
 constexpr int kMinSplit = 64;            // fewest entries per split (unless a row holds fewer)
 constexpr int kBalance = 1;              // 1: size splits so that every row fits the grid once; 0: kSplit
 constexpr int kGroups = kThreads / 16;   // 16-lane groups per workgroup
