@@ -717,8 +717,26 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
   const int A = rs.A, Ap = rs.Ap;
   const double target = rs.target;
   auto bin_of = [&](float v) { return min(kNB - 1, Ap - abs_bin(v)); };
-  // per unit: reference bin, scale, candidate count and base
+  // per unit: candidate count and base (consecutive units per thread, for the scan;
+  // their loads are issued first), reference bin and scale (units dealt round-robin,
+  // so that a row of up to 256 units costs every thread at most one float64 exp2)
   constexpr int PU = kMaxUnits / kThreads;
+  UnitCnt ucv[PU];
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid * PU + t;
+    ucv[t] = UnitCnt{0u, 0u};
+    if (u < g.U) ucv[t] = ws.ucnt[g.slot0 + u];
+  }
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid + t * kThreads;
+    if (u < g.U) {
+      const UnitMeta mt = ws.meta[g.slot0 + u];
+      A_s[u] = mt.A;
+      f_s[u] = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
+    }
+  }
   uint32_t nin = 0u, cmax = 0u;
   uint32_t vin[PU];
 #pragma unroll
@@ -726,10 +744,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
     const int u = tid * PU + t;
     vin[t] = 0u;
     if (u < g.U) {
-      const UnitMeta mt = ws.meta[g.slot0 + u];
-      const UnitCnt uc = ws.ucnt[g.slot0 + u];
-      A_s[u] = mt.A;
-      f_s[u] = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
+      const UnitCnt uc = ucv[t];
       vin[t] = uc.inbin;
       cab_s[u] = uc.above;
       cmem_s[u] = 0u;
