@@ -543,22 +543,18 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
       }
     }
   }
+  if (tid == 0) { cstar_s = kRowCoarse; clast_s = -1; nc_s = 0; }   // ordered by the scans' barriers
   {
-    double part, rest;
-    uint32_t partc, restc;
-    (void)block_exscan_f64_n<kThreads / 64>(cm, dtmp, part);
-    (void)block_exscan<uint32_t>(cc, utmp, partc);
-    // the open-ended last bin: the row's remainder
-    rest = fmax((cmode ? (double)g.L : Z) - part, 0.0);
-    restc = (uint32_t)g.L - partc;
-    if (tid == kRowCoarse - 1) { cm = rest; cc = restc; }
-  }
-  if (tid == 0) { cstar_s = kRowCoarse; clast_s = -1; nc_s = 0; }
-  {
-    double ctot;
-    uint32_t ctotc;
-    const double pre = block_exscan_f64_n<kThreads / 64>(cm, dtmp, ctot);
-    const uint32_t cpre = block_exscan<uint32_t>(cc, utmp, ctotc);
+    // one scan gives every bin's prefix and, the last bin holding 0 here, the total of
+    // the others: the open-ended last bin is the row's remainder
+    double part;
+    uint32_t partc;
+    const double pre = block_exscan_f64_n<kThreads / 64>(cm, dtmp, part);
+    const uint32_t cpre = block_exscan<uint32_t>(cc, utmp, partc);
+    if (tid == kRowCoarse - 1) {
+      cm = fmax((cmode ? (double)g.L : Z) - part, 0.0);
+      cc = (uint32_t)g.L - partc;
+    }
     if (cc > 0u && pre < target && pre + cm >= target) atomicMin(&cstar_s, tid);
     if (cc > 0u) atomicMax(&clast_s, tid);
     __syncthreads();
