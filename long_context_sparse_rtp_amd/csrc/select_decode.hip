@@ -155,6 +155,22 @@ __device__ __forceinline__ RowGeom row_geom(const ProbDev& p, int row) {
   return g;
 }
 
+// Work order of the score, collect and emit kernels: workgroups are dealt to the 8
+// XCDs round-robin by block id and each XCD has its own L2, so all units of a row go
+// to one XCD (block b: k = b / 8, row = 8 (k / U) + b % 8, unit k % U, U unit slots
+// per row), where the collect and emit steps find the row's histograms, scores and
+// candidates in L2.
+__host__ __device__ inline int unit_slots(const ProbDev& p) { return max(1, max_units(p)); }
+__host__ __device__ inline unsigned unit_blocks(const ProbDev& p) {
+  return 8u * (unsigned)((p.R * p.batch + 7) / 8) * (unsigned)unit_slots(p);
+}
+__device__ __forceinline__ void unit_of(const ProbDev& p, int b, int& row, int& c) {
+  const int U = unit_slots(p);
+  const int k = b >> 3;
+  row = 8 * (k / U) + (b & 7);
+  c = k % U;
+}
+
 // ---- block-wide helpers (256 threads, fixed evaluation order)
 template <typename V>
 __device__ V block_exscan(V x, V* tmp /* >= 4 */, V& total) {
@@ -323,8 +339,10 @@ __global__ __launch_bounds__(kThreads) void sel_dec_score(ProbDev p, const T* __
                                                           const float* __restrict__ w_q,
                                                           const T* __restrict__ k_idx, rtp_selection sel,
                                                           DecodeWs ws) {
-  const RowGeom g = row_geom(p, blockIdx.y);
-  const int c = blockIdx.x;
+  int row, c;
+  unit_of(p, blockIdx.x, row, c);
+  if (row >= p.R * p.batch) return;
+  const RowGeom g = row_geom(p, row);
   if (c >= g.U || g.U > kMaxUnits) return;
   const int tid = threadIdx.x;
   const int64_t slot = g.slot0 + c;
@@ -443,8 +461,10 @@ __device__ __forceinline__ double bin_mass(unsigned long long e, double f, bool 
 __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const float* __restrict__ top_p,
                                                             const int32_t* __restrict__ top_k, rtp_selection sel,
                                                             DecodeWs ws) {
-  const RowGeom g = row_geom(p, blockIdx.y);
-  const int c = blockIdx.x;
+  int row, c;
+  unit_of(p, blockIdx.x, row, c);
+  if (row >= p.R * p.batch) return;
+  const RowGeom g = row_geom(p, row);
   if (c >= g.U || g.U > kMaxUnits) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const bool cmode = top_k != nullptr;
@@ -670,8 +690,10 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
 // pattern and then positions.
 __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_t* __restrict__ top_k,
                                                          rtp_selection sel, DecodeWs ws) {
-  const RowGeom g = row_geom(p, blockIdx.y);
-  const int c = blockIdx.x;
+  int row, c;
+  unit_of(p, blockIdx.x, row, c);
+  if (row >= p.R * p.batch) return;
+  const RowGeom g = row_geom(p, row);
   if (c >= g.U || g.U > kMaxUnits || g.L == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const RowState rs = ws.rows[g.row];
@@ -1136,8 +1158,7 @@ hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, 
   if (p.R == 0) return hipSuccess;
   DecodeWs w;
   ws_layout(p, ws, &w);
-  const int nrows = p.R * p.batch;
-  dim3 grid(max(1, max_units(p)), nrows);
+  const dim3 grid(unit_blocks(p));
   if (bf16)
     hipLaunchKernelGGL(sel_dec_score<bf16_t>, grid, dim3(kThreads), 0, s, p, (const bf16_t*)q_pre, w_q,
                        (const bf16_t*)k_idx, sel, w);
