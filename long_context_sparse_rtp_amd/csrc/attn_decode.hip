@@ -335,6 +335,11 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, const
   float acc = 0.f, M = -INFINITY, sum = 0.f;
   for (int c0 = 0; c0 < ns; c0 += kMaxS) {
     const int cn = min(kMaxS, ns - c0);
+    // the first 32 splits' partial outputs do not depend on the weights: requested
+    // with the split maxima, so both arrive in one round trip
+    float v32[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v32[u] = (u < cn) ? rec_of(c0 + u)[2 + tid] : 0.f;
     // block max of the split maxima of this chunk
     float mloc = -INFINITY;
     for (int s = tid; s < cn; s += kHeadDim) mloc = fmaxf(mloc, rec_of(c0 + s)[0]);
@@ -360,9 +365,10 @@ __global__ __launch_bounds__(kHeadDim) void attn_decode_combine(ProbDev p, const
     if (tid == 0) sum_s = red2_s[0] + red2_s[1];
     // 32 independent loads in flight, summed in split order
     for (int s = 0; s < cn; s += 32) {
-      float v32[32];
+      if (s > 0) {
 #pragma unroll
-      for (int u = 0; u < 32; ++u) v32[u] = (s + u < cn) ? rec_of(c0 + s + u)[2 + tid] : 0.f;
+        for (int u = 0; u < 32; ++u) v32[u] = (s + u < cn) ? rec_of(c0 + s + u)[2 + tid] : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < 32; ++u)
         if (s + u < cn) acc = fmaf(v32[u], wgt_s[s + u], acc);
