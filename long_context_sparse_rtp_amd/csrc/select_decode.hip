@@ -467,6 +467,24 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
   const RowGeom g = row_geom(p, row);
   if (c >= g.U || g.U > kMaxUnits) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // this unit's scores and every unit's statistics are requested before the row's
+  // top-p (or k) arrives, so the loads share one round trip (their addresses depend
+  // on the row's geometry only)
+  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
+  const int n0 = c * kChunk + tid;
+  float s[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int n = n0 + j * kThreads;
+    s[j] = (n < g.L) ? sb[n] : 0.f;
+  }
+  constexpr int PU = kMaxUnits / kThreads;
+  UnitMeta mtv[PU];
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid + t * kThreads;
+    if (u < g.U) mtv[t] = ws.meta[g.slot0 + u];
+  }
   const bool cmode = top_k != nullptr;
   const int kk = cmode ? max(top_k[g.b], 1) : 0;
   const float pp = cmode ? 0.f : top_p[g.b];
@@ -483,15 +501,6 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
     }
     return;
   }
-  // this unit's scores, requested first so the loads overlap the merge
-  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
-  const int n0 = c * kChunk + tid;
-  float s[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int n = n0 + j * kThreads;
-    s[j] = (n < g.L) ? sb[n] : 0.f;
-  }
 
   __shared__ int A_s[kMaxUnits];
   __shared__ int used_s[kMaxUnits];
@@ -507,7 +516,6 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
   __shared__ uint32_t cab_c_s, cbin_c_s, cabove_s, bincnt_s;
 
   // ---- merge: reference bin A and per-unit scales 2^((A_u - A) / 128)
-  constexpr int PU = kMaxUnits / kThreads;
   int amax = -2147483647 - 1;
   unsigned long long zu[PU];
 #pragma unroll
@@ -515,7 +523,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
     const int u = tid + t * kThreads;
     zu[t] = 0ull;
     if (u < g.U) {
-      const UnitMeta mt = ws.meta[g.slot0 + u];
+      const UnitMeta mt = mtv[t];
       A_s[u] = mt.A;
       used_s[u] = mt.used;
       cused_s[u] = mt.cused;
@@ -696,10 +704,34 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
   const RowGeom g = row_geom(p, row);
   if (c >= g.U || g.U > kMaxUnits || g.L == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const RowState rs = ws.rows[g.row];
   int* out = sel.idx + (size_t)g.r * p.Tk + g.k0;
   constexpr int kSeg = kChunk / kThreads;
   const int nw = c * kChunk + wid * (64 * kSeg);
+  // this unit's scores and every unit's counts and statistics are requested with the
+  // row's state, so the loads share one round trip (their addresses depend on the
+  // row's geometry only; a row taken whole does not use them)
+  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
+  float sv[kSeg];
+#pragma unroll
+  for (int j = 0; j < kSeg; ++j) {
+    const int n = nw + j * 64 + lane;
+    sv[j] = (n < g.L) ? sb[n] : 0.f;
+  }
+  constexpr int PU = kMaxUnits / kThreads;
+  UnitCnt ucv[PU];
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid * PU + t;
+    ucv[t] = UnitCnt{0u, 0u};
+    if (u < g.U) ucv[t] = ws.ucnt[g.slot0 + u];
+  }
+  UnitMeta mtv[PU];
+#pragma unroll
+  for (int t = 0; t < PU; ++t) {
+    const int u = tid + t * kThreads;
+    if (u < g.U) mtv[t] = ws.meta[g.slot0 + u];
+  }
+  const RowState rs = ws.rows[g.row];
   if (rs.mode == ROW_ALL) {
 #pragma unroll
     for (int j = 0; j < kSeg; ++j) {
@@ -710,13 +742,6 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
   }
   if (rs.mode != ROW_NORMAL) return;
   const bool cmode = top_k != nullptr;
-  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
-  float sv[kSeg];
-#pragma unroll
-  for (int j = 0; j < kSeg; ++j) {
-    const int n = nw + j * 64 + lane;
-    sv[j] = (n < g.L) ? sb[n] : 0.f;
-  }
 
   __shared__ int A_s[kMaxUnits];
   __shared__ double f_s[kMaxUnits];
@@ -735,22 +760,14 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
   const int A = rs.A, Ap = rs.Ap;
   const double target = rs.target;
   auto bin_of = [&](float v) { return min(kNB - 1, Ap - abs_bin(v)); };
-  // per unit: candidate count and base (consecutive units per thread, for the scan;
-  // their loads are issued first), reference bin and scale (units dealt round-robin,
-  // so that a row of up to 256 units costs every thread at most one float64 exp2)
-  constexpr int PU = kMaxUnits / kThreads;
-  UnitCnt ucv[PU];
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid * PU + t;
-    ucv[t] = UnitCnt{0u, 0u};
-    if (u < g.U) ucv[t] = ws.ucnt[g.slot0 + u];
-  }
+  // per unit: candidate count and base (consecutive units per thread, for the scan),
+  // reference bin and scale (units dealt round-robin, so that a row of up to 256
+  // units costs every thread at most one float64 exp2)
 #pragma unroll
   for (int t = 0; t < PU; ++t) {
     const int u = tid + t * kThreads;
     if (u < g.U) {
-      const UnitMeta mt = ws.meta[g.slot0 + u];
+      const UnitMeta mt = mtv[t];
       A_s[u] = mt.A;
       f_s[u] = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
     }
