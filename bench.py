@@ -100,8 +100,8 @@ def _traffic(name):
 
 def _select_call(rtp, prob, inp, k_idx, mode, sel, ws, stream, top_k):
     if top_k is None:
-        return lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, mode, sel, ws, stream=stream)
-    return lambda: rtp.rtp_select_topk(prob, inp.q_pre, inp.w, k_idx, top_k, mode, sel, ws, stream=stream)
+        return lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w_q, k_idx, inp.top_p, mode, sel, ws, stream=stream)
+    return lambda: rtp.rtp_select_topk(prob, inp.q_pre, inp.w_q, k_idx, top_k, mode, sel, ws, stream=stream)
 
 
 def bench_prefill(args, torch, rtp, synth, inp=None, top_k=None):
@@ -121,7 +121,7 @@ def bench_prefill(args, torch, rtp, synth, inp=None, top_k=None):
 
     def step(t: Timer = None):
         calls = [
-            ("index_keys", lambda: rtp.rtp_index_keys(prob, inp.k_pre, inp.w, k_idx, stream=stream)),
+            ("index_keys", lambda: rtp.rtp_index_keys(prob, inp.k_pre, inp.w_k, k_idx, stream=stream)),
             ("select_topp" if top_k is None else "select_topk",
              _select_call(rtp, prob, inp, k_idx, rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream, top_k)),
             ("sparse_attn_prefill", lambda: rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel,
@@ -213,8 +213,8 @@ def bench_prefill_references(args, torch, rtp, synth, pre):
         rtp.rtp_local_attn(dense, inp.q, inp.k, inp.v, out, lse, stream=stream)
 
     def pages_step():
-        rtp.rtp_index_keys(prob, inp.k_pre, inp.w, k_idx, stream=stream)
-        rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, p_one, rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream=stream)
+        rtp.rtp_index_keys(prob, inp.k_pre, inp.w_k, k_idx, stream=stream)
+        rtp.rtp_select_topp(prob, inp.q_pre, inp.w_q, k_idx, p_one, rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream=stream)
         rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel, out, lse, stream=stream)
         rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, stream=stream)
 
@@ -246,7 +246,7 @@ def bench_decode(args, torch, rtp, synth, inp=None, top_k=None, blocks=False):
         inp = synth.make_inputs(cfg, dev)
     prob = rtp.Problem.from_inputs(inp)
     stream = torch.cuda.current_stream()
-    k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w, stream=stream)   # cache built before timing
+    k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w_k, stream=stream)   # cache built before timing
     sel = rtp.Selection.empty(prob, rtp.RTP_SEL_LIST, dev)
     ws_sel = torch.empty(rtp.rtp_workspace_size(prob, rtp.RTP_CALL_SELECT_BLOCKS if blocks else rtp.RTP_CALL_SELECT,
                                                  rtp.RTP_SEL_LIST), dtype=torch.uint8, device=dev)
@@ -260,7 +260,7 @@ def bench_decode(args, torch, rtp, synth, inp=None, top_k=None, blocks=False):
     def step(t: Timer = None):
         calls = [
             ("select_topp_blocks" if blocks else "select_topp" if top_k is None else "select_topk",
-             (lambda: rtp.rtp_select_topp_blocks(prob, inp.q_pre, inp.w, k_idx, inp.top_p, sel, ws_sel,
+             (lambda: rtp.rtp_select_topp_blocks(prob, inp.q_pre, inp.w_q, k_idx, inp.top_p, sel, ws_sel,
                                                  stream=stream)) if blocks else
              _select_call(rtp, prob, inp, k_idx, rtp.RTP_SEL_LIST, sel, ws_sel, stream, top_k)),
             ("sparse_attn_decode", lambda: rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse,

@@ -129,7 +129,7 @@ def from_inputs(inp, k_idx=None) -> Problem:
     cfg = inp.cfg
     return Problem(
         q=host(inp.q), k=host(inp.k), v=host(inp.v), q_pre=host(inp.q_pre), k_pre=host(inp.k_pre),
-        w_q=host(inp.w), w_k=host(inp.w),
+        w_q=host(inp.w_q), w_k=host(inp.w_k),
         cu_q=inp.cu_q.cpu().tolist(), cu_k=inp.cu_k.cpu().tolist(),
         ret_heads=list(cfg.ret_heads), top_p=[float(x) for x in inp.top_p.cpu().tolist()],
         window=cfg.window, n_sink=cfg.n_sink, dtype=cfg.dtype, k_idx=host(k_idx))

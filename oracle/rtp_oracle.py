@@ -45,13 +45,18 @@ dense causal attention from torch's SDPA when p = 1 and W >= L, closed forms
 example and the Table 6 sparsity values; top-k against a pairwise rank count,
 the argmax and the top-p set of the same size; block top-p against a worked
 example, the token-exact top-p it reduces to with one-token blocks and fine
-bins, and a brute-force scan over the cut bin.  Nothing in this module is "parity
-unpinned".
+bins, and a brute-force scan over the cut bin.  The composition of a whole
+retrieval row at p < 1 (which query is projected, which matrix on which side,
+which slot, which KV group) is pinned against a row written out from the
+definition with exact rational arithmetic and subset enumeration, with
+distinct q / q_pre, W^Q != W^K and a different pair per slot.  Every function
+here has a pin; what stays "parity unpinned" is anything that would need the
+pages' trained projections or their evaluation data, which this module does
+not model.
 """
 from __future__ import annotations
 
 import dataclasses
-from fractions import Fraction
 from typing import Optional, Sequence
 
 import numpy as np
@@ -84,26 +89,6 @@ def round_to(x, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return round_bf16(x)
     raise ValueError(dtype)
-
-
-def round_fraction_bf16(v: Fraction) -> Fraction:
-    """Exact round-half-even of a rational onto bfloat16 (for pinning ``project``)."""
-    if v == 0:
-        return Fraction(0)
-    sgn = -1 if v < 0 else 1
-    a = abs(v)
-    e = a.numerator.bit_length() - a.denominator.bit_length()
-    if Fraction(2) ** e > a:
-        e -= 1
-    while Fraction(2) ** (e + 1) <= a:
-        e += 1
-    quantum = Fraction(2) ** (max(e, -126) - 7)
-    n = a / quantum
-    fl = n.numerator // n.denominator
-    rem = n - fl
-    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
-        fl += 1
-    return sgn * fl * quantum
 
 
 # ---------------------------------------------------------------- indexer

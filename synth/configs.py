@@ -11,9 +11,12 @@ written next to the field they set:
 * ``ret_heads``: one retrieval head per KV group (0, 8, 16, 24 with 32 query
   heads over 4 KV heads) for the large workloads, heads {0, 1} for the tiny
   one.  GQA groups are contiguous: kv(h) = floor(h * Hkv / Hq).
-* The indexer score is s = (q_idx . k_idx) / sqrt(16); the projection is the
-  same seeded orthonormal 16x128 matrix for every retrieval head and for both
-  q and k.
+* The indexer score is s = (q_idx . k_idx) / sqrt(16).  The workloads use one
+  seeded orthonormal 16x128 projection for every retrieval head and for both q
+  and k (``proj = "shared"``); ``proj = "distinct"`` draws an independent one
+  per retrieval head and per side (W^Q_h, W^K_h), the form the method itself
+  trains (section 3.4 "Low-Dimensional Projection Mechanism and Stage-1
+  Training").
 """
 from __future__ import annotations
 
@@ -54,6 +57,9 @@ class Config:
     verify_rows: int = 0
     # explicit per-sequence KV lengths (prefill: L_q = L_k; decode: L_q = 1)
     seqlens: Optional[Tuple[int, ...]] = None
+    # indexer projections: "shared" (one W for every slot, q and k) or "distinct"
+    # (an independent W^Q_r and W^K_r per retrieval slot)
+    proj: str = "shared"
 
     @property
     def n_ret(self) -> int:

@@ -14,7 +14,9 @@ workload dtype when stored):
   Computed in float64 from the float64 pre-RoPE draw, then rounded;
 * the indexer projection: one orthonormal 16x128 matrix (QR of a 128x16
   Gaussian with the signs fixed so diag(R) > 0), stored as float32 and used
-  for every retrieval head, for q and for k;
+  for every retrieval head, for q and for k; with ``proj = "distinct"`` every
+  retrieval slot gets its own W^Q and W^K, each drawn the same way from a
+  stream of its own;
 * needles ("topic", prefill): per retrieval head a seeded unit direction t;
   floor(frac * L) key positions get k <- |k| (0.8 t + 0.6 u) with u the unit
   part of the original k orthogonal to t, and every query of that head is
@@ -61,7 +63,7 @@ def _gen(device, *tags) -> torch.Generator:
     return g
 
 
-_TAG = {"q": 1, "k": 2, "v": 3, "w": 4, "topic": 5, "npos": 6, "len": 7, "p": 8, "peaky": 9}
+_TAG = {"q": 1, "k": 2, "v": 3, "w": 4, "topic": 5, "npos": 6, "len": 7, "p": 8, "peaky": 9, "wq": 10, "wk": 11}
 
 
 def _randn_chunk(seed: int, tag: str, chunk: int, shape, device) -> torch.Tensor:
@@ -88,9 +90,9 @@ def rope_inplace(x: torch.Tensor, pos: torch.Tensor, theta: float) -> torch.Tens
     return x
 
 
-def orthonormal_projection(seed: int, r: int = 16, d: int = 128) -> torch.Tensor:
+def orthonormal_projection(seed: int, r: int = 16, d: int = 128, tag: str = "w", index: int = 0) -> torch.Tensor:
     """A [r, d] float64 matrix with orthonormal rows (QR of a Gaussian, sign-fixed)."""
-    g = _gen("cpu", seed, _TAG["w"], 0)
+    g = _gen("cpu", seed, _TAG[tag], index)
     a = torch.randn((d, r), generator=g, dtype=torch.float64)
     qm, rm = torch.linalg.qr(a)
     sgn = torch.sign(torch.diagonal(rm))
@@ -120,7 +122,9 @@ class Inputs:
     v: torch.Tensor            # [T_k, Hkv, 128] dtype
     q_pre: torch.Tensor        # [T_q, R, 128] pre-RoPE q of the retrieval heads, dtype
     k_pre: torch.Tensor        # [T_k, Hkv, 128] pre-RoPE k, dtype
-    w: torch.Tensor            # [R, 16, 128] float32 (w_q = w_k)
+    w_q: torch.Tensor          # [R, 16, 128] float32: W^Q of every retrieval slot
+    w_k: torch.Tensor          # [R, 16, 128] float32: W^K of every retrieval slot (the same tensor as w_q
+                               # when the projection is shared)
     cu_q: torch.Tensor         # [B+1] int32
     cu_k: torch.Tensor         # [B+1] int32
     top_p: torch.Tensor        # [B] float32
@@ -195,8 +199,17 @@ def make_inputs(cfg: Config, device="cpu") -> Inputs:
         kpos[cu_k[b]:cu_k[b + 1]] = torch.arange(lk[b])
         qpos[cu_q[b]:cu_q[b + 1]] = torch.arange(lk[b] - lq[b], lk[b])
 
-    w64 = orthonormal_projection(cfg.seed, cfg.idx_dim, d)
-    w = w64.to(torch.float32)[None].repeat(R, 1, 1).contiguous()
+    if cfg.proj == "shared":
+        w64 = orthonormal_projection(cfg.seed, cfg.idx_dim, d)
+        w_q = w64.to(torch.float32)[None].repeat(R, 1, 1).contiguous()
+        w_k = w_q
+    elif cfg.proj == "distinct":
+        w_q = torch.stack([orthonormal_projection(cfg.seed, cfg.idx_dim, d, "wq", r) for r in range(R)]
+                          ).to(torch.float32).contiguous() if R else torch.zeros((0, cfg.idx_dim, d))
+        w_k = torch.stack([orthonormal_projection(cfg.seed, cfg.idx_dim, d, "wk", r) for r in range(R)]
+                          ).to(torch.float32).contiguous() if R else torch.zeros((0, cfg.idx_dim, d))
+    else:
+        raise ValueError(f"unknown projection kind {cfg.proj!r}")
 
     # topic directions for prefill needles
     topics = None
@@ -277,8 +290,10 @@ def make_inputs(cfg: Config, device="cpu") -> Inputs:
         del x
         v[c0:c1] = _randn_chunk(cfg.seed, "v", c0 // CHUNK, (c1 - c0, Hkv, d), device).to(dt)
 
+    wq_dev = w_q.to(device)
+    wk_dev = wq_dev if w_k is w_q else w_k.to(device)
     return Inputs(
-        cfg=cfg, q=q, k=k, v=v, q_pre=q_pre, k_pre=k_pre, w=w.to(device),
+        cfg=cfg, q=q, k=k, v=v, q_pre=q_pre, k_pre=k_pre, w_q=wq_dev, w_k=wk_dev,
         cu_q=torch.tensor(cu_q, dtype=torch.int32, device=device),
         cu_k=torch.tensor(cu_k, dtype=torch.int32, device=device),
         top_p=torch.tensor(_top_p(cfg), dtype=torch.float32, device=device),

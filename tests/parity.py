@@ -22,9 +22,9 @@ def sync():
 
 def _select(rtp, prob, inp, k_idx, mode, top_k):
     if top_k is None:
-        return rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, mode)
+        return rtp.rtp_select_topp(prob, inp.q_pre, inp.w_q, k_idx, inp.top_p, mode)
     kt = torch.as_tensor(list(top_k), dtype=torch.int32, device=inp.q.device)
-    return rtp.rtp_select_topk(prob, inp.q_pre, inp.w, k_idx, kt, mode)
+    return rtp.rtp_select_topk(prob, inp.q_pre, inp.w_q, k_idx, kt, mode)
 
 
 def run_prefill(inp, top_k: Optional[Sequence[int]] = None) -> Dict[str, torch.Tensor]:
@@ -32,7 +32,7 @@ def run_prefill(inp, top_k: Optional[Sequence[int]] = None) -> Dict[str, torch.T
     ``top_k`` is given) -> sparse attention + local attention."""
     import long_context_sparse_rtp_amd as rtp
     prob = rtp.Problem.from_inputs(inp)
-    k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w)
+    k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w_k)
     sel = _select(rtp, prob, inp, k_idx, rtp.RTP_SEL_THRESHOLD, top_k)
     out = torch.full_like(inp.q, float("nan"))
     lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=inp.q.device)
@@ -238,7 +238,7 @@ def run_decode_blocks(inp, k_idx: torch.Tensor) -> Dict[str, torch.Tensor]:
     """Decode path with the pages' block-granular top-p: block LIST select -> sparse decode + local decode."""
     import long_context_sparse_rtp_amd as rtp
     prob = rtp.Problem.from_inputs(inp)
-    sel = rtp.rtp_select_topp_blocks(prob, inp.q_pre, inp.w, k_idx, inp.top_p)
+    sel = rtp.rtp_select_topp_blocks(prob, inp.q_pre, inp.w_q, k_idx, inp.top_p)
     out = torch.full_like(inp.q, float("nan"))
     lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=inp.q.device)
     rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse)

@@ -82,7 +82,7 @@ def test_blocks_deterministic():
     _say(f"[case] {cfg.name}")
     inp = make_inputs(cfg, DEV)
     import long_context_sparse_rtp_amd as rtp
-    k_idx = rtp.rtp_index_keys(rtp.Problem.from_inputs(inp), inp.k_pre, inp.w)
+    k_idx = rtp.rtp_index_keys(rtp.Problem.from_inputs(inp), inp.k_pre, inp.w_k)
     a = P.run_decode_blocks(inp, k_idx)
     b = P.run_decode_blocks(inp, k_idx)
     for k in ("count", "out", "tau"):

@@ -50,7 +50,7 @@ def _problem(inp, cap, lengths=None, ring=False, ret_heads=None, n_q_heads=None)
 def _decode_on(prob, inp, k, v, k_idx):
     """select (LIST) -> sparse decode + local decode on caches in prob's layout."""
     rtp = _rtp()
-    sel = rtp.rtp_select_topp(prob, inp.q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_LIST)
+    sel = rtp.rtp_select_topp(prob, inp.q_pre, inp.w_q, k_idx, inp.top_p, rtp.RTP_SEL_LIST)
     out = torch.full_like(inp.q, float("nan"))
     lse = torch.full((inp.cfg.n_q_heads, inp.total_q), float("nan"), dtype=torch.float32, device=DEV)
     rtp.rtp_sparse_attn_decode(prob, inp.q, k, v, sel, out, lse)
@@ -94,11 +94,11 @@ def test_capacity_layout_decode_matches_oracle_and_packed(cfg):
     cap = 8192
     prob = _problem(inp, cap)
     k, v, kp = (_to_capacity(x, cu, cap) for x in (inp.k, inp.v, inp.k_pre))
-    k_idx = rtp.rtp_index_keys(prob, kp, inp.w)
+    k_idx = rtp.rtp_index_keys(prob, kp, inp.w_k)
     sel, out, lse = _decode_on(prob, inp, k, v, k_idx)
     _check_decode_capacity(inp, cap, sel, out, lse, from_inputs(inp))
     # the same kernels on the packed layout give the same bits
-    g = P.run_decode(inp, rtp.rtp_index_keys(rtp.Problem.from_inputs(inp), inp.k_pre, inp.w))
+    g = P.run_decode(inp, rtp.rtp_index_keys(rtp.Problem.from_inputs(inp), inp.k_pre, inp.w_k))
     assert torch.equal(g["out"], out) and torch.equal(g["count"], sel.count)
 
 
@@ -120,8 +120,8 @@ def test_capacity_layout_prefill_chunk():
                        max_seqlen_k=700, total_q=2 * nq, total_k=2 * cap, k_capacity=cap)
     k, v, kp = (_to_capacity(x, cu, cap) for x in (inp.k, inp.v, inp.k_pre))
     q, q_pre = inp.q[qrows].contiguous(), inp.q_pre[qrows].contiguous()
-    k_idx = rtp.rtp_index_keys(prob, kp, inp.w)
-    sel = rtp.rtp_select_topp(prob, q_pre, inp.w, k_idx, inp.top_p, rtp.RTP_SEL_THRESHOLD)
+    k_idx = rtp.rtp_index_keys(prob, kp, inp.w_k)
+    sel = rtp.rtp_select_topp(prob, q_pre, inp.w_q, k_idx, inp.top_p, rtp.RTP_SEL_THRESHOLD)
     out = torch.full_like(q, float("nan"))
     lse = torch.full((8, 2 * nq), float("nan"), dtype=torch.float32, device=DEV)
     rtp.rtp_sparse_attn_prefill(prob, q, k, v, k_idx, sel, out, lse)
@@ -152,19 +152,19 @@ def test_append_step_bit_exact_then_decode():
         for t in (k, v, kp):
             t[b * cap + lens[b] - 1].zero_()
     before = _problem(inp, cap, lengths=[n - 1 for n in lens])
-    k_idx = rtp.rtp_index_keys(before, kp, inp.w)
+    k_idx = rtp.rtp_index_keys(before, kp, inp.w_k)
     # the step: append the last tokens (positions L - 1 of the grown sequences)
     after = _problem(inp, cap)
     cu_new = torch.arange(B + 1, dtype=torch.int32, device=DEV)
     k_new, v_new, kp_new = (x[last].contiguous() for x in (inp.k, inp.v, inp.k_pre))
-    rtp.rtp_append_kv(after, cu_new, B, k_new, v_new, k, v, k_pre_new=kp_new, w_k=inp.w, k_idx=k_idx)
+    rtp.rtp_append_kv(after, cu_new, B, k_new, v_new, k, v, k_pre_new=kp_new, w_k=inp.w_k, k_idx=k_idx)
     P.sync()
     for b in range(B):
         row = b * cap + lens[b] - 1
         assert torch.equal(k[row], inp.k[cu[b + 1] - 1]) and torch.equal(v[row], inp.v[cu[b + 1] - 1])
     # appended index keys: bit-identical to a one-pass projection and to the oracle
     kp[torch.tensor([b * cap + lens[b] - 1 for b in range(B)], device=DEV)] = kp_new
-    full = rtp.rtp_index_keys(after, kp, inp.w)
+    full = rtp.rtp_index_keys(after, kp, inp.w_k)
     P.sync()
     pr = from_inputs(inp)
     for b in range(B):
@@ -198,14 +198,14 @@ def test_serving_loop_three_steps():
     prob0 = _problem(inp, cap, lengths=start)
     k_idx = torch.zeros((cfg.n_ret, B * cap, 16), dtype=inp.k.dtype, device=DEV)
     rtp.rtp_append_kv(prob0, cu_new, int(sum(start)), inp.k[prompt_rows].contiguous(), inp.v[prompt_rows].contiguous(),
-                      k, v, k_pre_new=inp.k_pre[prompt_rows].contiguous(), w_k=inp.w, k_idx=k_idx)
+                      k, v, k_pre_new=inp.k_pre[prompt_rows].contiguous(), w_k=inp.w_k, k_idx=k_idx)
     for s in range(steps):
         _say(f"[case] serving loop step {s}")
         lens = [start[b] + s + 1 for b in range(B)]
         prob = _problem(inp, cap, lengths=lens)
         rows = torch.tensor([cu[b] + lens[b] - 1 for b in range(B)], device=DEV)
         rtp.rtp_append_kv(prob, torch.arange(B + 1, dtype=torch.int32, device=DEV), B, inp.k[rows].contiguous(),
-                          inp.v[rows].contiguous(), k, v, k_pre_new=inp.k_pre[rows].contiguous(), w_k=inp.w,
+                          inp.v[rows].contiguous(), k, v, k_pre_new=inp.k_pre[rows].contiguous(), w_k=inp.w_k,
                           k_idx=k_idx)
         # this step's queries: the generator's queries stand in for the new token's
         sel, out, lse = _decode_on(prob, inp, k, v, k_idx)

@@ -192,7 +192,7 @@ def test_selection_deterministic():
     dcfg = scaled(DECODE_32K, name="determinism_dec", batch=2, seqlen=9000)
     dinp = make_inputs(dcfg, DEV)
     import long_context_sparse_rtp_amd as rtp
-    k_idx = rtp.rtp_index_keys(rtp.Problem.from_inputs(dinp), dinp.k_pre, dinp.w)
+    k_idx = rtp.rtp_index_keys(rtp.Problem.from_inputs(dinp), dinp.k_pre, dinp.w_k)
     a = P.run_decode(dinp, k_idx)
     b = P.run_decode(dinp, k_idx)
     for k in ("count", "out", "tau", "tie"):

@@ -75,7 +75,7 @@ def test_index_keys_f32_and_bf16_exact():
         _say(f"[case] index keys {cfg.name}")
         inp = make_inputs(cfg, DEV)
         prob = rtp.Problem.from_inputs(inp)
-        k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w)
+        k_idx = rtp.rtp_index_keys(prob, inp.k_pre, inp.w_k)
         P.sync()
         pr = from_inputs(inp)
         assert P.check_index_keys(pr, P.to_host({"k": k_idx})["k"]) == 0

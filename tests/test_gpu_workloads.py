@@ -1,5 +1,5 @@
 """GPU parity at the full workload sizes: 128K prefill (512 sampled rows, all heads),
-1M prefill (128 sampled rows), ragged decode (every row).  The 32K decode and the tiny
+1M prefill (256 sampled rows), ragged decode (every row).  The 32K decode and the tiny
 prefill are checked in full in test_gpu_parity.py."""
 import pytest
 
@@ -48,7 +48,7 @@ def test_prefill_128k_sampled():
 
 
 def test_prefill_1m_sampled():
-    _sampled_prefill(PREFILL_1M, 128)
+    _sampled_prefill(PREFILL_1M, 256)
 
 
 def test_ragged_decode_b64_all_rows():

@@ -411,6 +411,105 @@ def test_local_pattern_counts():
         assert set(range(max(0, pos - 7), pos + 1)) <= set(kk.tolist())
 
 
+# ------------------------------------------------------------------ retrieval-row wiring
+# The whole retrieval row at p < 1 with every operand distinct: post-RoPE q and
+# pre-RoPE q_pre drawn independently, W^Q_r != W^K_r and a different pair per
+# slot, two KV groups.  The expected result is written out here from the
+# definition alone (section 3.4, "Low-Dimensional Projection Mechanism and
+# Stage-1 Training" and "Dynamic Top-p Selection Mechanism", Eq. 5 and the
+# attention equation after it): exact rational projections rounded once, exact
+# rational scores, then the minimal-cardinality subset of the causal prefix
+# whose softmax mass reaches p (the heaviest one when several have that size),
+# found by enumerating subsets, then softmax attention of the post-RoPE q over
+# it.  It shares nothing with the oracle's functions.
+def _wiring_problem(dtype, decode, seed=31):
+    rng = np.random.default_rng(seed)
+    Hq, Hkv, ret = 4, 2, [1, 2]                    # kv(1) = 0, kv(2) = 1
+    lk = [7, 10] if decode else [9]
+    lq = [1] * len(lk) if decode else list(lk)
+    Tq, Tk, R = sum(lq), sum(lk), len(ret)
+
+    def draw(*shape):
+        return O.round_to(rng.standard_normal(shape), dtype)
+    q, q_pre = draw(Tq, Hq, 128), draw(Tq, R, 128)
+    k, k_pre, v = draw(Tk, Hkv, 128), draw(Tk, Hkv, 128), draw(Tk, Hkv, 128)
+    # rows of norm about 1, so that the scores have unit scale and the sets several members
+    w_q = (rng.standard_normal((R, 16, 128)) / math.sqrt(128)).astype(np.float32).astype(np.float64)
+    w_k = (rng.standard_normal((R, 16, 128)) / math.sqrt(128)).astype(np.float32).astype(np.float64)
+    p = [0.75, 0.9] if decode else [0.8]
+    return Problem(q=q, k=k, v=v, q_pre=q_pre, k_pre=k_pre, w_q=w_q, w_k=w_k,
+                   cu_q=np.cumsum([0] + lq).tolist(), cu_k=np.cumsum([0] + lk).tolist(),
+                   ret_heads=ret, top_p=p, window=3, n_sink=1, dtype=dtype)
+
+
+def _brute_retrieval_row(raw, b, i, h):
+    """Expected (q_idx, set, output) of one retrieval row from the definition."""
+    bits = 8 if raw["dtype"] == "bf16" else 24
+    cu_q, cu_k = raw["cu_q"], raw["cu_k"]
+    Lq, Lk = cu_q[b + 1] - cu_q[b], cu_k[b + 1] - cu_k[b]
+    pos = Lk - Lq + i
+    qi, k0 = cu_q[b] + i, cu_k[b]
+    Hq, Hkv = raw["q"].shape[1], raw["k"].shape[1]
+    g = h * Hkv // Hq
+    r = raw["ret"].index(h)
+
+    def rdot(a, c):
+        return sum(Fraction(float(x)) * Fraction(float(y)) for x, y in zip(a, c))
+    qx = [round_fraction(rdot(raw["w_q"][r, j], raw["q_pre"][qi, r]), bits) for j in range(16)]
+    s = []
+    for n in range(pos + 1):
+        kx = [round_fraction(rdot(raw["w_k"][r, j], raw["k_pre"][k0 + n, g]), bits) for j in range(16)]
+        s.append(sum(a * c for a, c in zip(qx, kx)) / 4)
+    top = max(s)
+    e = np.array([math.exp(float(x - top)) for x in s])
+    mass = e / e.sum()
+    p = raw["top_p"][b]
+    best = None
+    for size in range(1, pos + 2):
+        for sub in itertools.combinations(range(pos + 1), size):
+            m = float(sum(mass[list(sub)]))
+            if m >= p and (best is None or m > best[0]):
+                best = (m, sub)
+        if best is not None:
+            break
+    S = list(best[1])
+    a = [float(rdot(raw["q"][qi, h], raw["k"][k0 + n, g])) / math.sqrt(128) for n in S]
+    am = max(a)
+    wts = [math.exp(x - am) for x in a]
+    tot = sum(wts)
+    out = np.zeros(128)
+    for wn, n in zip(wts, S):
+        out += (wn / tot) * raw["v"][k0 + n, g]
+    return np.array([float(x) for x in qx]), S, out
+
+
+def check_retrieval_wiring(dtype, decode):
+    pr = _wiring_problem(dtype, decode)
+    raw = dict(q=pr.q, q_pre=pr.q_pre, k=pr.k, k_pre=pr.k_pre, v=pr.v, w_q=pr.w_q, w_k=pr.w_k,
+               cu_q=pr.cu_q, cu_k=pr.cu_k, ret=list(pr.ret_heads), top_p=list(pr.top_p), dtype=dtype)
+    nb = len(pr.cu_q) - 1
+    n_strict = 0
+    for b in range(nb):
+        for i in range(pr.cu_q[b + 1] - pr.cu_q[b]):
+            for h in pr.ret_heads:
+                qx, S, out = _brute_retrieval_row(raw, b, i, h)
+                got = pr.row(b, i, h)
+                assert np.array_equal(got.q_idx, qx), (b, i, h, "q_idx")
+                assert got.topp.selected.tolist() == S, (b, i, h, got.topp.selected.tolist(), S)
+                assert np.allclose(got.attn.out, out, atol=1e-12, rtol=0), (b, i, h, "out")
+                n_strict += 2 <= len(S) < pr.pos_of(b, i) + 1
+    # the pin is only as good as its rows whose set is a strict subset of two or more keys
+    assert n_strict >= (3 if decode else 8), n_strict
+
+
+def test_retrieval_wiring_prefill_f32():
+    check_retrieval_wiring("f32", decode=False)
+
+
+def test_retrieval_wiring_decode_bf16():
+    check_retrieval_wiring("bf16", decode=True)
+
+
 # ------------------------------------------------------------------ metrics (pages' numbers)
 def test_table6_compute_sparsity():
     g = _golden("table6_sparsity.json")
@@ -559,3 +658,46 @@ def test_mutation_block_mass_from_max_caught(monkeypatch):
     monkeypatch.setattr(O, "block_top_p", mass_from_max)
     with pytest.raises(AssertionError):
         check_block_worked_example()
+
+
+# mistakes in the wiring of a retrieval row: each must fail the brute-force wiring pin
+def test_mutation_projects_post_rope_query_caught(monkeypatch):
+    monkeypatch.setattr(Problem, "q_pre_row", lambda self, qi, r: self.q_row(qi, self.ret_heads[r]))
+    with pytest.raises(AssertionError):
+        check_retrieval_wiring("f32", decode=False)
+
+
+def test_mutation_attends_with_pre_rope_query_caught(monkeypatch):
+    real = O.retrieval_row
+    monkeypatch.setattr(O, "retrieval_row", lambda q, q_pre, *a, **kw: real(q_pre, q_pre, *a, **kw))
+    with pytest.raises(AssertionError):
+        check_retrieval_wiring("f32", decode=False)
+
+
+def test_mutation_swapped_projections_caught(monkeypatch):
+    real = Problem.w
+    monkeypatch.setattr(Problem, "w", lambda self, which, r: real(self, {"w_q": "w_k", "w_k": "w_q"}[which], r))
+    with pytest.raises(AssertionError):
+        check_retrieval_wiring("bf16", decode=True)
+
+
+def test_mutation_slot0_projection_for_every_slot_caught(monkeypatch):
+    real = Problem.w
+    monkeypatch.setattr(Problem, "w", lambda self, which, r: real(self, which, 0))
+    with pytest.raises(AssertionError):
+        check_retrieval_wiring("bf16", decode=True)
+
+
+def test_mutation_wrong_kv_group_caught(monkeypatch):
+    monkeypatch.setattr(Problem, "kv_of", lambda self, h: h % self.n_kv_heads)
+    with pytest.raises(AssertionError):
+        check_retrieval_wiring("f32", decode=False)
+
+
+def test_mutation_keys_projected_with_query_matrix_caught(monkeypatch):
+    # only the key side is wrong (W^Q_r applied to k_pre): q_idx is still right, so the
+    # set or the output has to catch it
+    real = Problem.w
+    monkeypatch.setattr(Problem, "w", lambda self, which, r: real(self, "w_q", r))
+    with pytest.raises(AssertionError, match=r"\[|out"):
+        check_retrieval_wiring("f32", decode=False)
