@@ -26,6 +26,14 @@
 //          the raw dot product, summed in 64-bit LDS integers (exact and
 //          order-independent: the result is deterministic);
 //   K    = floor(u * 2^16) clamped to 32 bits (K >> 16 == floor(u)).
+// The fixed-point mass of a token is truncated (at most one unit lost), so a
+// row's total Z carries an error of at most (pos + 1) units.  After the first
+// full sweep a row is certified: when (pos + 1) exceeds 2^-20 Z (a row whose
+// mass sits in a few tokens far above a long tail, with a loose reference) the
+// row switches to a wide mass, 2^(ms - (top - s) log2 e) with ms = 42 as a
+// 64-bit integer, after its reference is lowered to within 1/8 octave of the
+// row maximum by the coarse sweep; the truncation error is then below 2^-21 Z
+// for rows up to 2^20 keys.
 // A first sweep reads every 8th full tile (and the diagonal tiles) and
 // histograms the mass over kNB1 bins of floor(u) (the last one open-ended);
 // 16 threads per row scan it for the bin where the cumulative mass reaches p
@@ -89,6 +97,7 @@ struct RowCtl {
   int sh;                     // digit shift of the range
   int phase, kind;
   int pos;
+  int wide;                   // the row's mass is the wide (64-bit) one
   int g0;                     // first fine bin (1/256 octave) of the window of the windowed sweep
   uint32_t cabove;            // tokens strictly better than the range (counted by the collect sweep)
   float tau;
@@ -99,6 +108,8 @@ struct RowCtl {
 struct RowK {
   float a20, b20;   // K as float = fma(dot, a20, b20)
   float am, bm;     // mass = 2^fma(dot, am, bm)
+  float bw;         // wide mass = 2^fma(dot, am, bw)
+  bool wide;
   float lo_f, hi_f; // float range of K for the fast range test
   float dA, dB;     // the same tests on the raw dot: K >= lo <=> d <= dA, K < hi <=> d > dB
   float a12, b12;   // fine bin coordinate (1/256 octave) = fma(dot, a12, b12) = K / 2^12 exactly
@@ -129,6 +140,20 @@ __device__ __forceinline__ float dot_bound(float a, float b, float t) {
 }
 __device__ __forceinline__ uint32_t mass31(float dot, float am, float bm) {
   return (uint32_t)__builtin_amdgcn_exp2f(fmaf(dot, am, bm));
+}
+// The wide mass: the float 2^fma(dot, am, bw) < 2^42 as an exact 64-bit integer
+// (its part above 2^32 is hi = floor(f / 2^32); f - hi 2^32 is exact in float).
+__device__ __forceinline__ unsigned long long mass_wide(float dot, float am, float bw) {
+  const float f = __builtin_amdgcn_exp2f(fmaf(dot, am, bw));
+  const uint32_t hi = (uint32_t)(f * 2.3283064365386963e-10f);
+  const uint32_t lo = (uint32_t)fmaf((float)hi, -4294967296.f, f);
+  return ((unsigned long long)hi << 32) | lo;
+}
+// Mass scale of a row in wide mode: 2^ws per token at most, so that the 64-bit
+// sums of up to 2^(62 - ws) tokens cannot overflow.
+__device__ __forceinline__ float wide_scale(int pos) {
+  const int nb = 32 - __clz((uint32_t)pos + 1u);   // bits of pos + 1
+  return (float)min(42, 62 - nb);
 }
 
 __global__ void kidx_norm_clear(uint32_t* p, int n) {
@@ -236,6 +261,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     c.above = 0ull;
     c.cabove = 0u;
     c.lo = 0u; c.sh = 16; c.kind = 0; c.kfix = 0u; c.dfix = 0u;
+    c.wide = 0;
     c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = c.pos + 1;
     c.target = 1.0;
     c.g0 = 1;
@@ -354,6 +380,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       rk.b20 = c.top * kLog2e * kBinsPerOctave * 65536.f;
       rk.am = kLog2e * 0.25f;
       rk.bm = 31.f - c.top * kLog2e;
+      rk.bw = wide_scale(c.pos) - c.top * kLog2e;
+      rk.wide = c.wide != 0;
       rk.lo = c.lo;
       rk.sh = c.sh;
       rk.kind = c.kind;
@@ -398,10 +426,23 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         atomicAdd(&h1[bin][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
       }
     };
+    // the same with the wide mass for rows that need it (the full coarse sweep only)
+    auto hist_coarse_w = [&](const f32x4& d, int t, bool check) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 16 * t + 4 * grp + i;
+        if (check && n > rk.pos) continue;
+        const float u = fmaf(d[i], a1, b1);
+        const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kNB1 - 1));
+        atomicAdd(&h1[bin][col], COUNT ? 1ull : rk.wide ? mass_wide(d[i], rk.am, rk.bw)
+                                                        : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+      }
+    };
+    const bool any_wide = __builtin_amdgcn_ballot_w64(rk.wide) != 0;
     if (sweep == PH_P0) {
       sweep_sample(hist_coarse);
     } else if (sweep == PH_HIST1) {
-      sweep_tiles(hist_coarse);
+      if (any_wide) sweep_tiles(hist_coarse_w); else sweep_tiles(hist_coarse);
     } else if (sweep == PH_HISTW) {
       // window of 254 bins of 1/256 octave; bin 0 holds everything above it, bin 255 everything below.
       // The coordinate is K / 2^12 exactly (a power-of-two scaling of the key's FMA) and
@@ -438,7 +479,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           for (int i = 0; i < 4; ++i) {
             if (inr[i]) {
               const uint32_t dig = (key20(fmaf(d[i], rk.a20, rk.b20)) - rk.lo) >> rk.sh;
-              atomicAdd(&hm2[dig][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+              atomicAdd(&hm2[dig][col], COUNT ? 1ull : rk.wide ? mass_wide(d[i], rk.am, rk.bw)
+                                                               : (unsigned long long)mass31(d[i], rk.am, rk.bm));
             }
           }
         }
@@ -502,7 +544,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           if (!inr) continue;
           if (sweep == PH_REFINE) {
             const uint32_t dig = dk2 >> rk.sh;
-            atomicAdd(&hm2[dig][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+            atomicAdd(&hm2[dig][col], COUNT ? 1ull : rk.wide ? mass_wide(d[i], rk.am, rk.bw)
+                                                             : (unsigned long long)mass31(d[i], rk.am, rk.bm));
           } else {
             const int slot = atomicAdd(&ccount_s[col], 1);
             if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
@@ -584,7 +627,12 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           Z += psum_s[srow][q];
         }
         const double target = COUNT ? (double)rc.kval : fmax((double)rc.pval * (double)Z, 1.0);
-        if ((double)pre < target && target <= (double)(pre + sp)) {
+        // certification: the truncation error of Z (at most one unit per key) must stay
+        // below 2^-20 Z; otherwise the row restarts from the coarse sweep with the wide mass
+        const bool certified = COUNT || (double)(rc.pos + 1) * 1048576.0 <= (double)Z;
+        if (!certified) {
+          if (spart == 0) rc.wide = 1;
+        } else if ((double)pre < target && target <= (double)(pre + sp)) {
           unsigned long long cm = pre;
           int jstar = spart * PB + PB - 1;
           for (int j = 0; j < PB; ++j) {
@@ -635,13 +683,19 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           Z += psum_s[srow][q];
           blo = min(blo, pidx_s[srow][q]);
         }
-        if (blo >= kNB1 / 2 || Z == 0ull) {
-          // loose bound (the best token sits >= 8 octaves below it): lower the
-          // reference to just above the best token and histogram again
+        // a narrow row whose truncation error bound fails the certification
+        // (see the PH_HISTW controller) switches to the wide mass and sweeps again
+        const bool uncertified = !COUNT && !rc.wide && (double)(rc.pos + 1) * 1048576.0 > (double)Z;
+        if (blo >= kNB1 / 2 || Z == 0ull || (rc.wide && blo > 2)) {
+          // loose bound (the best token sits >= 8 octaves below it; for a wide row, more
+          // than 1/8 octave): lower the reference to just above the best token and
+          // histogram again
           if (spart == 0) {
             const int bl = (blo >= kNB1) ? kNB1 - 1 : blo;
             rc.top = rc.top - (float)(bl - 1) / (kBinsPerOctave * kLog2e);
           }
+        } else if (uncertified) {
+          if (spart == 0) rc.wide = 1;
         } else {
           const double target = COUNT ? (double)rc.kval : fmax((double)rc.pval * (double)Z, 1.0);
           if ((double)pre < target && target <= (double)(pre + sp)) {
@@ -769,8 +823,12 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       // candidate if none does).  Thread q sums ranks [q E, q E + E); the part where
       // the cumulative mass crosses walks its ranks.
       const float am = kLog2e * 0.25f, bm = 31.f - ctl[srow].top * kLog2e;
-      auto cmass = [&](int k) -> uint32_t {
-        return COUNT ? 1u : mass31(undesc_key((uint32_t)(cd[perm[k]] >> 32)) * 4.f, am, bm);
+      const float bw = wide_scale(ctl[srow].pos) - ctl[srow].top * kLog2e;
+      const bool rwide = ctl[srow].wide != 0;
+      auto cmass = [&](int k) -> unsigned long long {
+        if (COUNT) return 1ull;
+        const float dk = undesc_key((uint32_t)(cd[perm[k]] >> 32)) * 4.f;
+        return rwide ? mass_wide(dk, am, bw) : (unsigned long long)mass31(dk, am, bm);
       };
       const int a0 = spart * E;
       unsigned long long sp = 0ull;
@@ -793,7 +851,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           int js = min(a0 + E, nc) - 1;
           unsigned long long cm = pre;
           for (int k = a0; k < min(a0 + E, nc); ++k) {
-            const uint32_t m = cmass(k);
+            const unsigned long long m = cmass(k);
             if ((double)(cm + m) >= target) { js = k; break; }
             cm += m;
           }
