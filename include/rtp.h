@@ -29,7 +29,8 @@
  * Ownership and execution: every pointer marked (dev) is device memory owned by
  * the caller.  The library allocates nothing, never synchronises, keeps no
  * pointer after a call returns, and keeps no state between calls except a
- * per-thread error string.  All work is enqueued on the caller's HIP stream
+ * per-thread error string and, for rtp_sparse_attn_decode_noalloc, the device
+ * address of its static scratch on each device.  All work is enqueued on the caller's HIP stream
  * (NULL = default stream); buffers must stay alive until that stream has run it.
  *
  * Errors: every argument check runs on the host before any launch, so a call
@@ -246,6 +247,26 @@ RTP_API rtp_status rtp_sparse_attn_prefill(const rtp_problem *prob, const void *
 RTP_API rtp_status rtp_sparse_attn_decode(const rtp_problem *prob, const void *q, const void *k,
                                   const void *v, const rtp_selection *sel, void *out, float *lse,
                                   void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * rtp_sparse_attn_decode_noalloc: rtp_sparse_attn_decode for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, result and kernels, but no
+ * workspace argument: the split partials live in the library's own static device
+ * scratch of RTP_NOALLOC_SCRATCH_BYTES bytes (one copy per device, held until the
+ * process ends, its address resolved on the first call on each device).  The call
+ * allocates and frees nothing.  A problem whose decode workspace,
+ * rtp_workspace_size(prob, RTP_CALL_SPARSE_DECODE, RTP_SEL_LIST), exceeds the
+ * scratch is rejected before any launch with RTP_ERR_WORKSPACE_TOO_SMALL
+ * (rtp_last_hip_error() then names both sizes).  Every call on one device shares
+ * that scratch: calls that overlap on a device (concurrent streams, or host
+ * threads enqueueing to different streams) race; calls on one stream are ordered
+ * by it and are safe.  Nothing in the scratch needs clearing between calls.
+ */
+#define RTP_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+RTP_API rtp_status rtp_sparse_attn_decode_noalloc(const rtp_problem *prob, const void *q, const void *k,
+                                          const void *v, const rtp_selection *sel, void *out, float *lse,
+                                          void *stream);
 
 /*
  * rtp_local_attn: every non-retrieval head attends to keys

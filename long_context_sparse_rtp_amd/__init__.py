@@ -19,7 +19,8 @@ from ._lib import (RTP_BF16, RTP_CALL_LOCAL, RTP_CALL_SELECT, RTP_CALL_SELECT_BL
                    RTP_CALL_SPARSE_PREFILL, RTP_F32, RTP_SEL_LIST, RTP_SEL_THRESHOLD)
 
 __all__ = ["Problem", "Selection", "rtp_workspace_size", "rtp_index_keys", "rtp_append_kv", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
-           "rtp_sparse_attn_prefill", "rtp_sparse_attn_decode", "rtp_local_attn", "RtpError",
+           "rtp_sparse_attn_prefill", "rtp_sparse_attn_decode", "rtp_sparse_attn_decode_noalloc", "rtp_local_attn",
+           "RtpError",
            "RTP_SEL_LIST", "RTP_SEL_THRESHOLD", "RTP_CALL_SELECT", "RTP_CALL_SPARSE_PREFILL",
            "RTP_CALL_SPARSE_DECODE", "RTP_CALL_LOCAL", "RTP_CALL_SELECT_BLOCKS", "library"]
 
@@ -232,6 +233,17 @@ def rtp_sparse_attn_decode(prob: Problem, q, k, v, sel: Selection, out: torch.Te
     st = _lib.load().rtp_sparse_attn_decode(prob.ref, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs), _ptr(out),
                                             _ptr(lse), _ptr(ws), nws, _stream(stream))
     _check(st, "rtp_sparse_attn_decode")
+    return out
+
+
+def rtp_sparse_attn_decode_noalloc(prob: Problem, q, k, v, sel: Selection, out: torch.Tensor,
+                                   lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """rtp_sparse_attn_decode on the library's static scratch: no workspace argument and
+    nothing allocated here or in the library (the caller owns q, k, v, sel, out, lse)."""
+    cs = sel.c()
+    st = _lib.load().rtp_sparse_attn_decode_noalloc(prob.ref, _ptr(q), _ptr(k), _ptr(v), ctypes.byref(cs),
+                                                    _ptr(out), _ptr(lse), _stream(stream))
+    _check(st, "rtp_sparse_attn_decode_noalloc")
     return out
 
 

@@ -11,10 +11,12 @@ RTP_OK, RTP_ERR_INVALID_ARG, RTP_ERR_UNSUPPORTED, RTP_ERR_WORKSPACE_TOO_SMALL, R
 RTP_F32, RTP_BF16 = 0, 1
 RTP_SEL_LIST, RTP_SEL_THRESHOLD = 0, 1
 RTP_CALL_SELECT, RTP_CALL_SPARSE_PREFILL, RTP_CALL_SPARSE_DECODE, RTP_CALL_LOCAL, RTP_CALL_SELECT_BLOCKS = 1, 2, 3, 4, 5
+RTP_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 EXPORTED = ("rtp_workspace_size", "rtp_index_keys", "rtp_append_kv", "rtp_select_topp", "rtp_select_topk", "rtp_select_topp_blocks",
             "rtp_sparse_attn_prefill",
-            "rtp_sparse_attn_decode", "rtp_local_attn", "rtp_status_str", "rtp_last_hip_error")
+            "rtp_sparse_attn_decode", "rtp_sparse_attn_decode_noalloc", "rtp_local_attn", "rtp_status_str",
+            "rtp_last_hip_error")
 
 
 class RtpProblem(ctypes.Structure):
@@ -80,6 +82,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtp_sparse_attn_prefill.restype = i32
     lib.rtp_sparse_attn_decode.argtypes = [P, vp, vp, vp, S, vp, vp, vp, sz, vp]
     lib.rtp_sparse_attn_decode.restype = i32
+    lib.rtp_sparse_attn_decode_noalloc.argtypes = [P, vp, vp, vp, S, vp, vp, vp]
+    lib.rtp_sparse_attn_decode_noalloc.restype = i32
     lib.rtp_local_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.rtp_local_attn.restype = i32
     lib.rtp_status_str.argtypes = [i32]

@@ -173,6 +173,20 @@ rtp_status select_common(const rtp_problem* prob, const void* q_pre, const float
   return finish(rtp::launch_select_prefill(p, bf16, q_pre, w_q, k_idx, top_p, top_k, *sel, ws, s));
 }
 
+// Argument checks shared by rtp_sparse_attn_decode and its no-alloc variant.
+rtp_status check_sparse_decode(const rtp_problem* prob, ProbDev* p, const void* q, const void* k, const void* v,
+                               const rtp_selection* sel, const void* out, const float* lse) {
+  rtp_status st = check_problem(prob, p);
+  if (st != RTP_OK) return st;
+  if (p->max_q != 1 || p->Tq != p->batch) return RTP_ERR_UNSUPPORTED;
+  if (p->R == 0) return RTP_OK;
+  if ((int64_t)p->R * p->batch > rtp::attn_decode_max_rows()) return RTP_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RTP_ERR_INVALID_ARG;
+  if (lse && !aligned4(lse)) return RTP_ERR_INVALID_ARG;
+  if (!sel || !aligned4(sel->idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
+  return RTP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -258,20 +272,35 @@ rtp_status rtp_sparse_attn_prefill(const rtp_problem* prob, const void* q, const
                                          (hipStream_t)stream));
 }
 
+
 rtp_status rtp_sparse_attn_decode(const rtp_problem* prob, const void* q, const void* k, const void* v,
                                   const rtp_selection* sel, void* out, float* lse, void* ws, size_t ws_bytes,
                                   void* stream) {
   ProbDev p;
-  rtp_status st = check_problem(prob, &p);
-  if (st != RTP_OK) return st;
-  if (p.max_q != 1 || p.Tq != p.batch) return RTP_ERR_UNSUPPORTED;
-  if (p.R == 0) return RTP_OK;
-  if ((int64_t)p.R * p.batch > rtp::attn_decode_max_rows()) return RTP_ERR_UNSUPPORTED;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RTP_ERR_INVALID_ARG;
-  if (lse && !aligned4(lse)) return RTP_ERR_INVALID_ARG;
-  if (!sel || !aligned4(sel->idx) || !aligned4(sel->count)) return RTP_ERR_INVALID_ARG;
+  rtp_status st = check_sparse_decode(prob, &p, q, k, v, sel, out, lse);
+  if (st != RTP_OK || p.R == 0) return st;
   st = check_ws(p, RTP_CALL_SPARSE_DECODE, RTP_SEL_LIST, ws, ws_bytes);
   if (st != RTP_OK) return st;
+  return finish(rtp::launch_attn_decode(p, prob->dtype == RTP_BF16, 0, q, k, v, sel, out, lse, ws,
+                                        (hipStream_t)stream));
+}
+
+rtp_status rtp_sparse_attn_decode_noalloc(const rtp_problem* prob, const void* q, const void* k, const void* v,
+                                          const rtp_selection* sel, void* out, float* lse, void* stream) {
+  ProbDev p;
+  rtp_status st = check_sparse_decode(prob, &p, q, k, v, sel, out, lse);
+  if (st != RTP_OK || p.R == 0) return st;
+  const size_t need = ws_need(p, RTP_CALL_SPARSE_DECODE, RTP_SEL_LIST);
+  if (need > rtp::decode_scratch_bytes()) {
+    snprintf(g_err, sizeof(g_err), "rtp_sparse_attn_decode_noalloc: the problem needs %zu bytes of scratch, "
+             "the library's static scratch holds %zu", need, rtp::decode_scratch_bytes());
+    return RTP_ERR_WORKSPACE_TOO_SMALL;
+  }
+  void* ws = nullptr;
+  if (need > 0) {
+    const hipError_t e = rtp::decode_scratch(&ws);
+    if (e != hipSuccess) return finish(e);
+  }
   return finish(rtp::launch_attn_decode(p, prob->dtype == RTP_BF16, 0, q, k, v, sel, out, lse, ws,
                                         (hipStream_t)stream));
 }

@@ -28,6 +28,8 @@
 //   - each group keeps an online-softmax state (max, sum, 8 accumulators) per
 //     head in registers; groups merge through LDS, splits merge in a second
 //     kernel by log-sum-exp.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -734,6 +736,38 @@ inline size_t max_work(const ProbDev& p, int mode, int rows) {
 }
 
 }  // namespace
+
+// ---- scratch of the entry point that allocates nothing (rtp_sparse_attn_decode_noalloc).
+// One copy per device, kept until the process ends; every call on a device shares it.
+// The decode attention kernels write each workspace word before reading it, so
+// nothing needs clearing between calls.
+namespace {
+constexpr size_t kScratchBytes = RTP_NOALLOC_SCRATCH_BYTES;
+__device__ __attribute__((aligned(256))) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};   // the array's device address, per device
+}  // namespace
+
+size_t decode_scratch_bytes() { return kScratchBytes; }
+
+hipError_t decode_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    // with this device current: the symbol's address in this device's copy of the module
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 int attn_decode_max_rows() { return kMaxRowsLds - 1; }
 int attn_decode_tile_heads() { return kMaxTileHeads; }

@@ -79,6 +79,11 @@ hipError_t launch_select_blocks(const ProbDev& p, bool bf16, const void* q_pre, 
                                 const void* k_idx, const float* top_p, const rtp_selection& sel, void* ws,
                                 hipStream_t s);
 // mode 0: retrieval heads over sel LIST; mode 1: local heads over window + sinks
+// The library's own scratch for callers that cannot allocate: a file-scope device
+// array of decode_scratch_bytes() bytes.  decode_scratch() returns its address on
+// the current device (resolved once per device, on that device's first call).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** out);
 hipError_t launch_attn_decode(const ProbDev& p, bool bf16, int mode, const void* q, const void* k,
                               const void* v, const rtp_selection* sel, void* out, float* lse,
                               void* ws, hipStream_t s);
