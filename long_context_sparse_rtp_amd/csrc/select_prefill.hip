@@ -22,18 +22,24 @@
 // Per token, with u = (top - s) log2(e) * B the distance below the reference
 // top >= max s in units of 1/B octave (B = kBinsPerOctave; top is a
 // Cauchy-Schwarz bound, rebased when loose):
-//   mass = 2^(31 - (top - s) log2 e) as an integer, one FMA and one exp2 of
+//   mass = 2^(31.98 - (top - s) log2 e) as an integer, one FMA and one exp2 of
 //          the raw dot product, summed in 64-bit LDS integers (exact and
 //          order-independent: the result is deterministic);
 //   K    = floor(u * 2^16) clamped to 32 bits (K >> 16 == floor(u)).
 // The fixed-point mass of a token is truncated (at most one unit lost), so a
-// row's total Z carries an error of at most (pos + 1) units.  After the first
-// full sweep a row is certified: when (pos + 1) exceeds 2^-20 Z (a row whose
-// mass sits in a few tokens far above a long tail, with a loose reference) the
-// row switches to a wide mass, 2^(ms - (top - s) log2 e) with ms = 42 as a
-// 64-bit integer, after its reference is lowered to within 1/8 octave of the
-// row maximum by the coarse sweep; the truncation error is then below 2^-21 Z
-// for rows up to 2^20 keys.
+// row's total Z and every cumulative mass carry an error of at most (pos + 1)
+// units; the rounding of the exponent's argument (half an ulp of a value below
+// 32) and of exp2 add about 8e-7 relative per token.  After the first full
+// sweep a row is certified when (pos + 1) <= 2^-17 Z, which keeps a crossing
+// within 7.6e-6 + 1.6e-6 of p in cumulative mass (the set tolerance is 1e-5).
+// The wide mass is 2^(ms - (top - s) log2 e) with ms = 42 as an exact 64-bit
+// integer.  A row whose sampled mean mass (first sweep) is below 2^18 units
+// takes it in the windowed sweep, together with every other row of that sweep;
+// a narrow row that fails the certification repeats the windowed sweep wide; a
+// wide row that fails (its mass in a few tokens far above a long tail, with a
+// loose reference) takes the full coarse sweep, which lowers its reference to
+// within 1/8 octave of the row maximum, where the truncation error is below
+// 2^-21 Z for rows up to 2^20 keys.
 // A first sweep reads every 8th full tile (and the diagonal tiles) and
 // histograms the mass over kNB1 bins of floor(u) (the last one open-ended);
 // 16 threads per row scan it for the bin where the cumulative mass reaches p
@@ -75,6 +81,9 @@ constexpr int kParts = kThreads / kRows;        // threads per row in the scans
 enum { PH_P0 = 0, PH_HIST1 = 1, PH_HISTW = 2, PH_REFINE = 3, PH_COLLECT = 4, PH_DONE = 5 };
 constexpr int kFineShift = 12;                  // window bins: 1/256 octave = 2^12 units of K
 constexpr int kSample = 8;                      // the first sweep reads every 8th full tile
+// Narrow mass scale: a token at the reference weighs 2^31.98 units, so that every
+// mass converts to a 32-bit integer (the argument's rounding stays far below 0.02)
+constexpr float kNarrowScale = 31.98f;
 
 __device__ __forceinline__ uint32_t desc_key(float s) {
   uint32_t u = __float_as_uint(s);
@@ -138,7 +147,7 @@ __device__ __forceinline__ float dot_bound(float a, float b, float t) {
   }
   return unord(lo);
 }
-__device__ __forceinline__ uint32_t mass31(float dot, float am, float bm) {
+__device__ __forceinline__ uint32_t mass_narrow(float dot, float am, float bm) {   // < 2^32
   return (uint32_t)__builtin_amdgcn_exp2f(fmaf(dot, am, bm));
 }
 // The wide mass: the float 2^fma(dot, am, bw) < 2^42 as an exact 64-bit integer
@@ -367,6 +376,15 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       int k = PH_DONE;
       for (int rr = 0; rr < kRows; ++rr) k = min(k, ctl[rr].phase);
       sweep_s = k;
+      // a windowed sweep is narrow or wide for all its rows: one wide row makes all wide
+      // (the wide mass is the more precise one; a row's later sweeps follow its mode)
+      if (k == PH_HISTW) {
+        bool anyw = false;
+        for (int rr = 0; rr < kRows; ++rr) anyw |= (ctl[rr].phase == PH_HISTW) && (ctl[rr].wide != 0);
+        if (anyw)
+          for (int rr = 0; rr < kRows; ++rr)
+            if (ctl[rr].phase == PH_HISTW) ctl[rr].wide = 1;
+      }
     }
     __syncthreads();
     const int sweep = sweep_s;
@@ -379,7 +397,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       rk.a20 = -kLog2e * 0.25f * kBinsPerOctave * 65536.f;
       rk.b20 = c.top * kLog2e * kBinsPerOctave * 65536.f;
       rk.am = kLog2e * 0.25f;
-      rk.bm = 31.f - c.top * kLog2e;
+      rk.bm = kNarrowScale - c.top * kLog2e;
       rk.bw = wide_scale(c.pos) - c.top * kLog2e;
       rk.wide = c.wide != 0;
       rk.lo = c.lo;
@@ -423,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         if (check && n > rk.pos) continue;
         const float u = fmaf(d[i], a1, b1);
         const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kNB1 - 1));
-        atomicAdd(&h1[bin][col], COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+        atomicAdd(&h1[bin][col], COUNT ? 1ull : (unsigned long long)mass_narrow(d[i], rk.am, rk.bm));
       }
     };
     // the same with the wide mass for rows that need it (the full coarse sweep only)
@@ -435,10 +453,11 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         const float u = fmaf(d[i], a1, b1);
         const uint32_t bin = (uint32_t)__builtin_amdgcn_fmed3f(u, 0.f, (float)(kNB1 - 1));
         atomicAdd(&h1[bin][col], COUNT ? 1ull : rk.wide ? mass_wide(d[i], rk.am, rk.bw)
-                                                        : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+                                                        : (unsigned long long)mass_narrow(d[i], rk.am, rk.bm));
       }
     };
-    const bool any_wide = __builtin_amdgcn_ballot_w64(rk.wide) != 0;
+    // wide rows among the rows this sweep serves (rk.pos < 0 marks a row in another phase)
+    const bool any_wide = __builtin_amdgcn_ballot_w64(rk.wide && rk.pos >= 0) != 0;
     if (sweep == PH_P0) {
       sweep_sample(hist_coarse);
     } else if (sweep == PH_HIST1) {
@@ -452,17 +471,31 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       // LDS base absorbs -c12 and the bin costs a clamp, a conversion and a shift-add
       const float c12hi = rk.c12 + 255.f;
       char* hbase = reinterpret_cast<char*>(&h1[0][col]) - (ptrdiff_t)(int)rk.c12 * (kRows * 8);
-      sweep_tiles([&](const f32x4& d, int t, bool check) {
+      if (!any_wide) {
+        sweep_tiles([&](const f32x4& d, int t, bool check) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = 16 * t + 4 * grp + i;
-          if (check && n > rk.pos) continue;
-          const float u12 = fmaf(d[i], rk.a12, rk.b12);
-          const uint32_t gb = (uint32_t)__builtin_amdgcn_fmed3f(u12, rk.c12, c12hi);
-          atomicAdd(reinterpret_cast<unsigned long long*>(hbase + (gb << 7)),
-                    COUNT ? 1ull : (unsigned long long)mass31(d[i], rk.am, rk.bm));
-        }
-      });
+          for (int i = 0; i < 4; ++i) {
+            const int n = 16 * t + 4 * grp + i;
+            if (check && n > rk.pos) continue;
+            const float u12 = fmaf(d[i], rk.a12, rk.b12);
+            const uint32_t gb = (uint32_t)__builtin_amdgcn_fmed3f(u12, rk.c12, c12hi);
+            atomicAdd(reinterpret_cast<unsigned long long*>(hbase + (gb << 7)),
+                      COUNT ? 1ull : (unsigned long long)mass_narrow(d[i], rk.am, rk.bm));
+          }
+        });
+      } else {   // every row in this sweep takes the wide mass (see the phase choice)
+        sweep_tiles([&](const f32x4& d, int t, bool check) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = 16 * t + 4 * grp + i;
+            if (check && n > rk.pos) continue;
+            const float u12 = fmaf(d[i], rk.a12, rk.b12);
+            const uint32_t gb = (uint32_t)__builtin_amdgcn_fmed3f(u12, rk.c12, c12hi);
+            atomicAdd(reinterpret_cast<unsigned long long*>(hbase + (gb << 7)),
+                      COUNT ? 1ull : mass_wide(d[i], rk.am, rk.bw));
+          }
+        });
+      }
     } else if (sweep == PH_REFINE && all_fast) {
       sweep_tiles([&](const f32x4& d, int t, bool check) {
         bool inr[4];
@@ -480,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
             if (inr[i]) {
               const uint32_t dig = (key20(fmaf(d[i], rk.a20, rk.b20)) - rk.lo) >> rk.sh;
               atomicAdd(&hm2[dig][col], COUNT ? 1ull : rk.wide ? mass_wide(d[i], rk.am, rk.bw)
-                                                               : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+                                                               : (unsigned long long)mass_narrow(d[i], rk.am, rk.bm));
             }
           }
         }
@@ -545,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           if (sweep == PH_REFINE) {
             const uint32_t dig = dk2 >> rk.sh;
             atomicAdd(&hm2[dig][col], COUNT ? 1ull : rk.wide ? mass_wide(d[i], rk.am, rk.bw)
-                                                             : (unsigned long long)mass31(d[i], rk.am, rk.bm));
+                                                             : (unsigned long long)mass_narrow(d[i], rk.am, rk.bm));
           } else {
             const int slot = atomicAdd(&ccount_s[col], 1);
             if (slot < kCap) cand[col * kCap + slot] = ((unsigned long long)desc_key(s) << 32) | (uint32_t)n;
@@ -606,6 +639,11 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
             // window of 254 fine bins (just under an octave) centred on the estimated bin
             rc.g0 = max(1, bstar * 16 + 8 - 127);
             rc.phase = PH_HISTW;
+            // a sample whose mean mass is below 2^18 units predicts a row that would fail
+            // the certification after the windowed sweep: it takes the wide mass there
+            // directly.  The sample holds every 8th full tile and the diagonal tiles.
+            const double nsamp = 16.0 * (double)((nfull + kSample - 1) / kSample) + (double)(rc.pos + 1 - 16 * nfull);
+            if (!COUNT && (double)Z < nsamp * 262144.0) rc.wide = 1;
           }
         }
       }
@@ -628,10 +666,15 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         }
         const double target = COUNT ? (double)rc.kval : fmax((double)rc.pval * (double)Z, 1.0);
         // certification: the truncation error of Z (at most one unit per key) must stay
-        // below 2^-20 Z; otherwise the row restarts from the coarse sweep with the wide mass
-        const bool certified = COUNT || (double)(rc.pos + 1) * 1048576.0 <= (double)Z;
+        // below 2^-17 Z; otherwise the row restarts from the coarse sweep with the wide mass
+        const bool certified = COUNT || (double)(rc.pos + 1) * 131072.0 <= (double)Z;
         if (!certified) {
-          if (spart == 0) rc.wide = 1;
+          // narrow: the windowed sweep again with the wide mass (its window still holds);
+          // already wide: the full coarse sweep, which also tightens the reference
+          if (spart == 0 && !rc.wide) {
+            rc.wide = 1;
+            rc.phase = PH_HISTW;
+          }
         } else if ((double)pre < target && target <= (double)(pre + sp)) {
           unsigned long long cm = pre;
           int jstar = spart * PB + PB - 1;
@@ -685,7 +728,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         }
         // a narrow row whose truncation error bound fails the certification
         // (see the PH_HISTW controller) switches to the wide mass and sweeps again
-        const bool uncertified = !COUNT && !rc.wide && (double)(rc.pos + 1) * 1048576.0 > (double)Z;
+        const bool uncertified = !COUNT && !rc.wide && (double)(rc.pos + 1) * 131072.0 > (double)Z;
         if (blo >= kNB1 / 2 || Z == 0ull || (rc.wide && blo > 2)) {
           // loose bound (the best token sits >= 8 octaves below it; for a wide row, more
           // than 1/8 octave): lower the reference to just above the best token and
@@ -822,13 +865,13 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       // the range plus the candidates' cumulative mass reaches the target (the last
       // candidate if none does).  Thread q sums ranks [q E, q E + E); the part where
       // the cumulative mass crosses walks its ranks.
-      const float am = kLog2e * 0.25f, bm = 31.f - ctl[srow].top * kLog2e;
+      const float am = kLog2e * 0.25f, bm = kNarrowScale - ctl[srow].top * kLog2e;
       const float bw = wide_scale(ctl[srow].pos) - ctl[srow].top * kLog2e;
       const bool rwide = ctl[srow].wide != 0;
       auto cmass = [&](int k) -> unsigned long long {
         if (COUNT) return 1ull;
         const float dk = undesc_key((uint32_t)(cd[perm[k]] >> 32)) * 4.f;
-        return rwide ? mass_wide(dk, am, bw) : (unsigned long long)mass31(dk, am, bm);
+        return rwide ? mass_wide(dk, am, bw) : (unsigned long long)mass_narrow(dk, am, bm);
       };
       const int a0 = spart * E;
       unsigned long long sp = 0ull;
