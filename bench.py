@@ -41,6 +41,16 @@ KERNELS = {
                             "profiles/attn_prefill_ret_128k_traffic.txt"),
     "local_attn": ("rtp::attn_prefill_kernel<MODE 1>", "long_context_sparse_rtp_amd/csrc/attn_prefill.hip",
                    "profiles/attn_prefill_local_128k_traffic.txt"),
+    "index_keys": ("rtp::index_keys_kernel", "long_context_sparse_rtp_amd/csrc/index_keys.hip",
+                   "profiles/index_keys_128k_traffic.txt"),
+    # decode calls (32K x 8): the traffic of a call sums its kernels
+    "select_decode": ("rtp::sel_dec_*", "long_context_sparse_rtp_amd/csrc/select_decode.hip",
+                      "profiles/select_decode_32k_traffic.txt"),
+    "sparse_attn_decode": ("rtp::attn_decode_kernel<MODE 0> + combine",
+                           "long_context_sparse_rtp_amd/csrc/attn_decode.hip",
+                           "profiles/attn_decode_ret_32k_traffic.txt"),
+    "local_attn_decode": ("rtp::group_decode<false> + combine", "long_context_sparse_rtp_amd/csrc/attn_decode.hip",
+                          "profiles/attn_decode_local_32k_traffic.txt"),
 }
 
 
@@ -53,6 +63,11 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-references", action="store_true", help="skip the dense and pages'-prefill references")
     ap.add_argument("--no-variants", action="store_true", help="skip the fixed top-k (k = 4096) steps")
+    ap.add_argument("--no-long", action="store_true", help="skip the 1M prefill and the 32K..1M prefill curve")
+    ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch-64 decode")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache decode steps")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("DIR", "KERNEL"),
+                    help="summarise a rocprofv3 --pmc output directory for one kernel (no GPU work)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -104,9 +119,27 @@ def _select_call(rtp, prob, inp, k_idx, mode, sel, ws, stream, top_k):
     return lambda: rtp.rtp_select_topk(prob, inp.q_pre, inp.w_q, k_idx, top_k, mode, sel, ws, stream=stream)
 
 
-def bench_prefill(args, torch, rtp, synth, inp=None, top_k=None):
-    """The prefill step; with ``top_k`` (int32 [batch]) the selection is the fixed top-k."""
-    cfg = synth.PREFILL_128K
+def _timed_steps(torch, stream, step, steps, warmup):
+    """Mean ms of ``steps`` consecutive steps (events on the launch stream) after ``warmup``."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / max(1, steps)
+
+
+def bench_prefill(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, steps=None, warmup=None):
+    """The prefill step of ``cfg`` (default the 128K workload); with ``top_k`` (int32 [batch])
+    the selection is the fixed top-k."""
+    cfg = cfg or synth.PREFILL_128K
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     dev = "cuda"
     if inp is None:
         inp = synth.make_inputs(cfg, dev)
@@ -118,6 +151,7 @@ def bench_prefill(args, torch, rtp, synth, inp=None, top_k=None):
                          dtype=torch.uint8, device=dev)
     out = torch.empty_like(inp.q)
     lse = torch.empty((cfg.n_q_heads, inp.total_q), dtype=torch.float32, device=dev)
+    side = torch.cuda.Stream()   # default priority, like the main stream
 
     def step(t: Timer = None):
         calls = [
@@ -144,21 +178,10 @@ def bench_prefill(args, torch, rtp, synth, inp=None, top_k=None):
         join.record(side)
         stream.wait_event(join)
 
-    side = torch.cuda.Stream()   # default priority, like the main stream
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = _timed_steps(torch, stream, step, steps, warmup)
     # per-kernel times: a second pass with an event pair around every call on the launch stream
     t = Timer(torch, stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(t)
     torch.cuda.synchronize()
     per = t.means_ms()
@@ -185,15 +208,51 @@ def bench_prefill(args, torch, rtp, synth, inp=None, top_k=None):
                 tokens=L, cfg=cfg, inp=inp, sel=sel)
 
 
-def bench_prefill_references(args, torch, rtp, synth, pre):
-    """Two references on the same 128K inputs:
-    - dense: causal attention of all 32 heads (our attention kernel with no
-      retrieval heads and a window covering the whole sequence), the baseline
-      the pages' prefill speedups are quoted against;
-    - pages_prefill: the pages' own prefill, where retrieval heads stay dense
-      (top-p = 1, so the selection keeps every key) and local heads attend to
-      sinks + window; the index cache is still built for the decode steps."""
-    cfg, inp = pre["cfg"], pre["inp"]
+def prefill_rooflines(pre):
+    """Per-kernel roofline objects of a prefill run, and the dominant kernel's name."""
+    per = pre["per_kernel_ms"]
+    roofs = {}
+    for k in ("select_topp", "sparse_attn_prefill", "local_attn", "index_keys"):
+        if k not in per:
+            continue
+        rt = per[k] * 1e-3
+        if k == "select_topp":   # bound by the exponential unit
+            ach = pre["exps_select"] / rt / 1e12
+            roofs[k] = {"kernel": KERNELS[k][0], "bound": "alu", "achieved": ach, "peak": EXP_PEAK_TEXPS,
+                        "unit": "Texp/s", "frac": ach / EXP_PEAK_TEXPS, "traffic": _traffic(k)}
+        elif k == "index_keys":  # bound by HBM
+            ach = pre["bytes_index_keys"] / rt / 1e9
+            roofs[k] = {"kernel": KERNELS[k][0], "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": _traffic(k)}
+        else:
+            ach = pre["flops"][k] / rt / 1e12
+            roofs[k] = {"kernel": KERNELS[k][0], "bound": "mfma", "achieved": ach,
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
+                        "traffic": _traffic(k)}
+    dom = max(("sparse_attn_prefill", "local_attn", "select_topp"), key=lambda k: per[k])
+    return roofs, dom
+
+
+def prefill_summary(pre):
+    roofs, dom = prefill_rooflines(pre)
+    per = pre["per_kernel_ms"]
+    return {"ms_per_step": pre["ms"], "tokens_per_s": pre["tokens"] / (pre["ms"] * 1e-3),
+            "per_kernel_ms": per, "per_kernel_roofline": roofs, "dominant_kernel": dom,
+            "per_kernel_tflops": {k: pre["flops"][k] / (per[k] * 1e-3) / 1e12 for k in pre["flops"]},
+            "algorithmic_tflop": pre["total_flops"] / 1e12,
+            "step_frac_of_mfma_roofline": (pre["total_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e12 * 1e3) / pre["ms"],
+            "mean_selected_fraction": pre["mean_frac_selected"]}
+
+
+def bench_prefill_references(args, torch, rtp, synth, cfg, inp, n=1, topp=False):
+    """References on one prefill input:
+    - dense: causal attention of all 32 heads (our attention kernel with no retrieval
+      heads and a window covering the whole sequence), the baseline the pages' prefill
+      speedups are quoted against;
+    - pages_prefill: the pages' own prefill, where retrieval heads stay dense (top-p = 1,
+      so the selection keeps every key) and local heads attend to sinks + window; the
+      index cache is still built for the decode steps;
+    - topp (optional): the top-p prefill step of this repository, all kernels in order."""
     dev = "cuda"
     stream = torch.cuda.current_stream()
     L = cfg.seqlen
@@ -212,35 +271,31 @@ def bench_prefill_references(args, torch, rtp, synth, pre):
     def dense_step():
         rtp.rtp_local_attn(dense, inp.q, inp.k, inp.v, out, lse, stream=stream)
 
-    def pages_step():
-        rtp.rtp_index_keys(prob, inp.k_pre, inp.w_k, k_idx, stream=stream)
-        rtp.rtp_select_topp(prob, inp.q_pre, inp.w_q, k_idx, p_one, rtp.RTP_SEL_THRESHOLD, sel, ws_sel, stream=stream)
-        rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel, out, lse, stream=stream)
-        rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, stream=stream)
+    def sparse_step(pvec):
+        def f():
+            rtp.rtp_index_keys(prob, inp.k_pre, inp.w_k, k_idx, stream=stream)
+            rtp.rtp_select_topp(prob, inp.q_pre, inp.w_q, k_idx, pvec, rtp.RTP_SEL_THRESHOLD, sel, ws_sel,
+                                stream=stream)
+            rtp.rtp_sparse_attn_prefill(prob, inp.q, inp.k, inp.v, k_idx, sel, out, lse, stream=stream)
+            rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, stream=stream)
+        return f
 
-    def timed(fn, n):
-        fn()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(n):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / n
-
-    n = max(1, min(args.steps, 3))
-    dense_ms = timed(dense_step, n)
-    pages_ms = timed(pages_step, n)
+    warm = 0 if L > (1 << 18) else 1    # the longest inputs: their first call is the measured one
+    res = dict(dense_ms=_timed_steps(torch, stream, dense_step, n, warm),
+               pages_ms=_timed_steps(torch, stream, sparse_step(p_one), n, warm))
+    if topp:
+        res["topp_ms"] = _timed_steps(torch, stream, sparse_step(inp.top_p), n, warm)
     dense_flop = 4 * 128 * cfg.n_q_heads * L * (L + 1) / 2
-    return dict(dense_ms=dense_ms, pages_ms=pages_ms, dense_tflops=dense_flop / (dense_ms * 1e-3) / 1e12)
+    res["dense_tflops"] = dense_flop / (res["dense_ms"] * 1e-3) / 1e12
+    return res
 
 
-def bench_decode(args, torch, rtp, synth, inp=None, top_k=None, blocks=False):
-    """The decode step; with ``top_k`` (int32 [batch]) the selection is the fixed top-k,
-    with ``blocks`` the pages' block-granular top-p."""
-    cfg = synth.DECODE_32K
+def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks=False, cold=0):
+    """The decode step of ``cfg`` (default the 32K x 8 workload); with ``top_k`` (int32 [batch])
+    the selection is the fixed top-k, with ``blocks`` the pages' block-granular top-p.
+    ``cold`` > 0 also times that many single steps, each after a 512 MiB write that
+    evicts the caches (L2 and the 256 MB Infinity Cache)."""
+    cfg = cfg or synth.DECODE_32K
     dev = "cuda"
     if inp is None:
         inp = synth.make_inputs(cfg, dev)
@@ -283,35 +338,110 @@ def bench_decode(args, torch, rtp, synth, inp=None, top_k=None, blocks=False):
         stream.wait_event(join)
 
     steps = args.decode_steps
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    ms = _timed_steps(torch, stream, step, steps, args.warmup)
+    # single steps, warm: median and min
+    singles = []
     for _ in range(steps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         step()
-    e1.record(stream)
+        e1.record(stream)
+        singles.append((e0, e1))
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    warm_us = sorted(a.elapsed_time(b) * 1e3 for a, b in singles)
+    cold_us = None
+    if cold:
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        pairs = []
+        for it in range(cold):
+            scrub.fill_(it & 0xFF)     # on the launch stream, before the step's first event
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+        del scrub
     t = Timer(torch, stream)
     for _ in range(steps):
         step(t)
     torch.cuda.synchronize()
     per = t.means_ms()
 
-    counts = sel.count.to(torch.float64).cpu()
-    B, L, W, ns = cfg.batch, cfg.seqlen, cfg.window, cfg.n_sink
+    # algorithmic bytes: per (sequence, KV group) the rows of U = S of its retrieval heads
+    # union window union sinks (K + V), the index keys of its retrieval heads, q and out
     kv_row = 2 * 128 * 2            # K + V bytes per token per KV head
-    sparse_bytes = float(counts.sum().item()) * kv_row
-    local_keys = min(W, L) + min(ns, max(0, L - W))
-    local_bytes = B * cfg.n_kv_heads * local_keys * kv_row   # each KV group's window once
-    idx_bytes = cfg.n_ret * B * L * 16 * 2
+    lens = inp.seqlens_k
+    cu = inp.cu_k.tolist()
+    B, W, ns = cfg.batch, cfg.window, cfg.n_sink
+    counts = sel.count.to(torch.int64).cpu()
+    groups_with_local = {cfg.kv_of(h) for h in cfg.local_heads}
+    union_rows = 0
+    for g in range(cfg.n_kv_heads):
+        slots = [r for r, h in enumerate(cfg.ret_heads) if cfg.kv_of(h) == g]
+        for b in range(B):
+            L = lens[b]
+            mark = torch.zeros(L, dtype=torch.bool, device=dev)
+            if g in groups_with_local:
+                mark[max(0, L - W):] = True
+                mark[:min(ns, L)] = True
+            for r in slots:
+                c = int(counts[r, b])
+                mark[sel.idx[r, cu[b]:cu[b] + c].long()] = True
+            union_rows += int(mark.sum().item())
+    kv_bytes = union_rows * kv_row
+    idx_bytes = cfg.n_ret * sum(lens) * 16 * 2
     qo_bytes = B * cfg.n_q_heads * 128 * 2 * 2
-    return dict(ms=ms, per_kernel_ms=per, bytes=dict(sparse_attn_decode=sparse_bytes, local_attn=local_bytes,
-                                                     select_topp=idx_bytes, q_out=qo_bytes),
-                total_bytes=sparse_bytes + local_bytes + idx_bytes + qo_bytes,
-                mean_frac_selected=float(counts.mean().item()) / L, inp=inp)
+    total = kv_bytes + idx_bytes + qo_bytes
+    sum_sel = float(counts.sum().item())
+    return dict(ms=ms, per_kernel_ms=per, warm_us=warm_us, cold_us=cold_us,
+                bytes=dict(kv_union=kv_bytes, index_keys=idx_bytes, q_out=qo_bytes),
+                total_bytes=total, union_rows=union_rows,
+                mean_frac_selected=sum_sel / (cfg.n_ret * sum(lens)), inp=inp, cfg=cfg)
+
+
+def decode_summary(dec):
+    d = {"step_us": dec["ms"] * 1e3, "per_kernel_us": {k: v * 1e3 for k, v in dec["per_kernel_ms"].items()},
+         "single_step_us": {"median": _median(dec["warm_us"]), "min": dec["warm_us"][0]},
+         "algorithmic_bytes": dec["total_bytes"], "bytes": dec["bytes"],
+         "achieved_GBps": dec["total_bytes"] / (dec["ms"] * 1e-3) / 1e9,
+         "step_frac_of_hbm_roofline": dec["total_bytes"] / (HBM_PEAK_GBS * 1e9) / (dec["ms"] * 1e-3),
+         "mean_selected_fraction": dec["mean_frac_selected"]}
+    if dec["cold_us"]:
+        c = dec["cold_us"]
+        d["cold"] = {"note": "single steps, each after a 512 MiB write that evicts L2 and the Infinity Cache",
+                     "median_us": _median(c), "min_us": c[0], "n": len(c),
+                     "step_frac_of_hbm_roofline_median": dec["total_bytes"] / (HBM_PEAK_GBS * 1e9) / (_median(c) * 1e-6)}
+    per = dec["per_kernel_ms"]
+    sk = [k for k in per if k.startswith("select")][0]
+    d["per_kernel_roofline"] = {
+        sk: _hbm_roof("select_decode" if sk in ("select_topp", "select_topk") else sk, dec["bytes"]["index_keys"],
+                      per[sk]),
+        "sparse_attn_decode": _hbm_roof("sparse_attn_decode", None, per["sparse_attn_decode"]),
+        "local_attn": _hbm_roof("local_attn_decode", None, per["local_attn"])}
+    return d
+
+
+def _median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return 0.5 * (xs[(n - 1) // 2] + xs[n // 2]) if n else None
+
+
+def _hbm_roof(name, algo_bytes, ms):
+    """HBM roofline object of a decode call: algorithmic bytes (when they split per call)
+    over the call time, and the counter traffic of its kernels when committed."""
+    o = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "time_us": ms * 1e3,
+         "traffic": _traffic(name) if name in KERNELS else None}
+    if algo_bytes is not None:
+        o["achieved"] = algo_bytes / (ms * 1e-3) / 1e9
+        o["frac"] = o["achieved"] / HBM_PEAK_GBS
+    if o["traffic"] is not None:
+        o["traffic_GBps"] = o["traffic"] / (ms * 1e-3) / 1e9
+    return o
 
 
 def cpu_baseline(args, pre):
@@ -347,7 +477,7 @@ def cpu_baseline(args, pre):
     wall = time.time() - t0
     # rows drawn uniformly over [0, L) so their mean cost is the mean over the prefill
     tok_s = done_rows / wall
-    return dict(value=tok_s, unit="tokens/s", cores=cores, kind="oracle",
+    return dict(value=tok_s, unit="tokens/s", cores=cores, kind="oracle", cpu=_cpu_model(),
                 sample=f"{done_rows} query rows drawn uniformly from the 128K prefill, all 32 heads each, "
                        f"float64 numpy, {cores} worker processes, {wall:.1f} s")
 
@@ -362,11 +492,45 @@ def _cpu_row_all_heads(i):
     return i
 
 
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def pmc_summary(d, kernel_substr):
+    """Sum of a rocprofv3 --pmc counter CSV over the dispatches of one kernel: prints the
+    counter's mean per dispatch (the counter-summary files under profiles/ quote it)."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    vals = {}
+    for f in files:
+        for row in csv.DictReader(open(f)):
+            if kernel_substr not in row.get("Kernel_Name", ""):
+                continue
+            key = (row.get("Dispatch_Id"), row["Counter_Name"])
+            vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    per = {}
+    for (disp, name), v in vals.items():
+        per.setdefault(name, []).append(v)
+    out = {name: {"mean_per_dispatch": sum(v) / len(v), "dispatches": len(v)} for name, v in per.items()}
+    print(json.dumps({"kernel": kernel_substr, "files": len(files), "counters": out}))
+
+
 def main():
     args = _args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 (no multi-GPU path)"}))
         sys.exit(2)
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary[0], args.pmc_summary[1])
+        return
     import torch
     if args.calibrate_copy:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -381,45 +545,27 @@ def main():
     rtp.library()  # fail loudly if the HIP library is missing
     print(f"[bench] device {torch.cuda.get_device_name(0)}", file=sys.stderr, flush=True)
 
+    def say(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
     line = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
             "data": "synthetic"}
     pre = dec = None
     if args.only in ("prefill", "both"):
-        print("[bench] prefill 128K ...", file=sys.stderr, flush=True)
+        say("prefill 128K ...")
         pre = bench_prefill(args, torch, rtp, synth)
-        tok_s = pre["tokens"] / (pre["ms"] * 1e-3)
-        per = pre["per_kernel_ms"]
-        dom = max(("sparse_attn_prefill", "local_attn", "select_topp"), key=lambda k: per[k])
-        fl = {k: pre["flops"][k] / (per[k] * 1e-3) / 1e12 for k in pre["flops"]}
-        line.update(value=tok_s, unit="tokens/s", ms_per_step=pre["ms"])
+        summ = prefill_summary(pre)
+        line.update(value=summ["tokens_per_s"], unit="tokens/s", ms_per_step=pre["ms"])
         line["config"] = {"workload": "prefill_128k: L=131072 causal, 32 q / 4 kv heads, d=128, bf16, "
                                       "4 retrieval heads (top-p 0.9, 16-dim indexer), 28 local heads "
                                       "(window 2048 + 4 sinks)",
                           "global_batch": 1, "seq_len": pre["tokens"], "parallelism": "none (1 GPU)"}
-        roofs = {}
-        for k in ("select_topp", "sparse_attn_prefill", "local_attn"):
-            rt = per[k] * 1e-3
-            if k == "select_topp":   # bound by the exponential unit
-                ach = pre["exps_select"] / rt / 1e12
-                roofs[k] = {"kernel": KERNELS[k][0], "bound": "alu", "achieved": ach, "peak": EXP_PEAK_TEXPS,
-                            "unit": "Texp/s", "frac": ach / EXP_PEAK_TEXPS, "traffic": _traffic(k)}
-            else:
-                ach = pre["flops"][k] / rt / 1e12
-                roofs[k] = {"kernel": KERNELS[k][0], "bound": "mfma", "achieved": ach,
-                            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                            "traffic": _traffic(k)}
-        line["roofline"] = roofs[dom]
-        line["prefill"] = {"ms_per_step": pre["ms"], "per_kernel_ms": per,
-                           "per_kernel_roofline": roofs,
-                           "per_kernel_tflops": fl,
-                           "algorithmic_tflop": pre["total_flops"] / 1e12,
-                           "step_frac_of_mfma_roofline": (pre["total_flops"] / MFMA_BF16_PEAK_TFLOPS / 1e12 * 1e3)
-                           / pre["ms"],
-                           "mean_selected_fraction": pre["mean_frac_selected"]}
+        line["roofline"] = summ["per_kernel_roofline"][summ["dominant_kernel"]]
+        line["prefill"] = summ
         if not args.no_references:
-            print("[bench] prefill references (dense, pages' prefill) ...", file=sys.stderr, flush=True)
-            ref = bench_prefill_references(args, torch, rtp, synth, pre)
+            say("prefill references at 128K (dense, pages' prefill) ...")
+            ref = bench_prefill_references(args, torch, rtp, synth, pre["cfg"], pre["inp"], n=max(1, min(args.steps, 3)))
             line["prefill"]["references"] = {
                 "dense_causal_ms": ref["dense_ms"], "dense_causal_tflops": ref["dense_tflops"],
                 "pages_prefill_ms": ref["pages_ms"],
@@ -428,54 +574,89 @@ def main():
                 "note": "dense = all 32 heads causal on our attention kernel; pages_prefill = retrieval heads "
                         "dense (top-p 1) + local heads, as the pages run prefill"}
     if args.only in ("decode", "both"):
-        print("[bench] decode 32K x 8 ...", file=sys.stderr, flush=True)
-        dec = bench_decode(args, torch, rtp, synth)
-        per = dec["per_kernel_ms"]
-        line["decode"] = {"workload": "decode_32k_b8: batch 8, KV 32768, 32 q / 4 kv heads, bf16, "
-                                      "4 retrieval heads (top-p 0.95), local window 1024 + 4 sinks",
-                          "step_us": dec["ms"] * 1e3, "per_kernel_us": {k: v * 1e3 for k, v in per.items()},
-                          "algorithmic_bytes": dec["total_bytes"],
-                          "achieved_GBps": dec["total_bytes"] / (dec["ms"] * 1e-3) / 1e9,
-                          "step_frac_of_hbm_roofline": dec["total_bytes"] / (HBM_PEAK_GBS * 1e9) / (dec["ms"] * 1e-3),
-                          "mean_selected_fraction": dec["mean_frac_selected"]}
+        say("decode 32K x 8 (warm, then cold) ...")
+        dec = bench_decode(args, torch, rtp, synth, cold=0 if args.no_cold else 20)
+        line["decode"] = dict({"workload": "decode_32k_b8: batch 8, KV 32768, 32 q / 4 kv heads, bf16, "
+                                           "4 retrieval heads (top-p 0.95), local window 1024 + 4 sinks"},
+                              **decode_summary(dec))
         if pre is None:
             line.update(value=dec["ms"] * 1e3, unit="us", higher_is_better=False, ms_per_step=dec["ms"])
     if not args.no_variants:
         # the pages' static-budget ablation: the same steps with the fixed top-k selection
         var = {"note": "fixed top-k, k = 4096 (the pages' top-k ablation) in place of top-p; same inputs"}
         if pre is not None:
-            print("[bench] prefill 128K, top-k 4096 ...", file=sys.stderr, flush=True)
+            say("prefill 128K, top-k 4096 ...")
             kt = torch.full((pre["cfg"].batch,), 4096, dtype=torch.int32, device="cuda")
             pk = bench_prefill(args, torch, rtp, synth, inp=pre["inp"], top_k=kt)
             var["prefill_128k"] = {"ms_per_step": pk["ms"], "tokens_per_s": pk["tokens"] / (pk["ms"] * 1e-3),
                                    "per_kernel_ms": pk["per_kernel_ms"],
                                    "mean_selected_fraction": pk["mean_frac_selected"]}
+            del pk
         if dec is not None:
-            print("[bench] decode 32K x 8, top-k 4096 ...", file=sys.stderr, flush=True)
+            say("decode 32K x 8, top-k 4096 ...")
             kt = torch.full((synth.DECODE_32K.batch,), 4096, dtype=torch.int32, device="cuda")
             dk = bench_decode(args, torch, rtp, synth, inp=dec["inp"], top_k=kt)
-            var["decode_32k_b8"] = {"step_us": dk["ms"] * 1e3,
-                                    "per_kernel_us": {k: v * 1e3 for k, v in dk["per_kernel_ms"].items()},
-                                    "algorithmic_bytes": dk["total_bytes"],
-                                    "step_frac_of_hbm_roofline": dk["total_bytes"] / (HBM_PEAK_GBS * 1e9)
-                                    / (dk["ms"] * 1e-3),
-                                    "mean_selected_fraction": dk["mean_frac_selected"]}
+            var["decode_32k_b8"] = {k: v for k, v in decode_summary(dk).items() if k != "per_kernel_roofline"}
         line["topk_4096"] = var
         if dec is not None:
-            print("[bench] decode 32K x 8, block top-p ...", file=sys.stderr, flush=True)
+            say("decode 32K x 8, block top-p ...")
             db = bench_decode(args, torch, rtp, synth, inp=dec["inp"], blocks=True)
             line["topp_blocks64"] = {
                 "note": "the pages' block-granular top-p (64-token blocks, 256-bin histogram of block masses "
                         "over block maxima) in place of the token-exact selection; same inputs and p",
-                "decode_32k_b8": {"step_us": db["ms"] * 1e3,
-                                  "per_kernel_us": {k: v * 1e3 for k, v in db["per_kernel_ms"].items()},
-                                  "algorithmic_bytes": db["total_bytes"],
-                                  "step_frac_of_hbm_roofline": db["total_bytes"] / (HBM_PEAK_GBS * 1e9)
-                                  / (db["ms"] * 1e-3),
-                                  "mean_selected_fraction": db["mean_frac_selected"],
-                                  "token_exact_mean_selected_fraction": dec["mean_frac_selected"]}}
+                "decode_32k_b8": dict({k: v for k, v in decode_summary(db).items() if k != "per_kernel_roofline"},
+                                      token_exact_mean_selected_fraction=dec["mean_frac_selected"])}
+    if args.only in ("decode", "both") and not args.no_ragged:
+        say("ragged decode, batch 64 ...")
+        rd = bench_decode(args, torch, rtp, synth, cfg=synth.RAGGED_DECODE)
+        line["ragged_decode"] = dict({"workload": "ragged_decode_b64: batch 64, KV lengths log-uniform in "
+                                                  "[4096, 262144] (sum %d), 32 q / 4 kv heads, bf16, per-sequence "
+                                                  "top-p in [0.8, 0.99], local window 1024 + 4 sinks, half the "
+                                                  "sequences peaky (256 needles)" % sum(rd["inp"].seqlens_k)},
+                                     **decode_summary(rd))
+        del rd
+    if args.only in ("prefill", "both") and not args.no_long:
+        say("prefill 1M ...")
+        c4 = bench_prefill(args, torch, rtp, synth, cfg=synth.PREFILL_1M, steps=2, warmup=1)
+        line["prefill_1m"] = dict({"workload": "prefill_1m: L=1048576 causal, 32 q / 4 kv heads, bf16, "
+                                               "4 retrieval heads (top-p 0.9), 28 local heads (window 4096 + 4 sinks)"},
+                                  **prefill_summary(c4))
+        line["prefill_1m"]["roofline"] = line["prefill_1m"]["per_kernel_roofline"][line["prefill_1m"]["dominant_kernel"]]
+        if not args.no_references:
+            # the shape of the pages' Fig. 1 (prefill speedup over dense attention against context
+            # length) on this GPU: our dense causal kernel against the pages' prefill (retrieval
+            # heads dense) and against this repository's top-p prefill, one call each
+            say("prefill curve 32K .. 1M (dense, pages' prefill, top-p) ...")
+            curve = []
+            for L in (32768, 65536, 131072, 524288, 1048576):
+                if L == 1048576:
+                    cfg, inp = c4["cfg"], c4["inp"]
+                elif L == 131072 and pre is not None:
+                    cfg, inp = pre["cfg"], pre["inp"]
+                else:
+                    base = synth.PREFILL_1M if L > 131072 else synth.PREFILL_128K
+                    cfg = synth.scaled(base, name=f"prefill_{L // 1024}k", seqlen=L)
+                    inp = synth.make_inputs(cfg, "cuda")
+                say(f"  curve L={L}")
+                ref = bench_prefill_references(args, torch, rtp, synth, cfg, inp, n=1, topp=True)
+                curve.append({"L": L, "window": cfg.window, "dense_ms": ref["dense_ms"],
+                              "pages_prefill_ms": ref["pages_ms"], "topp_prefill_ms": ref["topp_ms"],
+                              "pages_prefill_speedup": ref["dense_ms"] / ref["pages_ms"],
+                              "topp_prefill_speedup": ref["dense_ms"] / ref["topp_ms"],
+                              "dense_tflops": ref["dense_tflops"]})
+                del inp
+                torch.cuda.empty_cache()
+            line["prefill_1m"]["references"] = {
+                "curve": curve,
+                "pages_published_speedup_vs_flashattention2": {"32K": 2.83, "64K": 4.25, "512K": 8.62, "1M": 9.36},
+                "note": "dense = all 32 heads causal on our own attention kernel (the pages compare with "
+                        "FlashAttention-2 on unstated hardware: context only); pages_prefill = retrieval heads "
+                        "dense + local heads (sinks + window 2048 up to 128K, 4096 above); topp = this "
+                        "repository's top-p 0.9 prefill step, kernels in order"}
+        del c4
+        torch.cuda.empty_cache()
     if pre is not None and not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        say("cpu baseline (oracle) ...")
         line["cpu_baseline"] = cpu_baseline(args, pre)
     print(json.dumps(line))
 
