@@ -52,7 +52,6 @@ constexpr int kPer = kChunk / kThreads;       // keys per thread
 constexpr int kNB = 4096;                     // bins per unit / row histogram
 constexpr int kNC = kNB / 16 + 1;             // coarse bins per unit (16 absolute bins each)
 constexpr int kCap = 4096;                    // candidates per row (ranked in LDS)
-constexpr int kCapUnit = 1024;                // candidates stored per unit
 constexpr int kMaxUnits = 1024;               // units per row (4M keys)
 constexpr float kBinScale = 128.f * kLog2e;   // bins per unit of score
 constexpr int kCountShift = 51;
@@ -65,27 +64,11 @@ struct UnitMeta {
   int cused;                  // highest non-empty coarse bin
 };
 enum { ROW_NORMAL = 0, ROW_ALL = 1, ROW_EMPTY = 2 };
-struct UnitCnt {
-  uint32_t above;             // unit tokens in row bins before the crossing bin
-  uint32_t inbin;             // unit tokens in the crossing bin
-};
-struct RowState {
-  double above;               // mass of the row bins before the crossing bin
-  double target;              // p * Z (top-k: k)
-  int mode;
-  int A, Ap;                  // row reference bin, and A | 15 (the row bin grid J = Ap - a)
-  int jstar;                  // crossing row bin
-  uint32_t cabove;            // tokens before the crossing bin
-  uint32_t bincnt;            // tokens in the crossing bin
-};
 struct DecodeWs {
   float* scores;               // [R * Tk]
   UnitMeta* meta;              // [nslots]
   unsigned long long* hist;    // [nslots * kNB]
   unsigned long long* chist;   // [nslots * kNC]: 16 absolute bins per coarse bin
-  UnitCnt* ucnt;               // [nslots]
-  unsigned long long* cand;    // [nslots * kCapUnit]: (desc_key << 32) | position
-  RowState* rows;              // [R * batch]
 };
 
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -103,13 +86,9 @@ inline size_t ws_layout(const ProbDev& p, void* base, DecodeWs* w) {
   char* m = take(sizeof(UnitMeta) * nslots);
   char* h = take(sizeof(unsigned long long) * nslots * kNB);
   char* ch = take(sizeof(unsigned long long) * nslots * kNC);
-  char* uc = take(sizeof(UnitCnt) * nslots);
-  char* cd = take(sizeof(unsigned long long) * nslots * kCapUnit);
-  char* ro = take(sizeof(RowState) * (size_t)p.R * p.batch);
   if (w) {
     w->scores = (float*)s; w->meta = (UnitMeta*)m; w->hist = (unsigned long long*)h;
-    w->chist = (unsigned long long*)ch; w->ucnt = (UnitCnt*)uc; w->cand = (unsigned long long*)cd;
-    w->rows = (RowState*)ro;
+    w->chist = (unsigned long long*)ch;
   }
   return o;
 }
@@ -352,6 +331,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_score(ProbDev p, const T* __
   __shared__ int red_i[kThreads / 64];
   __shared__ unsigned long long red_u[kThreads / 64];
 
+
   // keys n = c*kChunk + tid + 256 j: a wave reads consecutive 32/64-byte rows.  The
   // first batch of keys is requested before the query projection so the loads overlap it.
   constexpr int kB = kPer;
@@ -442,62 +422,111 @@ __global__ __launch_bounds__(kThreads) void sel_dec_score(ProbDev p, const T* __
   }
 }
 
-// ======================================================================= 2. collect
-// Every unit finds the row's crossing bin (the same in every workgroup of the
-// row: fixed-order sums of the same data), then counts its own tokens above
-// it and stores its tokens inside it as candidates.  Row bins sit on the grid
-// J = Ap - a(s) with Ap = A | 15, A the highest unit bin, so that 16 row bins
-// form one coarse bin of the units' coarse histograms; the coarse crossing
-// is found first (one coarse bin per thread), then the fine bins inside it.
-// The last row bin (coarse and fine) is open-ended: its count is the row's
-// remainder and its mass what the others leave of Z.
-constexpr int kRowCoarse = kNB / 16;   // 256: one per thread
-static_assert(kRowCoarse == kThreads, "one coarse bin per thread");
+// ======================================================================= 2. finish
+// One workgroup (1024 threads) per row (retrieval slot, sequence) takes the row
+// from the units' statistics to its LIST:
+//   - the crossing bin: per-unit sums scaled by 2^((A_u - A) / 128) in float64
+//     in a fixed order (deterministic), first the coarse row bin where the
+//     cumulative mass reaches p * Z, then the fine bin inside it.  Row bins sit
+//     on the grid J = Ap - a(s) with Ap = A | 15, A the highest unit bin, so
+//     that 16 row bins form one coarse bin of every unit; the last row bin
+//     (coarse and fine) is open-ended and holds the row's remainder;
+//   - the crossing bin's tokens, gathered from the row's stored scores, which
+//     the workgroup holds in registers (32 per thread, chunks of 32K keys),
+//     loaded while the crossing is searched;
+//   - ranks of those candidates by (score desc, position asc), the walk of
+//     their masses to the crossing token (tau, tie_pos, count);
+//   - the members written in ascending order: per chunk, one ballot per wave
+//     and 64 positions, the wave counts scanned once, then the writes.
+// A crossing bin too crowded for the candidate buffer (mass piled on
+// near-identical scores) is resolved from the stored scores with radix digits
+// of the score's bit pattern and then positions.
+constexpr int kRowCoarse = kNB / 16;   // 256 coarse row bins
+constexpr int kFT = 1024;              // threads of the finish workgroup
+constexpr int kFW = kFT / 64;          // its waves
+constexpr int kFS = 32;                // scores per thread per chunk
+constexpr int kFChunk = kFS * kFT;     // keys per chunk
+static_assert(kMaxUnits <= kFT, "one unit per finish thread");
+static_assert(kCap % kFT == 0, "whole ranks per finish thread");
 
 __device__ __forceinline__ double bin_mass(unsigned long long e, double f, bool cmode) {
   return cmode ? (double)(uint32_t)(e >> kCountShift) : (double)(e & kMassMask) * f;
 }
 
-__global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const float* __restrict__ top_p,
-                                                            const int32_t* __restrict__ top_k, rtp_selection sel,
-                                                            DecodeWs ws) {
-  int row, c;
-  unit_of(p, blockIdx.x, row, c);
+// fixed-order block helpers over kFW waves (every thread of the workgroup calls them)
+template <typename V>
+__device__ V fblock_exscan(V x, V* tmp /* >= kFW */, V& total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  V inc = x;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const V y = __shfl_up(inc, d);
+    if (lane >= d) inc += y;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[wid] = inc;
+  __syncthreads();
+  V off = 0;
+  total = 0;
+  for (int w = 0; w < kFW; ++w) {
+    if (w < wid) off += tmp[w];
+    total += tmp[w];
+  }
+  __syncthreads();
+  return off + (inc - x);
+}
+__device__ int fblock_max(int x, int* tmp) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  __syncthreads();
+  if (lane == 0) tmp[wid] = x;
+  __syncthreads();
+  int m = tmp[0];
+  for (int w = 1; w < kFW; ++w) m = max(m, tmp[w]);
+  __syncthreads();
+  return m;
+}
+
+__global__ __launch_bounds__(kFT) void sel_dec_finish(ProbDev p, const float* __restrict__ top_p,
+                                                      const int32_t* __restrict__ top_k, rtp_selection sel,
+                                                      DecodeWs ws) {
+  const int row = blockIdx.x;
   if (row >= p.R * p.batch) return;
   const RowGeom g = row_geom(p, row);
-  if (c >= g.U || g.U > kMaxUnits) return;
+  if (g.U > kMaxUnits) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  // this unit's scores and every unit's statistics are requested before the row's
-  // top-p (or k) arrives, so the loads share one round trip (their addresses depend
-  // on the row's geometry only)
+  int* out = sel.idx + (size_t)g.r * p.Tk + g.k0;
+  const size_t ro = (size_t)g.r * p.Tq + g.qrow;
   const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
-  const int n0 = c * kChunk + tid;
-  float s[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int n = n0 + j * kThreads;
-    s[j] = (n < g.L) ? sb[n] : 0.f;
-  }
-  constexpr int PU = kMaxUnits / kThreads;
-  UnitMeta mtv[PU];
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid + t * kThreads;
-    if (u < g.U) mtv[t] = ws.meta[g.slot0 + u];
-  }
   const bool cmode = top_k != nullptr;
+  const int nchunks = (g.L + kFChunk - 1) / kFChunk;
+
+  // every unit's statistics and the first chunk of scores are requested before the
+  // row's top-p (or k) arrives
+  UnitMeta mt = {};
+  if (tid < g.U) mt = ws.meta[g.slot0 + tid];
+  float sv[kFS];
+  // wave w holds positions ch * kFChunk + w * kFS * 64 + 64 i + lane: a contiguous range
+  // per wave, so the emission scans kFW wave counts only
+  auto pos_of = [&](int ch, int i) { return ch * kFChunk + wid * (kFS * 64) + 64 * i + lane; };
+  auto load_chunk = [&](int ch) {
+#pragma unroll
+    for (int i = 0; i < kFS; ++i) {
+      const int n = pos_of(ch, i);
+      sv[i] = (n < g.L) ? sb[n] : 0.f;
+    }
+  };
+  load_chunk(0);
   const int kk = cmode ? max(top_k[g.b], 1) : 0;
   const float pp = cmode ? 0.f : top_p[g.b];
   if (g.L == 0 || (cmode ? kk >= g.L : !(pp < 1.f))) {   // empty row; every key (p >= 1 or NaN; k >= L)
-    if (c == 0 && tid == 0) {
+    for (int n = tid; n < g.L; n += kFT) out[n] = n;
+    if (tid == 0) {
       const bool empty = g.L == 0;
-      const size_t ro = (size_t)g.r * p.Tq + g.qrow;
       sel.count[ro] = empty ? 0 : g.L;
       if (sel.tau) sel.tau[ro] = empty ? INFINITY : -INFINITY;
       if (sel.tie_pos) sel.tie_pos[ro] = 0x7FFFFFFF;
-      RowState rs = {};
-      rs.mode = empty ? ROW_EMPTY : ROW_ALL;
-      ws.rows[g.row] = rs;
     }
     return;
   }
@@ -506,85 +535,92 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
   __shared__ int used_s[kMaxUnits];
   __shared__ int cused_s[kMaxUnits];
   __shared__ double f_s[kMaxUnits];
-  __shared__ double fm_s[kThreads / 64][16];
-  __shared__ uint32_t fc_s[kThreads / 64][16];
-  __shared__ double dtmp[kThreads / 64];
-  __shared__ int itmp[kThreads / 64];
-  __shared__ uint32_t utmp[kThreads / 64];
-  __shared__ int cstar_s, clast_s, jstar_s, nc_s;
+  __shared__ double cm_s[4][kRowCoarse];
+  __shared__ uint32_t cc_s[4][kRowCoarse];
+  __shared__ double fm_s[kFW][16];
+  __shared__ uint32_t fc_s[kFW][16];
+  __shared__ double fmt_s[16];
+  __shared__ uint32_t fct_s[16];
+  __shared__ unsigned long long cand_s[kCap];
+  __shared__ short order_s[kCap];
+  __shared__ double dtmp[kFW];
+  __shared__ int itmp[kFW];
+  __shared__ uint32_t utmp[kFW];
+  __shared__ int cstar_s, clast_s, jstar_s, js_s, tie_s, count_s, nc_s;
   __shared__ double cab_m_s, cbin_m_s, above_s;
   __shared__ uint32_t cab_c_s, cbin_c_s, cabove_s, bincnt_s;
+  __shared__ float tau_s;
 
-  // ---- merge: reference bin A and per-unit scales 2^((A_u - A) / 128)
-  int amax = -2147483647 - 1;
-  unsigned long long zu[PU];
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid + t * kThreads;
-    zu[t] = 0ull;
-    if (u < g.U) {
-      const UnitMeta mt = mtv[t];
-      A_s[u] = mt.A;
-      used_s[u] = mt.used;
-      cused_s[u] = mt.cused;
-      zu[t] = mt.Z;
-      if (mt.used >= 0) amax = max(amax, mt.A);
-    }
+  // ---- reference bin A and per-unit scales 2^((A_u - A) / 128)
+  if (tid < g.U) {
+    A_s[tid] = mt.A;
+    used_s[tid] = mt.used;
+    cused_s[tid] = mt.cused;
   }
-  const int A = block_max<int>(amax, itmp);
+  const int A = fblock_max((tid < g.U && mt.used >= 0) ? mt.A : (-2147483647 - 1), itmp);
   const int Ap = A | 15;
   double zl = 0.0;
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid + t * kThreads;
-    if (u < g.U) {
-      const double f = (used_s[u] >= 0) ? unit_scale(A_s[u], A) : 0.0;
-      f_s[u] = f;
-      zl += (double)zu[t] * f;
-    }
+  if (tid < g.U) {
+    const double f = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
+    f_s[tid] = f;
+    zl = (double)mt.Z * f;
   }
   double Z;
-  (void)block_exscan_f64_n<kThreads / 64>(zl, dtmp, Z);   // its barriers also publish f_s
+  (void)fblock_exscan<double>(zl, dtmp, Z);   // its barriers also publish A_s, used_s, f_s
   const double target = cmode ? (double)kk : fmax((double)pp * Z, 1.0);
 
-  // ---- coarse row bin tid: unit u's coarse bin tid - ((Ap >> 4) - (A_u >> 4)), eight units' loads at a time
-  double cm = 0.0;
-  uint32_t cc = 0u;
-  if (tid < kRowCoarse - 1) {
-    for (int u0 = 0; u0 < g.U; u0 += 8) {
-      unsigned long long e[8];
+  // ---- coarse row bins: thread (q, cb) sums units q, q + 4, ... of coarse row bin cb
+  {
+    const int cb = tid & (kRowCoarse - 1), q = tid >> 8;
+    double cm = 0.0;
+    uint32_t cc = 0u;
+    if (cb < kRowCoarse - 1) {
+      for (int u0 = q; u0 < g.U; u0 += 4 * 4) {
+        unsigned long long e[4];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int u = u0 + k;
-        e[k] = 0ull;
-        if (u < g.U && used_s[u] >= 0) {
-          const int cj = tid - ((Ap >> 4) - (A_s[u] >> 4));
-          if (cj >= 0 && cj <= cused_s[u]) e[k] = ws.chist[(g.slot0 + u) * kNC + cj];
+        for (int k = 0; k < 4; ++k) {
+          const int u = u0 + 4 * k;
+          e[k] = 0ull;
+          if (u < g.U && used_s[u] >= 0) {
+            const int cj = cb - ((Ap >> 4) - (A_s[u] >> 4));
+            if (cj >= 0 && cj <= cused_s[u]) e[k] = ws.chist[(g.slot0 + u) * kNC + cj];
+          }
         }
-      }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        if (u0 + k < g.U) {
-          cm += bin_mass(e[k], f_s[u0 + k], cmode);
-          cc += (uint32_t)(e[k] >> kCountShift);
+        for (int k = 0; k < 4; ++k) {
+          const int u = u0 + 4 * k;
+          if (u < g.U) {
+            cm += bin_mass(e[k], f_s[u], cmode);
+            cc += (uint32_t)(e[k] >> kCountShift);
+          }
         }
       }
     }
+    cm_s[q][cb] = cm;
+    cc_s[q][cb] = cc;
   }
-  if (tid == 0) { cstar_s = kRowCoarse; clast_s = -1; nc_s = 0; }   // ordered by the scans' barriers
+  if (tid == 0) { cstar_s = kRowCoarse; clast_s = -1; nc_s = 0; }
+  __syncthreads();
   {
-    // one scan gives every bin's prefix and, the last bin holding 0 here, the total of
-    // the others: the open-ended last bin is the row's remainder
+    // one scan gives every coarse bin's prefix and, the last bin holding 0 here, the
+    // total of the others: the open-ended last bin is the row's remainder
+    double cm = 0.0;
+    uint32_t cc = 0u;
+    if (tid < kRowCoarse) {
+      cm = ((cm_s[0][tid] + cm_s[1][tid]) + cm_s[2][tid]) + cm_s[3][tid];
+      cc = ((cc_s[0][tid] + cc_s[1][tid]) + cc_s[2][tid]) + cc_s[3][tid];
+    }
     double part;
     uint32_t partc;
-    const double pre = block_exscan_f64_n<kThreads / 64>(cm, dtmp, part);
-    const uint32_t cpre = block_exscan<uint32_t>(cc, utmp, partc);
+    const double pre = fblock_exscan<double>(cm, dtmp, part);
+    const uint32_t cpre = fblock_exscan<uint32_t>(cc, utmp, partc);
     if (tid == kRowCoarse - 1) {
       cm = fmax((cmode ? (double)g.L : Z) - part, 0.0);
       cc = (uint32_t)g.L - partc;
     }
-    if (cc > 0u && pre < target && pre + cm >= target) atomicMin(&cstar_s, tid);
-    if (cc > 0u) atomicMax(&clast_s, tid);
+    const bool mine = tid < kRowCoarse && cc > 0u;
+    if (mine && pre < target && pre + cm >= target) atomicMin(&cstar_s, tid);
+    if (mine) atomicMax(&clast_s, tid);
     __syncthreads();
     // rounding left the target just out of reach: the last non-empty coarse bin
     const int cs = (cstar_s < kRowCoarse) ? cstar_s : clast_s;
@@ -595,14 +631,14 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
   }
   const int cstar = cstar_s;
 
-  // ---- fine bins of the crossing coarse bin: lane group (i, q) sums units q, q + 16, ...
+  // ---- fine bins of the crossing coarse bin: lane group (i, q) sums units q, q + 64, ...
   {
     const int i = tid & 15, q = tid >> 4;
     const int J = cstar * 16 + i;
     double fm = 0.0;
     uint32_t fc = 0u;
     if (J < kNB - 1) {
-      for (int u = q; u < g.U; u += kThreads / 16) {
+      for (int u = q; u < g.U; u += kFT / 16) {
         if (used_s[u] < 0) continue;
         const int j = J - (Ap - A_s[u]);
         if (j >= 0 && j <= used_s[u]) {
@@ -619,6 +655,14 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
     fc += __shfl_xor(fc, 32);
     if (lane < 16) { fm_s[wid][i] = fm; fc_s[wid][i] = fc; }
     __syncthreads();
+    if (tid < 16) {   // bin tid over the waves, in a fixed order
+      double bm = 0.0;
+      uint32_t bc = 0u;
+      for (int w2 = 0; w2 < kFW; ++w2) { bm += fm_s[w2][tid]; bc += fc_s[w2][tid]; }
+      fmt_s[tid] = bm;
+      fct_s[tid] = bc;
+    }
+    __syncthreads();
     if (tid == 0) {
       double m = cab_m_s, rm = cbin_m_s;
       uint32_t cnt = cab_c_s, rc = cbin_c_s;
@@ -629,7 +673,8 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
         double bm = 0.0;
         uint32_t bc = 0u;
         if (cstar * 16 + b2 < kNB - 1) {
-          for (int w2 = 0; w2 < kThreads / 64; ++w2) { bm += fm_s[w2][b2]; bc += fc_s[w2][b2]; }
+          bm = fmt_s[b2];
+          bc = fct_s[b2];
           rm -= bm;
           rc -= bc;
         } else {   // the open-ended last bin: what the coarse bin leaves
@@ -649,169 +694,28 @@ __global__ __launch_bounds__(kThreads) void sel_dec_collect(ProbDev p, const flo
     __syncthreads();
   }
   const int jstar = jstar_s;
-
-  // ---- this unit: tokens above the crossing bin, and the bin's tokens as candidates
-  uint32_t nabove = 0u, nbin = 0u;
-  unsigned long long* cd = ws.cand + (g.slot0 + c) * kCapUnit;
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int n = n0 + j * kThreads;
-    if (n < g.L) {
-      const int J = min(kNB - 1, Ap - abs_bin(s[j]));
-      nabove += (J < jstar) ? 1u : 0u;
-      if (J == jstar) {
-        ++nbin;
-        const int sl = atomicAdd(&nc_s, 1);
-        if (sl < kCapUnit) cd[sl] = ((unsigned long long)desc_key(s[j]) << 32) | (uint32_t)n;
-      }
-    }
-  }
-  uint32_t tot_above, tot_bin;
-  (void)block_exscan<uint32_t>(nabove, utmp, tot_above);
-  (void)block_exscan<uint32_t>(nbin, utmp, tot_bin);
-  if (tid == 0) {
-    UnitCnt uc = {tot_above, tot_bin};
-    ws.ucnt[g.slot0 + c] = uc;
-    if (c == 0) {
-      RowState rs;
-      rs.above = above_s;
-      rs.target = target;
-      rs.mode = ROW_NORMAL;
-      rs.A = A;
-      rs.Ap = Ap;
-      rs.jstar = jstar;
-      rs.cabove = cabove_s;
-      rs.bincnt = bincnt_s;
-      ws.rows[g.row] = rs;
-    }
-  }
-}
-
-// ======================================================================= 3. emit
-// Every unit ranks the row's candidates by (score desc, position asc), walks
-// their masses to the crossing token (tau, tie_pos, count), derives its first
-// output slot from the per-unit counts and writes its members in ascending
-// order: within a wave's 1024 keys by ballots (keys j * 64 + lane in order j,
-// then lane), across the four waves by their counts.  A crossing bin too
-// crowded for the candidate lists (mass piled on near-identical scores) is
-// resolved from the row's stored scores, with radix digits of the score's bit
-// pattern and then positions.
-__global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_t* __restrict__ top_k,
-                                                         rtp_selection sel, DecodeWs ws) {
-  int row, c;
-  unit_of(p, blockIdx.x, row, c);
-  if (row >= p.R * p.batch) return;
-  const RowGeom g = row_geom(p, row);
-  if (c >= g.U || g.U > kMaxUnits || g.L == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  int* out = sel.idx + (size_t)g.r * p.Tk + g.k0;
-  constexpr int kSeg = kChunk / kThreads;
-  const int nw = c * kChunk + wid * (64 * kSeg);
-  // this unit's scores and every unit's counts and statistics are requested with the
-  // row's state, so the loads share one round trip (their addresses depend on the
-  // row's geometry only; a row taken whole does not use them)
-  const float* sb = ws.scores + (size_t)g.r * p.Tk + g.k0;
-  float sv[kSeg];
-#pragma unroll
-  for (int j = 0; j < kSeg; ++j) {
-    const int n = nw + j * 64 + lane;
-    sv[j] = (n < g.L) ? sb[n] : 0.f;
-  }
-  constexpr int PU = kMaxUnits / kThreads;
-  UnitCnt ucv[PU];
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid * PU + t;
-    ucv[t] = UnitCnt{0u, 0u};
-    if (u < g.U) ucv[t] = ws.ucnt[g.slot0 + u];
-  }
-  UnitMeta mtv[PU];
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid + t * kThreads;
-    if (u < g.U) mtv[t] = ws.meta[g.slot0 + u];
-  }
-  const RowState rs = ws.rows[g.row];
-  if (rs.mode == ROW_ALL) {
-#pragma unroll
-    for (int j = 0; j < kSeg; ++j) {
-      const int n = nw + j * 64 + lane;
-      if (n < g.L) out[n] = n;
-    }
-    return;
-  }
-  if (rs.mode != ROW_NORMAL) return;
-  const bool cmode = top_k != nullptr;
-
-  __shared__ int A_s[kMaxUnits];
-  __shared__ double f_s[kMaxUnits];
-  __shared__ uint32_t cmem_s[kMaxUnits];     // members per unit among the candidates
-  __shared__ uint32_t cbase_s[kMaxUnits];
-  __shared__ uint32_t cab_s[kMaxUnits];
-  __shared__ unsigned long long cand_s[kCap];
-  __shared__ short order_s[kCap];
-  __shared__ double dtmp[kThreads / 64];
-  __shared__ uint32_t utmp[kThreads / 64];
-  __shared__ float tau_s;
-  __shared__ int tie_s, count_s, js_s;
-  __shared__ uint32_t off_s;
-  __shared__ uint32_t wcnt_s[kThreads / 64];
-
-  const int A = rs.A, Ap = rs.Ap;
-  const double target = rs.target;
   auto bin_of = [&](float v) { return min(kNB - 1, Ap - abs_bin(v)); };
-  // per unit: candidate count and base (consecutive units per thread, for the scan),
-  // reference bin and scale (units dealt round-robin, so that a row of up to 256
-  // units costs every thread at most one float64 exp2)
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid + t * kThreads;
-    if (u < g.U) {
-      const UnitMeta mt = mtv[t];
-      A_s[u] = mt.A;
-      f_s[u] = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
-    }
-  }
-  uint32_t nin = 0u, cmax = 0u;
-  uint32_t vin[PU];
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid * PU + t;
-    vin[t] = 0u;
-    if (u < g.U) {
-      const UnitCnt uc = ucv[t];
-      vin[t] = uc.inbin;
-      cab_s[u] = uc.above;
-      cmem_s[u] = 0u;
-    }
-    nin += vin[t];
-    cmax = max(cmax, vin[t]);
-  }
-  uint32_t ntot;
-  uint32_t run = block_exscan<uint32_t>(nin, utmp, ntot);
-#pragma unroll
-  for (int t = 0; t < PU; ++t) {
-    const int u = tid * PU + t;
-    if (u < g.U) cbase_s[u] = run;
-    run += vin[t];
-  }
-  cmax = block_max<uint32_t>(cmax, utmp);
-  const bool fits = (ntot == rs.bincnt) && (ntot <= (uint32_t)kCap) && (cmax <= (uint32_t)kCapUnit) && ntot > 0u;
 
-  if (fits) {
-    const int nc = (int)ntot;
-    // gather: candidate k belongs to the last unit whose base is <= k
-    for (int kq = tid; kq < nc; kq += kThreads) {
-      int lo = 0, hi = g.U - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cbase_s[mid] <= (uint32_t)kq) lo = mid; else hi = mid - 1;
+  if (bincnt_s <= (uint32_t)kCap) {
+    // ---- the crossing bin's tokens from the scores in registers
+    for (int ch = 0; ch < nchunks; ++ch) {
+      if (ch > 0) load_chunk(ch);
+#pragma unroll
+      for (int i = 0; i < kFS; ++i) {
+        const int n = pos_of(ch, i);
+        if (n < g.L && bin_of(sv[i]) == jstar) {
+          const int sl = atomicAdd(&nc_s, 1);
+          if (sl < kCap) cand_s[sl] = ((unsigned long long)desc_key(sv[i]) << 32) | (uint32_t)n;
+        }
       }
-      cand_s[kq] = ws.cand[(g.slot0 + lo) * kCapUnit + (kq - (int)cbase_s[lo])];
     }
+    if (nchunks > 1) load_chunk(0);
     __syncthreads();
+  }
+  const int nc = nc_s;
+  if (nc > 0 && nc <= kCap && (uint32_t)nc == bincnt_s) {
     // rank of every candidate in (desc_key, position) order: keys are distinct
-    for (int i = tid; i < nc; i += kThreads) {
+    for (int i = tid; i < nc; i += kFT) {
       const unsigned long long ki = cand_s[i];
       int rank = 0;
       for (int j = 0; j < nc; ++j) rank += (cand_s[j] < ki) ? 1 : 0;
@@ -819,7 +723,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
     }
     __syncthreads();
     // cumulative masses in rank order: G consecutive ranks per thread, fixed order
-    constexpr int G = kCap / kThreads;
+    constexpr int G = kCap / kFT;
     double ms[G];
     double loc = 0.0;
 #pragma unroll
@@ -835,7 +739,7 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
       loc += ms[t];
     }
     double tt;
-    double pre = block_exscan_f64_n<kThreads / 64>(loc, dtmp, tt) + rs.above;
+    double pre = fblock_exscan<double>(loc, dtmp, tt) + above_s;
     if (tid == 0) js_s = nc - 1;   // if rounding hides the crossing: the last candidate
     __syncthreads();
 #pragma unroll
@@ -852,19 +756,8 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
       tie_s = (int)(uint32_t)(kv & 0xFFFFFFFFull);
       // every token scoring exactly tau is a candidate: if none is left out, S = {s >= tau}
       if (!(js + 1 < nc && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
-      count_s = (int)rs.cabove + js + 1;
+      count_s = (int)cabove_s + js + 1;
     }
-    for (int rk = tid; rk <= js; rk += kThreads) {
-      const uint32_t n = (uint32_t)(cand_s[order_s[rk]] & 0xFFFFFFFFull);
-      atomicAdd(&cmem_s[min(n / (uint32_t)kChunk, (uint32_t)(g.U - 1))], 1u);
-    }
-    __syncthreads();
-    // first output slot of this unit: members of the units before it
-    uint32_t ol = 0u;
-    for (int u = tid; u < c; u += kThreads) ol += cab_s[u] + cmem_s[u];
-    uint32_t otot;
-    (void)block_exscan<uint32_t>(ol, utmp, otot);
-    if (tid == 0) off_s = otot;
     __syncthreads();
   } else {
     // ---- crowded crossing bin: radix digits of desc_key inside the bin (11 + 11 + 10
@@ -872,20 +765,19 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
     // the digit histograms share the candidate buffer
     unsigned long long* hm2 = cand_s;
     uint32_t* hc2 = reinterpret_cast<uint32_t*>(cand_s + 2048);
-    __shared__ int dig_s, nc_s;
+    __shared__ int dig_s, nr_s;
     __shared__ double ab_s;
     __shared__ uint32_t cb_s, cnt_s;
-    const int jstar = rs.jstar;
-    if (tid == 0) { ab_s = rs.above; cb_s = rs.cabove; cnt_s = rs.bincnt; }
+    if (tid == 0) { ab_s = above_s; cb_s = cabove_s; cnt_s = bincnt_s; }
     __syncthreads();
     uint32_t prefix = 0u;
     int shift = 32;
     while (cnt_s > (uint32_t)kCap && shift > 0) {
       const int nbits = (shift >= 11) ? 11 : shift;
       const int nshift = shift - nbits;
-      for (int i = tid; i < 2048; i += kThreads) { hm2[i] = 0ull; hc2[i] = 0u; }
+      for (int i = tid; i < 2048; i += kFT) { hm2[i] = 0ull; hc2[i] = 0u; }
       __syncthreads();
-      for (int n = tid; n < g.L; n += kThreads) {
+      for (int n = tid; n < g.L; n += kFT) {
         const float v = sb[n];
         if (bin_of(v) != jstar) continue;
         const uint32_t key = desc_key(v);
@@ -921,22 +813,22 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
     if (cnt_s > (uint32_t)kCap) {
       // exact ties: the tied value is the key `prefix`; admit them by ascending position
       const float tv = undesc_key(prefix);
-      const double mt = cmode ? 1.0 : (double)mass38(tv, A);
+      const double mt2 = cmode ? 1.0 : (double)mass38(tv, A);
       const double need = target - ab_s;
-      long long kneed = (mt > 0.0) ? (long long)ceil(need / mt) : (long long)cnt_s;
+      long long kneed = (mt2 > 0.0) ? (long long)ceil(need / mt2) : (long long)cnt_s;
       kneed = max(1ll, min(kneed, (long long)cnt_s));
       __shared__ int runt_s, tiepos_s;
       if (tid == 0) { runt_s = 0; tiepos_s = -1; }
       __syncthreads();
-      for (int base = 0; base < g.L; base += kThreads) {
+      for (int base = 0; base < g.L; base += kFT) {
         const int n = base + tid;
         const uint32_t f = (n < g.L && sb[n] == tv) ? 1u : 0u;
-        uint32_t tt;
-        const uint32_t ex = block_exscan<uint32_t>(f, utmp, tt);
+        uint32_t tt2;
+        const uint32_t ex = fblock_exscan<uint32_t>(f, utmp, tt2);
         const int before = runt_s;
         if (f && (long long)(before + (int)ex + 1) == kneed) tiepos_s = n;
         __syncthreads();
-        if (tid == 0) runt_s = before + (int)tt;
+        if (tid == 0) runt_s = before + (int)tt2;
         __syncthreads();
         if ((long long)runt_s >= kneed) break;
       }
@@ -944,28 +836,28 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
       __syncthreads();
     } else {
       // the remaining range fits: collect it, rank it and walk it
-      if (tid == 0) nc_s = 0;
+      if (tid == 0) nr_s = 0;
       __syncthreads();
-      for (int n = tid; n < g.L; n += kThreads) {
+      for (int n = tid; n < g.L; n += kFT) {
         const float v = sb[n];
         if (bin_of(v) != jstar) continue;
         if (shift < 32 && (desc_key(v) >> shift) != prefix) continue;
-        const int sl = atomicAdd(&nc_s, 1);
+        const int sl = atomicAdd(&nr_s, 1);
         if (sl < kCap) cand_s[sl] = ((unsigned long long)desc_key(v) << 32) | (uint32_t)n;
       }
       __syncthreads();
-      const int nc = min(nc_s, kCap);
-      for (int i = tid; i < nc; i += kThreads) {
+      const int nr = min(nr_s, kCap);
+      for (int i = tid; i < nr; i += kFT) {
         const unsigned long long ki = cand_s[i];
         int rank = 0;
-        for (int j = 0; j < nc; ++j) rank += (cand_s[j] < ki) ? 1 : 0;
+        for (int j = 0; j < nr; ++j) rank += (cand_s[j] < ki) ? 1 : 0;
         order_s[rank] = (short)i;
       }
       __syncthreads();
       if (tid == 0) {
         double cm = ab_s;
-        int js = max(nc - 1, 0);
-        for (int i = 0; i < nc; ++i) {
+        int js = max(nr - 1, 0);
+        for (int i = 0; i < nr; ++i) {
           const float v = undesc_key((uint32_t)(cand_s[order_s[i]] >> 32));
           const double mi = cmode ? 1.0 : (double)mass38(v, A);
           if (cm + mi >= target) { js = i; break; }
@@ -974,49 +866,54 @@ __global__ __launch_bounds__(kThreads) void sel_dec_emit(ProbDev p, const int32_
         const unsigned long long kv = cand_s[order_s[js]];
         tau_s = undesc_key((uint32_t)(kv >> 32));
         tie_s = (int)(uint32_t)(kv & 0xFFFFFFFFull);
-        if (!(js + 1 < nc && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
+        if (!(js + 1 < nr && (uint32_t)(cand_s[order_s[js + 1]] >> 32) == (uint32_t)(kv >> 32))) tie_s = 0x7FFFFFFF;
         count_s = (int)cb_s + js + 1;
       }
       __syncthreads();
     }
-    // first output slot of this unit: members among the keys before it
-    const float tv = tau_s;
-    const int tp = tie_s;
-    uint32_t ol = 0u;
-    for (int n = tid; n < c * kChunk && n < g.L; n += kThreads) ol += is_member(sb[n], n, tv, tp) ? 1u : 0u;
-    uint32_t otot;
-    (void)block_exscan<uint32_t>(ol, utmp, otot);
-    if (tid == 0) off_s = otot;
-    __syncthreads();
   }
+
+  // ---- the members, ascending: per chunk, a ballot per (step, wave) of 64 positions,
+  // the ballot counts scanned in position order, then the writes
   const float tau = tau_s;
   const int tie = tie_s;
-  if (c == 0 && tid == 0) {
-    const size_t ro = (size_t)g.r * p.Tq + g.qrow;
+  if (tid == 0) {
     sel.count[ro] = count_s;
     if (sel.tau) sel.tau[ro] = tau;
     if (sel.tie_pos) sel.tie_pos[ro] = tie;
   }
-
-  // ---- this unit's members, ascending
-  auto member_mask = [&](int j) {
-    const int n = nw + j * 64 + lane;
-    return __builtin_amdgcn_ballot_w64(n < g.L && is_member(sv[j], n, tau, tie));
-  };
-  uint32_t wc = 0u;
-#pragma unroll
-  for (int j = 0; j < kSeg; ++j) wc += (uint32_t)__popcll(member_mask(j));
-  if (lane == 0) wcnt_s[wid] = wc;
-  __syncthreads();
-  uint32_t o = off_s;
-  for (int w2 = 0; w2 < wid; ++w2) o += wcnt_s[w2];
   const unsigned long long below = (1ull << lane) - 1ull;
+  uint32_t run = 0u;   // members of the chunks before
+  for (int ch = 0; ch < nchunks; ++ch) {
+    if (ch > 0) load_chunk(ch);
+    // the wave's members: one bit per step in a lane register, and their count
+    uint32_t bits = 0u, wc = 0u;
 #pragma unroll
-  for (int j = 0; j < kSeg; ++j) {
-    const unsigned long long mk = member_mask(j);
-    const uint32_t at = o + (uint32_t)__popcll(mk & below);
-    if (((mk >> lane) & 1ull) && at < (uint32_t)g.L) out[at] = nw + j * 64 + lane;
-    o += (uint32_t)__popcll(mk);
+    for (int i = 0; i < kFS; ++i) {
+      const int n = pos_of(ch, i);
+      const bool m = n < g.L && is_member(sv[i], n, tau, tie);
+      bits |= m ? (1u << i) : 0u;
+      wc += (uint32_t)__popcll(__builtin_amdgcn_ballot_w64(m));
+    }
+    if (lane == 0) utmp[wid] = wc;
+    __syncthreads();
+    uint32_t o = run, ctot = 0u;
+    for (int w2 = 0; w2 < kFW; ++w2) {
+      const uint32_t c = utmp[w2];
+      if (w2 < wid) o += c;
+      ctot += c;
+    }
+#pragma unroll
+    for (int i = 0; i < kFS; ++i) {
+      const unsigned long long mk = __builtin_amdgcn_ballot_w64((bits >> i) & 1u);
+      if ((bits >> i) & 1u) {
+        const uint32_t at = o + (uint32_t)__popcll(mk & below);
+        if (at < (uint32_t)g.L) out[at] = pos_of(ch, i);
+      }
+      o += (uint32_t)__popcll(mk);
+    }
+    run += ctot;
+    __syncthreads();
   }
 }
 
@@ -1182,8 +1079,7 @@ hipError_t launch_select_decode(const ProbDev& p, bool bf16, const void* q_pre, 
   else
     hipLaunchKernelGGL(sel_dec_score<float>, grid, dim3(kThreads), 0, s, p, (const float*)q_pre, w_q,
                        (const float*)k_idx, sel, w);
-  hipLaunchKernelGGL(sel_dec_collect, grid, dim3(kThreads), 0, s, p, top_p, top_k, sel, w);
-  hipLaunchKernelGGL(sel_dec_emit, grid, dim3(kThreads), 0, s, p, top_k, sel, w);
+  hipLaunchKernelGGL(sel_dec_finish, dim3(p.R * p.batch), dim3(kFT), 0, s, p, top_p, top_k, sel, w);
   return hipGetLastError();
 }
 
