@@ -592,6 +592,21 @@ def main():
                                    "per_kernel_ms": pk["per_kernel_ms"],
                                    "mean_selected_fraction": pk["mean_frac_selected"]}
             del pk
+            # clustered selections: the same step with every row's highest index scores in the
+            # first 32 64-key blocks (a shared prefix) and k = 2048, so that rows past 8K keys keep
+            # under a quarter of their prefix in 32 tiles (the sparse attention path skips the rest)
+            say("prefill 128K, clustered top-k 2048 ...")
+            import dataclasses
+            cinp = dataclasses.replace(pre["inp"], q_pre=pre["inp"].q_pre.clone(), k_pre=pre["inp"].k_pre.clone())
+            synth.gen.plant_blocks(cinp, blocks=list(range(32)))
+            kt = torch.full((pre["cfg"].batch,), 2048, dtype=torch.int32, device="cuda")
+            pc = bench_prefill(args, torch, rtp, synth, inp=cinp, top_k=kt)
+            var["prefill_128k_clustered_k2048"] = {
+                "ms_per_step": pc["ms"], "tokens_per_s": pc["tokens"] / (pc["ms"] * 1e-3),
+                "per_kernel_ms": pc["per_kernel_ms"], "mean_selected_fraction": pc["mean_frac_selected"],
+                "sparse_attn_tflops_on_selected_pairs": pc["flops"]["sparse_attn_prefill"]
+                / (pc["per_kernel_ms"]["sparse_attn_prefill"] * 1e-3) / 1e12}
+            del pc, cinp
         if dec is not None:
             say("decode 32K x 8, top-k 4096 ...")
             kt = torch.full((synth.DECODE_32K.batch,), 4096, dtype=torch.int32, device="cuda")

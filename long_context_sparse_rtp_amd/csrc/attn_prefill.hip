@@ -245,6 +245,10 @@ __device__ __forceinline__ Work work_of(int bid, int nheads, int batch, int tile
 }
 __host__ __device__ inline bool per_head_xcd(int mode, int nheads) { return mode == 0 && nheads <= 8 && 8 % nheads == 0; }
 
+// MODE 0: retrieval heads, masked-dense tiles; MODE 2: retrieval heads whose rows
+// keep under a quarter of their prefix, membership tested before the products so
+// that tiles without a selected pair are skipped; MODE 1: local heads.  Modes 0
+// and 2 run on the same grid and every workgroup is taken by exactly one of them.
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     ProbDev p, int nheads, int tiles_per_b, const T* __restrict__ q, const T* __restrict__ k,
@@ -252,22 +256,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     float* __restrict__ lse) {
   typedef typename Frag32<T>::type F;
   typedef typename IdxFrag<T>::type IF;
+  constexpr bool kRet = MODE != 1;   // retrieval heads
   constexpr int KS = Lds<T>::kStr, VS = Lds<T>::vStr;
   __shared__ __attribute__((aligned(16))) T k_s[2][KT * KS];
   __shared__ __attribute__((aligned(16))) T vt_s[2][kHeadDim * VS];
   // retrieval heads: the tile's 16-dim index keys, staged with K/V (one tile ahead)
-  constexpr int KXW = (MODE == 0) ? KT * kIdxDim * (int)sizeof(T) / 4 / kThreads : 0;   // words per thread
+  constexpr int KXW = kRet ? KT * kIdxDim * (int)sizeof(T) / 4 / kThreads : 0;   // words per thread
   // rows of 16-bit index keys padded to 10 words, so the 16 rows a fragment read
   // touches fall in distinct banks
   constexpr int KXWK = kIdxDim * (int)sizeof(T) / 4;                     // words per key
   constexpr int KXS = (sizeof(T) == 2) ? KXWK + 2 : KXWK;                 // row stride in words
-  __shared__ __attribute__((aligned(16))) uint32_t kx_s[2][(MODE == 0) ? KT * KXS : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t kx_s[2][kRet ? KT * KXS : 1];
   uint32_t kxr[KXW > 0 ? KXW : 1];
 
-  const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b, per_head_xcd(MODE, nheads));
+  const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b, per_head_xcd(kRet ? 0 : 1, nheads));
   if (!wk.ok) return;
   const int b = wk.b, hidx = wk.hidx;
-  const int h = (MODE == 0) ? p.ret_heads[hidx] : p.local_heads[hidx];
+  const int h = kRet ? p.ret_heads[hidx] : p.local_heads[hidx];
   const int g = kv_of(p, h);
   const int q0 = p.cu_q[b], Lq = p.cu_q[b + 1] - q0;
   const int k0 = key_row0(p, b), Lk = p.cu_k[b + 1] - p.cu_k[b];
@@ -289,9 +294,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     qi[c] = i0 + RW * w + 16 * c + col;
     qok[c] = qi[c] < Lq;
     qpos[c] = off + (qok[c] ? qi[c] : (Lq - 1));
-    const T* qp = q + ((size_t)(q0 + (qok[c] ? qi[c] : Lq - 1)) * p.Hq + h) * kHeadDim + 8 * grp;
-#pragma unroll
-    for (int kc = 0; kc < 4; ++kc) load_frag(qf[c][kc], qp + 32 * kc);
   }
   const int wpos_lo = off + min(i0 + RW * w, Lq - 1);
   const int wpos_hi = off + min(i0 + RW * w + RW - 1, Lq - 1);
@@ -303,7 +305,50 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
   bool exact_ties = false;
   bool all_keys = false;
   const T* kxb = nullptr;
-  if (MODE == 0) {
+  const int wt_last = wpos_hi / KT;
+  // does any row of this wave select a pair in key tile t? (wave-uniform)  Below the
+  // wave's lowest row and without exact ties a tile is needed iff its largest dot product
+  // reaches some row's threshold; on the diagonal or with ties each pair is tested.
+  auto load_tile = [&](IF (&dst)[4], int t) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int key = min(t * KT + 16 * ks + col, Lk - 1);
+      load_idx_frag(dst[ks], kxb + (size_t)key * kIdxDim + 4 * grp);
+    }
+  };
+  auto tile_hit = [&](const IF (&src)[4], int t) -> bool {
+    if (t > wt_last) return false;
+    bool hit = false;
+    if (!exact_ties && t * KT + KT - 1 <= wpos_lo) {
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const f32x4 dx = idx_dot_tile(src[ks], qxf[c]);
+          mx = fmaxf(mx, fmaxf(fmaxf(dx[0], dx[1]), fmaxf(dx[2], dx[3])));
+        }
+        hit |= mx >= tau4[c];
+      }
+    } else {
+      const int kb4 = t * KT + 4 * grp;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const f32x4 dx = idx_dot_tile(src[ks], qxf[c]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kb4 + 16 * ks + i;
+            const bool ok = (dx[i] > tau4[c]) | ((dx[i] == tau4[c]) & (key <= tie[c]));
+            hit |= ok & (key <= qpos[c]);
+          }
+        }
+    }
+    return __builtin_amdgcn_ballot_w64(hit) != 0ull;
+  };
+  if (kRet) {
+    bool dense_row = false;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const size_t qr = (size_t)hidx * p.Tq + q0 + (qok[c] ? qi[c] : Lq - 1);
@@ -311,15 +356,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
       tau4[c] = sel.tau[qr] * 4.f;   // compare raw dot products: dot / 4 vs tau is exact
       tie[c] = sel.tie_pos[qr];
       exact_ties |= (tie[c] != 0x7FFFFFFF);
+      dense_row |= 4ll * sel.count[qr] >= (long long)qpos[c] + 1;   // keeps a quarter of its prefix or more
     }
+    // the workgroup goes to MODE 2 when every row keeps under a quarter of its prefix and
+    // the sampled tile union below is sparse (bfloat16 only; float32 is masked-dense)
+    __shared__ int wg_dense_s;
+    if (tid == 0) wg_dense_s = 0;
+    __syncthreads();
+    if (__builtin_amdgcn_ballot_w64(dense_row) != 0 && lane == 0) atomicOr(&wg_dense_s, 1);
+    __syncthreads();
+    // (and the workgroup's causal range fits the tile list: keys up to 1M)
+    const int wg_tiles = (off + min(i0 + BQ, Lq) - 1) / KT + 1;
+    const bool wg_sparse = (sizeof(T) == 2) && wg_dense_s == 0 && wg_tiles <= (1 << 14);
+    if (MODE == 2 && !wg_sparse) return;
     exact_ties = __builtin_amdgcn_ballot_w64(exact_ties) != 0;
     kxb = k_idx + ((size_t)hidx * p.Tk + k0) * kIdxDim;
+    if (wg_sparse) {
+      // the tiles' union may still be dense (selections spread over the prefix): 16 tiles
+      // spread over the causal range, their index keys loaded at once, decide; more than
+      // half of them needed keeps the workgroup on the masked-dense path
+      __shared__ uint32_t samp_s;
+      if (tid == 0) samp_s = 0u;
+      __syncthreads();
+      constexpr int kSamp = 16;
+      const int ns = min(kSamp, wg_tiles);
+      IF kf[kSamp][4];
+#pragma unroll
+      for (int j = 0; j < kSamp; ++j) load_tile(kf[j], (min(j, ns - 1) * wg_tiles) / ns);
+#pragma unroll
+      for (int j = 0; j < kSamp; ++j)
+        if (j < ns && tile_hit(kf[j], (j * wg_tiles) / ns) && lane == 0) atomicOr(&samp_s, 1u << j);
+      __syncthreads();
+      const bool union_dense = 2 * __popc(samp_s) > ns;
+      if (MODE == 0 && !union_dense) return;
+      if (MODE == 2 && union_dense) return;
+    }
     // every row of this wave keeps its whole causal prefix (p >= 1, tau = -inf):
     // dense causal attention, no indexer work
     bool rows_all = true;
 #pragma unroll
     for (int c = 0; c < NC; ++c) rows_all &= (tau4[c] == -INFINITY);
     all_keys = __builtin_amdgcn_ballot_w64(!rows_all) == 0;
+  }
+  // (query fragments are loaded once the workgroup is known to run here)
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const T* qp = q + ((size_t)(q0 + (qok[c] ? qi[c] : Lq - 1)) * p.Hq + h) * kHeadDim + 8 * grp;
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) load_frag(qf[c][kc], qp + 32 * kc);
   }
 
   const float sl2 = 0.08838834764831845f * kLog2e;  // log2(e) / sqrt(128)
@@ -348,12 +432,75 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     kt_first = max(0, pos_lo - p.window + 1) / KT;
     sink_tile = (p.n_sink > 0) && (kt_first > 0);
   }
-  const int ntiles = kt_last - kt_first + 1 + (sink_tile ? 1 : 0);
-  auto tile_of = [&](int t) { return (sink_tile && t == 0) ? 0 : (kt_first + t - (sink_tile ? 1 : 0)); };
+  int ntiles = kt_last - kt_first + 1 + (sink_tile ? 1 : 0);
+  // MODE 2: the key tiles that hold a selected pair for some row of the workgroup,
+  // found from the index keys alone (32 bytes a key) before any K/V is staged
+  constexpr int kMaxTiles2 = (MODE == 2) ? (1 << 14) : 1;   // keys up to 1M
+  __shared__ uint32_t need_s[(kMaxTiles2 + 31) / 32];
+  __shared__ unsigned short list_s[kMaxTiles2];
+  __shared__ uint32_t nscan_s[kThreads / 64];
+  if (MODE == 2) {
+    const int nwords = (ntiles + 31) / 32;
+    for (int e = tid; e < nwords; e += kThreads) need_s[e] = 0u;
+    __syncthreads();
+    // every wave tests its rows against each of its causal tiles, three groups of four
+    // tiles' index keys in flight
+    IF kf[3][4][4];
+    auto load4 = [&](IF (&dst)[4][4], int t0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) load_tile(dst[u], t0 + u);
+    };
+    auto test4 = [&](const IF (&src)[4][4], int t0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (tile_hit(src[u], t0 + u) && lane == 0) atomicOr(&need_s[(t0 + u) >> 5], 1u << ((t0 + u) & 31));
+    };
+    load4(kf[0], 0);
+    load4(kf[1], 4);
+    for (int t0 = 0; t0 <= wt_last; t0 += 12) {
+      load4(kf[2], t0 + 8);
+      test4(kf[0], t0);
+      if (t0 + 4 > wt_last) break;
+      load4(kf[0], t0 + 12);
+      test4(kf[1], t0 + 4);
+      if (t0 + 8 > wt_last) break;
+      load4(kf[1], t0 + 16);
+      test4(kf[2], t0 + 8);
+    }
+    __syncthreads();
+    // the list of needed tiles, ascending: word counts scanned over the workgroup
+    uint32_t word = 0u, cnt = 0u;
+    if (tid < nwords) { word = need_s[tid]; cnt = (uint32_t)__popc(word); }
+    uint32_t inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(inc, d);
+      if (lane >= d) inc += y;
+    }
+    if (lane == 63) nscan_s[w] = inc;
+    __syncthreads();
+    uint32_t base = 0u, total = 0u;
+    for (int w2 = 0; w2 < kThreads / 64; ++w2) {
+      if (w2 < w) base += nscan_s[w2];
+      total += nscan_s[w2];
+    }
+    uint32_t o = base + inc - cnt;
+    while (word) {
+      const int b = __ffs(word) - 1;
+      list_s[o++] = (unsigned short)(32 * tid + b);
+      word &= word - 1u;
+    }
+    ntiles = (int)total;
+    __syncthreads();
+  }
+  auto tile_of = [&](int t) {
+    if (MODE == 2) return (int)list_s[t];
+    return (sink_tile && t == 0) ? 0 : (kt_first + t - (sink_tile ? 1 : 0));
+  };
 
   // index keys of a tile as 4-byte words (keys past the sequence read as 0)
   auto kx_load = [&](int kb0) {
-    if (MODE != 0) return;
+    if (!kRet) return;
     const uint32_t* src = reinterpret_cast<const uint32_t*>(kxb + (size_t)kb0 * kIdxDim);
     constexpr int kWordsPerKey = kIdxDim * (int)sizeof(T) / 4;
 #pragma unroll
@@ -363,7 +510,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     }
   };
   auto kx_store = [&](int b2) {
-    if (MODE != 0) return;
+    if (!kRet) return;
 #pragma unroll
     for (int w = 0; w < KXW; ++w) {
       const int e = w * kThreads + tid;
@@ -372,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
   };
 
   Stage<T> st;
-  {
+  if (ntiles > 0) {   // (MODE 2 could in principle find no tile: then the rows keep l = 0)
     const int fb = tile_of(0) * KT;
     st.load(kg + (size_t)fb * rstride, vg + (size_t)fb * rstride, rstride, min(KT, Lk - fb), tid);
     kx_load(fb);
@@ -402,13 +549,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
         need_mask |= (wpos_hi - kbase) >= p.window;                                // window edge inside
       }
     }
-    if (!skip) {
-      IF kxf[4];
-      if (MODE == 0 && !all_keys) {
-        const T* kxt = reinterpret_cast<const T*>(kx_s[buf]);
+    IF kxf[4];
+    if (!skip && kRet && !all_keys) {
+      const T* kxt = reinterpret_cast<const T*>(kx_s[buf]);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) load_idx_frag(kxf[ks], kxt + (16 * ks + col) * (KXS * 4 / (int)sizeof(T)) + 4 * grp);
-      }
+      for (int ks = 0; ks < 4; ++ks) load_idx_frag(kxf[ks], kxt + (16 * ks + col) * (KXS * 4 / (int)sizeof(T)) + 4 * grp);
+    }
+    if (!skip) {
       __builtin_amdgcn_s_setprio(0);   // matrix-core phase: waves in their ALU phase issue first
       // S^T = K Q^T
       f32x4 sacc[NC][4];
@@ -440,7 +587,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
         relq[c] = opaque_int(qpos[c] - kb4);   // key <= qpos  <=>  16 ks + i <= relq
         relt[c] = opaque_int(tie[c] - kb4);    // key <= tie   <=>  16 ks + i <= relt
       }
-      if (MODE == 0) {
+      if (kRet) {
         auto apply = [&](auto exact_t, auto mask_t) {
           constexpr bool kExact = decltype(exact_t)::value;
           constexpr bool kMask = decltype(mask_t)::value;
@@ -592,7 +739,12 @@ hipError_t launch_attn_prefill(const ProbDev& p, bool bf16, int mode, const void
   hipLaunchKernelGGL((attn_prefill_kernel<TT, MM>), grid, dim3(kThreads), 0, s, p, nheads, tiles_per_b,       \
                      (const TT*)q, (const TT*)k, (const TT*)v, (const TT*)k_idx, sl, (TT*)out, lse)
   if (bf16) {
-    if (mode == 0) RTP_LAUNCH(bf16_t, 0); else RTP_LAUNCH(bf16_t, 1);
+    if (mode == 0) {
+      RTP_LAUNCH(bf16_t, 0);
+      RTP_LAUNCH(bf16_t, 2);   // the workgroups whose rows are sparse
+    } else {
+      RTP_LAUNCH(bf16_t, 1);
+    }
   } else {
     if (mode == 0) RTP_LAUNCH(float, 0); else RTP_LAUNCH(float, 1);
   }

@@ -302,6 +302,37 @@ def make_inputs(cfg: Config, device="cpu") -> Inputs:
         needle_pos=needle_pos, peaky=peaky)
 
 
+def plant_blocks(inp: Inputs, blocks, seed: int = 11, key_scale: float = 4.0, query_mix: float = 3.0,
+                 jitter: float = 0.25) -> None:
+    """Clustered index scores (in place): every retrieval head's pre-RoPE query gets a
+    shared component along a seeded unit direction u (query_mix times its norm), and
+    the pre-RoPE keys of the listed 64-key blocks, in every KV group that holds a
+    retrieval head, are replaced by key_scale times their norm along u + jitter z / sqrt(d)
+    (z standard normal per key, the sum normalised), so that the planted keys score
+    highest but not alike (jitter 0: every planted key is key_scale sqrt(d) u, so they
+    tie exactly).  Every row's highest indexer scores then sit in those blocks,
+    as in selections that gather in a few contiguous spans.  The post-RoPE q and k
+    (attention) are left unchanged."""
+    cfg = inp.cfg
+    g = _gen("cpu", seed, _TAG["topic"], 1)
+    d = cfg.head_dim
+    u = torch.randn(d, generator=g, dtype=torch.float64)
+    u = u / torch.linalg.vector_norm(u)
+    dt = inp.q_pre.dtype
+    qp = inp.q_pre.to(torch.float64)
+    qn = torch.linalg.vector_norm(qp, dim=-1, keepdim=True)
+    inp.q_pre.copy_((qp + query_mix * qn * u.to(qp.device)).to(dt))
+    rows = torch.cat([torch.arange(64 * b, 64 * b + 64) for b in blocks])
+    for gk in sorted({cfg.kv_of(h) for h in cfg.ret_heads}):
+        dirs = u + jitter * torch.randn(len(rows), d, generator=g, dtype=torch.float64) / math.sqrt(d)
+        dirs = dirs / torch.linalg.vector_norm(dirs, dim=-1, keepdim=True)
+        r = rows.to(inp.k_pre.device)
+        kn = torch.linalg.vector_norm(inp.k_pre[r, gk].to(torch.float64), dim=-1, keepdim=True)
+        if jitter == 0.0:
+            kn = torch.full_like(kn, math.sqrt(d))     # identical keys: exact ties
+        inp.k_pre[r, gk] = (key_scale * kn * dirs.to(kn.device)).to(dt)
+
+
 def sample_rows(cfg: Config, n: int, extra: Optional[list] = None) -> List[int]:
     """Seeded uniform query rows in [0, L) plus forced edge rows (prefill)."""
     g = _gen("cpu", cfg.seed, 77, 0)

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 from synth import DECODE_32K, PREFILL_128K, TINY_PREFILL, make_inputs, sample_rows, scaled
+from synth.gen import plant_blocks
 from synth.configs import forced_edge_rows
 from oracle.problem import from_inputs
 
@@ -136,3 +137,29 @@ def test_topk_decode_exact_ties_all_equal():
     n, fails, stats = P.check_rows(pr, g, [(b, 0) for b in range(cfg.batch)], list(range(cfg.n_q_heads)),
                                    P.TOL[cfg.dtype], decode=True)
     assert not fails, fails[:5]
+
+
+@pytest.mark.parametrize("kind", ["topk", "topp", "topk_ties"])
+def test_clustered_selection_skips_tiles(kind):
+    # selections that sit in a few 64-key blocks: the sparse attention path finds the
+    # tiles that hold a selected pair from the index keys and skips every other tile.
+    # "topk_ties" plants collinear keys (no jitter), so the index scores tie exactly in
+    # bfloat16 and the threshold's tie position decides membership.
+    cfg = scaled(PREFILL_128K, name=f"clustered_{kind}", seqlen=9000, window=256, needles="none",
+                 top_p=0.5)
+    _say(f"[case] {cfg.name}")
+    inp = make_inputs(cfg, DEV)
+    plant_blocks(inp, blocks=(3, 20, 21, 77, 120), jitter=0.0 if kind == "topk_ties" else 0.25)
+    top_k = None if kind == "topp" else [192]
+    g = P.to_host(P.run_prefill(inp, top_k=top_k))
+    pr = from_inputs(inp)
+    if top_k is not None:
+        pr.top_k = top_k
+    rows = [(0, i) for i in sample_rows(cfg, 48, [0, 191, 192, 767, 768, 1343, 1344, 1345, 4999, 8999])]
+    n, fails, stats = P.check_rows(pr, g, rows, list(range(cfg.n_q_heads)), P.TOL[cfg.dtype])
+    ties = int((g["tie"] != 0x7FFFFFFF).sum())
+    _say(f"[result] {cfg.name}: {n} pairs, {len(fails)} failures, {stats}, mean count "
+         f"{float(g['count'].mean()):.1f}, rows with a tie position {ties}")
+    assert not fails, fails[:5]
+    if kind == "topk_ties":
+        assert ties > 0
