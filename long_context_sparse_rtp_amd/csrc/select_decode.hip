@@ -12,33 +12,31 @@
 // Robustness Checks") the same kernels walk token counts instead of masses:
 // the histogram already carries both.
 //
-// A row (retrieval slot, sequence) is cut into units of 4096 keys and every
-// kernel runs one workgroup per unit, so the whole device works on each step.
-// Workgroups never wait on each other inside a kernel (no device-wide fences
-// or tickets); the three kernel boundaries are the only synchronisation.
+// A row (retrieval slot, sequence) is cut into units of 4096 keys.  Two kernels,
+// whose boundary is the only synchronisation between workgroups (no device-wide
+// fences or tickets):
 //
-//  1. score: project the query (float64, fixed order, rounded once), score the
-//     unit's keys (fixed-order float32 FMA chain), store the scores, and
-//     histogram the unit's mass over 4096 bins of 1/128 octave.  Bins sit on
-//     an absolute grid a(s) = floor(s * 128 * log2(e)); a unit's bin
+//  1. score, one workgroup per unit: project the query (float64, fixed order,
+//     rounded once), score the unit's keys (fixed-order float32 FMA chain), store
+//     the scores, and histogram the unit's mass over 4096 bins of 1/128 octave.
+//     Bins sit on an absolute grid a(s) = floor(s * 128 * log2(e)); a unit's bin
 //     j = A_u - a(s) counts down from the bin A_u of its own maximum, and a
-//     token's mass is 38-bit fixed point of 2^(s log2 e - (A_u + 1) / 128).
-//     Mass and count share one 64-bit LDS integer per bin (count << 51), so
-//     one atomic per token keeps the sums exact and order-independent.  The
-//     fine bins are stored, and so are coarse bins of 16 absolute bins each.
-//  2. collect: every unit finds the row's crossing bin from the units'
-//     histograms (unit u's sums scaled by 2^((A_u - A) / 128) in float64, in
-//     a fixed order, so all workgroups of the row reach bit-identical sums):
-//     first the coarse bin where the cumulative mass reaches p * Z, then the
-//     fine bin inside it.  It then counts its own tokens above that bin and
-//     stores its tokens inside the bin as candidates.
-//  3. emit: every unit ranks the row's candidates by (score desc, position
-//     asc), walks their masses to the crossing token (tau, tie_pos, count),
-//     derives its first output slot from the per-unit counts and writes its
-//     members in ascending order.  A crossing bin too crowded for the
-//     candidate lists (mass piled on near-identical scores) is resolved from
-//     the row's stored scores, with radix digits of the score's bit pattern
-//     and then positions.
+//     token's mass is 38-bit fixed point of 2^(s log2 e - (A_u + 1) / 128).  Mass
+//     and count share one 64-bit LDS integer per bin (count << 51), so one atomic
+//     per token keeps the sums exact and order-independent.  The fine bins are
+//     stored, and so are coarse bins of 16 absolute bins each.
+//  2. finish, one workgroup per row: the crossing bin from the units' histograms
+//     (unit u's sums scaled by 2^((A_u - A) / 128) in float64, in a fixed order),
+//     first the coarse bin where the cumulative mass reaches p * Z, then the fine
+//     bin inside it; the bin's tokens from the row's stored scores, ranked by
+//     (score desc, position asc) and walked to the crossing token (tau, tie_pos,
+//     count); then the members written in ascending order.  A crossing bin too
+//     crowded for the candidate buffer (mass piled on near-identical scores) is
+//     resolved from the stored scores with radix digits of the score's bit
+//     pattern and then positions.
+// The finish is bound by the latency of its dependent steps on one compute unit
+// (statistics, coarse and fine bins, candidates, ranks, the members' stores), not
+// by bandwidth: a row's 128 KB of scores stream through that one unit.
 #include "common.h"
 #include "kernels.h"
 
@@ -551,24 +549,50 @@ __global__ __launch_bounds__(kFT) void sel_dec_finish(ProbDev p, const float* __
   __shared__ uint32_t cab_c_s, cbin_c_s, cabove_s, bincnt_s;
   __shared__ float tau_s;
 
-  // ---- reference bin A and per-unit scales 2^((A_u - A) / 128)
-  if (tid < g.U) {
-    A_s[tid] = mt.A;
-    used_s[tid] = mt.used;
-    cused_s[tid] = mt.cused;
-  }
-  const int A = fblock_max((tid < g.U && mt.used >= 0) ? mt.A : (-2147483647 - 1), itmp);
-  const int Ap = A | 15;
-  double zl = 0.0;
-  if (tid < g.U) {
-    const double f = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
-    f_s[tid] = f;
-    zl = (double)mt.Z * f;
-  }
+  // ---- reference bin A and per-unit scales 2^((A_u - A) / 128); up to 64 units in one
+  // wave (shuffle reductions, no block barriers), more with block reductions
+  int A;
   double Z;
-  (void)fblock_exscan<double>(zl, dtmp, Z);   // its barriers also publish A_s, used_s, f_s
+  if (g.U <= 64) {
+    __shared__ int a_sh;
+    __shared__ double z_sh;
+    if (wid == 0) {
+      const bool has = lane < g.U && mt.used >= 0;
+      int a = has ? mt.A : (-2147483647 - 1);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) a = max(a, __shfl_xor(a, o));
+      const double f = has ? unit_scale(mt.A, a) : 0.0;
+      double z = (lane < g.U) ? (double)mt.Z * f : 0.0;
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);   // lane 0's order is the one used
+      if (lane < g.U) {
+        A_s[lane] = mt.A;
+        used_s[lane] = mt.used;
+        cused_s[lane] = mt.cused;
+        f_s[lane] = f;
+      }
+      if (lane == 0) { a_sh = a; z_sh = z; }
+    }
+    __syncthreads();
+    A = a_sh;
+    Z = z_sh;
+  } else {
+    if (tid < g.U) {
+      A_s[tid] = mt.A;
+      used_s[tid] = mt.used;
+      cused_s[tid] = mt.cused;
+    }
+    A = fblock_max((tid < g.U && mt.used >= 0) ? mt.A : (-2147483647 - 1), itmp);
+    double zl = 0.0;
+    if (tid < g.U) {
+      const double f = (mt.used >= 0) ? unit_scale(mt.A, A) : 0.0;
+      f_s[tid] = f;
+      zl = (double)mt.Z * f;
+    }
+    (void)fblock_exscan<double>(zl, dtmp, Z);   // its barriers also publish A_s, used_s, f_s
+  }
+  const int Ap = A | 15;
   const double target = cmode ? (double)kk : fmax((double)pp * Z, 1.0);
-
   // ---- coarse row bins: thread (q, cb) sums units q, q + 4, ... of coarse row bin cb
   {
     const int cb = tid & (kRowCoarse - 1), q = tid >> 8;
