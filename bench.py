@@ -37,7 +37,7 @@ EXP_PEAK_TEXPS = 256 * 4 * 16 * 2.4e9 / 2 / 1e12
 KERNELS = {
     "select_topp": ("rtp::select_prefill_kernel", "long_context_sparse_rtp_amd/csrc/select_prefill.hip",
                     "profiles/select_prefill_128k_traffic.txt"),
-    "sparse_attn_prefill": ("rtp::attn_prefill_kernel<MODE 0>", "long_context_sparse_rtp_amd/csrc/attn_prefill.hip",
+    "sparse_attn_prefill": ("rtp::attn_prefill_kernel<MODE 0> + <MODE 2>", "long_context_sparse_rtp_amd/csrc/attn_prefill.hip",
                             "profiles/attn_prefill_ret_128k_traffic.txt"),
     "local_attn": ("rtp::attn_prefill_kernel<MODE 1>", "long_context_sparse_rtp_amd/csrc/attn_prefill.hip",
                    "profiles/attn_prefill_local_128k_traffic.txt"),
@@ -52,6 +52,62 @@ KERNELS = {
     "local_attn_decode": ("rtp::group_decode<false> + combine", "long_context_sparse_rtp_amd/csrc/attn_decode.hip",
                           "profiles/attn_decode_local_32k_traffic.txt"),
 }
+
+# the kernels each timed call launches, as substrings of their names in a rocprofv3 trace
+# (a call's counters and durations sum over its kernels)
+CALL_KERNELS = {
+    "select_topp": ["select_prefill_kernel<unsigned short, false>"],
+    "sparse_attn_prefill": ["attn_prefill_kernel<unsigned short, 0>", "attn_prefill_kernel<unsigned short, 2>"],
+    "local_attn": ["attn_prefill_kernel<unsigned short, 1>"],
+    "index_keys": ["index_keys_kernel<unsigned short>"],
+    "select_decode": ["sel_dec_score<unsigned short>", "sel_dec_finish"],
+    "sparse_attn_decode": ["attn_decode_kernel<unsigned short, 0>", "attn_decode_combine<unsigned short, 0>"],
+    "local_attn_decode": ["group_decode<false>", "group_decode_combine<false>"],
+}
+# the workload pass each call's counters come from
+CALL_PASS = {"select_topp": "pre", "sparse_attn_prefill": "pre", "local_attn": "pre", "index_keys": "pre",
+             "select_decode": "dec", "sparse_attn_decode": "dec", "local_attn_decode": "dec"}
+# the rocprofv3 passes behind the summaries under profiles/ (run from the repo root after
+# cd /tmp && export TMPDIR=/tmp; one counter set per pass)
+_PRE_ARGS = "--only prefill --steps 1 --warmup 0 --no-cpu-baseline --no-references --no-variants --no-long"
+_DEC_ARGS = ("--only decode --steps 1 --warmup 0 --decode-steps 2 --no-cpu-baseline --no-references --no-variants "
+             "--no-ragged --no-cold")
+_MFMA_COUNTERS = ("SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
+                  "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
+PMC_PASSES = {
+    "cal_fetch": ("FETCH_SIZE", "--calibrate-copy"),
+    "cal_write": ("WRITE_SIZE", "--calibrate-copy"),
+    "pre_fetch": ("FETCH_SIZE", _PRE_ARGS),
+    "pre_write": ("WRITE_SIZE", _PRE_ARGS),
+    "dec_fetch": ("FETCH_SIZE", _DEC_ARGS),
+    "dec_write": ("WRITE_SIZE", _DEC_ARGS),
+    "pre_mfma": (_MFMA_COUNTERS, _PRE_ARGS),
+}
+# what the algorithmic bytes of each call are (for the summaries' headers)
+ALGO_NOTE = {
+    "select_topp": "q_pre 134.2 MB + k_idx 16.8 MB read once; q_idx, tau, tie_pos, count written",
+    "sparse_attn_prefill": "q rows of 4 heads 134 MB + K,V of 4 KV groups 268 MB + k_idx/q_idx 34 MB read once; "
+                           "out 134 MB written (each 256-row query block re-reads the causal K/V prefix, from L2 "
+                           "or the Infinity Cache, which FETCH_SIZE also counts)",
+    "local_attn": "q rows of 28 heads 940 MB + the K,V window prefix of 4 KV groups 268 MB read; out 940 MB written",
+    "index_keys": "k_pre of 4 KV groups 134.2 MB read once; k_idx 16.8 MB written",
+    "select_decode": "k_idx of 4 retrieval heads x 8 x 32K 33.5 MB read; scores 4.2 MB written and read back; "
+                     "unit histograms and the lists written",
+    "sparse_attn_decode": "K,V rows of each group's selected union (about 386 MB at top-p 0.95) read once",
+    "local_attn_decode": "K,V rows of the 1028-key window + sinks of 8 sequences x 4 groups, 16.8 MB",
+}
+TRACE_ARGS = ("--steps 3 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-references --no-variants --no-long "
+              "--no-ragged --no-cold")
+
+
+def pmc_command(name):
+    counters, bargs = PMC_PASSES[name]
+    return (f"rocprofv3 --pmc {counters} -d gpurun_out/{name} -o p --output-format csv -- "
+            f"python3 bench.py {bargs}")
+
+
+def trace_command():
+    return f"rocprofv3 --kernel-trace --stats -d gpurun_out/ktrace -o kt --output-format csv -- python3 bench.py {TRACE_ARGS}"
 
 
 def _args():
@@ -70,6 +126,14 @@ def _args():
                     help="summarise a rocprofv3 --pmc output directory for one kernel (no GPU work)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["prefill", "decode", "both"], default="both")
+    ap.add_argument("--pmc-commands", action="store_true",
+                    help="print the rocprofv3 counter passes behind the summaries under profiles/, one per line")
+    ap.add_argument("--traffic-summary", metavar="CALL",
+                    help="print the HBM traffic summary of a timed call from the counter passes under gpurun_out/")
+    ap.add_argument("--mfma-summary", metavar="CALL",
+                    help="print the matrix-core summary of a prefill call from the pre_mfma counter pass")
+    ap.add_argument("--trace-summary", action="store_true",
+                    help="print the kernel table of the rocprofv3 kernel trace under gpurun_out/ktrace")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 4 times (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
@@ -523,6 +587,154 @@ def pmc_summary(d, kernel_substr):
     print(json.dumps({"kernel": kernel_substr, "files": len(files), "counters": out}))
 
 
+def _pmc_rows(d):
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def _pmc_means(d, substrs):
+    """{counter: (sum over the call's kernels of the mean per dispatch, dispatches of each kernel)}"""
+    out = {}
+    for sub in substrs:
+        per = {}
+        for row in _pmc_rows(d):
+            if sub not in row.get("Kernel_Name", ""):
+                continue
+            key = (row["Dispatch_Id"], row["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+        by = {}
+        for (disp, name), v in per.items():
+            by.setdefault(name, []).append(v)
+        for name, vs in by.items():
+            tot, ns = out.get(name, (0.0, []))
+            out[name] = (tot + sum(vs) / len(vs), ns + [len(vs)])
+    return out
+
+
+def _src_sha(call):
+    import hashlib
+    src = KERNELS[call][1]
+    return src, hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()
+
+
+def traffic_summary(call):
+    """HBM bytes per launch of one timed call: FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
+    summed over the call's kernels), each scaled by what the same counter reads per
+    dispatch for a device copy of 1 GiB."""
+    base = os.path.join(ROOT, "gpurun_out")
+    ps = CALL_PASS[call]
+    cal_f = _pmc_means(os.path.join(base, "cal_fetch"), ["copyBuffer"])["FETCH_SIZE"][0]
+    cal_w = _pmc_means(os.path.join(base, "cal_write"), ["copyBuffer"])["WRITE_SIZE"][0]
+    fs = (1 << 30) / (cal_f * 1024.0)
+    wsc = (1 << 30) / (cal_w * 1024.0)
+    f, nf = _pmc_means(os.path.join(base, f"{ps}_fetch"), CALL_KERNELS[call])["FETCH_SIZE"]
+    w, nw = _pmc_means(os.path.join(base, f"{ps}_write"), CALL_KERNELS[call])["WRITE_SIZE"]
+    fb, wb = f * 1024.0 * fs, w * 1024.0 * wsc
+    src, sha = _src_sha(call)
+    lines = [f"# HBM traffic of the {call} call ({' + '.join(CALL_KERNELS[call])}), "
+             f"{'prefill_128k' if ps == 'pre' else 'decode_32k_b8'} workload",
+             "# commands (cd /tmp && export TMPDIR=/tmp; then from the repo root):"]
+    for pn in ("cal_fetch", "cal_write", f"{ps}_fetch", f"{ps}_write"):
+        lines.append("#   " + pmc_command(pn))
+    lines += [f"#   python3 bench.py --traffic-summary {call}",
+              f"# calibration: a 1 GiB device copy reads FETCH_SIZE {cal_f:.0f} KiB and WRITE_SIZE {cal_w:.0f} KiB "
+              "per dispatch",
+              f"# algorithmic: {ALGO_NOTE[call]}",
+              f"fetch_size_kib_per_dispatch: {f:.1f}", f"write_size_kib_per_dispatch: {w:.1f}",
+              f"fetch_scale: {fs:.4f}", f"write_scale: {wsc:.4f}",
+              f"fetch_bytes_per_launch: {fb:.0f}", f"write_bytes_per_launch: {wb:.0f}",
+              f"traffic_bytes_per_launch: {fb + wb:.0f}",
+              f"dispatches_counted: {' + '.join(str(n) for n in nf)}",
+              f"kernel_source: {src}", f"kernel_source_sha256: {sha}"]
+    print("\n".join(lines))
+
+
+def mfma_summary(call):
+    """Matrix-core and instruction counters of a prefill call from the pre_mfma pass.
+    GRBM_GUI_ACTIVE is summed over the 8 XCDs; busy fractions are per SIMD (1024)."""
+    m = _pmc_means(os.path.join(ROOT, "gpurun_out", "pre_mfma"), CALL_KERNELS[call])
+    g = m["GRBM_GUI_ACTIVE"][0]
+    cyc = g / 8.0
+    simd_cycles = cyc * 1024.0
+    src, sha = _src_sha(call)
+    lines = [f"# matrix-core counters of the {call} call ({' + '.join(CALL_KERNELS[call])}), prefill_128k",
+             "# commands (cd /tmp && export TMPDIR=/tmp; then from the repo root):",
+             "#   " + pmc_command("pre_mfma"), f"#   python3 bench.py --mfma-summary {call}",
+             "# GRBM_GUI_ACTIVE sums the 8 XCDs' busy cycles; per-SIMD fractions divide by 1024 SIMDs x cycles"]
+    for k in sorted(m):
+        lines.append(f"{k.lower()}_per_launch: {m[k][0]:.0f}")
+    lines.append(f"kernel_cycles_2p4GHz: {cyc:.0f}")
+    lines.append(f"kernel_ms_from_cycles: {cyc / 2.4e6:.3f}")
+    lines.append(f"mfma_busy_frac: {m['SQ_VALU_MFMA_BUSY_CYCLES'][0] / simd_cycles:.4f}")
+    if "SQ_INSTS_MFMA" in m and "SQ_INSTS_VALU" in m:
+        lines.append(f"valu_insts_per_mfma_inst: {m['SQ_INSTS_VALU'][0] / max(m['SQ_INSTS_MFMA'][0], 1.0):.3f}")
+    if call == "select_topp" and "SQ_INSTS_VALU" in m:
+        # one wave instruction covers a 16-key x 16-row tile of (row, key) pairs (4 per lane)
+        L, R = 131072, 4
+        tiles = R * L * (L + 1) / 2 / 256
+        lines.append(f"causal_pair_tiles_per_launch: {tiles:.0f}")
+        lines.append(f"valu_insts_per_pair_tile_all_sweeps: {m['SQ_INSTS_VALU'][0] / tiles:.2f}")
+        lines.append(f"lds_insts_per_pair_tile_all_sweeps: {m['SQ_INSTS_LDS'][0] / tiles:.2f}")
+    lines.append(f"kernel_source: {src}")
+    lines.append(f"kernel_source_sha256: {sha}")
+    print("\n".join(lines))
+
+
+def trace_summary():
+    """Per-kernel table of the rtp:: kernels in the kernel trace: launches, mean, min and
+    max duration (us), and the resources of the code object."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(ROOT, "gpurun_out", "ktrace", "**", "*kernel_trace.csv"), recursive=True):
+        rows.extend(csv.DictReader(open(f)))
+    agg = {}
+    order = []
+    for r in sorted(rows, key=lambda r: int(r["Start_Timestamp"])):
+        name = r["Kernel_Name"]
+        if "rtp::" not in name:
+            continue
+        short = name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        key = (short, f'{r["Grid_Size_X"]}x{r["Grid_Size_Y"]}', r["Workgroup_Size_X"])
+        if key not in agg:
+            agg[key] = {"d": [], "vgpr": r["VGPR_Count"], "agpr": r["Accum_VGPR_Count"], "lds": r["LDS_Block_Size"],
+                        "scr": r["Scratch_Size"]}
+            order.append(key)
+        agg[key]["d"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"# every rtp:: kernel of the traced run, in order of first launch (durations in us)")
+    print("# commands (cd /tmp && export TMPDIR=/tmp; then from the repo root):")
+    print("#   " + trace_command())
+    print("#   python3 bench.py --trace-summary")
+    print(f"{'kernel':62s} {'grid':>12s} {'wg':>4s} {'calls':>5s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} "
+          f"{'vgpr':>4s} {'agpr':>4s} {'lds':>6s} {'scr':>4s}")
+    for key in order:
+        a = agg[key]
+        d = a["d"]
+        print(f"{key[0][:62]:62s} {key[1]:>12s} {key[2]:>4s} {len(d):5d} {sum(d) / len(d):10.1f} {min(d):10.1f} "
+              f"{max(d):10.1f} {a['vgpr']:>4s} {a['agpr']:>4s} {a['lds']:>6s} {a['scr']:>4s}")
+    # the bench's per-kernel pass runs every call alone on one stream after the timed steps:
+    # the last --steps launches of each prefill kernel and the last --decode-steps of each
+    # decode kernel (the step itself overlaps the local heads on a second stream)
+    ta = TRACE_ARGS.split()
+    n_pre, n_dec = int(ta[ta.index("--steps") + 1]), int(ta[ta.index("--decode-steps") + 1])
+    print()
+    print(f"# the per-kernel pass alone (last {n_pre} launches of each prefill kernel, last {n_dec} of each decode "
+          "kernel); the bench's per-call times are these sums")
+    print(f"{'kernel':62s} {'grid':>12s} {'calls':>5s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}")
+    for key in order:
+        d = agg[key]["d"]
+        dec = any(t in key[0] for t in ("sel_dec", "attn_decode", "group_decode"))
+        n = n_dec if dec else n_pre
+        if len(d) < n:
+            continue
+        d = d[-n:]
+        print(f"{key[0][:62]:62s} {key[1]:>12s} {len(d):5d} {sum(d) / len(d):10.1f} {min(d):10.1f} {max(d):10.1f}")
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -530,6 +742,19 @@ def main():
         sys.exit(2)
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1])
+        return
+    if args.pmc_commands:
+        print("\n".join(pmc_command(n) for n in PMC_PASSES))
+        print(trace_command())
+        return
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary)
+        return
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
+        return
+    if args.trace_summary:
+        trace_summary()
         return
     import torch
     if args.calibrate_copy:
