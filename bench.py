@@ -272,8 +272,11 @@ def bench_prefill(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, steps
                 tokens=L, cfg=cfg, inp=inp, sel=sel)
 
 
-def prefill_rooflines(pre):
-    """Per-kernel roofline objects of a prefill run, and the dominant kernel's name."""
+def prefill_rooflines(pre, counters=True):
+    """Per-kernel roofline objects of a prefill run, and the dominant kernel's name.
+    ``counters``: the run is the workload the committed counter summaries were taken on
+    (prefill_128k); on any other workload their traffic does not apply and is null."""
+    tr = _traffic if counters else (lambda k: None)
     per = pre["per_kernel_ms"]
     roofs = {}
     for k in ("select_topp", "sparse_attn_prefill", "local_attn", "index_keys"):
@@ -283,22 +286,22 @@ def prefill_rooflines(pre):
         if k == "select_topp":   # bound by the exponential unit
             ach = pre["exps_select"] / rt / 1e12
             roofs[k] = {"kernel": KERNELS[k][0], "bound": "alu", "achieved": ach, "peak": EXP_PEAK_TEXPS,
-                        "unit": "Texp/s", "frac": ach / EXP_PEAK_TEXPS, "traffic": _traffic(k)}
+                        "unit": "Texp/s", "frac": ach / EXP_PEAK_TEXPS, "traffic": tr(k)}
         elif k == "index_keys":  # bound by HBM
             ach = pre["bytes_index_keys"] / rt / 1e9
             roofs[k] = {"kernel": KERNELS[k][0], "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": _traffic(k)}
+                        "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": tr(k)}
         else:
             ach = pre["flops"][k] / rt / 1e12
             roofs[k] = {"kernel": KERNELS[k][0], "bound": "mfma", "achieved": ach,
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": ach / MFMA_BF16_PEAK_TFLOPS,
-                        "traffic": _traffic(k)}
+                        "traffic": tr(k)}
     dom = max(("sparse_attn_prefill", "local_attn", "select_topp"), key=lambda k: per[k])
     return roofs, dom
 
 
-def prefill_summary(pre):
-    roofs, dom = prefill_rooflines(pre)
+def prefill_summary(pre, counters=True):
+    roofs, dom = prefill_rooflines(pre, counters)
     per = pre["per_kernel_ms"]
     return {"ms_per_step": pre["ms"], "tokens_per_s": pre["tokens"] / (pre["ms"] * 1e-3),
             "per_kernel_ms": per, "per_kernel_roofline": roofs, "dominant_kernel": dom,
@@ -467,7 +470,7 @@ def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks
                 mean_frac_selected=sum_sel / (cfg.n_ret * sum(lens)), inp=inp, cfg=cfg)
 
 
-def decode_summary(dec):
+def decode_summary(dec, counters=True):
     d = {"step_us": dec["ms"] * 1e3, "per_kernel_us": {k: v * 1e3 for k, v in dec["per_kernel_ms"].items()},
          "single_step_us": {"median": _median(dec["warm_us"]), "min": dec["warm_us"][0]},
          "algorithmic_bytes": dec["total_bytes"], "bytes": dec["bytes"],
@@ -483,9 +486,9 @@ def decode_summary(dec):
     sk = [k for k in per if k.startswith("select")][0]
     d["per_kernel_roofline"] = {
         sk: _hbm_roof("select_decode" if sk in ("select_topp", "select_topk") else sk, dec["bytes"]["index_keys"],
-                      per[sk]),
-        "sparse_attn_decode": _hbm_roof("sparse_attn_decode", None, per["sparse_attn_decode"]),
-        "local_attn": _hbm_roof("local_attn_decode", None, per["local_attn"])}
+                      per[sk], counters),
+        "sparse_attn_decode": _hbm_roof("sparse_attn_decode", None, per["sparse_attn_decode"], counters),
+        "local_attn": _hbm_roof("local_attn_decode", None, per["local_attn"], counters)}
     return d
 
 
@@ -495,11 +498,12 @@ def _median(xs):
     return 0.5 * (xs[(n - 1) // 2] + xs[n // 2]) if n else None
 
 
-def _hbm_roof(name, algo_bytes, ms):
+def _hbm_roof(name, algo_bytes, ms, counters=True):
     """HBM roofline object of a decode call: algorithmic bytes (when they split per call)
-    over the call time, and the counter traffic of its kernels when committed."""
+    over the call time, and the counter traffic of its kernels when committed for this
+    workload (decode_32k_b8; ``counters`` False for any other)."""
     o = {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s", "time_us": ms * 1e3,
-         "traffic": _traffic(name) if name in KERNELS else None}
+         "traffic": _traffic(name) if (counters and name in KERNELS) else None}
     if algo_bytes is not None:
         o["achieved"] = algo_bytes / (ms * 1e-3) / 1e9
         o["frac"] = o["achieved"] / HBM_PEAK_GBS
@@ -853,14 +857,14 @@ def main():
                                                   "[4096, 262144] (sum %d), 32 q / 4 kv heads, bf16, per-sequence "
                                                   "top-p in [0.8, 0.99], local window 1024 + 4 sinks, half the "
                                                   "sequences peaky (256 needles)" % sum(rd["inp"].seqlens_k)},
-                                     **decode_summary(rd))
+                                     **decode_summary(rd, counters=False))
         del rd
     if args.only in ("prefill", "both") and not args.no_long:
         say("prefill 1M ...")
         c4 = bench_prefill(args, torch, rtp, synth, cfg=synth.PREFILL_1M, steps=2, warmup=1)
         line["prefill_1m"] = dict({"workload": "prefill_1m: L=1048576 causal, 32 q / 4 kv heads, bf16, "
                                                "4 retrieval heads (top-p 0.9), 28 local heads (window 4096 + 4 sinks)"},
-                                  **prefill_summary(c4))
+                                  **prefill_summary(c4, counters=False))
         line["prefill_1m"]["roofline"] = line["prefill_1m"]["per_kernel_roofline"][line["prefill_1m"]["dominant_kernel"]]
         if not args.no_references:
             # the shape of the pages' Fig. 1 (prefill speedup over dense attention against context
