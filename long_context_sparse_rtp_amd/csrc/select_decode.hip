@@ -132,11 +132,11 @@ __device__ __forceinline__ RowGeom row_geom(const ProbDev& p, int row) {
   return g;
 }
 
-// Work order of the score, collect and emit kernels: workgroups are dealt to the 8
-// XCDs round-robin by block id and each XCD has its own L2, so all units of a row go
-// to one XCD (block b: k = b / 8, row = 8 (k / U) + b % 8, unit k % U, U unit slots
-// per row), where the collect and emit steps find the row's histograms, scores and
-// candidates in L2.
+// Work order of the score kernel: workgroups are dealt to the 8 XCDs round-robin by
+// block id and each XCD has its own L2, so all units of a row go to one XCD (block b:
+// k = b / 8, row = 8 (k / U) + b % 8, unit k % U, U unit slots per row).  The finish
+// workgroup of a row is block `row`, on XCD row % 8, the same one, so it finds the
+// row's histograms and scores in that L2.
 __host__ __device__ inline int unit_slots(const ProbDev& p) { return max(1, max_units(p)); }
 __host__ __device__ inline unsigned unit_blocks(const ProbDev& p) {
   return 8u * (unsigned)((p.R * p.batch + 7) / 8) * (unsigned)unit_slots(p);
