@@ -79,7 +79,13 @@ constexpr int kParts = kThreads / kRows;        // threads per row in the scans
 // Sweeps in the order a row can need them; a workgroup runs the lowest phase any
 // of its rows is in.
 enum { PH_P0 = 0, PH_HIST1 = 1, PH_HISTW = 2, PH_REFINE = 3, PH_COLLECT = 4, PH_DONE = 5 };
-constexpr int kFineShift = 12;                  // window bins: 1/256 octave = 2^12 units of K
+constexpr int kFineShift = 12;                  // window bins of short rows: 1/256 octave = 2^12 units of K
+// Window bins of a row: 2^fine_shift(pos) units of K.  The number of tokens in the
+// crossing bin grows with the row's length, so longer rows take finer bins (down to
+// 1/4096 octave above 512K keys) and their crossing bin still fits the candidate buffer.
+__device__ __forceinline__ int fine_shift(int pos) {
+  return pos < 65536 ? 12 : pos < 131072 ? 11 : pos < 262144 ? 10 : pos < 524288 ? 9 : 8;
+}
 constexpr int kSample = 8;                      // the first sweep reads every 8th full tile
 // Narrow mass scale: a token at the reference weighs 2^31.98 units, so that every
 // mass converts to a 32-bit integer (the argument's rounding stays far below 0.02)
@@ -107,7 +113,8 @@ struct RowCtl {
   int phase, kind;
   int pos;
   int wide;                   // the row's mass is the wide (64-bit) one
-  int g0;                     // first fine bin (1/256 octave) of the window of the windowed sweep
+  int g0;                     // first fine bin of the window of the windowed sweep
+  int fsh;                    // its fine bins are 2^fsh units of K
   uint32_t cabove;            // tokens strictly better than the range (counted by the collect sweep)
   float tau;
   int tie, count;
@@ -274,6 +281,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     c.tau = -INFINITY; c.tie = 0x7FFFFFFF; c.count = c.pos + 1;
     c.target = 1.0;
     c.g0 = 1;
+    c.fsh = kFineShift;
     if (COUNT) {
       c.pval = 0.f;
       c.kval = max(top_k[b], 1);
@@ -416,8 +424,8 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       rk.hi_f = (hi >= 4294967040.0) ? INFINITY : (float)hi;
       rk.dA = dot_bound(rk.a20, rk.b20, rk.lo_f);
       rk.dB = dot_bound(rk.a20, rk.b20, rk.hi_f);
-      rk.a12 = rk.a20 * (1.f / 4096.f);
-      rk.b12 = rk.b20 * (1.f / 4096.f);
+      rk.a12 = ldexpf(rk.a20, -c.fsh);   // power-of-two scalings: exact
+      rk.b12 = ldexpf(rk.b20, -c.fsh);
       rk.c12 = (float)(c.g0 - 1);
     }
     {
@@ -636,8 +644,14 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
               if ((double)(cm + hv) >= target) { bstar = spart * PB + j; break; }
               cm += hv;
             }
-            // window of 254 fine bins (just under an octave) centred on the estimated bin
-            rc.g0 = max(1, bstar * 16 + 8 - 127);
+            // window of 254 fine bins centred on the estimate: the target's place inside
+            // the coarse bin by linear interpolation of the bin's sampled mass
+            const int fsh = fine_shift(rc.pos);
+            const unsigned long long hb = h1[bstar][srow];
+            const double fr = (hb != 0ull) ? fmin(fmax((target - (double)cm) / (double)hb, 0.0), 1.0) : 0.5;
+            const long long centre = ((long long)bstar << 16) + (long long)(fr * 65536.0);
+            rc.fsh = fsh;
+            rc.g0 = max(1, (int)(centre >> fsh) - 127);
             rc.phase = PH_HISTW;
             // a sample whose mean mass is below 2^18 units predicts a row that would fail
             // the certification after the windowed sweep: it takes the wide mass there
@@ -687,17 +701,17 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           rc.above = cm;
           const int g0 = rc.g0;
           if (jstar >= 1 && jstar <= 254) {        // inside the window: gather the bin's keys
-            rc.lo = (uint32_t)(g0 + jstar - 1) << kFineShift;
-            rc.sh = kFineShift;
+            rc.lo = (uint32_t)(g0 + jstar - 1) << rc.fsh;
+            rc.sh = rc.fsh;
             rc.phase = PH_COLLECT;
           } else if (jstar == 0) {                 // above the window: refine [0, g0 << 12)
-            const uint32_t span = ((uint32_t)g0 << kFineShift) - 1u;
+            const uint32_t span = ((uint32_t)g0 << rc.fsh) - 1u;
             const int wdt = 32 - __clz(span);
             rc.lo = 0u;
             rc.sh = max(wdt, 8) - 8;
             rc.phase = PH_REFINE;
           } else {                                 // below the window: refine the rest
-            rc.lo = (uint32_t)(g0 + 254) << kFineShift;
+            rc.lo = (uint32_t)(g0 + 254) << rc.fsh;
             rc.sh = 24;
             rc.phase = PH_REFINE;
           }
