@@ -33,8 +33,9 @@
 // sweep a row is certified when (pos + 1) <= 2^-17 Z, which keeps a crossing
 // within 7.6e-6 + 1.6e-6 of p in cumulative mass (the set tolerance is 1e-5).
 // The wide mass is 2^(ms - (top - s) log2 e) with ms = 42 as an exact 64-bit
-// integer.  A row whose sampled mean mass (first sweep) is below 2^18 units
-// takes it in the windowed sweep, together with every other row of that sweep;
+// integer.  A row whose sampled mean mass (first sweep) is below 2^18 units, or
+// whose best sampled key sits 8 octaves or more below the reference, takes it in
+// the windowed sweep, together with every other row of that sweep;
 // a narrow row that fails the certification repeats the windowed sweep wide; a
 // wide row that fails (its mass in a few tokens far above a long tail, with a
 // loose reference) takes the full coarse sweep, which lowers its reference to
@@ -44,15 +45,18 @@
 // histograms the mass over kNB1 bins of floor(u) (the last one open-ended);
 // 16 threads per row scan it for the bin where the cumulative mass reaches p
 // times the sampled total (top-k: k times the sampled share of the keys), an
-// estimate of the crossing.  The windowed sweep
-// then histograms every key's mass over 254 bins of 1/256 octave centred on
-// that estimate, plus one bin above and one below the window; the scan finds
-// the crossing bin exactly.  A collect sweep counts the tokens above the bin
+// estimate of the crossing, placed inside its bin by linear interpolation of the
+// bin's sampled mass.  The windowed sweep then histograms every key's mass over
+// 254 fine bins centred on that estimate (1/256 octave for rows under 64K keys,
+// halving per doubling of the row down to 1/4096 octave, so that long rows'
+// crossing bins stay collectable), plus one bin above and one below the window;
+// the scan finds the crossing bin exactly.  A collect sweep counts the tokens above the bin
 // and gathers the bin's tokens; if they are at most kCap, they are sorted by
 // (score desc, position asc) (ranks: every candidate against all, 16 threads
 // per row) and the crossing token gives tau and tie_pos.  A crossing outside
-// the window, a loose reference (the best sampled key far below it) or a bin
-// with more than kCap tokens fall back to refinement sweeps that histogram
+// the window, a sample with no key within 15 octaves of the reference (the full
+// coarse sweep first) or a bin with more than kCap tokens fall back to refinement
+// sweeps that histogram
 // the mass over the next 8 bits of K inside the chosen range; exact ties too
 // large to collect switch the key to the score's bit pattern and then to the
 // position (degenerate inputs only).  The refine and collect sweeps compare
@@ -606,8 +610,9 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     const bool act = ctl[srow].phase == sweep;
     if (sweep == PH_P0) {
       // estimate the crossing from the sample; the windowed sweep then bins finely
-      // around it.  A loose reference (best sampled key >= 8 octaves below it) or a
-      // crossing the scan does not find takes the full coarse sweep instead.
+      // around it.  A loose reference (best sampled key 8 to 15 octaves below it)
+      // takes the wide mass there; a sample with nothing above the last 16 bins, or
+      // a crossing the scan does not find, takes the full coarse sweep instead.
       constexpr int PB = kNB1 / kParts;
       unsigned long long sp = 0ull;
       int first = kNB1;
@@ -632,7 +637,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
           Z += psum_s[srow][q];
           blo = min(blo, pidx_s[srow][q]);
         }
-        if (blo < kNB1 / 2 && Z != 0ull) {
+        if (blo < kNB1 - 16 && Z != 0ull) {
           // the sample holds a share Z / (pos + 1) of the keys: scale a count target by it
           const double target = COUNT ? fmax((double)rc.kval * (double)Z / (double)(rc.pos + 1), 1.0)
                                       : fmax((double)rc.pval * (double)Z, 1.0);
@@ -657,7 +662,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
             // the certification after the windowed sweep: it takes the wide mass there
             // directly.  The sample holds every 8th full tile and the diagonal tiles.
             const double nsamp = 16.0 * (double)((nfull + kSample - 1) / kSample) + (double)(rc.pos + 1 - 16 * nfull);
-            if (!COUNT && (double)Z < nsamp * 262144.0) rc.wide = 1;
+            if (!COUNT && ((double)Z < nsamp * 262144.0 || blo >= kNB1 / 2)) rc.wide = 1;
           }
         }
       }
