@@ -22,7 +22,9 @@ def _sampled_prefill(cfg, n_rows):
     inp = make_inputs(cfg, DEV)
     _say(f"[case] prefill {cfg.name}: running the HIP path")
     g = P.run_prefill(inp)
-    rows = sample_rows(cfg, n_rows, forced_edge_rows(cfg))
+    # plus the rows where the selection's window bins change width (64K, 128K, 256K, 512K keys)
+    widths = [r for b in (65536, 131072, 262144, 524288) for r in (b - 2, b - 1, b) if r < cfg.seqlen]
+    rows = sample_rows(cfg, n_rows, forced_edge_rows(cfg) + widths)
     import torch
     ridx = torch.tensor(rows, device=DEV)
     # bring back only what the oracle compares
