@@ -68,7 +68,8 @@ CALL_KERNELS = {
 CALL_PASS = {"select_topp": "pre", "sparse_attn_prefill": "pre", "local_attn": "pre", "index_keys": "pre",
              "select_decode": "dec", "sparse_attn_decode": "dec", "local_attn_decode": "dec"}
 # the rocprofv3 passes behind the summaries under profiles/ (run from the repo root after
-# cd /tmp && export TMPDIR=/tmp; one counter set per pass)
+# cd /tmp && export TMPDIR=/tmp; one counter set per pass), written under PROF_OUT
+PROF_OUT = "prof_out"
 _PRE_ARGS = "--only prefill --steps 1 --warmup 0 --no-cpu-baseline --no-references --no-variants --no-long"
 _DEC_ARGS = ("--only decode --steps 1 --warmup 0 --decode-steps 2 --no-cpu-baseline --no-references --no-variants "
              "--no-ragged --no-cold")
@@ -102,12 +103,13 @@ TRACE_ARGS = ("--steps 3 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-ref
 
 def pmc_command(name):
     counters, bargs = PMC_PASSES[name]
-    return (f"rocprofv3 --pmc {counters} -d gpurun_out/{name} -o p --output-format csv -- "
+    return (f"rocprofv3 --pmc {counters} -d {PROF_OUT}/{name} -o p --output-format csv -- "
             f"python3 bench.py {bargs}")
 
 
 def trace_command():
-    return f"rocprofv3 --kernel-trace --stats -d gpurun_out/ktrace -o kt --output-format csv -- python3 bench.py {TRACE_ARGS}"
+    return (f"rocprofv3 --kernel-trace --stats -d {PROF_OUT}/ktrace -o kt --output-format csv -- "
+            f"python3 bench.py {TRACE_ARGS}")
 
 
 def _args():
@@ -129,11 +131,11 @@ def _args():
     ap.add_argument("--pmc-commands", action="store_true",
                     help="print the rocprofv3 counter passes behind the summaries under profiles/, one per line")
     ap.add_argument("--traffic-summary", metavar="CALL",
-                    help="print the HBM traffic summary of a timed call from the counter passes under gpurun_out/")
+                    help="print the HBM traffic summary of a timed call from the counter passes under prof_out/")
     ap.add_argument("--mfma-summary", metavar="CALL",
                     help="print the matrix-core summary of a prefill call from the pre_mfma counter pass")
     ap.add_argument("--trace-summary", action="store_true",
-                    help="print the kernel table of the rocprofv3 kernel trace under gpurun_out/ktrace")
+                    help="print the kernel table of the rocprofv3 kernel trace under prof_out/ktrace")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only copy a 1 GiB buffer 4 times (a known-size kernel for HBM counter calibration)")
     return ap.parse_args()
@@ -629,7 +631,7 @@ def traffic_summary(call):
     """HBM bytes per launch of one timed call: FETCH_SIZE and WRITE_SIZE (KiB per dispatch,
     summed over the call's kernels), each scaled by what the same counter reads per
     dispatch for a device copy of 1 GiB."""
-    base = os.path.join(ROOT, "gpurun_out")
+    base = os.path.join(ROOT, PROF_OUT)
     ps = CALL_PASS[call]
     cal_f = _pmc_means(os.path.join(base, "cal_fetch"), ["copyBuffer"])["FETCH_SIZE"][0]
     cal_w = _pmc_means(os.path.join(base, "cal_write"), ["copyBuffer"])["WRITE_SIZE"][0]
@@ -660,7 +662,7 @@ def traffic_summary(call):
 def mfma_summary(call):
     """Matrix-core and instruction counters of a prefill call from the pre_mfma pass.
     GRBM_GUI_ACTIVE is summed over the 8 XCDs; busy fractions are per SIMD (1024)."""
-    m = _pmc_means(os.path.join(ROOT, "gpurun_out", "pre_mfma"), CALL_KERNELS[call])
+    m = _pmc_means(os.path.join(ROOT, PROF_OUT, "pre_mfma"), CALL_KERNELS[call])
     g = m["GRBM_GUI_ACTIVE"][0]
     cyc = g / 8.0
     simd_cycles = cyc * 1024.0
@@ -694,7 +696,7 @@ def trace_summary():
     import csv
     import glob
     rows = []
-    for f in glob.glob(os.path.join(ROOT, "gpurun_out", "ktrace", "**", "*kernel_trace.csv"), recursive=True):
+    for f in glob.glob(os.path.join(ROOT, PROF_OUT, "ktrace", "**", "*kernel_trace.csv"), recursive=True):
         rows.extend(csv.DictReader(open(f)))
     agg = {}
     order = []
