@@ -91,6 +91,7 @@ __device__ __forceinline__ int fine_shift(int pos) {
   return pos < 65536 ? 12 : pos < 131072 ? 11 : pos < 262144 ? 10 : pos < 524288 ? 9 : 8;
 }
 constexpr int kSample = 8;                      // the first sweep reads every 8th full tile
+constexpr int kDepth = 4;                       // full tiles' index keys in flight per wave in a sweep
 // Narrow mass scale: a token at the reference weighs 2^31.98 units, so that every
 // mass converts to a 32-bit integer (the argument's rounding stays far below 0.02)
 constexpr float kNarrowScale = 31.98f;
@@ -317,11 +318,6 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     }
     return idx_dot_tile(kxf, qxf);
   };
-  // Two tiles per step over the full tiles (every key exists and lies below every
-  // row's position), their index keys loaded one step ahead with unconditional
-  // loads (a prefetch past the last pair re-reads the last full tile) into two
-  // register sets that alternate, so a step never waits on the loads it issues;
-  // then the diagonal tiles one at a time.
   // byte offsets from the row block's first index key: a scalar base plus one
   // 32-bit lane offset (the keys of one retrieval head span well under 4 GB)
   const char* kxc = reinterpret_cast<const char*>(kxb);
@@ -330,53 +326,42 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     const uint32_t tt = (uint32_t)__builtin_amdgcn_readfirstlane(min(t, nfull - 1));
     load_idx_frag(f, reinterpret_cast<const T*>(kxc + (tt * (16u * kIdxDim * (uint32_t)sizeof(T)) + lane_off)));
   };
-  auto sweep_tiles = [&](auto&& body) {
-    int t = w;
-    if (t + kWaves < nfull) {
-      IF a0, a1, b0, b1;
-      load_full(a0, t);
-      load_full(a1, t + kWaves);
-      while (true) {
-        load_full(b0, t + 2 * kWaves);
-        load_full(b1, t + 3 * kWaves);
-        {
-          const f32x4 d0 = idx_dot_tile(a0, qxf), d1 = idx_dot_tile(a1, qxf);
-          body(d0, t, false);
-          body(d1, t + kWaves, false);
+  // Full tiles t, t + stride, ... (every key exists and lies below every row's
+  // position) in groups of D with D tiles' index keys in flight: each register set
+  // is reloaded with the tile D strides ahead as soon as its product is issued
+  // (unconditional loads: past the last full tile they re-read it).  A sweep is
+  // bound by the latency of these loads, not by its arithmetic, unless several
+  // are in flight.  Returns the first tile of the wave not visited.
+  auto sweep_full = [&](auto depth, int t, int stride, auto&& body) -> int {
+    constexpr int D = decltype(depth)::value;
+    if (t + (D - 1) * stride < nfull) {
+      IF f[D];
+#pragma unroll
+      for (int j = 0; j < D; ++j) load_full(f[j], t + j * stride);
+      do {
+#pragma unroll
+        for (int j = 0; j < D; ++j) {
+          const f32x4 d = idx_dot_tile(f[j], qxf);
+          load_full(f[j], t + (D + j) * stride);
+          body(d, t + j * stride, false);
         }
-        t += 2 * kWaves;
-        if (!(t + kWaves < nfull)) break;
-        load_full(a0, t + 2 * kWaves);
-        load_full(a1, t + 3 * kWaves);
-        {
-          const f32x4 d0 = idx_dot_tile(b0, qxf), d1 = idx_dot_tile(b1, qxf);
-          body(d0, t, false);
-          body(d1, t + kWaves, false);
-        }
-        t += 2 * kWaves;
-        if (!(t + kWaves < nfull)) break;
-      }
+        t += D * stride;
+      } while (t + (D - 1) * stride < nfull);
     }
+    return t;
+  };
+  // every tile of the wave: the full tiles kDepth, then two, in flight, then the
+  // rest (the diagonal tiles, bounds-checked) one at a time
+  auto sweep_tiles = [&](auto&& body) {
+    int t = sweep_full(std::integral_constant<int, kDepth>{}, w, kWaves, body);
+    t = sweep_full(std::integral_constant<int, 2>{}, t, kWaves, body);
     for (; t < ntile; t += kWaves) body(tile_dot(t), t, t >= nfull);
   };
   // every kSample-th full tile (same prefetch scheme), then every diagonal tile
   auto sweep_sample = [&](auto&& body) {
     constexpr int kStride = kSample * kWaves;
-    int t = kSample * w;
-    if (t < nfull) {
-      IF a, bb;
-      load_full(a, t);
-      while (true) {
-        load_full(bb, t + kStride);
-        body(idx_dot_tile(a, qxf), t, false);
-        t += kStride;
-        if (t >= nfull) break;
-        load_full(a, t + kStride);
-        body(idx_dot_tile(bb, qxf), t, false);
-        t += kStride;
-        if (t >= nfull) break;
-      }
-    }
+    int t = sweep_full(std::integral_constant<int, kDepth>{}, kSample * w, kStride, body);
+    for (; t < nfull; t += kStride) body(tile_dot(t), t, false);
     for (int td = nfull + w; td < ntile; td += kWaves) body(tile_dot(td), td, true);
   };
 
