@@ -523,9 +523,11 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
         for (int i = 0; i < 4; ++i) {
           const int n = 16 * t + 4 * grp + i;
           const bool valid = !check || n <= rk.pos;
-          const bool above = d[i] > rk.dA;   // scores are finite: not above <=> d <= dA
-          better += (valid && above) ? 1u : 0u;
-          inr[i] = valid && !above && d[i] > rk.dB;
+          // counted: every token above the range's lower edge (the range's own tokens,
+          // which ccount counts, are taken off after the sweep); scores are finite
+          const bool gtb = valid && d[i] > rk.dB;
+          better += gtb ? 1u : 0u;
+          inr[i] = gtb && d[i] <= rk.dA;
           any |= inr[i];
         }
         if (__builtin_amdgcn_ballot_w64(any)) {
@@ -589,6 +591,10 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       if (grp == 0) atomicAdd(&cbetter_s[col], better);
     }
     __syncthreads();
+    if (sweep == PH_COLLECT && all_fast) {   // the fast collect counted the range's tokens too
+      if (tid < kRows) cbetter_s[tid] -= (uint32_t)ccount_s[tid];
+      __syncthreads();
+    }
 
     // ---- per-row controller.  The histogram scans run on 16 threads per row:
     // part sums, then the part holding the crossing walks its bins.
