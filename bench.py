@@ -744,7 +744,7 @@ def trace_summary():
 def main():
     args = _args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1 (no multi-GPU path)"}))
+        print(json.dumps({"error": "runs on one GPU only: --gpus must be 1 (the library has no multi-GPU path)"}))
         sys.exit(2)
     if args.pmc_summary:
         pmc_summary(args.pmc_summary[0], args.pmc_summary[1])
