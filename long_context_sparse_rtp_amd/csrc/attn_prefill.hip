@@ -16,8 +16,12 @@
 //     halves the re-reads of the causal K/V prefix against 128-row tiles
 //     (a 4-wave, 128-row variant needs more than 128 VGPRs per lane and
 //     spills at two workgroups per CU);
-//   - the next tile's K/V is loaded into registers while the current one is
-//     computed and written to the other half of a double-buffered LDS;
+//   - a later tile's K/V is loaded into registers while the current one is
+//     computed, then written to a free LDS slot: bfloat16 keeps four slots,
+//     stages two tiles ahead and synchronises the workgroup every second tile
+//     (between barriers a wave that finished its tile goes on with the next,
+//     beside the slower wave of its SIMD); float32 and the tile-skipping
+//     instance keep two slots and a barrier per tile;
 //   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (f32 path: 16x16x4 steps), K
 //     tile staged row-major in LDS; the S^T output layout (a lane holds 4 keys
 //     of one query column) is already the B-operand layout of O^T = V^T P^T,
@@ -258,15 +262,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
   typedef typename IdxFrag<T>::type IF;
   constexpr bool kRet = MODE != 1;   // retrieval heads
   constexpr int KS = Lds<T>::kStr, VS = Lds<T>::vStr;
-  __shared__ __attribute__((aligned(16))) T k_s[2][KT * KS];
-  __shared__ __attribute__((aligned(16))) T vt_s[2][kHeadDim * VS];
+  // LDS tile slots: bfloat16 outside MODE 2 keeps four and synchronises the
+  // workgroup every second tile (tiles are staged two ahead); otherwise two, every tile
+  constexpr int NBUF = (sizeof(T) == 2 && MODE != 2) ? 4 : 2;
+  constexpr int kSync = NBUF / 2;   // tiles per barrier = staging distance
+  __shared__ __attribute__((aligned(16))) T k_s[NBUF][KT * KS];
+  __shared__ __attribute__((aligned(16))) T vt_s[NBUF][kHeadDim * VS];
   // retrieval heads: the tile's 16-dim index keys, staged with K/V (one tile ahead)
   constexpr int KXW = kRet ? KT * kIdxDim * (int)sizeof(T) / 4 / kThreads : 0;   // words per thread
   // rows of 16-bit index keys padded to 10 words, so the 16 rows a fragment read
   // touches fall in distinct banks
   constexpr int KXWK = kIdxDim * (int)sizeof(T) / 4;                     // words per key
   constexpr int KXS = (sizeof(T) == 2) ? KXWK + 2 : KXWK;                 // row stride in words
-  __shared__ __attribute__((aligned(16))) uint32_t kx_s[2][kRet ? KT * KXS : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t kx_s[NBUF][kRet ? KT * KXS : 1];
   uint32_t kxr[KXW > 0 ? KXW : 1];
 
   const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b, per_head_xcd(kRet ? 0 : 1, nheads));
@@ -519,21 +527,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
   };
 
   Stage<T> st;
-  if (ntiles > 0) {   // (MODE 2 could in principle find no tile: then the rows keep l = 0)
-    const int fb = tile_of(0) * KT;
-    st.load(kg + (size_t)fb * rstride, vg + (size_t)fb * rstride, rstride, min(KT, Lk - fb), tid);
-    kx_load(fb);
+#pragma unroll
+  for (int j = 0; j < kSync; ++j) {
+    if (j < ntiles) {   // (MODE 2 could in principle find no tile: then the rows keep l = 0)
+      const int fb = tile_of(j) * KT;
+      st.load(kg + (size_t)fb * rstride, vg + (size_t)fb * rstride, rstride, min(KT, Lk - fb), tid);
+      kx_load(fb);
+    }
+    st.store(k_s[j], vt_s[j], tid);
+    kx_store(j);
   }
-  st.store(k_s[0], vt_s[0], tid);
-  kx_store(0);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const bool sink_only = sink_tile && (t == 0);
     const int kbase = tile_of(t) * KT;
-    const int buf = t & 1;
-    if (t + 1 < ntiles) {
-      const int nb = tile_of(t + 1) * KT;
+    const int buf = t % NBUF;
+    if (t + kSync < ntiles) {
+      const int nb = tile_of(t + kSync) * KT;
       st.load(kg + (size_t)nb * rstride, vg + (size_t)nb * rstride, rstride, min(KT, Lk - nb), tid);
       kx_load(nb);
     }
@@ -696,11 +707,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
       }
     }
     __builtin_amdgcn_s_setprio(2);
-    if (t + 1 < ntiles) {
-      st.store(k_s[buf ^ 1], vt_s[buf ^ 1], tid);
-      kx_store(buf ^ 1);
+    // the tile kSync ahead goes to the slot of tile t + kSync - NBUF, which every wave
+    // finished before the last barrier; it is visible after the next one
+    if (t + kSync < ntiles) {
+      const int nbuf = (t + kSync) % NBUF;
+      st.store(k_s[nbuf], vt_s[nbuf], tid);
+      kx_store(nbuf);
     }
-    __syncthreads();
+    if ((t + 1) % kSync == 0) __syncthreads();
   }
 
   // ---- normalise and store
