@@ -163,3 +163,21 @@ def test_clustered_selection_skips_tiles(kind):
     assert not fails, fails[:5]
     if kind == "topk_ties":
         assert ties > 0
+
+
+def test_clustered_topk_128k_sampled():
+    # the 128K prefill with every row's highest index scores in the first 32 64-key blocks
+    # and k = 2048: the k-th key sits in the thin lower tail of the planted scores, where
+    # the sampled first sweep places the windowed sweep with wider bins
+    cfg = PREFILL_128K
+    _say("[case] clustered top-k 2048 at 128K")
+    inp = make_inputs(cfg, DEV)
+    plant_blocks(inp, blocks=list(range(32)))
+    top_k = [2048]
+    g = P.to_host(P.run_prefill(inp, top_k=top_k))
+    pr = from_inputs(inp)
+    pr.top_k = top_k
+    rows = [(0, i) for i in sample_rows(cfg, 24, [2047, 2048, 2049, 4095, 4096, 65535, 131071])]
+    n, fails, stats = P.check_rows(pr, g, rows, list(cfg.ret_heads), P.TOL[cfg.dtype], workers=P.n_workers())
+    _say(f"[result] clustered top-k 128K: {n} pairs, {len(fails)} failures, {stats}")
+    assert not fails, fails[:5]
