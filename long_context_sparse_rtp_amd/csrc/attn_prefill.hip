@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
   constexpr int kSync = NBUF / 2;   // tiles per barrier = staging distance
   __shared__ __attribute__((aligned(16))) T k_s[NBUF][KT * KS];
   __shared__ __attribute__((aligned(16))) T vt_s[NBUF][kHeadDim * VS];
-  // retrieval heads: the tile's 16-dim index keys, staged with K/V (one tile ahead)
+  // retrieval heads: the tile's 16-dim index keys, staged with its K/V into the same slot
   constexpr int KXW = kRet ? KT * kIdxDim * (int)sizeof(T) / 4 / kThreads : 0;   // words per thread
   // rows of 16-bit index keys padded to 10 words, so the 16 rows a fragment read
   // touches fall in distinct banks
