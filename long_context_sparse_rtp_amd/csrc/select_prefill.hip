@@ -120,6 +120,7 @@ struct RowCtl {
   int wide;                   // the row's mass is the wide (64-bit) one
   int g0;                     // first fine bin of the window of the windowed sweep
   int fsh;                    // its fine bins are 2^fsh units of K
+  int csh;                    // the first sweep's bins are 2^(16 + csh) units of K
   uint32_t cabove;            // tokens strictly better than the range (counted by the collect sweep)
   float tau;
   int tie, count;
@@ -135,6 +136,7 @@ struct RowK {
   float dA, dB;     // the same tests on the raw dot: K >= lo <=> d <= dA, K < hi <=> d > dB
   float a12, b12;   // fine bin coordinate (1/256 octave) = fma(dot, a12, b12) = K / 2^12 exactly
   float c12;        // g0 - 1: window bin = clamp(floor(coordinate), c12, c12 + 255) - c12
+  int csh;          // the row's first-sweep bin width (RowCtl::csh)
   uint32_t lo;
   int sh, kind, pos;
   uint32_t kfix, dfix;
@@ -287,6 +289,15 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     c.target = 1.0;
     c.g0 = 1;
     c.fsh = kFineShift;
+    // A count target needs the keys far below the maximum too (a mass target does not:
+    // they weigh nothing), so the first sweep's 256 bins must span the row's score range,
+    // at most 2 top log2(e) octaves: bins of 1/16 octave cover 16, and a wide range takes
+    // bins 2^csh times as wide (up to half the range may fall in the last, open bin).
+    c.csh = 0;
+    if (COUNT) {
+      const float range = 2.f * c.top * kLog2e;
+      while (c.csh < 8 && range > 32.f * (float)(1 << c.csh)) ++c.csh;
+    }
     if (COUNT) {
       c.pval = 0.f;
       c.kval = max(top_k[b], 1);
@@ -416,6 +427,7 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
       rk.a12 = ldexpf(rk.a20, -c.fsh);   // power-of-two scalings: exact
       rk.b12 = ldexpf(rk.b20, -c.fsh);
       rk.c12 = (float)(c.g0 - 1);
+      rk.csh = c.csh;
     }
     {
       uint32_t* z = reinterpret_cast<uint32_t*>(un_s);
@@ -427,7 +439,10 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
     __syncthreads();
 
     const bool all_fast = __builtin_amdgcn_ballot_w64(!rk.fast) == 0;
-    const float a1 = rk.a20 * (1.f / 65536.f), b1 = rk.b20 * (1.f / 65536.f);
+    // coarse bin coordinate K / 2^16 (exact power-of-two scaling); the first sweep's bins
+    // are 2^csh times wider for rows whose count target needs a wide score range
+    const int cs = 16 + ((sweep == PH_P0) ? rk.csh : 0);
+    const float a1 = ldexpf(rk.a20, -cs), b1 = ldexpf(rk.b20, -cs);
     uint32_t better = 0u;
 
     // coarse histogram: bins of 1/16 octave below the reference, the last open-ended
@@ -641,13 +656,34 @@ __global__ __launch_bounds__(kThreads, 4) void select_prefill_kernel(
               cm += hv;
             }
             // window of 254 fine bins centred on the estimate: the target's place inside
-            // the coarse bin by linear interpolation of the bin's sampled mass
-            const int fsh = fine_shift(rc.pos);
+            // the coarse bin by linear interpolation of the bin's sampled mass.  The fine
+            // bins keep their share of a coarse bin when the coarse bins are wider.
+            const int cw = 16 + rc.csh;                               // coarse bin: 2^cw units of K
+            int fsh = fine_shift(rc.pos) + rc.csh;
             const unsigned long long hb = h1[bstar][srow];
             const double fr = (hb != 0ull) ? fmin(fmax((target - (double)cm) / (double)hb, 0.0), 1.0) : 0.5;
-            const long long centre = ((long long)bstar << 16) + (long long)(fr * 65536.0);
+            long long centre = ((long long)bstar << cw) + (long long)(fr * (double)(1ll << cw));
+            if (COUNT) {
+              // A count target's sampled rank is off by about sqrt(target) keys; where the
+              // sample is sparse (a thin tail of high scores) that spans many coarse bins.
+              // The window then takes wider bins so that it covers the coarse bins where
+              // the sampled count is within three deviations of the target.
+              const double dev = 3.0 * sqrt(target) + 1.0;
+              int b1 = bstar;
+              unsigned long long c1 = cm;                                   // count above b1
+              while (b1 > 0 && (double)c1 >= target - dev) { --b1; c1 -= h1[b1][srow]; }
+              int b2 = bstar;
+              unsigned long long c2 = cm + hb;                              // count down to b2
+              while (b2 < kNB1 - 2 && (double)c2 < target + dev) { ++b2; c2 += h1[b2][srow]; }
+              const long long span = (long long)(b2 - b1 + 1) << cw;
+              if ((254ll << fsh) < span) {
+                while (fsh < 24 && (254ll << fsh) < span) ++fsh;
+                centre = ((long long)b1 << cw) + span / 2;
+              }
+            }
             rc.fsh = fsh;
-            rc.g0 = max(1, (int)(centre >> fsh) - 127);
+            // (the window's last bin must end inside the 32-bit key: (g0 + 254) << fsh < 2^32)
+            rc.g0 = max(1, min((int)(centre >> fsh) - 127, (int)(0xFFFFFFFFu >> fsh) - 254));
             rc.phase = PH_HISTW;
             // a sample whose mean mass is below 2^18 units predicts a row that would fail
             // the certification after the windowed sweep: it takes the wide mass there
