@@ -46,12 +46,16 @@
 // 16 threads per row scan it for the bin where the cumulative mass reaches p
 // times the sampled total (top-k: k times the sampled share of the keys), an
 // estimate of the crossing, placed inside its bin by linear interpolation of the
-// bin's sampled mass.  The windowed sweep then histograms every key's mass over
-// 254 fine bins centred on that estimate (1/256 octave for rows under 64K keys,
-// halving per doubling of the row down to 1/4096 octave, so that long rows'
-// crossing bins stay collectable), plus one bin above and one below the window;
-// the scan finds the crossing bin exactly.  A collect sweep counts the tokens above the bin
-// and gathers the bin's tokens; if they are at most kCap, they are sorted by
+// bin's sampled mass (a top-k target, which needs keys far below the maximum
+// too, takes bins wide enough to span the row's score range).  The windowed
+// sweep then histograms every key's mass over 254 fine bins centred on that
+// estimate (1/256 octave for rows under 64K keys, halving per doubling of the
+// row down to 1/4096 octave, so that long rows' crossing bins stay collectable;
+// a top-k target's fine bins scale with its sample's bins and widen until the
+// window covers three deviations of the sampled rank), plus one bin above and
+// one below the window; the scan finds the crossing bin exactly.  A collect sweep
+// counts the tokens above the bin's lower edge (taking off the bin's own, which it
+// counts as it gathers them) and gathers the bin's tokens; if they are at most kCap, they are sorted by
 // (score desc, position asc) (ranks: every candidate against all, 16 threads
 // per row) and the crossing token gives tau and tie_pos.  A crossing outside
 // the window, a sample with no key within 15 octaves of the reference (the full
