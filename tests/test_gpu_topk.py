@@ -181,3 +181,31 @@ def test_clustered_topk_128k_sampled():
     n, fails, stats = P.check_rows(pr, g, rows, list(cfg.ret_heads), P.TOL[cfg.dtype], workers=P.n_workers())
     _say(f"[result] clustered top-k 128K: {n} pairs, {len(fails)} failures, {stats}")
     assert not fails, fails[:5]
+
+
+@pytest.mark.parametrize("kind", ["topk", "topp"])
+def test_clustered_decode_wide_score_range(kind):
+    # planted keys (the first 32 64-key blocks of sequence 0) score tens of octaves of
+    # softmax mass above the rest and spread over tens more, so a count target's k-th
+    # key sits far below the row maximum: the units' 32-octave histograms clamp it into
+    # their last bin and the crossing is resolved from the stored scores
+    cfg = scaled(DECODE_32K, name=f"clustered_decode_{kind}", batch=2, seqlen=16384, needles="none", top_p=0.9)
+    _say(f"[case] {cfg.name}")
+    inp = make_inputs(cfg, DEV)
+    plant_blocks(inp, blocks=list(range(32)))
+    pr = from_inputs(inp)
+    top_k = [2048, 2048] if kind == "topk" else None
+    if top_k is not None:
+        pr.top_k = top_k
+    k_idx = P.oracle_index_keys(pr, inp.q.dtype, DEV)
+    pr.k_idx = k_idx.cpu()
+    g = P.to_host(P.run_decode(inp, k_idx, top_k=top_k))
+    n, fails, stats = P.check_rows(pr, g, [(b, 0) for b in range(cfg.batch)], list(range(cfg.n_q_heads)),
+                                   P.TOL[cfg.dtype], decode=True)
+    _say(f"[result] {cfg.name}: {n} pairs, {len(fails)} failures, {stats}, counts "
+         f"{[int(c) for c in np.asarray(g['count']).reshape(-1)]}")
+    assert not fails, fails[:5]
+    if top_k is not None:
+        for r in range(cfg.n_ret):
+            for b in range(cfg.batch):
+                assert int(g["count"][r, b]) == 2048
