@@ -275,7 +275,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
   constexpr int KXWK = kIdxDim * (int)sizeof(T) / 4;                     // words per key
   constexpr int KXS = (sizeof(T) == 2) ? KXWK + 2 : KXWK;                 // row stride in words
   __shared__ __attribute__((aligned(16))) uint32_t kx_s[NBUF][kRet ? KT * KXS : 1];
-  uint32_t kxr[KXW > 0 ? KXW : 1];
+  uint32_t kxr[KXW > 0 ? KXW : 1] = {};
 
   const Work wk = work_of(blockIdx.x, nheads, p.batch, tiles_per_b, per_head_xcd(kRet ? 0 : 1, nheads));
   if (!wk.ok) return;
@@ -526,7 +526,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
     }
   };
 
-  Stage<T> st;
+  Stage<T> st{};   // (zeroed: a slot past the last tile is stored but never read)
 #pragma unroll
   for (int j = 0; j < kSync; ++j) {
     if (j < ntiles) {   // (MODE 2 could in principle find no tile: then the rows keep l = 0)
