@@ -8,10 +8,14 @@
 // Design: one thread per (token, retrieval head).  The thread streams its
 // 256-byte (bf16) key row with 16-byte loads, accumulates the 16 outputs in
 // float64 (products of a bf16/f32 element and an f32 weight are exact in
-// float64) and rounds each result once to the storage type.  W^K_r (8 KB) sits
-// in LDS; all lanes read the same weight at the same time (broadcast).  The
-// kernel is bound by HBM reads of k_pre at bf16 and by float64 FMA rate at
-// f32; either way it is a small share of a prefill.
+// float64) and rounds each result once to the storage type.  W^K_r sits in LDS
+// already widened to float64 and transposed (dimension-major, the 16 outputs of
+// one dimension in 128 bytes): all lanes read the same two weights with one
+// 16-byte broadcast, and the inner loop holds float64 FMAs only.  Every output
+// is one FMA chain over the 128 dimensions in order, which the append path
+// repeats, so both give identical bits.  An LDS read returns its bytes to every
+// lane, broadcast or not, so the weights' LDS return rate and the float64 FMA
+// rate (2048 FMAs per token and head) bound the kernel.
 #include "common.h"
 #include "kernels.h"
 
@@ -25,10 +29,14 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void index_keys_kernel(ProbDev p, const T* __restrict__ k_pre,
                                                               const float* __restrict__ w_k,
                                                               T* __restrict__ k_idx) {
-  __shared__ float w_s[kIdxDim * kHeadDim];
+  // w_s[d][j] = W^K_r[j][d] as float64
+  __shared__ __attribute__((aligned(16))) double w_s[kHeadDim * kIdxDim];
   const int r = blockIdx.y;
   const float* w = w_k + (size_t)r * kIdxDim * kHeadDim;
-  for (int i = threadIdx.x; i < kIdxDim * kHeadDim; i += kThreads) w_s[i] = w[i];
+  for (int i = threadIdx.x; i < kIdxDim * kHeadDim; i += kThreads) {
+    const int j = i / kHeadDim, d = i % kHeadDim;
+    w_s[d * kIdxDim + j] = (double)w[i];
+  }
   __syncthreads();
 
   const int64_t n = (int64_t)blockIdx.x * kThreads + threadIdx.x;
@@ -48,8 +56,13 @@ __global__ __launch_bounds__(kThreads) void index_keys_kernel(ProbDev p, const T
 #pragma unroll
     for (int t = 0; t < kVec; ++t) {
       const double xv = (double)Elem<T>::to_f(e[t]);
+      const double2* wd = reinterpret_cast<const double2*>(w_s + (d0 + t) * kIdxDim);
 #pragma unroll
-      for (int j = 0; j < kIdxDim; ++j) acc[j] = fma(xv, (double)w_s[j * kHeadDim + d0 + t], acc[j]);
+      for (int j2 = 0; j2 < kIdxDim / 2; ++j2) {
+        const double2 wv = wd[j2];
+        acc[2 * j2] = fma(xv, wv.x, acc[2 * j2]);
+        acc[2 * j2 + 1] = fma(xv, wv.y, acc[2 * j2 + 1]);
+      }
     }
   }
 
