@@ -98,7 +98,7 @@ ALGO_NOTE = {
     "local_attn_decode": "K,V rows of the 1028-key window + sinks of 8 sequences x 4 groups, 16.8 MB",
 }
 TRACE_ARGS = ("--steps 3 --warmup 1 --decode-steps 20 --no-cpu-baseline --no-references --no-variants --no-long "
-              "--no-ragged --no-cold")
+              "--no-ragged --no-cold --no-graph")
 
 
 def pmc_command(name):
@@ -124,6 +124,8 @@ def _args():
     ap.add_argument("--no-long", action="store_true", help="skip the 1M prefill and the 32K..1M prefill curve")
     ap.add_argument("--no-ragged", action="store_true", help="skip the ragged batch-64 decode")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache decode steps")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the decode step replayed from a HIP graph")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("DIR", "KERNEL"),
                     help="summarise a rocprofv3 --pmc output directory for one kernel (no GPU work)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -359,11 +361,12 @@ def bench_prefill_references(args, torch, rtp, synth, cfg, inp, n=1, topp=False)
     return res
 
 
-def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks=False, cold=0):
+def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks=False, cold=0, graph=False):
     """The decode step of ``cfg`` (default the 32K x 8 workload); with ``top_k`` (int32 [batch])
     the selection is the fixed top-k, with ``blocks`` the pages' block-granular top-p.
     ``cold`` > 0 also times that many single steps, each after a 512 MiB write that
-    evicts the caches (L2 and the 256 MB Infinity Cache)."""
+    evicts the caches (L2 and the 256 MB Infinity Cache); ``graph`` also times the step
+    captured in a HIP graph and replayed."""
     cfg = cfg or synth.DECODE_32K
     dev = "cuda"
     if inp is None:
@@ -381,15 +384,16 @@ def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks
 
     side = torch.cuda.Stream()   # default priority, like the main stream
 
-    def step(t: Timer = None):
+    def step(t: Timer = None, main=None):
+        m = stream if main is None else main
         calls = [
             ("select_topp_blocks" if blocks else "select_topp" if top_k is None else "select_topk",
              (lambda: rtp.rtp_select_topp_blocks(prob, inp.q_pre, inp.w_q, k_idx, inp.top_p, sel, ws_sel,
-                                                 stream=stream)) if blocks else
-             _select_call(rtp, prob, inp, k_idx, rtp.RTP_SEL_LIST, sel, ws_sel, stream, top_k)),
+                                                 stream=m)) if blocks else
+             _select_call(rtp, prob, inp, k_idx, rtp.RTP_SEL_LIST, sel, ws_sel, m, top_k)),
             ("sparse_attn_decode", lambda: rtp.rtp_sparse_attn_decode(prob, inp.q, inp.k, inp.v, sel, out, lse,
-                                                                      ws_dec, stream=stream)),
-            ("local_attn", lambda: rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, ws_loc, stream=stream)),
+                                                                      ws_dec, stream=m)),
+            ("local_attn", lambda: rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, ws_loc, stream=m)),
         ]
         if t is not None:   # per-kernel breakdown: everything in order on one stream
             for name, fn in calls:
@@ -397,14 +401,14 @@ def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks
             return
         # the step: local heads on a second stream, overlapping selection + sparse attention
         fork = torch.cuda.Event()
-        fork.record(stream)
+        fork.record(m)
         side.wait_event(fork)
         rtp.rtp_local_attn(prob, inp.q, inp.k, inp.v, out, lse, ws_loc, stream=side)
         calls[0][1]()
         calls[1][1]()
         join = torch.cuda.Event()
         join.record(side)
-        stream.wait_event(join)
+        m.wait_event(join)
 
     steps = args.decode_steps
     ms = _timed_steps(torch, stream, step, steps, args.warmup)
@@ -434,6 +438,29 @@ def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks
         torch.cuda.synchronize()
         cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
         del scrub
+    # the same step captured once in a HIP graph and replayed (as a serving loop would):
+    # kernel nodes only (the library records no memset); back-to-back replays and single ones
+    graph_ms = graph_us = None
+    if graph and args.graph:
+        cap = torch.cuda.Stream()   # default priority; capture needs a stream other than the null one
+        cap.wait_stream(stream)
+        torch.cuda.synchronize()
+        cg = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(cg, stream=cap):
+            step(main=cap)
+        torch.cuda.synchronize()
+        graph_ms = _timed_steps(torch, stream, cg.replay, steps, args.warmup)
+        pairs = []
+        for _ in range(steps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            cg.replay()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        graph_us = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+        del cg
     t = Timer(torch, stream)
     for _ in range(steps):
         step(t)
@@ -466,7 +493,7 @@ def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks
     qo_bytes = B * cfg.n_q_heads * 128 * 2 * 2
     total = kv_bytes + idx_bytes + qo_bytes
     sum_sel = float(counts.sum().item())
-    return dict(ms=ms, per_kernel_ms=per, warm_us=warm_us, cold_us=cold_us,
+    return dict(ms=ms, per_kernel_ms=per, warm_us=warm_us, cold_us=cold_us, graph_ms=graph_ms, graph_us=graph_us,
                 bytes=dict(kv_union=kv_bytes, index_keys=idx_bytes, q_out=qo_bytes),
                 total_bytes=total, union_rows=union_rows,
                 mean_frac_selected=sum_sel / (cfg.n_ret * sum(lens)), inp=inp, cfg=cfg)
@@ -479,6 +506,10 @@ def decode_summary(dec, counters=True):
          "achieved_GBps": dec["total_bytes"] / (dec["ms"] * 1e-3) / 1e9,
          "step_frac_of_hbm_roofline": dec["total_bytes"] / (HBM_PEAK_GBS * 1e9) / (dec["ms"] * 1e-3),
          "mean_selected_fraction": dec["mean_frac_selected"]}
+    if dec.get("graph_ms"):
+        d["graph"] = {"note": "the same step captured once in a HIP graph and replayed (kernel nodes only)",
+                      "step_us": dec["graph_ms"] * 1e3, "single_step_median_us": _median(dec["graph_us"]),
+                      "step_frac_of_hbm_roofline": dec["total_bytes"] / (HBM_PEAK_GBS * 1e9) / (dec["graph_ms"] * 1e-3)}
     if dec["cold_us"]:
         c = dec["cold_us"]
         d["cold"] = {"note": "single steps, each after a 512 MiB write that evicts L2 and the Infinity Cache",
@@ -806,7 +837,7 @@ def main():
                         "dense (top-p 1) + local heads, as the pages run prefill"}
     if args.only in ("decode", "both"):
         say("decode 32K x 8 (warm, then cold) ...")
-        dec = bench_decode(args, torch, rtp, synth, cold=0 if args.no_cold else 20)
+        dec = bench_decode(args, torch, rtp, synth, cold=0 if args.no_cold else 20, graph=True)
         line["decode"] = dict({"workload": "decode_32k_b8: batch 8, KV 32768, 32 q / 4 kv heads, bf16, "
                                            "4 retrieval heads (top-p 0.95), local window 1024 + 4 sinks"},
                               **decode_summary(dec))
