@@ -5,6 +5,7 @@ from __future__ import annotations
 import itertools
 import math
 import os
+import time
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -362,14 +363,35 @@ def _worker_task(idx):
     return _check_task(args)
 
 
+class _Progress:
+    """A line every 30 s while the oracle works, so a long check is visibly alive."""
+
+    def __init__(self, n):
+        self.n, self.t0 = n, time.time()
+        self.last = self.t0
+
+    def tick(self, done):
+        now = time.time()
+        if now - self.last >= 30.0:
+            print(f"[progress] oracle: {done}/{self.n} (row, head) pairs in {now - self.t0:.0f} s", flush=True)
+            self.last = now
+
+
 def _map(fn, arglist, workers):
+    prog = _Progress(len(arglist))
+    out = []
     if workers <= 1 or len(arglist) < 8:
-        return [fn(a) for a in arglist]
+        for a in arglist:
+            out.append(fn(a))
+            prog.tick(len(out))
+        return out
     import multiprocessing as mp
     _SHARED["args"] = arglist
     ctx = mp.get_context("fork")
     with ctx.Pool(workers) as pool:
-        out = pool.map(_worker_task, range(len(arglist)), chunksize=max(1, len(arglist) // (4 * workers)))
+        for r in pool.imap(_worker_task, range(len(arglist)), chunksize=max(1, len(arglist) // (16 * workers))):
+            out.append(r)
+            prog.tick(len(out))
     _SHARED.clear()
     return out
 
