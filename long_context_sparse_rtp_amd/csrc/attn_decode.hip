@@ -564,8 +564,7 @@ __global__ __launch_bounds__(64) void group_decode(ProbDev p, int nsplit, int nr
         sc[t][i] = ok ? sc[t][i] * qscale : -INFINITY;
         mx = fmaxf(mx, sc[t][i]);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = col4_max(mx);
     const float mn = fmaxf(m_run, mx);
     const float mref = (mn == -INFINITY) ? 0.f : mn;   // a head with no key yet keeps l = 0
     const float rs = __builtin_amdgcn_exp2f(m_run - mref);
@@ -578,8 +577,7 @@ __global__ __launch_bounds__(64) void group_decode(ProbDev p, int nsplit, int nr
         ls += pe;
         if (col < kGH) p_s[16 * t + 4 * g + i][col] = pe;
       }
-    ls += __shfl_xor(ls, 16);
-    ls += __shfl_xor(ls, 32);
+    ls = col4_sum(ls);
     l_run = l_run * rs + ls;
     m_run = mn;
     if (g == 0 && col < kGH) scale_s[col] = rs;

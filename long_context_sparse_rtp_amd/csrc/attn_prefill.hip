@@ -660,8 +660,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_prefill_kernel(
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, sacc[c][ks][i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = col4_max(tmax);
         const float mnew = fmaxf(m_[c], tmax * sl2);
         live |= (mnew != -INFINITY);
         // The reference m_ moves (and O, l are rescaled) only when the row maximum

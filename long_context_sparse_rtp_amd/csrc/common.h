@@ -155,6 +155,29 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
+// Max / sum over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of a 16x16 MFMA
+// output tile), the same value in all four.  gfx950's row and half-wave swaps run on
+// the VALU (a shuffle through ds_bpermute takes the LDS pipe, an index computation and
+// a wait for every outstanding LDS read).  Each swap leaves x[l] in one result and
+// x[l ^ 16] (or x[l ^ 32]) in the other, so max and + see the same pairs as an xor
+// butterfly and give the same bits.  All 64 lanes must be active.
+__device__ __forceinline__ float col4_max(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col4_sum(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
