@@ -72,7 +72,7 @@ CALL_PASS = {"select_topp": "pre", "sparse_attn_prefill": "pre", "local_attn": "
 PROF_OUT = "prof_out"
 _PRE_ARGS = "--only prefill --steps 1 --warmup 0 --no-cpu-baseline --no-references --no-variants --no-long"
 _DEC_ARGS = ("--only decode --steps 1 --warmup 0 --decode-steps 2 --no-cpu-baseline --no-references --no-variants "
-             "--no-ragged --no-cold")
+             "--no-ragged --no-cold --no-graph")
 _MFMA_COUNTERS = ("SQ_WAVES SQ_BUSY_CYCLES SQ_WAVE_CYCLES SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA "
                   "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE")
 PMC_PASSES = {
