@@ -178,6 +178,83 @@ __device__ __forceinline__ float col4_sum(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// ------------------------------------------------------------ register-only wave scans
+// DPP moves of the GFX9 family, 32 bits at a time (64-bit values move as two halves):
+// row_shr:n (0x110 + n) moves a value n lanes up inside each 16-lane row, lanes with no
+// source reading 0; row_bcast:15 (0x142) adds lane 15's value into the next row, and
+// row_bcast:31 (0x143) lane 31's into rows 2 and 3 (rows outside the row mask read 0).
+// None of them touches LDS or needs lane-index arithmetic.
+template <int CTRL, int ROWS, bool BC, typename V>
+__device__ __forceinline__ V dppv(V x) {
+  if constexpr (sizeof(V) == 4) {
+    return __builtin_bit_cast(V, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, BC));
+  } else {
+    static_assert(sizeof(V) == 8, "32- or 64-bit values");
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROWS, 0xF, BC);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROWS, 0xF, BC);
+    return __builtin_bit_cast(V, ((unsigned long long)hi << 32) | lo);
+  }
+}
+// Inclusive sum over lanes 0..l of a wave (all 64 lanes active): a Hillis-Steele scan
+// inside each row, then the row totals carried up by the two broadcasts.
+template <typename V>
+__device__ __forceinline__ V wave_scan_add(V x) {
+  x += dppv<0x111, 0xF, true>(x);
+  x += dppv<0x112, 0xF, true>(x);
+  x += dppv<0x114, 0xF, true>(x);
+  x += dppv<0x118, 0xF, true>(x);
+  x += dppv<0x142, 0xA, false>(x);
+  x += dppv<0x143, 0xC, false>(x);
+  return x;
+}
+// The partner values of a row swap (lane l ^ 16) or half-wave swap (lane l ^ 32): op is
+// applied to the swap's two results, which hold x[l] and its partner in either order.
+template <bool HALF, typename V, typename Op>
+__device__ __forceinline__ V swap_op(V x, Op op) {
+  if constexpr (sizeof(V) == 4) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto a = HALF ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                        : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__builtin_bit_cast(V, (uint32_t)a[0]), __builtin_bit_cast(V, (uint32_t)a[1]));
+  } else {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+    const uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+    const auto a = HALF ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                        : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto b = HALF ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                        : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const V v0 = __builtin_bit_cast(V, ((unsigned long long)(uint32_t)b[0] << 32) | (uint32_t)a[0]);
+    const V v1 = __builtin_bit_cast(V, ((unsigned long long)(uint32_t)b[1] << 32) | (uint32_t)a[1]);
+    return op(v0, v1);
+  }
+}
+// op over all 64 lanes, the same value in every lane: quad swaps, half-row and row
+// mirrors, then the row and half-wave swaps.  Every lane combines the same pairs, so a
+// commutative op (max, or a float sum) gives identical bits in all lanes.
+// (Within a row this is the xor 1, 2, 4, 8 butterfly: after the two quad steps all lanes
+// of a quad hold the same value, so the mirrors pair the same values as xor 4 and xor 8.)
+template <typename V, typename Op>
+__device__ __forceinline__ V row16_allreduce(V x, Op op) {
+  x = op(x, dppv<0xB1, 0xF, false>(x));    // quad_perm [1,0,3,2]
+  x = op(x, dppv<0x4E, 0xF, false>(x));    // quad_perm [2,3,0,1]
+  x = op(x, dppv<0x141, 0xF, false>(x));   // row_half_mirror
+  return op(x, dppv<0x140, 0xF, false>(x));   // row_mirror
+}
+template <typename V, typename Op>
+__device__ __forceinline__ V wave_allreduce(V x, Op op) {
+  x = row16_allreduce(x, op);
+  x = swap_op<false>(x, op);
+  return swap_op<true>(x, op);
+}
+// op over the four lanes l, l ^ 16, l ^ 32, l ^ 48 (one column of a 16x16 MFMA tile)
+template <typename V, typename Op>
+__device__ __forceinline__ V col4_op(V x, Op op) {
+  return swap_op<true>(swap_op<false>(x, op), op);
+}
+struct OpAdd { template <typename V> __device__ __forceinline__ V operator()(V a, V b) const { return a + b; } };
+struct OpMax { template <typename V> __device__ __forceinline__ V operator()(V a, V b) const { return a > b ? a : b; } };
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));

@@ -152,12 +152,7 @@ __device__ __forceinline__ void unit_of(const ProbDev& p, int b, int& row, int& 
 template <typename V>
 __device__ V block_exscan(V x, V* tmp /* >= 4 */, V& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  V inc = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    V y = __shfl_up(inc, d);
-    if (lane >= d) inc += y;
-  }
+  V inc = wave_scan_add(x);   // inclusive, register-only (DPP)
   __syncthreads();
   if (lane == 63) tmp[wid] = inc;
   __syncthreads();
@@ -174,8 +169,7 @@ __device__ V block_exscan(V x, V* tmp /* >= 4 */, V& total) {
 template <typename V>
 __device__ V block_max(V x, V* tmp) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  x = wave_allreduce(x, OpMax());
   __syncthreads();
   if (lane == 0) tmp[wid] = x;
   __syncthreads();
@@ -187,8 +181,7 @@ __device__ V block_max(V x, V* tmp) {
 }
 __device__ double block_sum_f64(double x, double* tmp) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  x = wave_allreduce(x, OpAdd());
   __syncthreads();
   if (lane == 0) tmp[wid] = x;
   __syncthreads();
@@ -199,12 +192,7 @@ __device__ double block_sum_f64(double x, double* tmp) {
 // exclusive float64 scan over the threads (fixed order), plus the total
 __device__ double block_exscan_f64(double x, double* tmp, double& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  double inc = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(inc, d);
-    if (lane >= d) inc += y;
-  }
+  double inc = wave_scan_add(x);   // inclusive, register-only (DPP)
   __syncthreads();
   if (lane == 63) tmp[wid] = inc;
   __syncthreads();
@@ -219,12 +207,7 @@ __device__ double block_exscan_f64(double x, double* tmp, double& total) {
 template <int NW>
 __device__ double block_exscan_f64_n(double x, double* tmp, double& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  double inc = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const double y = __shfl_up(inc, d);
-    if (lane >= d) inc += y;
-  }
+  double inc = wave_scan_add(x);   // inclusive, register-only (DPP)
   __syncthreads();
   if (lane == 63) tmp[wid] = inc;
   __syncthreads();
@@ -301,8 +284,7 @@ __device__ __forceinline__ void project_query(const ProbDev& p, const RowGeom& g
   double acc = 0.0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc = fma((double)x[i], (double)wv[i], acc);
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) acc += __shfl_xor(acc, o);
+  acc = row16_allreduce(acc, OpAdd());   // the xor 1, 2, 4, 8 tree, register-only
   if (part == 0) {
     const T qv = Elem<T>::from_d(acc);
     q_s[dim] = qv;
@@ -455,12 +437,7 @@ __device__ __forceinline__ double bin_mass(unsigned long long e, double f, bool 
 template <typename V>
 __device__ V fblock_exscan(V x, V* tmp /* >= kFW */, V& total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  V inc = x;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const V y = __shfl_up(inc, d);
-    if (lane >= d) inc += y;
-  }
+  V inc = wave_scan_add(x);   // inclusive, register-only (DPP)
   __syncthreads();
   if (lane == 63) tmp[wid] = inc;
   __syncthreads();
@@ -475,8 +452,7 @@ __device__ V fblock_exscan(V x, V* tmp /* >= kFW */, V& total) {
 }
 __device__ int fblock_max(int x, int* tmp) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = max(x, __shfl_xor(x, o));
+  x = wave_allreduce(x, OpMax());
   __syncthreads();
   if (lane == 0) tmp[wid] = x;
   __syncthreads();
@@ -559,12 +535,10 @@ __global__ __launch_bounds__(kFT) void sel_dec_finish(ProbDev p, const float* __
     if (wid == 0) {
       const bool has = lane < g.U && mt.used >= 0;
       int a = has ? mt.A : (-2147483647 - 1);
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) a = max(a, __shfl_xor(a, o));
+      a = wave_allreduce(a, OpMax());
       const double f = has ? unit_scale(mt.A, a) : 0.0;
       double z = (lane < g.U) ? (double)mt.Z * f : 0.0;
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o);   // lane 0's order is the one used
+      z = wave_allreduce(z, OpAdd());   // the same bits in every lane
       if (lane < g.U) {
         A_s[lane] = mt.A;
         used_s[lane] = mt.used;
@@ -673,10 +647,8 @@ __global__ __launch_bounds__(kFT) void sel_dec_finish(ProbDev p, const float* __
       }
     }
     // lanes i, i + 16, i + 32, i + 48 of a wave hold four groups of bin i
-    fm += __shfl_xor(fm, 16);
-    fc += __shfl_xor(fc, 16);
-    fm += __shfl_xor(fm, 32);
-    fc += __shfl_xor(fc, 32);
+    fm = col4_op(fm, OpAdd());
+    fc = col4_op(fc, OpAdd());
     if (lane < 16) { fm_s[wid][i] = fm; fc_s[wid][i] = fc; }
     __syncthreads();
     if (tid < 16) {   // bin tid over the waves, in a fixed order
