@@ -147,8 +147,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int ro
       tot_entries += vv[t];
     }
     // target split size: the entries spread over the grid once, within [kMinSplit, kSplit]
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) tot_entries += __shfl_xor(tot_entries, o);
+    tot_entries = wave_allreduce(tot_entries, OpAdd());
     if (lane == 0) wsum_s[wid] = (int)min(tot_entries, (long long)0x7FFFFFFF);
     __syncthreads();
     if (tid == 0) {
@@ -169,12 +168,7 @@ __global__ __launch_bounds__(kThreads) void attn_decode_kernel(ProbDev p, int ro
 #pragma unroll
     for (int t = 0; t < PR; ++t) {
       if (t >= nchunks) break;
-      int inc = vv[t];
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(inc, d);
-        if (lane >= d) inc += y;
-      }
+      const int inc = wave_scan_add(vv[t]);   // inclusive, register-only (DPP)
       if (lane == 63) wsum_s[wid] = inc;
       __syncthreads();
       int off = carry, tot = 0;

@@ -255,15 +255,9 @@ __device__ __forceinline__ V col4_op(V x, Op op) {
 struct OpAdd { template <typename V> __device__ __forceinline__ V operator()(V a, V b) const { return a + b; } };
 struct OpMax { template <typename V> __device__ __forceinline__ V operator()(V a, V b) const { return a > b ? a : b; } };
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
+struct OpFmax { __device__ __forceinline__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+// max / sum over the 64 lanes of a wave, the same value in every lane (register-only)
+__device__ __forceinline__ float wave_max(float x) { return wave_allreduce(x, OpFmax()); }
+__device__ __forceinline__ float wave_sum(float x) { return wave_allreduce(x, OpAdd()); }
 
 }  // namespace rtp
