@@ -183,7 +183,9 @@ __device__ __forceinline__ float col4_sum(float x) {
 // row_shr:n (0x110 + n) moves a value n lanes up inside each 16-lane row, lanes with no
 // source reading 0; row_bcast:15 (0x142) adds lane 15's value into the next row, and
 // row_bcast:31 (0x143) lane 31's into rows 2 and 3 (rows outside the row mask read 0).
-// None of them touches LDS or needs lane-index arithmetic.
+// None of them touches LDS or needs lane-index arithmetic.  Every helper below reads
+// other lanes' registers, so it must be called with all 64 lanes of the wave active
+// (uniform control flow), as every caller in this library does.
 template <int CTRL, int ROWS, bool BC, typename V>
 __device__ __forceinline__ V dppv(V x) {
   if constexpr (sizeof(V) == 4) {
