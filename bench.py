@@ -181,6 +181,41 @@ def _traffic(name):
         return None
 
 
+def local_key_total(L, window, n_sink):
+    """Keys a local head attends over a causal prefill of L rows, summed over the rows.
+
+    Row i keeps its last `window` positions (i - window, i] clipped at 0, and the first
+    `n_sink` positions (the attention sinks) that lie before that window.
+    """
+    total = 0
+    for i in range(min(L, window)):             # the window reaches back to position 0
+        total += i + 1
+    for i in range(window, L):                  # full window, plus the sinks before it
+        total += window + min(i - window + 1, n_sink)
+    return total
+
+
+def decode_union_rows(torch, lens, cu, counts, idx, window, n_sink, groups):
+    """K/V rows one decode step must read: per (sequence, KV group), the union of the
+    group's retrieval LISTs, and of its window and sinks when the group holds local heads.
+
+    `groups` lists, per KV group, (has_local_heads, retrieval slots of the group);
+    `counts[r, b]` members of slot r in sequence b sit at idx[r, cu[b]:cu[b] + counts[r, b]].
+    """
+    rows = 0
+    for has_local, slots in groups:
+        for b, L in enumerate(lens):
+            mark = torch.zeros(L, dtype=torch.bool, device=idx.device)
+            if has_local:
+                mark[max(0, L - window):] = True
+                mark[:min(n_sink, L)] = True
+            for r in slots:
+                c = int(counts[r, b])
+                mark[idx[r, cu[b]:cu[b] + c].long()] = True
+            rows += int(mark.sum().item())
+    return rows
+
+
 def _select_call(rtp, prob, inp, k_idx, mode, sel, ws, stream, top_k):
     if top_k is None:
         return lambda: rtp.rtp_select_topp(prob, inp.q_pre, inp.w_q, k_idx, inp.top_p, mode, sel, ws, stream=stream)
@@ -259,10 +294,7 @@ def bench_prefill(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, steps
     sum_S = float(sel.count.to(torch.float64).sum().item())
     causal_pairs = L * (L + 1) / 2
     n_local = cfg.n_q_heads - cfg.n_ret
-    W, ns = cfg.window, cfg.n_sink
-    i = torch.arange(L, dtype=torch.float64)
-    local_keys = torch.minimum(i + 1, torch.full_like(i, W)) + torch.clamp(torch.minimum(i - W + 1, torch.full_like(i, ns)), min=0)
-    sum_local = float(local_keys.sum().item()) * n_local
+    sum_local = float(local_key_total(L, cfg.window, cfg.n_sink)) * n_local
     flops = {
         "sparse_attn_prefill": 4 * d * sum_S,
         "local_attn": 4 * d * sum_local,
@@ -471,23 +503,13 @@ def bench_decode(args, torch, rtp, synth, cfg=None, inp=None, top_k=None, blocks
     # union window union sinks (K + V), the index keys of its retrieval heads, q and out
     kv_row = 2 * 128 * 2            # K + V bytes per token per KV head
     lens = inp.seqlens_k
-    cu = inp.cu_k.tolist()
-    B, W, ns = cfg.batch, cfg.window, cfg.n_sink
+    B = cfg.batch
     counts = sel.count.to(torch.int64).cpu()
     groups_with_local = {cfg.kv_of(h) for h in cfg.local_heads}
-    union_rows = 0
-    for g in range(cfg.n_kv_heads):
-        slots = [r for r, h in enumerate(cfg.ret_heads) if cfg.kv_of(h) == g]
-        for b in range(B):
-            L = lens[b]
-            mark = torch.zeros(L, dtype=torch.bool, device=dev)
-            if g in groups_with_local:
-                mark[max(0, L - W):] = True
-                mark[:min(ns, L)] = True
-            for r in slots:
-                c = int(counts[r, b])
-                mark[sel.idx[r, cu[b]:cu[b] + c].long()] = True
-            union_rows += int(mark.sum().item())
+    groups = [(g in groups_with_local, [r for r, h in enumerate(cfg.ret_heads) if cfg.kv_of(h) == g])
+              for g in range(cfg.n_kv_heads)]
+    union_rows = decode_union_rows(torch, lens, inp.cu_k.tolist(), counts, sel.idx, cfg.window, cfg.n_sink,
+                                   groups)
     kv_bytes = union_rows * kv_row
     idx_bytes = cfg.n_ret * sum(lens) * 16 * 2
     qo_bytes = B * cfg.n_q_heads * 128 * 2 * 2
